@@ -1,0 +1,363 @@
+"""Benchmark of the CSF block-scale decoder on one MI355X.
+
+One step = one full decode (fixed-stream pass + exception pass) of the
+512-expert gate-like NVFP4 stack (512 x 800 x 128 E4M3 scale bytes, 3 %
+outliers) into its dense workspace.  Steps rotate over several device copies
+of the compressed stack and workspace (together larger than the 256 MB
+Infinity Cache), so every step reads and writes HBM.
+
+Prints ONE JSON line on stdout:
+  value       whole-run throughput, GB/s = (compressed bytes read + dense
+              bytes written) per step x steps / elapsed time
+  roofline    the fixed-stream kernel (the dominant one): its algorithmic
+              bytes per launch / its mean launch time from HIP events on its
+              stream, against the MI355X HBM3E peak (8 TB/s)
+  cpu_baseline the CPU oracle decoding the same stack on one host core
+
+  python bench.py [--steps K] [--warmup W] [--sets N] [--all] [--no-cpu]
+
+--all also measures the other workloads (down-like, MXFP4, routed paired,
+tiny) and a plain copy, one line each on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "CSF decode GB/s (compressed read + dense write) and µs per 512-expert stack"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t timing through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.hip = ctypes.CDLL(path or "libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.record = self.hip.hipEventRecord
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            evs.append(e.value)
+        return evs
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def stack_bytes(stack, active=None, es_bytes=0):
+    """Algorithmic bytes of one decode: (fixed-stream bytes, exception bytes,
+    dense bytes).  active: boolean mask of routed experts, or None for all."""
+    import numpy as np
+    E = stack.E
+    n_act = E if active is None else int(np.count_nonzero(active))
+    prefix = stack.prefix.cpu().numpy()
+    if active is None:
+        entries = stack.num_exceptions
+    else:
+        entries = int(np.diff(prefix)[np.asarray(active, dtype=bool)].sum())
+    fixed = n_act * (stack.R + stack.stride)          # bases + offsets read
+    exc = 4 * entries + 4 * (E + 1)                   # entries + prefix read
+    dense = n_act * stack.P                           # written
+    return fixed, exc, dense
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("moe_weight_decode_amd/csrc/csf_kernels.hip", "moe_weight_decode_amd/csrc/csf_launch.h",
+                "moe_weight_decode_amd/csrc/csf_api.cpp"):
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    rec = data.get(f"{kernel}/{workload}")
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_sets(mwd, torch, stack, nsets, dev):
+    sets = []
+    for i in range(nsets):
+        s = stack if i == 0 else stack.clone()
+        ws = torch.empty(stack.dense_bytes, dtype=torch.uint8, device=dev)
+        sets.append((s, ws))
+    return sets
+
+
+def timed_loop(mwd, torch, ev, launches, steps, warmup, per_pass=True):
+    """Run `steps` steps (after `warmup`), rotating over `launches`.  Returns
+    (wall ms per step, event ms per step, [fixed-pass ms], [exception-pass ms]).
+    With per_pass, an event pair brackets each pass on the launch stream."""
+    stream = launches[0].stream
+    for i in range(warmup):
+        launches[i % len(launches)]()
+    torch.cuda.synchronize()
+    evs = ev.create(2 * steps + 2 if per_pass else 2)
+    rec = ev.record
+    FIXED, EXC = mwd.PASS_FIXED, mwd.PASS_EXCEPTIONS
+    t0 = time.perf_counter()
+    rec(evs[-2], stream)
+    if per_pass:
+        for i in range(steps):
+            L = launches[i % len(launches)]
+            rec(evs[2 * i], stream)
+            L(FIXED)
+            rec(evs[2 * i + 1], stream)
+            L(EXC)
+    else:
+        for i in range(steps):
+            launches[i % len(launches)]()
+    rec(evs[-1], stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = ev.ms(evs[-2], evs[-1])
+    fixed, exc = [], []
+    if per_pass:
+        for i in range(steps):
+            fixed.append(ev.ms(evs[2 * i], evs[2 * i + 1]))
+            nxt = evs[2 * (i + 1)] if i + 1 < steps else evs[-1]
+            exc.append(ev.ms(evs[2 * i + 1], nxt))
+    ev.destroy(evs)
+    return wall_ms / steps, total_ms / steps, fixed, exc
+
+
+def check_equal(torch, ws, x, what):
+    import numpy as np
+    got = ws.cpu().numpy().reshape(x.shape)
+    if not np.array_equal(got, x):
+        raise SystemExit(f"{what}: GPU decode differs from the input in {(got != x).sum()} bytes")
+
+
+def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev):
+    x = spec.generate()
+    stack = mwd.prepare(x, spec.fmt).to(dev)
+    sets = make_sets(mwd, torch, stack, nsets, dev)
+    launches = [mwd.Launch(s, ws) for s, ws in sets]
+    launches[0]()
+    torch.cuda.synchronize()
+    check_equal(torch, sets[0][1], x, spec.name)
+    wall, evt, fixed, exc = timed_loop(mwd, torch, ev, launches, steps, warmup)
+    fb, eb, db = stack_bytes(stack)
+    step_ms = max(wall, evt)
+    return dict(x=x, stack=stack, fixed_bytes=fb, exc_bytes=eb, dense_bytes=db,
+                step_ms=step_ms, wall_ms=wall, event_ms=evt,
+                fixed_ms=statistics.mean(fixed), fixed_ms_median=statistics.median(fixed),
+                exc_ms=statistics.mean(exc), launches=launches, sets=sets)
+
+
+def cpu_baseline(spec, x, budget_s=10.0):
+    """The oracle (plain C, one thread) decoding the whole stack, repeated for
+    about `budget_s` seconds; GB/s on the same byte formula as the GPU."""
+    import oracle
+    orc = oracle.load()
+    st = orc.encode(spec.fmt, x)
+    ws = orc.decode(st)
+    if not (ws == x).all():
+        raise SystemExit("oracle round trip failed")
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t = time.perf_counter()
+        orc.decode(st, None, ws)
+        times.append(time.perf_counter() - t)
+    E = spec.E
+    comp = E * spec.R + E * st["stride"] + 4 * st["exceptions"].size + 4 * (E + 1)
+    sec = statistics.median(times)
+    return dict(value=round((comp + x.size) / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                us_per_stack=round(sec * 1e6, 1),
+                sample=f"whole {spec.name} stack ({spec.E}x{spec.R}x{spec.C}), decoded {len(times)} "
+                       f"times on one host core, median")
+
+
+def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev):
+    import numpy as np
+    gspec, dspec = workloads.ROUTED.stacks
+    xg, xd = gspec.generate(), dspec.generate()
+    g = mwd.prepare(xg, gspec.fmt).to(dev)
+    d = mwd.prepare(xd, dspec.fmt).to(dev)
+    es = workloads.ROUTED.expert_start()
+    es_t = torch.from_numpy(es).to(dev)
+    wg = torch.full((g.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+    wd = torch.full((d.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+    L = mwd.Launch(g, wg, d, wd, es_t)
+    L()
+    torch.cuda.synchronize()
+    active = np.diff(es) > 0
+    hg = wg.cpu().numpy().reshape(xg.shape)
+    hd = wd.cpu().numpy().reshape(xd.shape)
+    if not (np.array_equal(hg[active], xg[active]) and np.all(hg[~active] == 0xA5)
+            and np.array_equal(hd[active], xd[active]) and np.all(hd[~active] == 0xA5)):
+        raise SystemExit("routed paired decode is wrong")
+    wall, evt, fixed, exc = timed_loop(mwd, torch, ev, [L], steps, warmup)
+    b = [stack_bytes(s, active) for s in (g, d)]
+    total = sum(f + e + dn for f, e, dn in b) + 4 * len(es)
+    return dict(step_ms=max(wall, evt), bytes=total, fixed_ms=statistics.mean(fixed),
+                exc_ms=statistics.mean(exc), active=int(active.sum()))
+
+
+def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
+    srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    for i in range(10):
+        dsts[i % nsets].copy_(srcs[i % nsets])
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for i in range(steps):
+        dsts[i % nsets].copy_(srcs[i % nsets])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) * 1e3 / steps
+    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--sets", type=int, default=8, help="rotating device copies (HBM, not cache)")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads on stderr")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the CSF decode path is rank-local and has no "
+              "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_weight_decode_amd as mwd
+    import workloads
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    ev = HipEvents()
+    spec = workloads.GATE
+    log(f"[bench] {spec.name}: generating and encoding {spec.E}x{spec.R}x{spec.C}")
+    r = bench_stack(mwd, torch, ev, spec, args.steps, args.warmup, args.sets, dev)
+    stack = r["stack"]
+    step_bytes = r["fixed_bytes"] + r["exc_bytes"] + r["dense_bytes"]
+    gbps = step_bytes / (r["step_ms"] * 1e-3) / 1e9
+    fixed_alg = r["fixed_bytes"] + r["dense_bytes"]
+    achieved = fixed_alg / (r["fixed_ms"] * 1e-3) / 1e9
+    log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
+        f"{r['event_ms'] * 1e3:.2f}); fixed pass {r['fixed_ms'] * 1e3:.2f} us, exception pass "
+        f"{r['exc_ms'] * 1e3:.2f} us; {gbps:.1f} GB/s")
+    traffic = pmc_traffic("csf_fixed_kernel", spec.name)
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 6),
+        "us_per_stack": round(r["step_ms"] * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}: full-stack CSF decode of {spec.E} experts x {spec.R} rows x "
+                        f"{spec.C} E4M3 scale columns (K={spec.K}), 3% outliers, seed {spec.seed}",
+            "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": "NVFP4 (E4M3 scales)",
+            "exception_entries": stack.num_exceptions,
+            "compressed_bytes": r["fixed_bytes"] + r["exc_bytes"],
+            "dense_bytes": r["dense_bytes"],
+            "bytes_per_step": step_bytes,
+            "rotating_sets": args.sets,
+            "fixed_pass_us": round(r["fixed_ms"] * 1e3, 3),
+            "exception_pass_us": round(r["exc_ms"] * 1e3, 3),
+        },
+        "roofline": {
+            "kernel": "csf_fixed_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": fixed_alg,
+            "mean_launch_us": round(r["fixed_ms"] * 1e3, 3),
+        },
+    }
+    if args.all:
+        extra = {}
+        for name in ("down_nvfp4", "mxfp4", "tiny_nvfp4"):
+            s = workloads.STACKS[name]
+            log(f"[bench] {name}")
+            rr = bench_stack(mwd, torch, ev, s, min(args.steps, 2000), args.warmup,
+                             args.sets if s.E > 4 else 2, dev)
+            b = rr["fixed_bytes"] + rr["exc_bytes"] + rr["dense_bytes"]
+            extra[name] = dict(us=round(rr["step_ms"] * 1e3, 2), gbps=round(b / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                               fixed_us=round(rr["fixed_ms"] * 1e3, 2), exc_us=round(rr["exc_ms"] * 1e3, 2),
+                               bytes=b, entries=rr["stack"].num_exceptions)
+            log(f"[bench] {name}: {extra[name]}")
+            del rr
+            torch.cuda.empty_cache()
+        log("[bench] routed_paired")
+        rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev)
+        extra["routed_paired"] = dict(us=round(rr["step_ms"] * 1e3, 2),
+                                      gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                                      fixed_us=round(rr["fixed_ms"] * 1e3, 2),
+                                      exc_us=round(rr["exc_ms"] * 1e3, 2), bytes=rr["bytes"],
+                                      active=rr["active"])
+        log(f"[bench] routed_paired: {extra['routed_paired']}")
+        cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
+        extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
+        log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
+        os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+        json.dump(extra, open(os.path.join(ROOT, "gpurun_out", "bench_all.json"), "w"), indent=1)
+    if not args.no_cpu:
+        log(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(spec, r["x"], args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * csf.h — C ABI of the CSF block-scale decoder for MI355X (gfx950).
+ *
+ * CSF ("finegrained-kernels: decode losslessly compressed NVFP4 scales (CSF)",
+ * kernels-community PR 1236, format paragraph) stores the FP8 block-scale bytes
+ * of stacked MoE expert projections as one base byte per row, a resident stream
+ * of small offsets from that base, and an exception stream for the values the
+ * offsets cannot reach; decoding gives back the original bytes exactly.
+ * Offsets are 4 bits wide for NVFP4 (E4M3 scale per 16 weights) and 1 bit for
+ * MXFP4 (UE8M0 scale per 32 weights), reordered for contiguous decoding
+ * ("NVFP4-CSF: expand_scales() for ahead-of-call scale expansion (canonical
+ * twin of #477)", b12x PR 478, commit messages).
+ *
+ * Layout of one compressed stack (format, E experts, R rows, C scale columns;
+ * w = offset bits, G = 128 / w positions per 16-byte group, P = R * C):
+ *   bases       u8[E * R]            row-major (expert, row)
+ *   offsets     u8[E * stride]       stride >= 16 * ceil(P / G), multiple of 16;
+ *                                    position p of expert e is byte
+ *                                    e*stride + 16*(p/G) + p%16, bits
+ *                                    [w*f, w*f + w) with f = (p % G) / 16
+ *   exceptions  u32[n]               (p << 8) | byte, expert-major, ascending p
+ *   exc_prefix  i32[E + 1]           exclusive prefix of per-expert entry counts
+ *   dense       u8[E][R][C]          plane e at workspace + e * P
+ * Fields at exception positions and past the plane are zero.
+ *
+ * Error behaviour: every function returns a csf_status; nothing aborts and no
+ * C++ exception crosses this boundary.  Decode functions check their arguments
+ * on the host (no device reads, no synchronisation) and launch nothing when a
+ * check fails.
+ */
+#ifndef CSF_H
+#define CSF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSF_ABI_VERSION 1
+
+/* Largest expert count a decode accepts (routing maps are kept on chip). */
+#define CSF_MAX_EXPERTS 2048
+
+typedef enum csf_format {
+    CSF_NVFP4_E4M3 = 0,  /* 4-bit offsets, one scale per 16 weights */
+    CSF_MXFP4_UE8M0 = 1  /* 1-bit offsets, one scale per 32 weights */
+} csf_format;
+
+typedef enum csf_status {
+    CSF_OK = 0,
+    CSF_E_NULL = 1,     /* a required pointer is NULL */
+    CSF_E_SHAPE = 2,    /* E, R or C <= 0, R*C >= 2^24, or E > CSF_MAX_EXPERTS */
+    CSF_E_FORMAT = 3,   /* unknown format */
+    CSF_E_SIZE = 4,     /* stride or exception count inconsistent with the shape */
+    CSF_E_ALIGN = 5,    /* offsets not 16-byte aligned, or exceptions/prefix not 4-byte aligned */
+    CSF_E_CORRUPT = 6,  /* csf_validate: the stream breaks the layout */
+    CSF_E_MISMATCH = 7, /* paired stacks have different expert counts */
+    CSF_E_HIP = 8       /* the HIP runtime refused a launch */
+} csf_status;
+
+/* Buffer sizes of one compressed stack, in bytes unless named otherwise. */
+typedef struct csf_sizes {
+    int64_t dense_bytes;       /* E * R * C */
+    int64_t bases_bytes;       /* E * R */
+    int64_t offsets_stride;    /* 16 * ceil(R * C / G) */
+    int64_t offsets_bytes;     /* E * offsets_stride */
+    int64_t num_exceptions;    /* entries */
+    int64_t exceptions_bytes;  /* 4 * num_exceptions */
+    int64_t prefix_bytes;      /* 4 * (E + 1) */
+    int64_t compressed_bytes;  /* bases + offsets + exceptions + prefix */
+} csf_sizes;
+
+/*
+ * Descriptor of one compressed stack.  The struct itself lives in host memory
+ * and is copied into the kernel arguments; the pointers are device pointers.
+ * exceptions may be NULL iff num_exceptions == 0.
+ */
+typedef struct csf_stack {
+    int32_t format;
+    int32_t num_experts;
+    int32_t rows;
+    int32_t cols;
+    int64_t offsets_stride;
+    int64_t num_exceptions;
+    const uint8_t *bases;
+    const uint8_t *offsets;
+    const uint32_t *exceptions;
+    const int32_t *exc_prefix;
+} csf_stack;
+
+int csf_abi_version(void);
+const char *csf_status_str(csf_status status);
+
+/*
+ * Encode a dense stack (PR 1236, API paragraph: the preparation helper).
+ * dense_host: u8[E][R][C] in host memory.  Two-call pattern: with bases,
+ * offsets, exceptions and exc_prefix all NULL only *out_sizes is filled; with
+ * all four non-NULL (host buffers of at least the reported sizes;
+ * exceptions may be NULL when num_exceptions is 0) the stack is encoded.  Any
+ * other mix returns CSF_E_NULL.  The output is deterministic: the base of a row
+ * is the row value v with the most row values in [v, v + 2^w - 1], ties to the
+ * smallest v.  Host memory only; the caller copies the buffers to the device.
+ * Errors: CSF_E_FORMAT, CSF_E_SHAPE, CSF_E_NULL.
+ */
+csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
+                       const uint8_t *dense_host, csf_sizes *out_sizes, uint8_t *bases,
+                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix);
+
+/*
+ * Expand a compressed stack into the dense workspace (PR 1236, API paragraph:
+ * decoding on the GPU into reusable, caller-owned workspace; fixed stream then
+ * exception pass; with the grouped-routing expert_start tensor only experts
+ * with routed tokens are expanded and every other plane is left untouched; no
+ * selection buffer and no CPU synchronisation; without it the whole stack).
+ *
+ * workspace: device u8[E*R*C], any byte alignment (PR 1236, validation
+ *   paragraph: odd-offset workspace).
+ * expert_start: NULL, or device int32[E + 1]; expert e is expanded iff
+ *   expert_start[e + 1] > expert_start[e].  It is read on the device only.
+ * hip_stream: a hipStream_t (NULL = the null stream).  The call enqueues the
+ *   fixed-stream kernel then the exception kernel and returns; it allocates
+ *   nothing, synchronises nothing and keeps no state, so it can be captured in
+ *   a HIP graph.  The caller orders other users of the workspace.
+ * Errors: CSF_E_NULL, CSF_E_FORMAT, CSF_E_SHAPE, CSF_E_SIZE, CSF_E_ALIGN,
+ *   CSF_E_HIP (launch refused).
+ */
+csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace,
+                      const int32_t *expert_start, void *hip_stream);
+
+/*
+ * Gate/up and down stacks of the same experts in one call: each pass is a
+ * single launch covering both stacks (PR 478, commit messages: decode only
+ * routed experts and pair gate/up and down scales without adding streams).
+ * Formats and shapes may differ between the stacks; expert counts must match
+ * (CSF_E_MISMATCH).  expert_start is shared and may be NULL.  Otherwise as
+ * csf_decode.
+ */
+csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up,
+                             const csf_stack *down, uint8_t *ws_down,
+                             const int32_t *expert_start, void *hip_stream);
+
+/* Pass selection for csf_decode_passes. */
+#define CSF_PASS_FIXED 1u      /* base + offset expansion of every position */
+#define CSF_PASS_EXCEPTIONS 2u /* exception entries overwrite their positions */
+#define CSF_PASS_ALL 3u
+
+/*
+ * The passes csf_decode / csf_decode_paired enqueue, selectable one at a time
+ * so a caller can schedule or time them separately.  second may be NULL (then
+ * ws_second is ignored).  CSF_PASS_EXCEPTIONS is only meaningful after
+ * CSF_PASS_FIXED of the same call arguments has run earlier in stream order.
+ * passes must be a non-zero subset of CSF_PASS_ALL (else CSF_E_SIZE).
+ */
+csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first,
+                             const csf_stack *second, uint8_t *ws_second,
+                             const int32_t *expert_start, uint32_t passes,
+                             void *hip_stream);
+
+/*
+ * Full host-side check of a stack whose buffers are in HOST memory: prefix
+ * starts at 0, is non-decreasing and ends at num_exceptions; entries ascend
+ * strictly within each expert and stay inside the plane; no entry byte lies in
+ * its row's offset window; offset fields past the plane and at exception
+ * positions are zero.  Returns CSF_E_CORRUPT on a violation.  Not called by the
+ * decoder, which never reads device memory from the host.
+ */
+csf_status csf_validate(const csf_stack *host_copy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSF_H */

@@ -1,0 +1,299 @@
+"""CSF block-scale decode for MI355X: Python binding of ``libcsf.so``.
+
+Argument marshalling only: every decode step runs in the library's gfx950
+kernels, and the binding has no other implementation to fall back to.  PyTorch
+provides device memory and streams.  If the library has not been built, every
+call raises ``RuntimeError`` (build it with ``python -m
+moe_weight_decode_amd.build``).
+
+The functions mirror the C ABI in ``include/csf.h``:
+
+* ``prepare(dense, fmt)`` -> ``CompressedStack`` on ``dense``'s device
+  (the preparation helper of "finegrained-kernels: decode losslessly
+  compressed NVFP4 scales (CSF)", kernels-community PR 1236, API paragraph,
+  which keeps the input's device);
+* ``decode(stack, workspace, expert_start=None, stream=None)``;
+* ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``;
+* ``decode_passes(...)`` to enqueue the fixed-stream or exception pass alone;
+* ``validate(stack)`` (host-side layout check).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # load torch's HIP runtime first so libcsf binds to the same one
+
+NVFP4 = 0
+MXFP4 = 1
+PASS_FIXED = 1
+PASS_EXCEPTIONS = 2
+PASS_ALL = 3
+MAX_EXPERTS = 2048
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsf.so")
+
+STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: "CSF_E_SIZE",
+          5: "CSF_E_ALIGN", 6: "CSF_E_CORRUPT", 7: "CSF_E_MISMATCH", 8: "CSF_E_HIP"}
+
+EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_decode", "csf_decode_paired",
+           "csf_decode_passes", "csf_validate")
+
+
+class CsfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        msg = _lib().csf_status_str(status).decode() if _LIB is not None else ""
+        super().__init__(f"{where}: {self.name} ({msg})")
+
+
+class csf_sizes(ctypes.Structure):
+    _fields_ = [("dense_bytes", ctypes.c_int64), ("bases_bytes", ctypes.c_int64),
+                ("offsets_stride", ctypes.c_int64), ("offsets_bytes", ctypes.c_int64),
+                ("num_exceptions", ctypes.c_int64), ("exceptions_bytes", ctypes.c_int64),
+                ("prefix_bytes", ctypes.c_int64), ("compressed_bytes", ctypes.c_int64)]
+
+
+class csf_stack(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("offsets_stride", ctypes.c_int64), ("num_exceptions", ctypes.c_int64),
+                ("bases", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("exceptions", ctypes.c_void_p), ("exc_prefix", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is not built; run `python -m moe_weight_decode_amd.build`")
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.csf_abi_version.restype = ctypes.c_int
+        lib.csf_abi_version.argtypes = []
+        lib.csf_status_str.restype = ctypes.c_char_p
+        lib.csf_status_str.argtypes = [ctypes.c_int]
+        lib.csf_prepare.restype = ctypes.c_int
+        lib.csf_prepare.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(csf_sizes), vp, vp, vp, vp]
+        lib.csf_decode.restype = ctypes.c_int
+        lib.csf_decode.argtypes = [ctypes.POINTER(csf_stack), vp, vp, vp]
+        lib.csf_decode_paired.restype = ctypes.c_int
+        lib.csf_decode_paired.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp,
+                                          vp, vp]
+        lib.csf_decode_passes.restype = ctypes.c_int
+        lib.csf_decode_passes.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp,
+                                          vp, ctypes.c_uint32, vp]
+        lib.csf_validate.restype = ctypes.c_int
+        lib.csf_validate.argtypes = [ctypes.POINTER(csf_stack)]
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ``ctypes.CDLL`` of libcsf.so (raises if it is not built)."""
+    return _lib()
+
+
+@dataclass
+class CompressedStack:
+    """One compressed stack; tensors share one device (CPU or GPU)."""
+    fmt: int
+    E: int
+    R: int
+    C: int
+    stride: int
+    num_exceptions: int
+    bases: torch.Tensor       # uint8 [E*R]
+    offsets: torch.Tensor     # uint8 [E*stride]
+    exceptions: torch.Tensor  # int32 [max(n, 1)], holding the u32 entry words
+    prefix: torch.Tensor      # int32 [E+1]
+
+    @property
+    def P(self) -> int:
+        return self.R * self.C
+
+    @property
+    def dense_bytes(self) -> int:
+        return self.E * self.R * self.C
+
+    @property
+    def compressed_bytes(self) -> int:
+        return self.E * self.R + self.E * self.stride + 4 * self.num_exceptions + 4 * (self.E + 1)
+
+    @property
+    def device(self) -> torch.device:
+        return self.offsets.device
+
+    def to(self, device) -> "CompressedStack":
+        mv = lambda t: t.to(device, non_blocking=False).contiguous()
+        return CompressedStack(self.fmt, self.E, self.R, self.C, self.stride, self.num_exceptions,
+                               mv(self.bases), mv(self.offsets), mv(self.exceptions), mv(self.prefix))
+
+    def clone(self) -> "CompressedStack":
+        return CompressedStack(self.fmt, self.E, self.R, self.C, self.stride, self.num_exceptions,
+                               self.bases.clone(), self.offsets.clone(), self.exceptions.clone(),
+                               self.prefix.clone())
+
+    def descriptor(self) -> csf_stack:
+        d = csf_stack()
+        d.format, d.num_experts, d.rows, d.cols = self.fmt, self.E, self.R, self.C
+        d.offsets_stride, d.num_exceptions = self.stride, self.num_exceptions
+        d.bases = self.bases.data_ptr()
+        d.offsets = self.offsets.data_ptr()
+        d.exceptions = self.exceptions.data_ptr() if self.num_exceptions > 0 else None
+        d.exc_prefix = self.prefix.data_ptr()
+        return d
+
+    def numpy(self) -> dict:
+        """Host copies of the buffers (uint32 entries)."""
+        return dict(fmt=self.fmt, E=self.E, R=self.R, C=self.C, stride=self.stride,
+                    bases=self.bases.cpu().numpy().copy(), offsets=self.offsets.cpu().numpy().copy(),
+                    exceptions=self.exceptions.cpu().numpy()[:self.num_exceptions].view(np.uint32).copy(),
+                    prefix=self.prefix.cpu().numpy().copy())
+
+
+def from_numpy(d: dict, device="cpu") -> CompressedStack:
+    """Wrap host arrays (``fmt, E, R, C, stride, bases, offsets, exceptions, prefix``)."""
+    exc = np.ascontiguousarray(d["exceptions"], dtype=np.uint32)
+    n = int(exc.size)
+    exc_t = torch.from_numpy(exc.view(np.int32).copy() if n else np.zeros(1, dtype=np.int32))
+    st = CompressedStack(int(d["fmt"]), int(d["E"]), int(d["R"]), int(d["C"]), int(d["stride"]), n,
+                         torch.from_numpy(np.ascontiguousarray(d["bases"], dtype=np.uint8).copy()),
+                         torch.from_numpy(np.ascontiguousarray(d["offsets"], dtype=np.uint8).copy()),
+                         exc_t,
+                         torch.from_numpy(np.ascontiguousarray(d["prefix"], dtype=np.int32).copy()))
+    return st.to(device) if str(device) != "cpu" else st
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CsfError(status, where)
+
+
+def prepare(dense, fmt: int) -> CompressedStack:
+    """Encode ``dense`` (uint8 [E, R, C], tensor or array) with the library's
+    encoder; the result lives on ``dense``'s device."""
+    lib = _lib()
+    device = dense.device if isinstance(dense, torch.Tensor) else torch.device("cpu")
+    x = dense.detach().cpu().numpy() if isinstance(dense, torch.Tensor) else np.asarray(dense)
+    if x.dtype != np.uint8 or x.ndim != 3:
+        raise ValueError("dense must be uint8 [E, R, C]")
+    x = np.ascontiguousarray(x)
+    E, R, C = (int(v) for v in x.shape)
+    sz = csf_sizes()
+    _check(lib.csf_prepare(fmt, E, R, C, x.ctypes.data, ctypes.byref(sz), None, None, None, None),
+           "csf_prepare(sizes)")
+    n = int(sz.num_exceptions)
+    bases = np.empty(E * R, dtype=np.uint8)
+    offsets = np.empty(int(sz.offsets_bytes), dtype=np.uint8)
+    exc = np.empty(max(n, 1), dtype=np.uint32)
+    prefix = np.empty(E + 1, dtype=np.int32)
+    _check(lib.csf_prepare(fmt, E, R, C, x.ctypes.data, ctypes.byref(sz), bases.ctypes.data,
+                           offsets.ctypes.data, exc.ctypes.data, prefix.ctypes.data), "csf_prepare")
+    return from_numpy(dict(fmt=fmt, E=E, R=R, C=C, stride=int(sz.offsets_stride), bases=bases,
+                           offsets=offsets, exceptions=exc[:n], prefix=prefix), device)
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_device(stack: CompressedStack, ws: torch.Tensor, name: str):
+    if stack.device.type != "cuda":
+        raise ValueError(f"{name}: compressed stack must be on a GPU")
+    for t in (stack.bases, stack.offsets, stack.exceptions, stack.prefix):
+        if t.device != stack.device or not t.is_contiguous():
+            raise ValueError(f"{name}: stack tensors must be contiguous on one device")
+    if not isinstance(ws, torch.Tensor) or ws.device != stack.device or ws.dtype != torch.uint8:
+        raise ValueError(f"{name}: workspace must be a uint8 tensor on {stack.device}")
+    if not ws.is_contiguous() or ws.numel() < stack.dense_bytes:
+        raise ValueError(f"{name}: workspace must be contiguous with >= {stack.dense_bytes} bytes")
+
+
+def _es_ptr(expert_start, stack: CompressedStack):
+    if expert_start is None:
+        return None
+    if (not isinstance(expert_start, torch.Tensor) or expert_start.dtype != torch.int32
+            or expert_start.device != stack.device or expert_start.numel() != stack.E + 1
+            or not expert_start.is_contiguous()):
+        raise ValueError(f"expert_start must be a contiguous int32[{stack.E + 1}] tensor on {stack.device}")
+    return expert_start.data_ptr()
+
+
+def decode(stack: CompressedStack, workspace: torch.Tensor, expert_start=None, stream=None):
+    """Enqueue the full decode of ``stack`` into ``workspace`` on ``stream``."""
+    _check_device(stack, workspace, "decode")
+    d = stack.descriptor()
+    _check(_lib().csf_decode(ctypes.byref(d), workspace.data_ptr(), _es_ptr(expert_start, stack),
+                             _stream_handle(stream, stack.device)), "csf_decode")
+
+
+def decode_paired(gate_up: CompressedStack, ws_gate_up: torch.Tensor, down: CompressedStack,
+                  ws_down: torch.Tensor, expert_start=None, stream=None):
+    """Enqueue the decode of two stacks of the same experts (one launch per pass)."""
+    _check_device(gate_up, ws_gate_up, "decode_paired")
+    _check_device(down, ws_down, "decode_paired")
+    a, b = gate_up.descriptor(), down.descriptor()
+    _check(_lib().csf_decode_paired(ctypes.byref(a), ws_gate_up.data_ptr(), ctypes.byref(b),
+                                    ws_down.data_ptr(), _es_ptr(expert_start, gate_up),
+                                    _stream_handle(stream, gate_up.device)), "csf_decode_paired")
+
+
+def decode_passes(first: CompressedStack, ws_first: torch.Tensor, second=None, ws_second=None,
+                  expert_start=None, passes: int = PASS_ALL, stream=None):
+    """Enqueue the selected passes only (see ``csf_decode_passes``)."""
+    _check_device(first, ws_first, "decode_passes")
+    a = first.descriptor()
+    b_ref, ws_b = None, None
+    if second is not None:
+        _check_device(second, ws_second, "decode_passes")
+        b = second.descriptor()
+        b_ref, ws_b = ctypes.byref(b), ws_second.data_ptr()
+    _check(_lib().csf_decode_passes(ctypes.byref(a), ws_first.data_ptr(), b_ref, ws_b,
+                                    _es_ptr(expert_start, first), passes,
+                                    _stream_handle(stream, first.device)), "csf_decode_passes")
+
+
+class Launch:
+    """A decode call with its arguments marshalled once, for enqueueing the same
+    decode many times (benchmark loops, graph capture): each call is a single
+    C-ABI call.  Keeps references to every tensor it points at."""
+
+    def __init__(self, first: CompressedStack, ws_first: torch.Tensor, second=None, ws_second=None,
+                 expert_start=None, stream=None):
+        _check_device(first, ws_first, "Launch")
+        if second is not None:
+            _check_device(second, ws_second, "Launch")
+        self._keep = (first, ws_first, second, ws_second, expert_start)
+        self._a = first.descriptor()
+        self._b = second.descriptor() if second is not None else None
+        self._args_ws = (ws_first.data_ptr(), ws_second.data_ptr() if second is not None else None)
+        self._es = _es_ptr(expert_start, first)
+        self._stream = _stream_handle(stream, first.device)
+        self._fn = _lib().csf_decode_passes
+
+    @property
+    def stream(self) -> int:
+        return self._stream
+
+    def __call__(self, passes: int = PASS_ALL):
+        st = self._fn(ctypes.byref(self._a), self._args_ws[0],
+                      ctypes.byref(self._b) if self._b is not None else None, self._args_ws[1],
+                      self._es, passes, self._stream)
+        if st != 0:
+            raise CsfError(st, "csf_decode_passes")
+
+
+def validate(stack: CompressedStack):
+    """Check the layout invariants on a host copy; raises ``CsfError`` (CSF_E_CORRUPT)."""
+    h = stack.to("cpu") if stack.device.type != "cpu" else stack
+    d = h.descriptor()
+    _check(_lib().csf_validate(ctypes.byref(d)), "csf_validate")

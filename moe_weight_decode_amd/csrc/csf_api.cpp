@@ -1,0 +1,432 @@
+// C ABI of the CSF decoder: argument checks, launch planning, the host
+// encoder and the host-side stream validator.  Declarations and the layout are
+// in include/csf.h; the kernels are in csf_kernels.hip.
+#include "csf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "csf_launch.h"
+
+namespace {
+
+using csf::DecodeArgs;
+using csf::StackArgs;
+
+constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of an entry
+
+// Offset groups per lane per fixed-stream unit, by format and mode.
+#ifndef CSF_SLOTS_NVFP4
+#define CSF_SLOTS_NVFP4 4
+#endif
+#ifndef CSF_SLOTS_MXFP4
+#define CSF_SLOTS_MXFP4 2
+#endif
+#ifndef CSF_SLOTS_ROUTED
+#define CSF_SLOTS_ROUTED 1
+#endif
+// Workgroups per CU the grids aim for.
+#ifndef CSF_FIXED_WG_PER_CU
+#define CSF_FIXED_WG_PER_CU 64
+#endif
+#ifndef CSF_EXC_WG_PER_CU
+#define CSF_EXC_WG_PER_CU 8
+#endif
+#ifndef CSF_ROUTED_WG_PER_CU
+#define CSF_ROUTED_WG_PER_CU 4
+#endif
+
+int offset_bits(int32_t format) {
+    if (format == CSF_NVFP4_E4M3) return 4;
+    if (format == CSF_MXFP4_UE8M0) return 1;
+    return 0;
+}
+
+csf_status check_shape(int32_t format, int32_t E, int32_t R, int32_t C) {
+    if (offset_bits(format) == 0) return CSF_E_FORMAT;
+    if (E <= 0 || R <= 0 || C <= 0) return CSF_E_SHAPE;
+    if (int64_t(R) * C >= kMaxPlane) return CSF_E_SHAPE;
+    return CSF_OK;
+}
+
+int64_t min_stride(int32_t format, int32_t R, int32_t C) {
+    const int64_t G = 128 / offset_bits(format);
+    return 16 * ((int64_t(R) * C + G - 1) / G);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Everything a decode can check without touching device memory.
+csf_status check_stack(const csf_stack *s, const uint8_t *ws) {
+    if (s == nullptr || ws == nullptr) return CSF_E_NULL;
+    csf_status st = check_shape(s->format, s->num_experts, s->rows, s->cols);
+    if (st != CSF_OK) return st;
+    if (s->num_experts > CSF_MAX_EXPERTS) return CSF_E_SHAPE;
+    if (s->bases == nullptr || s->offsets == nullptr || s->exc_prefix == nullptr) return CSF_E_NULL;
+    if (s->num_exceptions < 0 || s->num_exceptions >= (int64_t(1) << 31)) return CSF_E_SIZE;
+    if (s->num_exceptions > 0 && s->exceptions == nullptr) return CSF_E_NULL;
+    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0)
+        return CSF_E_SIZE;
+    if (!aligned(s->offsets, 16) || !aligned(s->exc_prefix, 4)) return CSF_E_ALIGN;
+    if (s->num_exceptions > 0 && !aligned(s->exceptions, 4)) return CSF_E_ALIGN;
+    return CSF_OK;
+}
+
+void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t slots) {
+    const uint32_t w = uint32_t(offset_bits(s.format));
+    const uint32_t G = 128u / w;
+    const uint32_t P = uint32_t(s.rows) * uint32_t(s.cols);
+    const uint32_t C = uint32_t(s.cols);
+    a.bases = s.bases;
+    a.offsets = s.offsets;
+    a.exc = s.exceptions;
+    a.prefix = s.exc_prefix;
+    a.ws = ws;
+    a.stride = s.offsets_stride;
+    a.rcp_cols = 1.0 / double(C);
+    a.n_exc = uint32_t(s.num_exceptions);
+    a.P = P;
+    a.R = uint32_t(s.rows);
+    a.C = C;
+    a.groups = (P + G - 1) / G;
+    a.wbits = w;
+    a.row_mode = (C % 16 == 0) ? csf::kRowSplat : (C >= 16 ? csf::kRowTwo : csf::kRowBytes);
+    a.pad_ = 0;
+    // A unit's rows (at most floor((u*G - 1) / C) + 2 of them) must fit the LDS stage.
+    const uint64_t lds_cap = uint64_t(csf::kBasesLds - 2) * C / G;
+    uint64_t cap = std::min<uint64_t>(uint64_t(csf::kBlock) * slots, std::max<uint64_t>(lds_cap, 1));
+    const uint32_t units = uint32_t((a.groups + cap - 1) / cap);
+    a.units = units;
+    a.unit_groups = (a.groups + units - 1) / units;
+}
+
+uint32_t cu_count(hipStream_t stream) {
+    int dev = 0;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) dev = -1;
+    } else {
+        dev = -1;
+    }
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 256;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return uint32_t(n);
+}
+
+csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8_t *ws1,
+                   const int32_t *expert_start, uint32_t passes, void *hip_stream) {
+    if (passes == 0 || (passes & ~CSF_PASS_ALL) != 0) return CSF_E_SIZE;
+    csf_status st = check_stack(s0, ws0);
+    if (st != CSF_OK) return st;
+    if (s1 != nullptr) {
+        st = check_stack(s1, ws1);
+        if (st != CSF_OK) return st;
+        if (s1->num_experts != s0->num_experts) return CSF_E_MISMATCH;
+    }
+    const bool routed = expert_start != nullptr;
+    if (routed && !aligned(expert_start, 4)) return CSF_E_ALIGN;
+
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.expert_start = expert_start;
+    a.nstacks = s1 ? 2u : 1u;
+    a.E = uint32_t(s0->num_experts);
+    const uint32_t slots0 = routed ? CSF_SLOTS_ROUTED
+                                   : (s0->format == CSF_NVFP4_E4M3 ? CSF_SLOTS_NVFP4 : CSF_SLOTS_MXFP4);
+    fill_stack(a.st[0], *s0, ws0, slots0);
+    if (s1) {
+        const uint32_t slots1 = routed ? CSF_SLOTS_ROUTED
+                                       : (s1->format == CSF_NVFP4_E4M3 ? CSF_SLOTS_NVFP4 : CSF_SLOTS_MXFP4);
+        fill_stack(a.st[1], *s1, ws1, slots1);
+    } else {
+        a.st[1] = a.st[0];  // never read: nstacks == 1
+    }
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const uint32_t cus = cu_count(stream);
+
+    if (passes & CSF_PASS_FIXED) {
+        const uint64_t units = uint64_t(a.E) * a.st[0].units + (s1 ? uint64_t(a.E) * a.st[1].units : 0);
+        const uint64_t cap = uint64_t(cus) * (routed ? CSF_ROUTED_WG_PER_CU : CSF_FIXED_WG_PER_CU);
+        const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(units, cap)));
+        if (csf::launch_fixed(a, grid, stream) != hipSuccess) return CSF_E_HIP;
+    }
+    if (passes & CSF_PASS_EXCEPTIONS) {
+        const uint64_t entries = uint64_t(a.st[0].n_exc) + (s1 ? uint64_t(a.st[1].n_exc) : 0);
+        if (entries > 0) {
+            const uint64_t per = uint64_t(csf::kBlock) * csf::kExcPerLane;
+            const uint64_t chunks = (entries + per - 1) / per;
+            const uint64_t cap = uint64_t(cus) * (routed ? CSF_ROUTED_WG_PER_CU : CSF_EXC_WG_PER_CU);
+            const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(chunks, cap)));
+            if (csf::launch_exceptions(a, grid, stream) != hipSuccess) return CSF_E_HIP;
+        }
+    }
+    return CSF_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Host encoder.  Same definition as the format in csf.h; written as a
+// sliding-window base search, a per-position field pass and a group packing
+// pass.
+// ---------------------------------------------------------------------------
+struct EncodeShape {
+    int w, W, G, F;
+    int64_t R, C, P, S;
+};
+
+// Base of each row: slide a W-wide window over the row's 256-bin histogram.
+void choose_row_bases(const EncodeShape &sh, const uint8_t *plane, uint8_t *bases) {
+    uint32_t hist[256 + 16];
+    for (int64_t r = 0; r < sh.R; ++r) {
+        std::memset(hist, 0, sizeof(hist));
+        const uint8_t *row = plane + r * sh.C;
+        for (int64_t c = 0; c < sh.C; ++c) ++hist[row[c]];
+        uint32_t win = 0;
+        for (int v = 0; v < sh.W; ++v) win += hist[v];
+        uint32_t best = 0;
+        int best_v = 0;
+        for (int v = 0; v < 256; ++v) {
+            if (hist[v] != 0 && win > best) {
+                best = win;
+                best_v = v;
+            }
+            win += hist[v + sh.W];
+            win -= hist[v];
+        }
+        bases[r] = uint8_t(best_v);
+    }
+}
+
+int64_t count_outside(const EncodeShape &sh, const uint8_t *plane, const uint8_t *bases) {
+    int64_t n = 0;
+    for (int64_t r = 0; r < sh.R; ++r) {
+        const unsigned b = bases[r];
+        const uint8_t *row = plane + r * sh.C;
+        for (int64_t c = 0; c < sh.C; ++c) n += (unsigned(row[c]) - b) >= unsigned(sh.W);
+    }
+    return n;
+}
+
+// Offsets and exception words of one expert.
+void encode_plane(const EncodeShape &sh, const uint8_t *plane, const uint8_t *bases, uint8_t *seg,
+                  uint32_t *exc, std::vector<uint8_t> &field) {
+    field.assign(size_t(sh.S / 16) * sh.G, 0);  // one byte per position, padded to whole groups
+    int64_t n = 0;
+    for (int64_t r = 0; r < sh.R; ++r) {
+        const unsigned b = bases[r];
+        for (int64_t c = 0; c < sh.C; ++c) {
+            const int64_t p = r * sh.C + c;
+            const unsigned d = unsigned(plane[p]) - b;
+            if (d < unsigned(sh.W)) {
+                field[size_t(p)] = uint8_t(d);
+            } else {
+                exc[n++] = (uint32_t(p) << 8) | plane[p];
+            }
+        }
+    }
+    const int64_t groups = sh.S / 16;
+    for (int64_t g = 0; g < groups; ++g) {
+        const uint8_t *fg = field.data() + g * sh.G;
+        for (int j = 0; j < 16; ++j) {
+            unsigned byte = 0;
+            for (int f = 0; f < sh.F; ++f) byte |= unsigned(fg[16 * f + j]) << (sh.w * f);
+            seg[g * 16 + j] = uint8_t(byte);
+        }
+    }
+}
+
+template <class Fn>
+void parallel_experts(int32_t E, Fn fn) {
+    const unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    const unsigned nt = std::min<unsigned>(hw, unsigned(E));
+    if (nt <= 1) {
+        for (int32_t e = 0; e < E; ++e) fn(e);
+        return;
+    }
+    std::vector<std::thread> pool;
+    pool.reserve(nt);
+    for (unsigned t = 0; t < nt; ++t)
+        pool.emplace_back([&, t] {
+            for (int32_t e = int32_t(t); e < E; e += int32_t(nt)) fn(e);
+        });
+    for (auto &th : pool) th.join();
+}
+
+csf_status prepare_impl(int32_t format, int32_t E, int32_t R, int32_t C, const uint8_t *dense,
+                        csf_sizes *out, uint8_t *bases, uint8_t *offsets, uint32_t *exceptions,
+                        int32_t *exc_prefix) {
+    csf_status st = check_shape(format, E, R, C);
+    if (st != CSF_OK) return st;
+    if (dense == nullptr || out == nullptr) return CSF_E_NULL;
+    const bool query = bases == nullptr && offsets == nullptr && exceptions == nullptr && exc_prefix == nullptr;
+    if (!query && (bases == nullptr || offsets == nullptr || exc_prefix == nullptr)) return CSF_E_NULL;
+
+    EncodeShape sh;
+    sh.w = offset_bits(format);
+    sh.W = 1 << sh.w;
+    sh.G = 128 / sh.w;
+    sh.F = 8 / sh.w;
+    sh.R = R;
+    sh.C = C;
+    sh.P = int64_t(R) * C;
+    sh.S = min_stride(format, R, C);
+
+    std::vector<uint8_t> scratch_bases;
+    uint8_t *b = bases;
+    if (query) {
+        scratch_bases.resize(size_t(E) * R);
+        b = scratch_bases.data();
+    }
+    std::vector<int64_t> counts(size_t(E), 0);
+    parallel_experts(E, [&](int32_t e) {
+        const uint8_t *plane = dense + int64_t(e) * sh.P;
+        choose_row_bases(sh, plane, b + int64_t(e) * R);
+        counts[size_t(e)] = count_outside(sh, plane, b + int64_t(e) * R);
+    });
+    int64_t n = 0;
+    for (int64_t c : counts) n += c;
+    if (n >= (int64_t(1) << 31)) return CSF_E_SIZE;
+
+    out->dense_bytes = int64_t(E) * sh.P;
+    out->bases_bytes = int64_t(E) * R;
+    out->offsets_stride = sh.S;
+    out->offsets_bytes = int64_t(E) * sh.S;
+    out->num_exceptions = n;
+    out->exceptions_bytes = 4 * n;
+    out->prefix_bytes = 4 * (int64_t(E) + 1);
+    out->compressed_bytes = out->bases_bytes + out->offsets_bytes + out->exceptions_bytes + out->prefix_bytes;
+    if (query) return CSF_OK;
+    if (n > 0 && exceptions == nullptr) return CSF_E_NULL;
+
+    std::vector<int64_t> start(size_t(E) + 1, 0);
+    for (int32_t e = 0; e < E; ++e) start[size_t(e) + 1] = start[size_t(e)] + counts[size_t(e)];
+    for (int32_t e = 0; e <= E; ++e) exc_prefix[e] = int32_t(start[size_t(e)]);
+    parallel_experts(E, [&](int32_t e) {
+        thread_local std::vector<uint8_t> field;
+        encode_plane(sh, dense + int64_t(e) * sh.P, b + int64_t(e) * R, offsets + int64_t(e) * sh.S,
+                     exceptions + start[size_t(e)], field);
+    });
+    return CSF_OK;
+}
+
+csf_status validate_impl(const csf_stack *s) {
+    if (s == nullptr) return CSF_E_NULL;
+    csf_status st = check_shape(s->format, s->num_experts, s->rows, s->cols);
+    if (st != CSF_OK) return st;
+    if (s->bases == nullptr || s->offsets == nullptr || s->exc_prefix == nullptr) return CSF_E_NULL;
+    if (s->num_exceptions < 0) return CSF_E_SIZE;
+    if (s->num_exceptions > 0 && s->exceptions == nullptr) return CSF_E_NULL;
+    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0)
+        return CSF_E_SIZE;
+    const int w = offset_bits(s->format);
+    const unsigned W = 1u << w;
+    const int64_t G = 128 / w;
+    const int64_t R = s->rows, C = s->cols, P = R * C, S = s->offsets_stride;
+    const int32_t *pf = s->exc_prefix;
+    if (pf[0] != 0 || pf[s->num_experts] != s->num_exceptions) return CSF_E_CORRUPT;
+    std::vector<uint8_t> is_exc(static_cast<size_t>(P));
+    for (int32_t e = 0; e < s->num_experts; ++e) {
+        if (pf[e + 1] < pf[e]) return CSF_E_CORRUPT;
+        const uint8_t *base = s->bases + int64_t(e) * R;
+        const uint8_t *seg = s->offsets + int64_t(e) * S;
+        std::fill(is_exc.begin(), is_exc.end(), 0);
+        int64_t prev = -1;
+        for (int64_t k = pf[e]; k < pf[e + 1]; ++k) {
+            const uint32_t x = s->exceptions[k];
+            const int64_t pos = x >> 8;
+            if (pos <= prev || pos >= P) return CSF_E_CORRUPT;
+            prev = pos;
+            if (unsigned(x & 0xffu) - base[pos / C] < W) return CSF_E_CORRUPT;  // fits the window
+            is_exc[size_t(pos)] = 1;
+        }
+        for (int64_t byte = 0; byte < S; ++byte) {
+            const int64_t g = byte / 16, j = byte % 16;
+            for (int f = 0; f < 8 / w; ++f) {
+                const int64_t p = g * G + 16 * f + j;
+                const unsigned field = (unsigned(seg[byte]) >> (w * f)) & (W - 1);
+                if (field == 0) continue;
+                if (p >= P || is_exc[size_t(p)]) return CSF_E_CORRUPT;  // must be zero
+                if (base[p / C] + field > 255u) return CSF_E_CORRUPT;    // would wrap
+            }
+        }
+    }
+    return CSF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csf_abi_version(void) { return CSF_ABI_VERSION; }
+
+const char *csf_status_str(csf_status s) {
+    switch (s) {
+        case CSF_OK: return "ok";
+        case CSF_E_NULL: return "a required pointer is NULL";
+        case CSF_E_SHAPE: return "bad shape (E, R, C must be positive, R*C < 2^24, E <= CSF_MAX_EXPERTS)";
+        case CSF_E_FORMAT: return "unknown format";
+        case CSF_E_SIZE: return "stride, exception count or pass selection inconsistent";
+        case CSF_E_ALIGN: return "misaligned buffer (offsets need 16 bytes, exceptions/prefix/expert_start 4)";
+        case CSF_E_CORRUPT: return "compressed stream breaks the layout";
+        case CSF_E_MISMATCH: return "paired stacks have different expert counts";
+        case CSF_E_HIP: return "HIP runtime refused the launch";
+    }
+    return "unknown status";
+}
+
+csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
+                       const uint8_t *dense_host, csf_sizes *out_sizes, uint8_t *bases,
+                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix) {
+    try {
+        return prepare_impl(format, num_experts, rows, cols, dense_host, out_sizes, bases, offsets,
+                            exceptions, exc_prefix);
+    } catch (...) {
+        return CSF_E_SIZE;  // allocation failure in the host encoder
+    }
+}
+
+csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace, const int32_t *expert_start,
+                      void *hip_stream) {
+    try {
+        return enqueue(compressed, workspace, nullptr, nullptr, expert_start, CSF_PASS_ALL, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up, const csf_stack *down,
+                             uint8_t *ws_down, const int32_t *expert_start, void *hip_stream) {
+    if (down == nullptr) return CSF_E_NULL;
+    try {
+        return enqueue(gate_up, ws_gate_up, down, ws_down, expert_start, CSF_PASS_ALL, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
+                             uint8_t *ws_second, const int32_t *expert_start, uint32_t passes,
+                             void *hip_stream) {
+    try {
+        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, passes,
+                       hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_validate(const csf_stack *host_copy) {
+    try {
+        return validate_impl(host_copy);
+    } catch (...) {
+        return CSF_E_SIZE;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,383 @@
+// CSF block-scale decode kernels for gfx950 (CDNA4, wave64).
+//
+// Two passes, as the decoder on "finegrained-kernels: decode losslessly
+// compressed NVFP4 scales (CSF)" (kernels-community PR 1236, API paragraph) is
+// described: a fixed stream that writes base + offset for every position, then
+// an exception pass that overwrites the positions whose byte the offsets could
+// not reach.  With the grouped-routing expert_start tensor both passes skip
+// experts with no routed tokens and never address their planes; the routing is
+// read on the device only.  One launch of each pass covers one or two stacks
+// (gate/up + down, "NVFP4-CSF: expand_scales() for ahead-of-call scale
+// expansion (canonical twin of #477)", b12x PR 478, commit messages).
+//
+// The work is a byte expansion bound by HBM bandwidth: no matrix cores, a few
+// integer ops per output byte.  What matters is wide coalesced traffic and
+// enough bytes in flight per CU.
+#include "csf_launch.h"
+
+namespace csf {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Byte-wise sum modulo 256 of four packed bytes: no carry crosses a byte.
+__device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b) {
+    const uint32_t s = (a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu);
+    return s ^ ((a ^ b) & 0x80808080u);
+}
+
+__device__ __forceinline__ u32x4 add_bytes4(u32x4 a, u32x4 b) {
+    return (u32x4){add_bytes(a.x, b.x), add_bytes(a.y, b.y), add_bytes(a.z, b.z),
+                   add_bytes(a.w, b.w)};
+}
+
+// floor(n / d) for n, d < 2^24 with rcp = 1.0 / d.  (n + 0.5) / d lies at least
+// 0.5 / d >= 2^-25 away from an integer while the fp64 error stays below 2^-28.
+__device__ __forceinline__ uint32_t div_exact(uint32_t n, double rcp) {
+    return (uint32_t)(((double)n + 0.5) * rcp);
+}
+
+// Mask of the first k bytes of a 32-bit word, k clamped to [0, 4].
+__device__ __forceinline__ uint32_t low_bytes_mask(int k) {
+    return k >= 4 ? 0xffffffffu : (k <= 0 ? 0u : ((1u << (8 * k)) - 1u));
+}
+
+// Row bases of the 16 positions pos .. pos+15 of one plane, packed like the
+// output.  lds holds the bases of rows r_lo, r_lo+1, ... of the current unit.
+template <int MODE>
+__device__ __forceinline__ u32x4 run_bases(const uint8_t *lds, uint32_t pos, uint32_t r_lo,
+                                           uint32_t C, double rcp) {
+    const uint32_t r0 = div_exact(pos, rcp);
+    const uint32_t s0 = (uint32_t)lds[r0 - r_lo] * 0x01010101u;
+    if constexpr (MODE == kRowSplat) {
+        return (u32x4){s0, s0, s0, s0};
+    } else if constexpr (MODE == kRowTwo) {
+        // C >= 16: the run ends inside row r0 or r0 + 1.
+        const int left = (int)((r0 + 1) * C - pos);
+        if (left >= 16) return (u32x4){s0, s0, s0, s0};
+        const uint32_t s1 = (uint32_t)lds[r0 + 1 - r_lo] * 0x01010101u;
+        u32x4 out;
+        uint32_t m;
+        m = low_bytes_mask(left);      out.x = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 4);  out.y = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 8);  out.z = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 12); out.w = (s0 & m) | (s1 & ~m);
+        return out;
+    } else {
+        // C < 16: walk the row boundaries byte by byte.
+        uint32_t r = r0;
+        uint32_t next = (r0 + 1) * C;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (pos + j == next) {
+                ++r;
+                next += C;
+            }
+            w[j >> 2] |= (uint32_t)lds[r - r_lo] << (8 * (j & 3));
+        }
+        return (u32x4){w[0], w[1], w[2], w[3]};
+    }
+}
+
+// Store up to 16 bytes of v at dst.  Full, 16-byte aligned runs (every run of
+// an aligned plane whose size is a multiple of 16) take one 128-bit store.
+__device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t nvalid) {
+    if (nvalid >= 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+        *reinterpret_cast<u32x4 *>(dst) = v;
+        return;
+    }
+    const uint32_t n = nvalid < 16 ? nvalid : 16;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (uint32_t j = 0; j < 16; ++j)
+        if (j < n) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+}
+
+// Expand the offset groups a lane loaded for one unit: field f of group g is
+// the 16 positions g*G + 16f .. +15 (the contiguous-decoding order).
+template <int WB, int MODE>
+__device__ __forceinline__ void expand_unit(const StackArgs &st, const u32x4 *v, uint32_t g_begin,
+                                            uint32_t g_end, uint8_t *plane, const uint8_t *lds,
+                                            uint32_t r_lo) {
+    constexpr uint32_t G = 128 / WB;
+    constexpr int F = 8 / WB;
+    constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
+#pragma unroll
+    for (int i = 0; i < kFixedMaxSlots; ++i) {
+        const uint32_t g = g_begin + threadIdx.x + i * kBlock;
+        if (g >= g_end) break;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const uint32_t pos = g * G + 16u * f;
+            if (pos >= st.P) break;
+            const u32x4 field = (v[i] >> (uint32_t)(WB * f)) & MASK;
+            const u32x4 base = run_bases<MODE>(lds, pos, r_lo, st.C, st.rcp_cols);
+            store_run(plane + pos, add_bytes4(field, base), st.P - pos);
+        }
+    }
+}
+
+__device__ __forceinline__ StackArgs pick(const DecodeArgs &a, uint32_t s) {
+    return s ? a.st[1] : a.st[0];
+}
+
+// Wave 0 of the workgroup: list the active experts (expert_start[e+1] >
+// expert_start[e], or all when es is null) in increasing order into act[];
+// for each stack s < ns also the exclusive prefix M_s over the listed experts
+// of their entry counts (prefix[e+1] - prefix[e], clamped to [0, n_exc]),
+// capped at n_exc.  Returns the number of active experts.  A wave-level
+// prefix: ballot + popcount for the positions, a shuffle scan for the counts.
+__device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uint32_t ns,
+                               const int32_t *pfx0, const int32_t *pfx1, uint32_t n0,
+                               uint32_t n1, uint32_t *M0, uint32_t *M1) {
+    const uint32_t lane = threadIdx.x;
+    uint32_t n = 0;
+    uint64_t run0 = 0, run1 = 0;
+    if (lane == 0 && ns > 0) {
+        M0[0] = 0;
+        if (ns > 1) M1[0] = 0;
+    }
+    for (uint32_t base = 0; base < E; base += kWave) {
+        const uint32_t e = base + lane;
+        const bool on = e < E && (es == nullptr || es[e + 1] > es[e]);
+        const uint64_t mask = __ballot(on);
+        const uint32_t slot = n + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+        if (on) act[slot] = (uint16_t)e;
+        if (ns > 0) {
+            int64_t c0 = on ? (int64_t)pfx0[e + 1] - (int64_t)pfx0[e] : 0;
+            c0 = c0 < 0 ? 0 : (c0 > (int64_t)n0 ? (int64_t)n0 : c0);
+            uint64_t s0 = (uint64_t)c0;
+            int64_t c1 = 0;
+            if (ns > 1) {
+                c1 = on ? (int64_t)pfx1[e + 1] - (int64_t)pfx1[e] : 0;
+                c1 = c1 < 0 ? 0 : (c1 > (int64_t)n1 ? (int64_t)n1 : c1);
+            }
+            uint64_t s1 = (uint64_t)c1;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const uint64_t y0 = __shfl_up(s0, d, kWave);
+                const uint64_t y1 = __shfl_up(s1, d, kWave);
+                if (lane >= (uint32_t)d) {
+                    s0 += y0;
+                    s1 += y1;
+                }
+            }
+            if (on) {
+                const uint64_t t0 = run0 + s0;
+                M0[slot + 1] = (uint32_t)(t0 < n0 ? t0 : n0);
+                if (ns > 1) {
+                    const uint64_t t1 = run1 + s1;
+                    M1[slot + 1] = (uint32_t)(t1 < n1 ? t1 : n1);
+                }
+            }
+            run0 += __shfl(s0, kWave - 1, kWave);
+            run1 += __shfl(s1, kWave - 1, kWave);
+        }
+        n += (uint32_t)__popcll(mask);
+    }
+    return n;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: fixed-stream expansion.
+//
+// Work unit = (stack, active expert, range of up to kBlock*kFixedMaxSlots
+// offset groups).  A workgroup loads its lanes' 16-byte offset groups
+// (coalesced 128-bit loads), stages the unit's row bases in LDS, then every
+// lane widens each field to 16 output bytes, adds the row bases with a
+// byte-wise add and stores 16 bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+    __shared__ __align__(16) uint8_t lds_bases[kBasesLds + kBasesLdsSlack];
+    __shared__ uint32_t s_nact;
+
+    const bool routed = a.expert_start != nullptr;
+    uint16_t *act = reinterpret_cast<uint16_t *>(dyn_lds);
+    uint32_t nact = a.E;
+    if (routed) {
+        int32_t *es = reinterpret_cast<int32_t *>(dyn_lds + ((2u * a.E + 15u) & ~15u));
+        for (uint32_t i = threadIdx.x; i <= a.E; i += kBlock) es[i] = a.expert_start[i];
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const uint32_t n = build_maps(es, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
+            if (threadIdx.x == 0) s_nact = n;
+        }
+        __syncthreads();
+        nact = s_nact;
+    }
+
+    const uint32_t u0 = nact * a.st[0].units;
+    const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].units : 0u);
+    for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
+        const uint32_t s = u >= u0 ? 1u : 0u;
+        const StackArgs st = pick(a, s);
+        const uint32_t uu = u - (s ? u0 : 0u);
+        const uint32_t k = uu / st.units;
+        const uint32_t c = uu - k * st.units;
+        const uint32_t e = routed ? (uint32_t)act[k] : k;
+
+        const uint32_t G = 128u / st.wbits;
+        const uint32_t g_begin = c * st.unit_groups;
+        const uint32_t g_end = min(g_begin + st.unit_groups, st.groups);
+        const uint32_t p_last = min(g_end * G, st.P) - 1u;
+        const uint32_t r_lo = div_exact(g_begin * G, st.rcp_cols);
+        const uint32_t nrows = div_exact(p_last, st.rcp_cols) - r_lo + 1u;
+
+        // Offsets first, so their latency overlaps the base staging.
+        const u32x4 *seg = reinterpret_cast<const u32x4 *>(st.offsets + (uint64_t)e * st.stride);
+        u32x4 v[kFixedMaxSlots];
+#pragma unroll
+        for (int i = 0; i < kFixedMaxSlots; ++i) {
+            const uint32_t g = g_begin + threadIdx.x + i * kBlock;
+            v[i] = g < g_end ? seg[g] : (u32x4){0u, 0u, 0u, 0u};
+        }
+        if (u != blockIdx.x) __syncthreads();  // previous unit is done with lds_bases
+        const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
+        for (uint32_t t = threadIdx.x; t < nrows; t += kBlock) lds_bases[t] = brow[t];
+        __syncthreads();
+
+        uint8_t *plane = st.ws + (uint64_t)e * st.P;
+        const uint32_t variant = (st.wbits == 4 ? 0u : 3u) + st.row_mode;
+        switch (variant) {
+            case 0: expand_unit<4, kRowSplat>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+            case 1: expand_unit<4, kRowTwo>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+            case 2: expand_unit<4, kRowBytes>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+            case 3: expand_unit<1, kRowSplat>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+            case 4: expand_unit<1, kRowTwo>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+            default: expand_unit<1, kRowBytes>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+        }
+    }
+}
+
+// Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
+__device__ __forceinline__ uint32_t find_expert(const uint32_t *M, uint32_t k, uint32_t n,
+                                                uint32_t t) {
+    uint32_t lo = k, hi = k + 1, step = 1;
+    while (hi < n && M[hi] <= t) {
+        lo = hi;
+        step <<= 1;
+        hi = lo + step;
+    }
+    if (hi > n) hi = n;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (M[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: exception scatter.
+//
+// The entries of all active experts of both stacks form one index space
+// [0, N0 + N1), laid out by the wave-level prefixes M_s.  Workgroups take
+// chunks of kBlock*kExcPerLane consecutive indices; lane l handles index
+// t = chunk + l + i*kBlock, so each load instruction of a wave reads 64
+// consecutive entries.  Entry t of stack s belongs to the listed expert k with
+// M_s[k] <= t < M_s[k+1]; it is word prefix_s[act[k]] + (t - M_s[k]).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+    __shared__ uint32_t s_nact;
+
+    const uint32_t E = a.E;
+    const uint32_t ns = a.nstacks;
+    const uint32_t words = (E + 1u + 3u) & ~3u;  // one int32[E+1] map, padded to 16 B
+    int32_t *es = reinterpret_cast<int32_t *>(dyn_lds);
+    int32_t *p0 = es + words;
+    int32_t *p1 = p0 + words;
+    uint32_t *M0 = reinterpret_cast<uint32_t *>(p1 + words);
+    uint32_t *M1 = M0 + words;
+    uint16_t *act = reinterpret_cast<uint16_t *>(M1 + words);
+
+    const bool routed = a.expert_start != nullptr;
+    for (uint32_t i = threadIdx.x; i <= E; i += kBlock) {
+        if (routed) es[i] = a.expert_start[i];
+        p0[i] = a.st[0].prefix[i];
+        if (ns > 1) p1[i] = a.st[1].prefix[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t n = build_maps(routed ? es : nullptr, E, act, ns, p0, p1, a.st[0].n_exc,
+                                      ns > 1 ? a.st[1].n_exc : 0u, M0, M1);
+        if (threadIdx.x == 0) s_nact = n;
+    }
+    __syncthreads();
+    const uint32_t nact = s_nact;
+    if (nact == 0) return;
+    const uint32_t N0 = M0[nact];
+    const uint32_t N = N0 + (ns > 1 ? M1[nact] : 0u);
+    const uint32_t chunk = kBlock * kExcPerLane;
+
+    for (uint32_t c0 = blockIdx.x * chunk; c0 < N; c0 += gridDim.x * chunk) {
+        uint32_t word[kExcPerLane];
+        uint8_t *dst[kExcPerLane];
+        uint32_t k = 0, prev_s = 0;
+        // Locate every entry first so the loads below are all in flight together.
+#pragma unroll
+        for (int i = 0; i < kExcPerLane; ++i) {
+            const uint32_t t = c0 + threadIdx.x + i * kBlock;
+            dst[i] = nullptr;
+            if (t >= N) continue;
+            const uint32_t s = t >= N0 ? 1u : 0u;
+            const uint32_t tt = t - (s ? N0 : 0u);
+            if (s != prev_s) {
+                k = 0;
+                prev_s = s;
+            }
+            const uint32_t *M = s ? M1 : M0;
+            k = find_expert(M, k, nact, tt);
+            const uint32_t e = act[k];
+            const int32_t *pf = s ? p1 : p0;
+            const uint32_t idx = (uint32_t)pf[e] + (tt - M[k]);
+            const StackArgs st = pick(a, s);
+            if (idx < st.n_exc) {
+                word[i] = idx;
+                dst[i] = st.ws + (uint64_t)e * st.P;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kExcPerLane; ++i) {
+            if (dst[i] == nullptr) continue;
+            const uint32_t t = c0 + threadIdx.x + i * kBlock;
+            const uint32_t *exc = t >= N0 ? a.st[1].exc : a.st[0].exc;
+            word[i] = exc[word[i]];
+        }
+#pragma unroll
+        for (int i = 0; i < kExcPerLane; ++i) {
+            if (dst[i] == nullptr) continue;
+            const uint32_t t = c0 + threadIdx.x + i * kBlock;
+            const uint32_t P = t >= N0 ? a.st[1].P : a.st[0].P;
+            const uint32_t pos = word[i] >> 8;
+            if (pos < P) dst[i][pos] = (uint8_t)(word[i] & 0xffu);
+        }
+    }
+}
+
+}  // namespace
+
+size_t fixed_lds_bytes(const DecodeArgs &a) {
+    if (a.expert_start == nullptr) return 0;
+    return ((2u * a.E + 15u) & ~15u) + 4u * (a.E + 1u);
+}
+
+size_t exc_lds_bytes(const DecodeArgs &a) {
+    const size_t words = (a.E + 1u + 3u) & ~3u;
+    return 5u * 4u * words + 2u * a.E;
+}
+
+hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL(csf_fixed_kernel, dim3(grid), dim3(kBlock), fixed_lds_bytes(a), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL(csf_exc_kernel, dim3(grid), dim3(kBlock), exc_lds_bytes(a), stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace csf

@@ -1,0 +1,204 @@
+"""Host-side tests of the C ABI (no GPU): exports, the library encoder against
+the oracle encoder, the stream validator, and argument errors that must be
+returned before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+
+mwd = pytest.importorskip("moe_weight_decode_amd")
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "csf.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mwd.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csf_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(mwd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.csf_abi_version() == 1
+    for s in range(9):
+        assert lib.csf_status_str(s)
+    assert lib.csf_status_str(99) == b"unknown status"
+
+
+def _same_stack(a: dict, b: dict):
+    for k in ("fmt", "E", "R", "C", "stride"):
+        assert a[k] == b[k], k
+    for k in ("bases", "offsets", "exceptions", "prefix"):
+        assert np.array_equal(np.asarray(a[k]).ravel(), np.asarray(b[k]).ravel()), k
+
+
+ENCODE_CASES = [
+    ("tiny", workloads.NVFP4, lambda: workloads.TINY.generate()),
+    ("gate_slice", workloads.NVFP4, lambda: workloads.nvfp4_stack(6, 80, 128, 1, 0.03)),
+    ("down_slice", workloads.NVFP4, lambda: workloads.nvfp4_stack(6, 200, 50, 2, 0.10, hot_row_frac=0.01)),
+    ("mx_slice", workloads.MXFP4, lambda: workloads.mxfp4_stack(5, 100, 160, 4, 0.15)),
+    ("uniform_nv", workloads.NVFP4, lambda: workloads.uniform_bytes(3, 31, 37, 8)),
+    ("uniform_mx", workloads.MXFP4, lambda: workloads.uniform_bytes(3, 31, 37, 9)),
+    ("one_col", workloads.NVFP4, lambda: workloads.uniform_bytes(2, 7, 1, 10)),
+    ("c_eight", workloads.MXFP4, lambda: workloads.uniform_bytes(2, 3, 8, 11)),
+]
+
+
+@pytest.mark.parametrize("name,fmt,gen", ENCODE_CASES, ids=[c[0] for c in ENCODE_CASES])
+def test_library_encoder_matches_oracle(orc, name, fmt, gen):
+    x = gen()
+    lib_stack = mwd.prepare(x, fmt).numpy()
+    _same_stack(lib_stack, orc.encode(fmt, x))
+
+
+def test_library_encoder_two_column_exhaustive(orc):
+    a, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
+    x = np.stack([a.ravel(), b.ravel()], axis=1).astype(np.uint8).reshape(4, 16384, 2)
+    for fmt in (workloads.NVFP4, workloads.MXFP4):
+        _same_stack(mwd.prepare(x, fmt).numpy(), orc.encode(fmt, x))
+
+
+def test_prepare_sizes_closed_form():
+    x = workloads.TINY.generate()
+    st = mwd.prepare(x, workloads.NVFP4)
+    assert st.stride == 256 and st.offsets.numel() == 4 * 256
+    assert st.dense_bytes == 2048
+    assert st.compressed_bytes == 4 * 64 + 4 * 256 + 4 * st.num_exceptions + 4 * 5
+
+
+def test_validate_accepts_encoded_stacks():
+    for _, fmt, gen in ENCODE_CASES:
+        mwd.validate(mwd.prepare(gen(), fmt))
+
+
+def _corrupt(st, what):
+    st = st.clone()
+    exc = st.exceptions.numpy().view(np.uint32)
+    if what == "prefix_start":
+        st.prefix[0] = 1
+    elif what == "prefix_decreasing":
+        st.prefix[2] = st.prefix[1] - 1
+    elif what == "prefix_end":
+        st.prefix[-1] = st.prefix[-1] - 1
+    elif what == "unsorted":
+        exc[[0, 1]] = exc[[1, 0]]
+    elif what == "duplicate":
+        exc[1] = (exc[0] & ~np.uint32(0xFF)) | (exc[1] & np.uint32(0xFF))
+    elif what == "out_of_plane":
+        exc[int(st.prefix[1]) - 1] = np.uint32((st.P << 8) | 0x99)
+    elif what == "fits_window":
+        p = int(exc[0] >> 8)
+        base = int(st.bases[p // st.C])
+        exc[0] = np.uint32((p << 8) | base)
+    elif what == "field_at_exception":
+        p = int(exc[0] >> 8)
+        st.offsets[16 * (p // 32) + p % 16] |= np.uint8(1 << (4 * ((p % 32) // 16)))
+    return st
+
+
+@pytest.mark.parametrize("what", ["prefix_start", "prefix_decreasing", "prefix_end", "unsorted",
+                                  "duplicate", "out_of_plane", "fits_window", "field_at_exception"])
+def test_validate_rejects_corruption(what):
+    x = workloads.TINY.generate()
+    st = mwd.prepare(x, workloads.NVFP4)
+    bad = _corrupt(st, what)
+    with pytest.raises(mwd.CsfError) as ei:
+        mwd.validate(bad)
+    assert ei.value.name == "CSF_E_CORRUPT"
+
+
+def test_validate_rejects_fields_past_plane():
+    x = workloads.uniform_bytes(1, 5, 7, 3)  # P = 35: second group holds positions 32..63
+    st = mwd.prepare(x, workloads.NVFP4)
+    st.offsets[16 + 5] |= np.uint8(0x01)  # position 37
+    with pytest.raises(mwd.CsfError):
+        mwd.validate(st)
+
+
+def test_validate_rejects_wrapping_field():
+    x = np.full((1, 1, 4), 250, dtype=np.uint8)
+    st = mwd.prepare(x, workloads.NVFP4)
+    st.offsets[0] = 0x0F  # 250 + 15 > 255
+    with pytest.raises(mwd.CsfError):
+        mwd.validate(st)
+
+
+# --- decode argument errors: rejected on the host, before any HIP call -------
+
+def _fake(fmt=0, E=4, R=64, C=8, stride=256, n=10, bases=0x1000, offsets=0x2000, exc=0x3000,
+          prefix=0x4000):
+    d = mwd.csf_stack()
+    d.format, d.num_experts, d.rows, d.cols = fmt, E, R, C
+    d.offsets_stride, d.num_exceptions = stride, n
+    d.bases, d.offsets, d.exceptions, d.exc_prefix = bases, offsets, exc, prefix
+    return d
+
+
+DECODE_ERRORS = [
+    ("null_stack", None, 0x5000, "CSF_E_NULL"),
+    ("null_ws", _fake(), None, "CSF_E_NULL"),
+    ("null_offsets", _fake(offsets=None), 0x5000, "CSF_E_NULL"),
+    ("null_exc_with_entries", _fake(exc=None), 0x5000, "CSF_E_NULL"),
+    ("bad_format", _fake(fmt=5), 0x5000, "CSF_E_FORMAT"),
+    ("zero_experts", _fake(E=0), 0x5000, "CSF_E_SHAPE"),
+    ("negative_rows", _fake(R=-1), 0x5000, "CSF_E_SHAPE"),
+    ("plane_too_big", _fake(R=4096, C=4096, stride=16 * 524288), 0x5000, "CSF_E_SHAPE"),
+    ("too_many_experts", _fake(E=4096), 0x5000, "CSF_E_SHAPE"),
+    ("short_stride", _fake(stride=240), 0x5000, "CSF_E_SIZE"),
+    ("odd_stride", _fake(stride=264), 0x5000, "CSF_E_SIZE"),
+    ("negative_entries", _fake(n=-1), 0x5000, "CSF_E_SIZE"),
+    ("misaligned_offsets", _fake(offsets=0x2008), 0x5000, "CSF_E_ALIGN"),
+    ("misaligned_prefix", _fake(prefix=0x4002), 0x5000, "CSF_E_ALIGN"),
+    ("misaligned_exc", _fake(exc=0x3001), 0x5000, "CSF_E_ALIGN"),
+]
+
+
+@pytest.mark.parametrize("name,desc,ws,want", DECODE_ERRORS, ids=[e[0] for e in DECODE_ERRORS])
+def test_decode_rejects_bad_arguments(lib, name, desc, ws, want):
+    ref = ctypes.byref(desc) if desc is not None else None
+    st = lib.csf_decode(ref, ws, None, None)
+    assert mwd.STATUS[st] == want
+
+
+def test_paired_and_passes_errors(lib):
+    a, b = _fake(E=4), _fake(E=5)
+    assert mwd.STATUS[lib.csf_decode_paired(ctypes.byref(a), 0x5000, ctypes.byref(b), 0x6000, None,
+                                            None)] == "CSF_E_MISMATCH"
+    assert mwd.STATUS[lib.csf_decode_paired(ctypes.byref(a), 0x5000, None, 0x6000, None,
+                                            None)] == "CSF_E_NULL"
+    assert mwd.STATUS[lib.csf_decode_paired(ctypes.byref(a), 0x5000, ctypes.byref(a), None, None,
+                                            None)] == "CSF_E_NULL"
+    for passes in (0, 4, 7):
+        assert mwd.STATUS[lib.csf_decode_passes(ctypes.byref(a), 0x5000, None, None, None, passes,
+                                                None)] == "CSF_E_SIZE"
+    assert mwd.STATUS[lib.csf_decode(ctypes.byref(a), 0x5000, 0x7002, None)] == "CSF_E_ALIGN"
+
+
+def test_prepare_errors(lib):
+    sz = mwd.csf_sizes()
+    x = np.zeros((2, 3, 4), dtype=np.uint8)
+    st = lib.csf_prepare(9, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None)
+    assert mwd.STATUS[st] == "CSF_E_FORMAT"
+    st = lib.csf_prepare(0, 2, 0, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None)
+    assert mwd.STATUS[st] == "CSF_E_SHAPE"
+    st = lib.csf_prepare(0, 2, 3, 4, None, ctypes.byref(sz), None, None, None, None)
+    assert mwd.STATUS[st] == "CSF_E_NULL"
+    buf = np.zeros(64, dtype=np.uint8)
+    st = lib.csf_prepare(0, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), buf.ctypes.data, None, None, None)
+    assert mwd.STATUS[st] == "CSF_E_NULL"

@@ -1,0 +1,357 @@
+"""GPU parity: the HIP decoder, called through the C ABI, against the CPU oracle.
+
+Every comparison is byte-exact over whole planes.  Inputs come from the seeded
+generators; the compressed streams fed to the GPU are the oracle's encodings
+(and, separately, the library encoder's), and the expected bytes are the
+oracle's decode of the same stream (which the oracle pins tie to the input x).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+mwd = pytest.importorskip("moe_weight_decode_amd")
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0xA5
+GUARD = 0x5A
+GUARD_BYTES = 4096
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return torch.device("cuda:0")
+
+
+def upload(st: dict, dev) -> "mwd.CompressedStack":
+    return mwd.from_numpy(st, dev)
+
+
+def run_decode(stack, dev, es=None, fill=POISON, offset=0):
+    """Decode into a guarded workspace starting `offset` bytes into its buffer;
+    returns the dense bytes and asserts the guard bands are intact."""
+    n = stack.dense_bytes
+    buf = torch.full((GUARD_BYTES + offset + n + GUARD_BYTES,), GUARD, dtype=torch.uint8, device=dev)
+    ws = buf[GUARD_BYTES + offset: GUARD_BYTES + offset + n]
+    ws.fill_(fill)
+    es_t = None if es is None else torch.from_numpy(np.ascontiguousarray(es, dtype=np.int32)).to(dev)
+    mwd.decode(stack, ws, es_t)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert np.all(h[:GUARD_BYTES + offset] == GUARD), "write before the workspace"
+    assert np.all(h[GUARD_BYTES + offset + n:] == GUARD), "write past the workspace"
+    return h[GUARD_BYTES + offset: GUARD_BYTES + offset + n].reshape(stack.E, stack.R, stack.C)
+
+
+def oracle_expect(orc, st: dict, es=None, fill=POISON):
+    ws = np.full((st["E"], st["R"], st["C"]), fill, dtype=np.uint8)
+    return orc.decode(st, es, ws)
+
+
+def assert_bytes_equal(got, want, what=""):
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        e, r, c = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} bytes differ; first at expert {e} row {r} col {c}: "
+                             f"gpu {got[e, r, c]:#x} oracle {want[e, r, c]:#x}")
+
+
+# -- full-size and small stacks ------------------------------------------------
+
+_cache = {}
+
+
+def stack_case(name, orc):
+    if name not in _cache:
+        spec = workloads.STACKS[name]
+        x = spec.generate()
+        _cache[name] = (spec, x, orc.encode(spec.fmt, x))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "gate_nvfp4", "down_nvfp4", "mxfp4"])
+def test_full_decode_matches_oracle(orc, dev, name):
+    spec, x, st = stack_case(name, orc)
+    print(f"[parity] full decode {name} {x.shape} entries={st['exceptions'].size}", flush=True)
+    got = run_decode(upload(st, dev), dev)
+    want = oracle_expect(orc, st)
+    assert_bytes_equal(got, want, name)
+    assert_bytes_equal(got, x, name + " vs input")
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "down_nvfp4", "mxfp4"])
+def test_library_encoded_stream_decodes(orc, dev, name):
+    spec, x, st = stack_case(name, orc)
+    lib_stack = mwd.prepare(torch.from_numpy(x).to(dev), spec.fmt)
+    assert lib_stack.device.type == "cuda"  # preparation keeps the input's device
+    got = run_decode(lib_stack, dev)
+    assert_bytes_equal(got, x, name)
+
+
+RAGGED = [
+    # (fmt, E, R, C): plane sizes with tails, every row mode, tiny and wide planes
+    (workloads.NVFP4, 3, 5, 7),
+    (workloads.NVFP4, 2, 7, 50),
+    (workloads.NVFP4, 5, 33, 17),
+    (workloads.NVFP4, 4, 1, 1),
+    (workloads.NVFP4, 2, 300, 1),
+    (workloads.NVFP4, 3, 9, 8),
+    (workloads.NVFP4, 2, 41, 16),
+    (workloads.NVFP4, 1, 1000, 129),
+    (workloads.MXFP4, 3, 5, 7),
+    (workloads.MXFP4, 2, 65, 160),
+    (workloads.MXFP4, 3, 17, 18),
+    (workloads.MXFP4, 2, 700, 3),
+    (workloads.MXFP4, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("fmt,E,R,C", RAGGED, ids=[f"f{c[0]}_{c[1]}x{c[2]}x{c[3]}" for c in RAGGED])
+def test_ragged_uniform_bytes(orc, dev, fmt, E, R, C):
+    x = workloads.uniform_bytes(E, R, C, seed=E * 1000 + R * 10 + C)
+    st = orc.encode(fmt, x)
+    got = run_decode(upload(st, dev), dev)
+    assert_bytes_equal(got, oracle_expect(orc, st), "uniform")
+    assert_bytes_equal(got, x, "uniform vs input")
+
+
+@pytest.mark.parametrize("fmt,E,R,C", [(workloads.NVFP4, 3, 1000, 50), (workloads.MXFP4, 3, 800, 160),
+                                       (workloads.NVFP4, 2, 64, 8), (workloads.NVFP4, 2, 250, 130)])
+def test_generated_distributions_small(orc, dev, fmt, E, R, C):
+    if fmt == workloads.NVFP4:
+        x = workloads.nvfp4_stack(E, R, C, 21, 0.10, hot_row_frac=0.02)
+    else:
+        x = workloads.mxfp4_stack(E, R, C, 22, 0.15)
+    st = orc.encode(fmt, x)
+    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "generated")
+
+
+def test_largest_plane(orc, dev):
+    # R*C = 2^24 - 16: the largest plane an entry's 24-bit position can address
+    R, C = 1048575, 16
+    x = workloads.nvfp4_stack(1, R, C, 31, 0.05)
+    st = orc.encode(workloads.NVFP4, x)
+    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "largest plane")
+
+
+def test_most_experts(orc, dev):
+    x = workloads.nvfp4_stack(mwd.MAX_EXPERTS, 4, 24, 32, 0.2)
+    st = orc.encode(workloads.NVFP4, x)
+    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "2048 experts")
+    es = workloads.routing(mwd.MAX_EXPERTS, 300, 5, seed=33)
+    got = run_decode(upload(st, dev), dev, es=es)
+    assert_bytes_equal(got, oracle_expect(orc, st, es), "2048 experts routed")
+
+
+def test_no_exceptions(orc, dev):
+    x = workloads.nvfp4_stack(4, 64, 128, 5, 0.0)
+    st = orc.encode(workloads.NVFP4, x)
+    assert st["exceptions"].size == 0
+    stack = upload(st, dev)
+    assert stack.num_exceptions == 0 and stack.descriptor().exceptions is None
+    assert_bytes_equal(run_decode(stack, dev), x, "no exceptions")
+
+
+def test_alternative_bases(orc, dev):
+    rng = np.random.default_rng(41)
+    for fmt in (workloads.NVFP4, workloads.MXFP4):
+        x = workloads.uniform_bytes(3, 50, 50, 42 + fmt)
+        st = orc.encode_with_bases(fmt, x, rng.integers(0, 256, (3, 50), dtype=np.uint8))
+        assert_bytes_equal(run_decode(upload(st, dev), dev), x, "random bases")
+
+
+def test_arbitrary_offset_fields(orc, dev):
+    """Streams the encoder never writes (random fields everywhere, wrapping
+    sums, fields past the plane) still decode exactly as the oracle does."""
+    rng = np.random.default_rng(43)
+    for fmt, (E, R, C) in ((workloads.NVFP4, (3, 37, 50)), (workloads.MXFP4, (2, 21, 33))):
+        st = orc.encode(fmt, workloads.uniform_bytes(E, R, C, 44))
+        st = dict(st)
+        st["offsets"] = rng.integers(0, 256, st["offsets"].size, dtype=np.uint8)
+        st["bases"] = rng.integers(0, 256, st["bases"].size, dtype=np.uint8)
+        assert_bytes_equal(run_decode(upload(st, dev), dev), oracle_expect(orc, st), "random fields")
+
+
+def test_entries_outside_plane_are_dropped(orc, dev):
+    x = np.full((3, 2, 8), 0x40, dtype=np.uint8)
+    st = dict(orc.encode(workloads.NVFP4, x))
+    st["exceptions"] = np.array([(3 << 8) | 0x99, (16 << 8) | 0x77, (20 << 8) | 0x11,
+                                 (15 << 8) | 0x33, (1 << 23 | 5) << 8 | 0x44], dtype=np.uint32)
+    st["prefix"] = np.array([0, 3, 4, 5], dtype=np.int32)
+    for es in (None, np.array([0, 1, 1, 2], dtype=np.int32)):
+        got = run_decode(upload(st, dev), dev, es=es)
+        assert_bytes_equal(got, oracle_expect(orc, st, es), "out-of-plane entries")
+
+
+# -- routing -------------------------------------------------------------------
+
+def test_tiny_every_routed_subset(orc, dev):
+    spec, x, st = stack_case("tiny_nvfp4", orc)
+    stack = upload(st, dev)
+    for m in range(1 << spec.E):
+        mask = np.array([(m >> e) & 1 for e in range(spec.E)])
+        es = workloads.expert_start_from_mask(mask, tokens=2)
+        got = run_decode(stack, dev, es=es)
+        assert_bytes_equal(got, oracle_expect(orc, st, es), f"subset {mask}")
+
+
+def test_routed_garbage_expert_start(orc, dev):
+    spec, x, st = stack_case("tiny_nvfp4", orc)
+    es = np.array([0, 5, 5, 3, -7], dtype=np.int32)  # only expert 0 has tokens
+    got = run_decode(upload(st, dev), dev, es=es)
+    assert_bytes_equal(got, oracle_expect(orc, st, es), "garbage expert_start")
+
+
+def _paired(orc, dev, es, fill=POISON):
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev), upload(sd, dev)
+    wg = torch.full((g.dense_bytes,), fill, dtype=torch.uint8, device=dev)
+    wd = torch.full((d.dense_bytes,), fill, dtype=torch.uint8, device=dev)
+    es_t = None if es is None else torch.from_numpy(es).to(dev)
+    mwd.decode_paired(g, wg, d, wd, es_t)
+    torch.cuda.synchronize()
+    return (wg.cpu().numpy().reshape(xg.shape), wd.cpu().numpy().reshape(xd.shape),
+            oracle_expect(orc, sg, es, fill), oracle_expect(orc, sd, es, fill))
+
+
+def test_routed_paired_gate_down(orc, dev):
+    es = workloads.ROUTED.expert_start()
+    print(f"[parity] routed paired, active experts {np.nonzero(np.diff(es))[0].tolist()}", flush=True)
+    gg, gd, wg, wd = _paired(orc, dev, es)
+    assert_bytes_equal(gg, wg, "routed gate")
+    assert_bytes_equal(gd, wd, "routed down")
+    inactive = np.diff(es) <= 0
+    assert np.all(gg[inactive] == POISON) and np.all(gd[inactive] == POISON)
+
+
+def test_paired_full_and_all_inactive(orc, dev):
+    gg, gd, wg, wd = _paired(orc, dev, None)
+    assert_bytes_equal(gg, wg, "paired gate")
+    assert_bytes_equal(gd, wd, "paired down")
+    es = np.zeros(513, dtype=np.int32)
+    gg, gd, _, _ = _paired(orc, dev, es)
+    assert np.all(gg == POISON) and np.all(gd == POISON), "no expert routed: nothing written"
+
+
+def test_paired_all_active_equals_full(orc, dev):
+    es = workloads.expert_start_from_mask(np.ones(512, dtype=np.int64), tokens=1)
+    gg, gd, wg, wd = _paired(orc, dev, es)
+    _, xg, _ = stack_case("gate_nvfp4", orc)
+    _, xd, _ = stack_case("down_nvfp4", orc)
+    assert_bytes_equal(gg, xg, "all active gate")
+    assert_bytes_equal(gd, xd, "all active down")
+
+
+def test_paired_mixed_formats(orc, dev):
+    xa = workloads.nvfp4_stack(16, 100, 50, 51, 0.1)
+    xb = workloads.mxfp4_stack(16, 60, 160, 52, 0.15)
+    sa, sb = orc.encode(workloads.NVFP4, xa), orc.encode(workloads.MXFP4, xb)
+    a, b = upload(sa, dev), upload(sb, dev)
+    es = workloads.routing(16, 5, 9, seed=53)
+    wa = torch.full((a.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    wb = torch.full((b.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode_paired(a, wa, b, wb, torch.from_numpy(es).to(dev))
+    torch.cuda.synchronize()
+    assert_bytes_equal(wa.cpu().numpy().reshape(xa.shape), oracle_expect(orc, sa, es), "mixed a")
+    assert_bytes_equal(wb.cpu().numpy().reshape(xb.shape), oracle_expect(orc, sb, es), "mixed b")
+
+
+# -- workspace, passes, streams, graphs -----------------------------------------
+
+@pytest.mark.parametrize("offset", [1, 3, 7, 15])
+def test_odd_offset_workspace(orc, dev, offset):
+    for name in ("tiny_nvfp4", "mxfp4"):
+        spec, x, st = stack_case(name, orc)
+        got = run_decode(upload(st, dev), dev, offset=offset)
+        assert_bytes_equal(got, x, f"{name} at offset {offset}")
+    es = workloads.expert_start_from_mask(np.array([1, 0, 1, 1]), tokens=1)
+    spec, x, st = stack_case("tiny_nvfp4", orc)
+    got = run_decode(upload(st, dev), dev, es=es, offset=offset)
+    assert_bytes_equal(got, oracle_expect(orc, st, es), "routed odd offset")
+
+
+def test_passes_one_at_a_time(orc, dev):
+    spec, x, st = stack_case("down_nvfp4", orc)
+    stack = upload(st, dev)
+    ws = torch.full((stack.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode_passes(stack, ws, passes=mwd.PASS_FIXED)
+    torch.cuda.synchronize()
+    fixed_only = ws.cpu().numpy().reshape(x.shape)
+    # after the fixed stream alone every exception position holds its row base
+    no_exc = dict(st)
+    no_exc["exceptions"] = np.zeros(0, dtype=np.uint32)
+    no_exc["prefix"] = np.zeros(spec.E + 1, dtype=np.int32)
+    assert_bytes_equal(fixed_only, orc.decode(no_exc), "fixed pass")
+    mwd.decode_passes(stack, ws, passes=mwd.PASS_EXCEPTIONS)
+    torch.cuda.synchronize()
+    assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), x, "fixed then exceptions")
+
+
+def test_repeat_is_deterministic(orc, dev):
+    spec, x, st = stack_case("mxfp4", orc)
+    stack = upload(st, dev)
+    ws = torch.empty(stack.dense_bytes, dtype=torch.uint8, device=dev)
+    ref = torch.from_numpy(x.reshape(-1)).to(dev)
+    for i in range(20):
+        ws.fill_(i)
+        mwd.decode(stack, ws)
+        assert torch.equal(ws, ref), f"repeat {i}"
+
+
+def test_side_stream_ordering(orc, dev):
+    spec, x, st = stack_case("gate_nvfp4", orc)
+    stack = upload(st, dev)
+    ws = torch.full((stack.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        mwd.decode(stack, ws)  # current stream is the side stream
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.current_stream(dev).wait_event(done)
+    ref = torch.from_numpy(x.reshape(-1)).to(dev)
+    assert torch.equal(ws, ref)
+
+
+def test_graph_replay_follows_routing(orc, dev):
+    """One captured paired decode replayed with three routings, poisoned
+    workspaces in between; the library allocates nothing during capture."""
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev), upload(sd, dev)
+    wg = torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev)
+    wd = torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)
+    es_t = torch.zeros(513, dtype=torch.int32, device=dev)
+    routings = [workloads.ROUTED.expert_start(), workloads.routing(512, 40, 3, seed=61),
+                workloads.expert_start_from_mask(np.ones(512, dtype=np.int64))]
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):  # warm the launch path outside capture
+        mwd.decode_paired(g, wg, d, wd, es_t)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        # the capture context allocates graph-safe RNG state of its own; the
+        # decode call itself must allocate nothing
+        allocated, reserved = torch.cuda.memory_allocated(dev), torch.cuda.memory_reserved(dev)
+        mwd.decode_paired(g, wg, d, wd, es_t)
+        assert torch.cuda.memory_allocated(dev) == allocated
+        assert torch.cuda.memory_reserved(dev) == reserved
+    for rnd in range(2):
+        for i, es in enumerate(routings):
+            wg.fill_(POISON)
+            wd.fill_(POISON)
+            es_t.copy_(torch.from_numpy(es))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert_bytes_equal(wg.cpu().numpy().reshape(xg.shape), oracle_expect(orc, sg, es),
+                               f"replay {rnd}.{i} gate")
+            assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), oracle_expect(orc, sd, es),
+                               f"replay {rnd}.{i} down")
