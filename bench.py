@@ -1,23 +1,27 @@
 """Benchmark of the CSF block-scale decoder on one MI355X.
 
-One step = one full decode (fixed-stream pass + exception pass) of the
-512-expert gate-like NVFP4 stack (512 x 800 x 128 E4M3 scale bytes, 3 %
-outliers) into its dense workspace.  Steps rotate over several device copies
-of the compressed stack and workspace (together larger than the 256 MB
-Infinity Cache), so every step reads and writes HBM.
+One step = one full decode of the 512-expert gate-like NVFP4 stack (512 x 800
+x 128 E4M3 scale bytes, 3 % outliers, with its tile index) into its dense
+workspace: a single launch of the fused kernel (fixed stream + exceptions
+patched on chip).  Steps rotate over several device copies of the compressed
+stack and workspace (together larger than the 256 MB Infinity Cache), so
+every step reads and writes HBM.
 
 Prints ONE JSON line on stdout:
   value       whole-run throughput, GB/s = (compressed bytes read + dense
               bytes written) per step x steps / elapsed time
-  roofline    the fixed-stream kernel (the dominant one): its algorithmic
-              bytes per launch / its mean launch time from HIP events on its
-              stream, against the MI355X HBM3E peak (8 TB/s)
+  roofline    the fused kernel (the only kernel of a step): its algorithmic
+              bytes per launch / its mean launch time, from two HIP events on
+              its stream bracketing the back-to-back launches of the timed
+              region (no event sits between two launches), against the MI355X
+              HBM3E peak (8 TB/s)
   cpu_baseline the CPU oracle decoding the same stack on one host core
 
   python bench.py [--steps K] [--warmup W] [--sets N] [--all] [--no-cpu]
 
 --all also measures the other workloads (down-like, MXFP4, routed paired,
-tiny) and a plain copy, one line each on stderr.
+tiny), the two-pass decode of each (fixed-stream kernel, then exception
+kernel), and a plain copy; one line each on stderr.
 """
 from __future__ import annotations
 
@@ -79,9 +83,11 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def stack_bytes(stack, active=None, es_bytes=0):
-    """Algorithmic bytes of one decode: (fixed-stream bytes, exception bytes,
-    dense bytes).  active: boolean mask of routed experts, or None for all."""
+def stack_bytes(stack, active=None):
+    """Algorithmic bytes of one decode: (fixed-stream bytes read, exception
+    bytes read, dense bytes written).  Exception bytes include the prefix and,
+    for an indexed stack, the tile index.  active: boolean mask of routed
+    experts, or None for all."""
     import numpy as np
     E = stack.E
     n_act = E if active is None else int(np.count_nonzero(active))
@@ -90,9 +96,11 @@ def stack_bytes(stack, active=None, es_bytes=0):
         entries = stack.num_exceptions
     else:
         entries = int(np.diff(prefix)[np.asarray(active, dtype=bool)].sum())
-    fixed = n_act * (stack.R + stack.stride)          # bases + offsets read
-    exc = 4 * entries + 4 * (E + 1)                   # entries + prefix read
-    dense = n_act * stack.P                           # written
+    fixed = n_act * (stack.R + stack.stride)          # bases + offsets
+    exc = 4 * entries + 4 * (E + 1)                   # entries + prefix
+    if stack.tile_index is not None:
+        exc += 4 * (E * stack.index_tiles + 1)
+    dense = n_act * stack.P
     return fixed, exc, dense
 
 
@@ -126,41 +134,37 @@ def make_sets(mwd, torch, stack, nsets, dev):
     return sets
 
 
-def timed_loop(mwd, torch, ev, launches, steps, warmup, per_pass=True):
-    """Run `steps` steps (after `warmup`), rotating over `launches`.  Returns
-    (wall ms per step, event ms per step, [fixed-pass ms], [exception-pass ms]).
-    With per_pass, an event pair brackets each pass on the launch stream."""
-    stream = launches[0].stream
+def timed_loop(torch, ev, calls, steps, warmup):
+    """Run `steps` calls (after `warmup`), rotating over `calls`, with one HIP
+    event before and one after the whole run on the launch stream.  Returns
+    (wall-clock ms per step, event ms per step)."""
+    stream = calls[0].stream
     for i in range(warmup):
-        launches[i % len(launches)]()
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
-    evs = ev.create(2 * steps + 2 if per_pass else 2)
-    rec = ev.record
-    FIXED, EXC = mwd.PASS_FIXED, mwd.PASS_EXCEPTIONS
+    evs = ev.create(2)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    rec(evs[-2], stream)
-    if per_pass:
-        for i in range(steps):
-            L = launches[i % len(launches)]
-            rec(evs[2 * i], stream)
-            L(FIXED)
-            rec(evs[2 * i + 1], stream)
-            L(EXC)
-    else:
-        for i in range(steps):
-            launches[i % len(launches)]()
-    rec(evs[-1], stream)
+    ev.record(evs[0], stream)
+    n = len(calls)
+    for i in range(steps):
+        calls[i % n]()
+    ev.record(evs[1], stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    total_ms = ev.ms(evs[-2], evs[-1])
-    fixed, exc = [], []
-    if per_pass:
-        for i in range(steps):
-            fixed.append(ev.ms(evs[2 * i], evs[2 * i + 1]))
-            nxt = evs[2 * (i + 1)] if i + 1 < steps else evs[-1]
-            exc.append(ev.ms(evs[2 * i + 1], nxt))
+    total_ms = ev.ms(evs[0], evs[1])
     ev.destroy(evs)
-    return wall_ms / steps, total_ms / steps, fixed, exc
+    return wall_ms / steps, total_ms / steps
+
+
+class Passes:
+    """A Launch restricted to some passes (for the two-pass split)."""
+
+    def __init__(self, launch, passes):
+        self.launch, self.passes, self.stream = launch, passes, launch.stream
+
+    def __call__(self):
+        self.launch(self.passes)
 
 
 def check_equal(torch, ws, x, what):
@@ -170,7 +174,9 @@ def check_equal(torch, ws, x, what):
         raise SystemExit(f"{what}: GPU decode differs from the input in {(got != x).sum()} bytes")
 
 
-def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev):
+def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
+    """Time the full decode of `spec` (fused, indexed stack); with `split`
+    also the two-pass decode of the same stack and its fixed pass alone."""
     x = spec.generate()
     stack = mwd.prepare(x, spec.fmt).to(dev)
     sets = make_sets(mwd, torch, stack, nsets, dev)
@@ -178,13 +184,19 @@ def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev):
     launches[0]()
     torch.cuda.synchronize()
     check_equal(torch, sets[0][1], x, spec.name)
-    wall, evt, fixed, exc = timed_loop(mwd, torch, ev, launches, steps, warmup)
+    wall, evt = timed_loop(torch, ev, launches, steps, warmup)
     fb, eb, db = stack_bytes(stack)
-    step_ms = max(wall, evt)
-    return dict(x=x, stack=stack, fixed_bytes=fb, exc_bytes=eb, dense_bytes=db,
-                step_ms=step_ms, wall_ms=wall, event_ms=evt,
-                fixed_ms=statistics.mean(fixed), fixed_ms_median=statistics.median(fixed),
-                exc_ms=statistics.mean(exc), launches=launches, sets=sets)
+    out = dict(x=x, stack=stack, fixed_bytes=fb, exc_bytes=eb, dense_bytes=db,
+               step_ms=max(wall, evt), wall_ms=wall, event_ms=evt)
+    if split:
+        two = [mwd.Launch(s.without_index(), ws) for s, ws in sets]
+        two[0]()
+        torch.cuda.synchronize()
+        check_equal(torch, sets[0][1], x, spec.name + " two-pass")
+        w2, e2 = timed_loop(torch, ev, two, steps, warmup)
+        wf, ef = timed_loop(torch, ev, [Passes(L, mwd.PASS_FIXED) for L in two], steps, warmup)
+        out.update(two_pass_ms=max(w2, e2), fixed_only_ms=max(wf, ef))
+    return out
 
 
 def cpu_baseline(spec, x, budget_s=10.0):
@@ -211,12 +223,12 @@ def cpu_baseline(spec, x, budget_s=10.0):
                        f"times on one host core, median")
 
 
-def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev):
+def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True):
     import numpy as np
     gspec, dspec = workloads.ROUTED.stacks
     xg, xd = gspec.generate(), dspec.generate()
-    g = mwd.prepare(xg, gspec.fmt).to(dev)
-    d = mwd.prepare(xd, dspec.fmt).to(dev)
+    g = mwd.prepare(xg, gspec.fmt, index=indexed).to(dev)
+    d = mwd.prepare(xd, dspec.fmt, index=indexed).to(dev)
     es = workloads.ROUTED.expert_start()
     es_t = torch.from_numpy(es).to(dev)
     wg = torch.full((g.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
@@ -230,11 +242,10 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev):
     if not (np.array_equal(hg[active], xg[active]) and np.all(hg[~active] == 0xA5)
             and np.array_equal(hd[active], xd[active]) and np.all(hd[~active] == 0xA5)):
         raise SystemExit("routed paired decode is wrong")
-    wall, evt, fixed, exc = timed_loop(mwd, torch, ev, [L], steps, warmup)
+    wall, evt = timed_loop(torch, ev, [L], steps, warmup)
     b = [stack_bytes(s, active) for s in (g, d)]
     total = sum(f + e + dn for f, e, dn in b) + 4 * len(es)
-    return dict(step_ms=max(wall, evt), bytes=total, fixed_ms=statistics.mean(fixed),
-                exc_ms=statistics.mean(exc), active=int(active.sum()))
+    return dict(step_ms=max(wall, evt), bytes=total, active=int(active.sum()))
 
 
 def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
@@ -280,12 +291,11 @@ def main():
     stack = r["stack"]
     step_bytes = r["fixed_bytes"] + r["exc_bytes"] + r["dense_bytes"]
     gbps = step_bytes / (r["step_ms"] * 1e-3) / 1e9
-    fixed_alg = r["fixed_bytes"] + r["dense_bytes"]
-    achieved = fixed_alg / (r["fixed_ms"] * 1e-3) / 1e9
+    launch_us = r["event_ms"] * 1e3
+    achieved = step_bytes / (r["event_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
-        f"{r['event_ms'] * 1e3:.2f}); fixed pass {r['fixed_ms'] * 1e3:.2f} us, exception pass "
-        f"{r['exc_ms'] * 1e3:.2f} us; {gbps:.1f} GB/s")
-    traffic = pmc_traffic("csf_fixed_kernel", spec.name)
+        f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
+    traffic = pmc_traffic("csf_fused_kernel", spec.name)
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -304,56 +314,61 @@ def main():
             "workload": f"{spec.name}: full-stack CSF decode of {spec.E} experts x {spec.R} rows x "
                         f"{spec.C} E4M3 scale columns (K={spec.K}), 3% outliers, seed {spec.seed}",
             "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": "NVFP4 (E4M3 scales)",
+            "decode": "single pass (fused kernel, tile index)",
             "exception_entries": stack.num_exceptions,
             "compressed_bytes": r["fixed_bytes"] + r["exc_bytes"],
             "dense_bytes": r["dense_bytes"],
             "bytes_per_step": step_bytes,
             "rotating_sets": args.sets,
-            "fixed_pass_us": round(r["fixed_ms"] * 1e3, 3),
-            "exception_pass_us": round(r["exc_ms"] * 1e3, 3),
         },
         "roofline": {
-            "kernel": "csf_fixed_kernel",
+            "kernel": "csf_fused_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": fixed_alg,
-            "mean_launch_us": round(r["fixed_ms"] * 1e3, 3),
+            "algorithmic_bytes_per_launch": step_bytes,
+            "mean_launch_us": round(launch_us, 3),
         },
     }
     if args.all:
         extra = {}
-        for name in ("down_nvfp4", "mxfp4", "tiny_nvfp4"):
+        del r
+        for name in ("gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4"):
             s = workloads.STACKS[name]
             log(f"[bench] {name}")
             rr = bench_stack(mwd, torch, ev, s, min(args.steps, 2000), args.warmup,
-                             args.sets if s.E > 4 else 2, dev)
+                             args.sets if s.E > 4 else 2, dev, split=True)
             b = rr["fixed_bytes"] + rr["exc_bytes"] + rr["dense_bytes"]
-            extra[name] = dict(us=round(rr["step_ms"] * 1e3, 2), gbps=round(b / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                               fixed_us=round(rr["fixed_ms"] * 1e3, 2), exc_us=round(rr["exc_ms"] * 1e3, 2),
+            extra[name] = dict(us=round(rr["step_ms"] * 1e3, 2),
+                               gbps=round(b / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                               two_pass_us=round(rr["two_pass_ms"] * 1e3, 2),
+                               fixed_only_us=round(rr["fixed_only_ms"] * 1e3, 2),
                                bytes=b, entries=rr["stack"].num_exceptions)
             log(f"[bench] {name}: {extra[name]}")
             del rr
             torch.cuda.empty_cache()
-        log("[bench] routed_paired")
-        rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev)
-        extra["routed_paired"] = dict(us=round(rr["step_ms"] * 1e3, 2),
-                                      gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                                      fixed_us=round(rr["fixed_ms"] * 1e3, 2),
-                                      exc_us=round(rr["exc_ms"] * 1e3, 2), bytes=rr["bytes"],
-                                      active=rr["active"])
-        log(f"[bench] routed_paired: {extra['routed_paired']}")
+        for indexed in (True, False):
+            key = "routed_paired" + ("" if indexed else "_two_pass")
+            log(f"[bench] {key}")
+            rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed)
+            extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2),
+                              gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                              bytes=rr["bytes"], active=rr["active"])
+            log(f"[bench] {key}: {extra[key]}")
         cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
         extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
         log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
         os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
         json.dump(extra, open(os.path.join(ROOT, "gpurun_out", "bench_all.json"), "w"), indent=1)
+        x_head = spec.generate()
+    else:
+        x_head = r["x"]
     if not args.no_cpu:
         log(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(spec, r["x"], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(spec, x_head, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

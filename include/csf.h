@@ -20,8 +20,16 @@
  *                                    [w*f, w*f + w) with f = (p % G) / 16
  *   exceptions  u32[n]               (p << 8) | byte, expert-major, ascending p
  *   exc_prefix  i32[E + 1]           exclusive prefix of per-expert entry counts
+ *   tile_index  i32[E * NT + 1]      optional; NT = ceil(P / CSF_INDEX_TILE):
+ *                                    tile_index[e*NT + j] = exc_prefix[e] +
+ *                                    #{entries of e with p < j*CSF_INDEX_TILE},
+ *                                    tile_index[E*NT] = n
  *   dense       u8[E][R][C]          plane e at workspace + e * P
- * Fields at exception positions and past the plane are zero.
+ * Fields at exception positions and past the plane are zero.  The tile index
+ * is the exception index built at preparation ("Load native FP4 experts with
+ * optional lossless CSF scales", vLLM PR 964, preparation paragraphs; PR 478
+ * commits on indexed reconstruction with exception lookup); it lets the
+ * decoder patch every exception before the dense bytes are stored.
  *
  * Error behaviour: every function returns a csf_status; nothing aborts and no
  * C++ exception crosses this boundary.  Decode functions check their arguments
@@ -38,7 +46,10 @@
 extern "C" {
 #endif
 
-#define CSF_ABI_VERSION 1
+#define CSF_ABI_VERSION 2
+
+/* Positions per exception-index tile. */
+#define CSF_INDEX_TILE 2048
 
 /* Largest expert count a decode accepts (routing maps are kept on chip). */
 #define CSF_MAX_EXPERTS 2048
@@ -69,13 +80,16 @@ typedef struct csf_sizes {
     int64_t num_exceptions;    /* entries */
     int64_t exceptions_bytes;  /* 4 * num_exceptions */
     int64_t prefix_bytes;      /* 4 * (E + 1) */
-    int64_t compressed_bytes;  /* bases + offsets + exceptions + prefix */
+    int64_t index_tiles;       /* NT = ceil(R * C / CSF_INDEX_TILE) per expert */
+    int64_t index_bytes;       /* 4 * (E * NT + 1) */
+    int64_t compressed_bytes;  /* bases + offsets + exceptions + prefix + index */
 } csf_sizes;
 
 /*
  * Descriptor of one compressed stack.  The struct itself lives in host memory
  * and is copied into the kernel arguments; the pointers are device pointers.
- * exceptions may be NULL iff num_exceptions == 0.
+ * exceptions may be NULL iff num_exceptions == 0.  tile_index may be NULL:
+ * the decode then runs the fixed stream and the exception pass as two kernels.
  */
 typedef struct csf_stack {
     int32_t format;
@@ -88,6 +102,7 @@ typedef struct csf_stack {
     const uint8_t *offsets;
     const uint32_t *exceptions;
     const int32_t *exc_prefix;
+    const int32_t *tile_index;
 } csf_stack;
 
 int csf_abi_version(void);
@@ -96,17 +111,27 @@ const char *csf_status_str(csf_status status);
 /*
  * Encode a dense stack (PR 1236, API paragraph: the preparation helper).
  * dense_host: u8[E][R][C] in host memory.  Two-call pattern: with bases,
- * offsets, exceptions and exc_prefix all NULL only *out_sizes is filled; with
- * all four non-NULL (host buffers of at least the reported sizes;
- * exceptions may be NULL when num_exceptions is 0) the stack is encoded.  Any
- * other mix returns CSF_E_NULL.  The output is deterministic: the base of a row
+ * offsets, exceptions, exc_prefix and tile_index all NULL only *out_sizes is
+ * filled; with bases, offsets and exc_prefix non-NULL (host buffers of at least
+ * the reported sizes; exceptions may be NULL only when num_exceptions is 0)
+ * the stack is encoded, and the tile index too when tile_index is non-NULL.
+ * Any other mix returns CSF_E_NULL.  The output is deterministic: the base of a row
  * is the row value v with the most row values in [v, v + 2^w - 1], ties to the
  * smallest v.  Host memory only; the caller copies the buffers to the device.
  * Errors: CSF_E_FORMAT, CSF_E_SHAPE, CSF_E_NULL.
  */
 csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
                        const uint8_t *dense_host, csf_sizes *out_sizes, uint8_t *bases,
-                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix);
+                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix,
+                       int32_t *tile_index);
+
+/*
+ * Build the tile index of a stack on the GPU from its exceptions and prefix
+ * (device buffers, as in the descriptor; compressed->tile_index is ignored),
+ * into device int32[E * NT + 1] at tile_index.  For streams prepared without an
+ * index.  Enqueued on hip_stream; allocates nothing.  Errors as csf_decode.
+ */
+csf_status csf_build_index(const csf_stack *compressed, int32_t *tile_index, void *hip_stream);
 
 /*
  * Expand a compressed stack into the dense workspace (PR 1236, API paragraph:
@@ -119,10 +144,12 @@ csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_
  *   paragraph: odd-offset workspace).
  * expert_start: NULL, or device int32[E + 1]; expert e is expanded iff
  *   expert_start[e + 1] > expert_start[e].  It is read on the device only.
- * hip_stream: a hipStream_t (NULL = the null stream).  The call enqueues the
- *   fixed-stream kernel then the exception kernel and returns; it allocates
- *   nothing, synchronises nothing and keeps no state, so it can be captured in
- *   a HIP graph.  The caller orders other users of the workspace.
+ * hip_stream: a hipStream_t (NULL = the null stream).  With a tile index the
+ *   call enqueues one kernel that writes every dense byte once (exceptions are
+ *   patched on chip); without one, the fixed-stream kernel then the exception
+ *   kernel.  It returns after enqueueing; it allocates nothing, synchronises
+ *   nothing and keeps no state, so it can be captured in a HIP graph.  The
+ *   caller orders other users of the workspace.
  * Errors: CSF_E_NULL, CSF_E_FORMAT, CSF_E_SHAPE, CSF_E_SIZE, CSF_E_ALIGN,
  *   CSF_E_HIP (launch refused).
  */
@@ -134,7 +161,8 @@ csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace,
  * single launch covering both stacks (PR 478, commit messages: decode only
  * routed experts and pair gate/up and down scales without adding streams).
  * Formats and shapes may differ between the stacks; expert counts must match
- * (CSF_E_MISMATCH).  expert_start is shared and may be NULL.  Otherwise as
+ * (CSF_E_MISMATCH).  expert_start is shared and may be NULL.  The single-pass
+ * kernel is used when both stacks carry a tile index.  Otherwise as
  * csf_decode.
  */
 csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up,
@@ -147,11 +175,13 @@ csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up,
 #define CSF_PASS_ALL 3u
 
 /*
- * The passes csf_decode / csf_decode_paired enqueue, selectable one at a time
- * so a caller can schedule or time them separately.  second may be NULL (then
- * ws_second is ignored).  CSF_PASS_EXCEPTIONS is only meaningful after
- * CSF_PASS_FIXED of the same call arguments has run earlier in stream order.
- * passes must be a non-zero subset of CSF_PASS_ALL (else CSF_E_SIZE).
+ * The two passes of the unindexed decode, selectable one at a time so a caller
+ * can schedule or time them separately: CSF_PASS_FIXED enqueues the fixed
+ * stream alone, CSF_PASS_EXCEPTIONS the exception pass alone (meaningful only
+ * after CSF_PASS_FIXED of the same arguments, earlier in stream order; it needs
+ * no tile index).  CSF_PASS_ALL is exactly csf_decode / csf_decode_paired.
+ * second may be NULL (then ws_second is ignored).  passes must be a non-zero
+ * subset of CSF_PASS_ALL (else CSF_E_SIZE).
  */
 csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first,
                              const csf_stack *second, uint8_t *ws_second,
@@ -163,7 +193,8 @@ csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first,
  * starts at 0, is non-decreasing and ends at num_exceptions; entries ascend
  * strictly within each expert and stay inside the plane; no entry byte lies in
  * its row's offset window; offset fields past the plane and at exception
- * positions are zero.  Returns CSF_E_CORRUPT on a violation.  Not called by the
+ * positions are zero, and no field makes base + field exceed 255; the tile
+ * index, when present, equals the one the entries define.  Returns CSF_E_CORRUPT on a violation.  Not called by the
  * decoder, which never reads device memory from the host.
  */
 csf_status csf_validate(const csf_stack *host_copy);

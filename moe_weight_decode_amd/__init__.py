@@ -15,7 +15,12 @@ The functions mirror the C ABI in ``include/csf.h``:
 * ``decode(stack, workspace, expert_start=None, stream=None)``;
 * ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``;
 * ``decode_passes(...)`` to enqueue the fixed-stream or exception pass alone;
+* ``build_index(stack)`` (the per-tile exception index, built on the GPU);
 * ``validate(stack)`` (host-side layout check).
+
+A stack with a tile index decodes in one kernel that writes every dense byte
+once; without one the decode runs the fixed stream and the exception pass as
+two kernels.
 """
 from __future__ import annotations
 
@@ -32,14 +37,15 @@ PASS_FIXED = 1
 PASS_EXCEPTIONS = 2
 PASS_ALL = 3
 MAX_EXPERTS = 2048
+INDEX_TILE = 2048
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsf.so")
 
 STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: "CSF_E_SIZE",
           5: "CSF_E_ALIGN", 6: "CSF_E_CORRUPT", 7: "CSF_E_MISMATCH", 8: "CSF_E_HIP"}
 
-EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_decode", "csf_decode_paired",
-           "csf_decode_passes", "csf_validate")
+EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_build_index", "csf_decode",
+           "csf_decode_paired", "csf_decode_passes", "csf_validate")
 
 
 class CsfError(RuntimeError):
@@ -54,7 +60,8 @@ class csf_sizes(ctypes.Structure):
     _fields_ = [("dense_bytes", ctypes.c_int64), ("bases_bytes", ctypes.c_int64),
                 ("offsets_stride", ctypes.c_int64), ("offsets_bytes", ctypes.c_int64),
                 ("num_exceptions", ctypes.c_int64), ("exceptions_bytes", ctypes.c_int64),
-                ("prefix_bytes", ctypes.c_int64), ("compressed_bytes", ctypes.c_int64)]
+                ("prefix_bytes", ctypes.c_int64), ("index_tiles", ctypes.c_int64),
+                ("index_bytes", ctypes.c_int64), ("compressed_bytes", ctypes.c_int64)]
 
 
 class csf_stack(ctypes.Structure):
@@ -62,7 +69,8 @@ class csf_stack(ctypes.Structure):
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
                 ("offsets_stride", ctypes.c_int64), ("num_exceptions", ctypes.c_int64),
                 ("bases", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
-                ("exceptions", ctypes.c_void_p), ("exc_prefix", ctypes.c_void_p)]
+                ("exceptions", ctypes.c_void_p), ("exc_prefix", ctypes.c_void_p),
+                ("tile_index", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -80,7 +88,9 @@ def _lib():
         lib.csf_status_str.restype = ctypes.c_char_p
         lib.csf_status_str.argtypes = [ctypes.c_int]
         lib.csf_prepare.restype = ctypes.c_int
-        lib.csf_prepare.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(csf_sizes), vp, vp, vp, vp]
+        lib.csf_prepare.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(csf_sizes), vp, vp, vp, vp, vp]
+        lib.csf_build_index.restype = ctypes.c_int
+        lib.csf_build_index.argtypes = [ctypes.POINTER(csf_stack), vp, vp]
         lib.csf_decode.restype = ctypes.c_int
         lib.csf_decode.argtypes = [ctypes.POINTER(csf_stack), vp, vp, vp]
         lib.csf_decode_paired.restype = ctypes.c_int
@@ -113,6 +123,11 @@ class CompressedStack:
     offsets: torch.Tensor     # uint8 [E*stride]
     exceptions: torch.Tensor  # int32 [max(n, 1)], holding the u32 entry words
     prefix: torch.Tensor      # int32 [E+1]
+    tile_index: torch.Tensor | None = None  # int32 [E*index_tiles + 1], optional
+
+    @property
+    def index_tiles(self) -> int:
+        return (self.R * self.C + INDEX_TILE - 1) // INDEX_TILE
 
     @property
     def P(self) -> int:
@@ -124,21 +139,31 @@ class CompressedStack:
 
     @property
     def compressed_bytes(self) -> int:
-        return self.E * self.R + self.E * self.stride + 4 * self.num_exceptions + 4 * (self.E + 1)
+        n = self.E * self.R + self.E * self.stride + 4 * self.num_exceptions + 4 * (self.E + 1)
+        if self.tile_index is not None:
+            n += 4 * (self.E * self.index_tiles + 1)
+        return n
 
     @property
     def device(self) -> torch.device:
         return self.offsets.device
 
-    def to(self, device) -> "CompressedStack":
-        mv = lambda t: t.to(device, non_blocking=False).contiguous()
+    def _map(self, fn) -> "CompressedStack":
         return CompressedStack(self.fmt, self.E, self.R, self.C, self.stride, self.num_exceptions,
-                               mv(self.bases), mv(self.offsets), mv(self.exceptions), mv(self.prefix))
+                               fn(self.bases), fn(self.offsets), fn(self.exceptions), fn(self.prefix),
+                               None if self.tile_index is None else fn(self.tile_index))
+
+    def to(self, device) -> "CompressedStack":
+        return self._map(lambda t: t.to(device, non_blocking=False).contiguous())
 
     def clone(self) -> "CompressedStack":
-        return CompressedStack(self.fmt, self.E, self.R, self.C, self.stride, self.num_exceptions,
-                               self.bases.clone(), self.offsets.clone(), self.exceptions.clone(),
-                               self.prefix.clone())
+        return self._map(lambda t: t.clone())
+
+    def without_index(self) -> "CompressedStack":
+        """The same stack with no tile index (decoded by the two-pass kernels)."""
+        st = self._map(lambda t: t)
+        st.tile_index = None
+        return st
 
     def descriptor(self) -> csf_stack:
         d = csf_stack()
@@ -148,18 +173,23 @@ class CompressedStack:
         d.offsets = self.offsets.data_ptr()
         d.exceptions = self.exceptions.data_ptr() if self.num_exceptions > 0 else None
         d.exc_prefix = self.prefix.data_ptr()
+        d.tile_index = self.tile_index.data_ptr() if self.tile_index is not None else None
         return d
 
     def numpy(self) -> dict:
         """Host copies of the buffers (uint32 entries)."""
-        return dict(fmt=self.fmt, E=self.E, R=self.R, C=self.C, stride=self.stride,
-                    bases=self.bases.cpu().numpy().copy(), offsets=self.offsets.cpu().numpy().copy(),
-                    exceptions=self.exceptions.cpu().numpy()[:self.num_exceptions].view(np.uint32).copy(),
-                    prefix=self.prefix.cpu().numpy().copy())
+        d = dict(fmt=self.fmt, E=self.E, R=self.R, C=self.C, stride=self.stride,
+                 bases=self.bases.cpu().numpy().copy(), offsets=self.offsets.cpu().numpy().copy(),
+                 exceptions=self.exceptions.cpu().numpy()[:self.num_exceptions].view(np.uint32).copy(),
+                 prefix=self.prefix.cpu().numpy().copy())
+        if self.tile_index is not None:
+            d["tile_index"] = self.tile_index.cpu().numpy().copy()
+        return d
 
 
 def from_numpy(d: dict, device="cpu") -> CompressedStack:
-    """Wrap host arrays (``fmt, E, R, C, stride, bases, offsets, exceptions, prefix``)."""
+    """Wrap host arrays (``fmt, E, R, C, stride, bases, offsets, exceptions, prefix`` and
+    optionally ``tile_index``)."""
     exc = np.ascontiguousarray(d["exceptions"], dtype=np.uint32)
     n = int(exc.size)
     exc_t = torch.from_numpy(exc.view(np.int32).copy() if n else np.zeros(1, dtype=np.int32))
@@ -168,6 +198,8 @@ def from_numpy(d: dict, device="cpu") -> CompressedStack:
                          torch.from_numpy(np.ascontiguousarray(d["offsets"], dtype=np.uint8).copy()),
                          exc_t,
                          torch.from_numpy(np.ascontiguousarray(d["prefix"], dtype=np.int32).copy()))
+    if d.get("tile_index") is not None:
+        st.tile_index = torch.from_numpy(np.ascontiguousarray(d["tile_index"], dtype=np.int32).copy())
     return st.to(device) if str(device) != "cpu" else st
 
 
@@ -176,9 +208,10 @@ def _check(status: int, where: str):
         raise CsfError(status, where)
 
 
-def prepare(dense, fmt: int) -> CompressedStack:
+def prepare(dense, fmt: int, index: bool = True) -> CompressedStack:
     """Encode ``dense`` (uint8 [E, R, C], tensor or array) with the library's
-    encoder; the result lives on ``dense``'s device."""
+    encoder, with the tile index unless ``index`` is False; the result lives on
+    ``dense``'s device."""
     lib = _lib()
     device = dense.device if isinstance(dense, torch.Tensor) else torch.device("cpu")
     x = dense.detach().cpu().numpy() if isinstance(dense, torch.Tensor) else np.asarray(dense)
@@ -187,17 +220,19 @@ def prepare(dense, fmt: int) -> CompressedStack:
     x = np.ascontiguousarray(x)
     E, R, C = (int(v) for v in x.shape)
     sz = csf_sizes()
-    _check(lib.csf_prepare(fmt, E, R, C, x.ctypes.data, ctypes.byref(sz), None, None, None, None),
+    _check(lib.csf_prepare(fmt, E, R, C, x.ctypes.data, ctypes.byref(sz), None, None, None, None, None),
            "csf_prepare(sizes)")
     n = int(sz.num_exceptions)
     bases = np.empty(E * R, dtype=np.uint8)
     offsets = np.empty(int(sz.offsets_bytes), dtype=np.uint8)
     exc = np.empty(max(n, 1), dtype=np.uint32)
     prefix = np.empty(E + 1, dtype=np.int32)
+    tidx = np.empty(int(sz.index_bytes) // 4, dtype=np.int32) if index else None
     _check(lib.csf_prepare(fmt, E, R, C, x.ctypes.data, ctypes.byref(sz), bases.ctypes.data,
-                           offsets.ctypes.data, exc.ctypes.data, prefix.ctypes.data), "csf_prepare")
+                           offsets.ctypes.data, exc.ctypes.data, prefix.ctypes.data,
+                           tidx.ctypes.data if index else None), "csf_prepare")
     return from_numpy(dict(fmt=fmt, E=E, R=R, C=C, stride=int(sz.offsets_stride), bases=bases,
-                           offsets=offsets, exceptions=exc[:n], prefix=prefix), device)
+                           offsets=offsets, exceptions=exc[:n], prefix=prefix, tile_index=tidx), device)
 
 
 def _stream_handle(stream, device) -> int:
@@ -209,7 +244,12 @@ def _stream_handle(stream, device) -> int:
 def _check_device(stack: CompressedStack, ws: torch.Tensor, name: str):
     if stack.device.type != "cuda":
         raise ValueError(f"{name}: compressed stack must be on a GPU")
-    for t in (stack.bases, stack.offsets, stack.exceptions, stack.prefix):
+    tensors = [stack.bases, stack.offsets, stack.exceptions, stack.prefix]
+    if stack.tile_index is not None:
+        tensors.append(stack.tile_index)
+        if stack.tile_index.numel() != stack.E * stack.index_tiles + 1 or stack.tile_index.dtype != torch.int32:
+            raise ValueError(f"{name}: tile_index must be int32[{stack.E * stack.index_tiles + 1}]")
+    for t in tensors:
         if t.device != stack.device or not t.is_contiguous():
             raise ValueError(f"{name}: stack tensors must be contiguous on one device")
     if not isinstance(ws, torch.Tensor) or ws.device != stack.device or ws.dtype != torch.uint8:
@@ -290,6 +330,19 @@ class Launch:
                       self._es, passes, self._stream)
         if st != 0:
             raise CsfError(st, "csf_decode_passes")
+
+
+def build_index(stack: CompressedStack, stream=None) -> torch.Tensor:
+    """Enqueue the GPU construction of ``stack``'s tile index; returns the new
+    int32 tensor (also attached to ``stack``)."""
+    if stack.device.type != "cuda":
+        raise ValueError("build_index: stack must be on a GPU")
+    out = torch.empty(stack.E * stack.index_tiles + 1, dtype=torch.int32, device=stack.device)
+    d = stack.descriptor()
+    _check(_lib().csf_build_index(ctypes.byref(d), out.data_ptr(), _stream_handle(stream, stack.device)),
+           "csf_build_index")
+    stack.tile_index = out
+    return out
 
 
 def validate(stack: CompressedStack):

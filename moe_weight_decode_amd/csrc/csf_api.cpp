@@ -20,25 +20,15 @@ using csf::StackArgs;
 
 constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of an entry
 
-// Offset groups per lane per fixed-stream unit, by format and mode.
-#ifndef CSF_SLOTS_NVFP4
-#define CSF_SLOTS_NVFP4 4
-#endif
-#ifndef CSF_SLOTS_MXFP4
-#define CSF_SLOTS_MXFP4 2
-#endif
-#ifndef CSF_SLOTS_ROUTED
-#define CSF_SLOTS_ROUTED 1
-#endif
-// Workgroups per CU the grids aim for.
-#ifndef CSF_FIXED_WG_PER_CU
-#define CSF_FIXED_WG_PER_CU 64
+// Workgroups per CU the grids aim for (persistent tile loops).
+#ifndef CSF_TILE_WG_PER_CU
+#define CSF_TILE_WG_PER_CU 8
 #endif
 #ifndef CSF_EXC_WG_PER_CU
 #define CSF_EXC_WG_PER_CU 8
 #endif
 #ifndef CSF_ROUTED_WG_PER_CU
-#define CSF_ROUTED_WG_PER_CU 4
+#define CSF_ROUTED_WG_PER_CU 2
 #endif
 
 int offset_bits(int32_t format) {
@@ -74,18 +64,24 @@ csf_status check_stack(const csf_stack *s, const uint8_t *ws) {
         return CSF_E_SIZE;
     if (!aligned(s->offsets, 16) || !aligned(s->exc_prefix, 4)) return CSF_E_ALIGN;
     if (s->num_exceptions > 0 && !aligned(s->exceptions, 4)) return CSF_E_ALIGN;
+    if (s->tile_index != nullptr && !aligned(s->tile_index, 4)) return CSF_E_ALIGN;
     return CSF_OK;
 }
 
-void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t slots) {
-    const uint32_t w = uint32_t(offset_bits(s.format));
-    const uint32_t G = 128u / w;
+int64_t index_tiles(int32_t R, int32_t C) {
+    return (int64_t(R) * C + CSF_INDEX_TILE - 1) / CSF_INDEX_TILE;
+}
+
+static_assert(CSF_INDEX_TILE == csf::kIndexTile, "index tile of the ABI and the kernels");
+
+void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws) {
     const uint32_t P = uint32_t(s.rows) * uint32_t(s.cols);
     const uint32_t C = uint32_t(s.cols);
     a.bases = s.bases;
     a.offsets = s.offsets;
     a.exc = s.exceptions;
     a.prefix = s.exc_prefix;
+    a.tile_index = s.tile_index;
     a.ws = ws;
     a.stride = s.offsets_stride;
     a.rcp_cols = 1.0 / double(C);
@@ -93,16 +89,17 @@ void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t slots) {
     a.P = P;
     a.R = uint32_t(s.rows);
     a.C = C;
-    a.groups = (P + G - 1) / G;
-    a.wbits = w;
+    a.tiles = (P + csf::kTile - 1) / csf::kTile;
+    a.index_tiles = uint32_t(index_tiles(s.rows, s.cols));
+    a.wbits = uint32_t(offset_bits(s.format));
     a.row_mode = (C % 16 == 0) ? csf::kRowSplat : (C >= 16 ? csf::kRowTwo : csf::kRowBytes);
-    a.pad_ = 0;
-    // A unit's rows (at most floor((u*G - 1) / C) + 2 of them) must fit the LDS stage.
-    const uint64_t lds_cap = uint64_t(csf::kBasesLds - 2) * C / G;
-    uint64_t cap = std::min<uint64_t>(uint64_t(csf::kBlock) * slots, std::max<uint64_t>(lds_cap, 1));
-    const uint32_t units = uint32_t((a.groups + cap - 1) / cap);
-    a.units = units;
-    a.unit_groups = (a.groups + units - 1) / units;
+}
+
+// LDS for one tile's row bases: a tile of kTile positions touches at most
+// (kTile - 1) / C + 2 rows; edge runs read up to kBasesSlack rows further.
+uint32_t bases_stage_bytes(uint32_t C) {
+    const uint32_t rows = (csf::kTile - 1) / C + 2 + csf::kBasesSlack;
+    return (rows + 15u) & ~15u;
 }
 
 uint32_t cu_count(hipStream_t stream) {
@@ -137,25 +134,28 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     a.expert_start = expert_start;
     a.nstacks = s1 ? 2u : 1u;
     a.E = uint32_t(s0->num_experts);
-    const uint32_t slots0 = routed ? CSF_SLOTS_ROUTED
-                                   : (s0->format == CSF_NVFP4_E4M3 ? CSF_SLOTS_NVFP4 : CSF_SLOTS_MXFP4);
-    fill_stack(a.st[0], *s0, ws0, slots0);
+    fill_stack(a.st[0], *s0, ws0);
+    a.bases_stage = bases_stage_bytes(a.st[0].C);
     if (s1) {
-        const uint32_t slots1 = routed ? CSF_SLOTS_ROUTED
-                                       : (s1->format == CSF_NVFP4_E4M3 ? CSF_SLOTS_NVFP4 : CSF_SLOTS_MXFP4);
-        fill_stack(a.st[1], *s1, ws1, slots1);
+        fill_stack(a.st[1], *s1, ws1);
+        a.bases_stage = std::max(a.bases_stage, bases_stage_bytes(a.st[1].C));
     } else {
         a.st[1] = a.st[0];  // never read: nstacks == 1
     }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const uint32_t cus = cu_count(stream);
+    const uint64_t tile_units = uint64_t(a.E) * a.st[0].tiles + (s1 ? uint64_t(a.E) * a.st[1].tiles : 0);
+    const uint64_t tile_cap = uint64_t(cus) * (routed ? CSF_ROUTED_WG_PER_CU : CSF_TILE_WG_PER_CU);
+    const uint32_t tile_grid = uint32_t(std::max<uint64_t>(1, std::min(tile_units, tile_cap)));
 
+    const bool indexed = s0->tile_index != nullptr && (s1 == nullptr || s1->tile_index != nullptr);
+    if (passes == CSF_PASS_ALL && indexed) {
+        if (csf::launch_fused(a, tile_grid, stream) != hipSuccess) return CSF_E_HIP;
+        return CSF_OK;
+    }
     if (passes & CSF_PASS_FIXED) {
-        const uint64_t units = uint64_t(a.E) * a.st[0].units + (s1 ? uint64_t(a.E) * a.st[1].units : 0);
-        const uint64_t cap = uint64_t(cus) * (routed ? CSF_ROUTED_WG_PER_CU : CSF_FIXED_WG_PER_CU);
-        const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(units, cap)));
-        if (csf::launch_fixed(a, grid, stream) != hipSuccess) return CSF_E_HIP;
+        if (csf::launch_fixed(a, tile_grid, stream) != hipSuccess) return CSF_E_HIP;
     }
     if (passes & CSF_PASS_EXCEPTIONS) {
         const uint64_t entries = uint64_t(a.st[0].n_exc) + (s1 ? uint64_t(a.st[1].n_exc) : 0);
@@ -167,6 +167,20 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
             if (csf::launch_exceptions(a, grid, stream) != hipSuccess) return CSF_E_HIP;
         }
     }
+    return CSF_OK;
+}
+
+csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_stream) {
+    if (tile_index == nullptr) return CSF_E_NULL;
+    csf_status st = check_stack(s, reinterpret_cast<const uint8_t *>(tile_index));
+    if (st != CSF_OK) return st;
+    if (!aligned(tile_index, 4)) return CSF_E_ALIGN;
+    StackArgs a;
+    fill_stack(a, *s, nullptr);
+    if (a.n_exc == 0) a.exc = nullptr;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (csf::launch_build_index(a, uint32_t(s->num_experts), tile_index, stream) != hipSuccess)
+        return CSF_E_HIP;
     return CSF_OK;
 }
 
@@ -258,13 +272,25 @@ void parallel_experts(int32_t E, Fn fn) {
     for (auto &th : pool) th.join();
 }
 
+// Tile index of one expert: walk its ascending entries once, closing tile j
+// at the first entry whose position reaches j * CSF_INDEX_TILE.
+void index_expert(const uint32_t *exc, int64_t begin, int64_t end, int64_t NT, int32_t *out) {
+    int64_t k = begin;
+    for (int64_t j = 0; j < NT; ++j) {
+        const int64_t bound = j * CSF_INDEX_TILE;
+        while (k < end && int64_t(exc[k] >> 8) < bound) ++k;
+        out[j] = int32_t(k);
+    }
+}
+
 csf_status prepare_impl(int32_t format, int32_t E, int32_t R, int32_t C, const uint8_t *dense,
                         csf_sizes *out, uint8_t *bases, uint8_t *offsets, uint32_t *exceptions,
-                        int32_t *exc_prefix) {
+                        int32_t *exc_prefix, int32_t *tile_index) {
     csf_status st = check_shape(format, E, R, C);
     if (st != CSF_OK) return st;
     if (dense == nullptr || out == nullptr) return CSF_E_NULL;
-    const bool query = bases == nullptr && offsets == nullptr && exceptions == nullptr && exc_prefix == nullptr;
+    const bool query = bases == nullptr && offsets == nullptr && exceptions == nullptr &&
+                       exc_prefix == nullptr && tile_index == nullptr;
     if (!query && (bases == nullptr || offsets == nullptr || exc_prefix == nullptr)) return CSF_E_NULL;
 
     EncodeShape sh;
@@ -300,7 +326,10 @@ csf_status prepare_impl(int32_t format, int32_t E, int32_t R, int32_t C, const u
     out->num_exceptions = n;
     out->exceptions_bytes = 4 * n;
     out->prefix_bytes = 4 * (int64_t(E) + 1);
-    out->compressed_bytes = out->bases_bytes + out->offsets_bytes + out->exceptions_bytes + out->prefix_bytes;
+    out->index_tiles = index_tiles(R, C);
+    out->index_bytes = 4 * (int64_t(E) * out->index_tiles + 1);
+    out->compressed_bytes = out->bases_bytes + out->offsets_bytes + out->exceptions_bytes +
+                            out->prefix_bytes + out->index_bytes;
     if (query) return CSF_OK;
     if (n > 0 && exceptions == nullptr) return CSF_E_NULL;
 
@@ -311,7 +340,11 @@ csf_status prepare_impl(int32_t format, int32_t E, int32_t R, int32_t C, const u
         thread_local std::vector<uint8_t> field;
         encode_plane(sh, dense + int64_t(e) * sh.P, b + int64_t(e) * R, offsets + int64_t(e) * sh.S,
                      exceptions + start[size_t(e)], field);
+        if (tile_index != nullptr)
+            index_expert(exceptions, start[size_t(e)], start[size_t(e) + 1], out->index_tiles,
+                         tile_index + int64_t(e) * out->index_tiles);
     });
+    if (tile_index != nullptr) tile_index[int64_t(E) * out->index_tiles] = int32_t(n);
     return CSF_OK;
 }
 
@@ -356,6 +389,16 @@ csf_status validate_impl(const csf_stack *s) {
             }
         }
     }
+    if (s->tile_index != nullptr) {
+        const int64_t NT = index_tiles(s->rows, s->cols);
+        std::vector<int32_t> want(static_cast<size_t>(NT));
+        for (int32_t e = 0; e < s->num_experts; ++e) {
+            index_expert(s->exceptions, pf[e], pf[e + 1], NT, want.data());
+            for (int64_t j = 0; j < NT; ++j)
+                if (s->tile_index[e * NT + j] != want[size_t(j)]) return CSF_E_CORRUPT;
+        }
+        if (s->tile_index[int64_t(s->num_experts) * NT] != s->num_exceptions) return CSF_E_CORRUPT;
+    }
     return CSF_OK;
 }
 
@@ -382,12 +425,21 @@ const char *csf_status_str(csf_status s) {
 
 csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
                        const uint8_t *dense_host, csf_sizes *out_sizes, uint8_t *bases,
-                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix) {
+                       uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix,
+                       int32_t *tile_index) {
     try {
         return prepare_impl(format, num_experts, rows, cols, dense_host, out_sizes, bases, offsets,
-                            exceptions, exc_prefix);
+                            exceptions, exc_prefix, tile_index);
     } catch (...) {
         return CSF_E_SIZE;  // allocation failure in the host encoder
+    }
+}
+
+csf_status csf_build_index(const csf_stack *compressed, int32_t *tile_index, void *hip_stream) {
+    try {
+        return build_index_impl(compressed, tile_index, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
     }
 }
 

@@ -1,18 +1,29 @@
 // CSF block-scale decode kernels for gfx950 (CDNA4, wave64).
 //
-// Two passes, as the decoder on "finegrained-kernels: decode losslessly
-// compressed NVFP4 scales (CSF)" (kernels-community PR 1236, API paragraph) is
-// described: a fixed stream that writes base + offset for every position, then
-// an exception pass that overwrites the positions whose byte the offsets could
-// not reach.  With the grouped-routing expert_start tensor both passes skip
-// experts with no routed tokens and never address their planes; the routing is
-// read on the device only.  One launch of each pass covers one or two stacks
-// (gate/up + down, "NVFP4-CSF: expand_scales() for ahead-of-call scale
-// expansion (canonical twin of #477)", b12x PR 478, commit messages).
+// The decoder on "finegrained-kernels: decode losslessly compressed NVFP4
+// scales (CSF)" (kernels-community PR 1236, API paragraph) is a fixed stream
+// that writes base + offset for every position plus an exception pass that
+// writes the bytes the offsets cannot reach.  With the grouped-routing
+// expert_start tensor both skip experts with no routed tokens and never address
+// their planes; the routing is read on the device only.  Every launch covers
+// one or two stacks (gate/up + down, "NVFP4-CSF: expand_scales() for
+// ahead-of-call scale expansion (canonical twin of #477)", b12x PR 478, commit
+// messages).
+//
+// Three kernels:
+//   csf_fused_kernel  both parts in one pass: a tile is expanded into LDS, the
+//                     tile's exception entries (found through the per-tile
+//                     exception index) are patched into LDS, then the tile is
+//                     written with full-line stores.  Every dense byte is
+//                     written once.
+//   csf_fixed_kernel  the fixed stream alone, stored straight from registers.
+//   csf_exc_kernel    the exception pass alone, indexed by a wave-level prefix
+//                     over per-expert entry counts (needs no tile index).
 //
 // The work is a byte expansion bound by HBM bandwidth: no matrix cores, a few
-// integer ops per output byte.  What matters is wide coalesced traffic and
-// enough bytes in flight per CU.
+// integer ops per output byte.  Lane l of a workgroup owns the 16-byte output
+// runs l, l + 256, ... of a tile, so every store instruction of a wave covers
+// 1 KiB of contiguous output.
 #include "csf_launch.h"
 
 namespace csf {
@@ -20,7 +31,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWave = 64;
+constexpr uint32_t kWave = 64;
 
 // Byte-wise sum modulo 256 of four packed bytes: no carry crosses a byte.
 __device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b) {
@@ -45,7 +56,7 @@ __device__ __forceinline__ uint32_t low_bytes_mask(int k) {
 }
 
 // Row bases of the 16 positions pos .. pos+15 of one plane, packed like the
-// output.  lds holds the bases of rows r_lo, r_lo+1, ... of the current unit.
+// output.  lds holds the bases of rows r_lo, r_lo+1, ... of the current tile.
 template <int MODE>
 __device__ __forceinline__ u32x4 run_bases(const uint8_t *lds, uint32_t pos, uint32_t r_lo,
                                            uint32_t C, double rcp) {
@@ -96,30 +107,6 @@ __device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t nvalid
         if (j < n) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
 }
 
-// Expand the offset groups a lane loaded for one unit: field f of group g is
-// the 16 positions g*G + 16f .. +15 (the contiguous-decoding order).
-template <int WB, int MODE>
-__device__ __forceinline__ void expand_unit(const StackArgs &st, const u32x4 *v, uint32_t g_begin,
-                                            uint32_t g_end, uint8_t *plane, const uint8_t *lds,
-                                            uint32_t r_lo) {
-    constexpr uint32_t G = 128 / WB;
-    constexpr int F = 8 / WB;
-    constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
-#pragma unroll
-    for (int i = 0; i < kFixedMaxSlots; ++i) {
-        const uint32_t g = g_begin + threadIdx.x + i * kBlock;
-        if (g >= g_end) break;
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-            const uint32_t pos = g * G + 16u * f;
-            if (pos >= st.P) break;
-            const u32x4 field = (v[i] >> (uint32_t)(WB * f)) & MASK;
-            const u32x4 base = run_bases<MODE>(lds, pos, r_lo, st.C, st.rcp_cols);
-            store_run(plane + pos, add_bytes4(field, base), st.P - pos);
-        }
-    }
-}
-
 __device__ __forceinline__ StackArgs pick(const DecodeArgs &a, uint32_t s) {
     return s ? a.st[1] : a.st[0];
 }
@@ -157,10 +144,10 @@ __device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uin
             }
             uint64_t s1 = (uint64_t)c1;
 #pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
+            for (uint32_t d = 1; d < kWave; d <<= 1) {
                 const uint64_t y0 = __shfl_up(s0, d, kWave);
                 const uint64_t y1 = __shfl_up(s1, d, kWave);
-                if (lane >= (uint32_t)d) {
+                if (lane >= d) {
                     s0 += y0;
                     s1 += y1;
                 }
@@ -181,76 +168,162 @@ __device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uin
     return n;
 }
 
-// ---------------------------------------------------------------------------
-// Pass 1: fixed-stream expansion.
-//
-// Work unit = (stack, active expert, range of up to kBlock*kFixedMaxSlots
-// offset groups).  A workgroup loads its lanes' 16-byte offset groups
-// (coalesced 128-bit loads), stages the unit's row bases in LDS, then every
-// lane widens each field to 16 output bytes, adds the row bases with a
-// byte-wise add and stores 16 bytes.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
-    extern __shared__ __align__(16) uint8_t dyn_lds[];
-    __shared__ __align__(16) uint8_t lds_bases[kBasesLds + kBasesLdsSlack];
+// Routed mode: the active-expert list in LDS (all threads take part).
+__device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, int32_t *es) {
     __shared__ uint32_t s_nact;
+    for (uint32_t i = threadIdx.x; i <= a.E; i += kBlock) es[i] = a.expert_start[i];
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t n = build_maps(es, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
+        if (threadIdx.x == 0) s_nact = n;
+    }
+    __syncthreads();
+    return s_nact;
+}
+
+// Expand this lane's runs of one tile: tile positions q0 .. q1-1, lds_bases
+// holding rows from r_lo.  FUSED writes the runs into the LDS tile; otherwise
+// they are stored to the plane directly.
+template <int WB, int MODE, bool FUSED>
+__device__ __forceinline__ void expand_tile(const StackArgs &st, const u32x4 *v, uint32_t q0,
+                                            uint32_t q1, const uint8_t *lds_bases, uint32_t r_lo,
+                                            uint8_t *tile, uint8_t *plane) {
+    constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
+    constexpr uint32_t FMASK = 8 / WB - 1;  // fields per group - 1
+#pragma unroll
+    for (uint32_t i = 0; i < kRunsPerLane; ++i) {
+        const uint32_t j = i * kBlock + threadIdx.x;
+        const uint32_t pos = q0 + 16u * j;
+        if (pos >= q1) break;
+        const uint32_t f = (pos >> 4) & FMASK;
+        const u32x4 field = (v[i] >> (uint32_t)(WB * f)) & MASK;
+        const u32x4 out = add_bytes4(field, run_bases<MODE>(lds_bases, pos, r_lo, st.C, st.rcp_cols));
+        if constexpr (FUSED) {
+            *reinterpret_cast<u32x4 *>(tile + 16u * j) = out;
+        } else {
+            store_run(plane + pos, out, st.P - pos);
+        }
+    }
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void expand_dispatch(const StackArgs &st, const u32x4 *v, uint32_t q0,
+                                                uint32_t q1, const uint8_t *lds_bases,
+                                                uint32_t r_lo, uint8_t *tile, uint8_t *plane) {
+    switch ((st.wbits == 4 ? 0u : 3u) + st.row_mode) {
+        case 0: expand_tile<4, kRowSplat, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 1: expand_tile<4, kRowTwo, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 2: expand_tile<4, kRowBytes, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 3: expand_tile<1, kRowSplat, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 4: expand_tile<1, kRowTwo, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        default: expand_tile<1, kRowBytes, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tile loop shared by the fused and the fixed-stream kernels.
+//
+// Work unit = (stack, active expert, tile of kTile positions).  Per tile the
+// workgroup loads each lane's 16-byte offset groups with 128-bit loads (lanes
+// reading fields of the same group share one load), stages the tile's row
+// bases in LDS, widens each lane's field to 16 bytes and adds the row bases
+// byte-wise.  FUSED then patches the tile's exception entries into the LDS
+// tile and stores the finished tile.
+// ---------------------------------------------------------------------------
+template <bool FUSED>
+__device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+    uint8_t *lds_bases = dyn;
+    uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
+    int32_t *es = reinterpret_cast<int32_t *>(dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u));
 
     const bool routed = a.expert_start != nullptr;
-    uint16_t *act = reinterpret_cast<uint16_t *>(dyn_lds);
-    uint32_t nact = a.E;
-    if (routed) {
-        int32_t *es = reinterpret_cast<int32_t *>(dyn_lds + ((2u * a.E + 15u) & ~15u));
-        for (uint32_t i = threadIdx.x; i <= a.E; i += kBlock) es[i] = a.expert_start[i];
-        __syncthreads();
-        if (threadIdx.x < kWave) {
-            const uint32_t n = build_maps(es, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
-            if (threadIdx.x == 0) s_nact = n;
-        }
-        __syncthreads();
-        nact = s_nact;
-    }
+    const uint32_t nact = routed ? active_experts(a, act, es) : a.E;
+    const uint32_t u0 = nact * a.st[0].tiles;
+    const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
 
-    const uint32_t u0 = nact * a.st[0].units;
-    const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].units : 0u);
     for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
         const uint32_t s = u >= u0 ? 1u : 0u;
         const StackArgs st = pick(a, s);
         const uint32_t uu = u - (s ? u0 : 0u);
-        const uint32_t k = uu / st.units;
-        const uint32_t c = uu - k * st.units;
+        const uint32_t k = uu / st.tiles;
+        const uint32_t t = uu - k * st.tiles;
         const uint32_t e = routed ? (uint32_t)act[k] : k;
+        const uint32_t q0 = t * kTile;
+        const uint32_t q1 = min(q0 + kTile, st.P);
 
-        const uint32_t G = 128u / st.wbits;
-        const uint32_t g_begin = c * st.unit_groups;
-        const uint32_t g_end = min(g_begin + st.unit_groups, st.groups);
-        const uint32_t p_last = min(g_end * G, st.P) - 1u;
-        const uint32_t r_lo = div_exact(g_begin * G, st.rcp_cols);
-        const uint32_t nrows = div_exact(p_last, st.rcp_cols) - r_lo + 1u;
-
-        // Offsets first, so their latency overlaps the base staging.
+        // Offset groups: run q (positions 16q .. 16q+15) is field q % F of
+        // group q / F, F = 8 / w fields per group.
         const u32x4 *seg = reinterpret_cast<const u32x4 *>(st.offsets + (uint64_t)e * st.stride);
-        u32x4 v[kFixedMaxSlots];
+        const uint32_t gshift = st.wbits == 4 ? 1u : 3u;
+        u32x4 v[kRunsPerLane];
 #pragma unroll
-        for (int i = 0; i < kFixedMaxSlots; ++i) {
-            const uint32_t g = g_begin + threadIdx.x + i * kBlock;
-            v[i] = g < g_end ? seg[g] : (u32x4){0u, 0u, 0u, 0u};
+        for (uint32_t i = 0; i < kRunsPerLane; ++i) {
+            const uint32_t pos = q0 + 16u * (i * kBlock + threadIdx.x);
+            v[i] = pos < q1 ? seg[(pos >> 4) >> gshift] : (u32x4){0u, 0u, 0u, 0u};
         }
-        if (u != blockIdx.x) __syncthreads();  // previous unit is done with lds_bases
+
+        // The tile's exception entries, prefetched into registers.
+        uint32_t lo = 0, hi = 0;
+        uint32_t w[kExcRegs];
+        if constexpr (FUSED) {
+            const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles + t * kIndexPerTile;
+            const uint32_t last = min(kIndexPerTile, st.index_tiles - t * kIndexPerTile);
+            const int32_t l0 = ti[0], h0 = ti[last];
+            hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
+            lo = l0 < 0 ? 0u : min((uint32_t)l0, hi);
+#pragma unroll
+            for (uint32_t i = 0; i < kExcRegs; ++i) {
+                const uint32_t kk = lo + i * kBlock + threadIdx.x;
+                w[i] = kk < hi ? st.exc[kk] : 0xffffffffu;  // position 2^24 - 1: never in a tile
+            }
+        }
+
+        // Row bases of the tile into LDS.
+        const uint32_t r_lo = div_exact(q0, st.rcp_cols);
+        const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
+        if (!FUSED && u != blockIdx.x) __syncthreads();  // previous tile done with lds_bases
         const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
-        for (uint32_t t = threadIdx.x; t < nrows; t += kBlock) lds_bases[t] = brow[t];
+        for (uint32_t r = threadIdx.x; r < nrows; r += kBlock) lds_bases[r] = brow[r];
         __syncthreads();
 
         uint8_t *plane = st.ws + (uint64_t)e * st.P;
-        const uint32_t variant = (st.wbits == 4 ? 0u : 3u) + st.row_mode;
-        switch (variant) {
-            case 0: expand_unit<4, kRowSplat>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
-            case 1: expand_unit<4, kRowTwo>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
-            case 2: expand_unit<4, kRowBytes>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
-            case 3: expand_unit<1, kRowSplat>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
-            case 4: expand_unit<1, kRowTwo>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
-            default: expand_unit<1, kRowBytes>(st, v, g_begin, g_end, plane, lds_bases, r_lo); break;
+        expand_dispatch<FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane);
+
+        if constexpr (FUSED) {
+            __syncthreads();  // tile expanded
+#pragma unroll
+            for (uint32_t i = 0; i < kExcRegs; ++i) {
+                const uint32_t pos = w[i] >> 8;
+                if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(w[i] & 0xffu);
+            }
+            for (uint32_t kk = lo + kExcRegs * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
+                const uint32_t x = st.exc[kk];
+                const uint32_t pos = x >> 8;
+                if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
+            }
+            __syncthreads();  // tile patched
+#pragma unroll
+            for (uint32_t i = 0; i < kRunsPerLane; ++i) {
+                const uint32_t j = i * kBlock + threadIdx.x;
+                const uint32_t pos = q0 + 16u * j;
+                if (pos >= q1) break;
+                store_run(plane + pos, *reinterpret_cast<const u32x4 *>(tile + 16u * j), st.P - pos);
+            }
+            // The next tile's first barrier orders these LDS reads before the
+            // next expansion overwrites the tile.
         }
     }
+}
+
+__global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+    __shared__ __align__(16) uint8_t tile[kTile];
+    tile_loop<true>(a, dyn_lds, tile);
+}
+
+__global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+    tile_loop<false>(a, dyn_lds, nullptr);
 }
 
 // Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
@@ -271,7 +344,7 @@ __device__ __forceinline__ uint32_t find_expert(const uint32_t *M, uint32_t k, u
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: exception scatter.
+// Exception pass alone.
 //
 // The entries of all active experts of both stacks form one index space
 // [0, N0 + N1), laid out by the wave-level prefixes M_s.  Workgroups take
@@ -319,7 +392,7 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
         uint32_t k = 0, prev_s = 0;
         // Locate every entry first so the loads below are all in flight together.
 #pragma unroll
-        for (int i = 0; i < kExcPerLane; ++i) {
+        for (uint32_t i = 0; i < kExcPerLane; ++i) {
             const uint32_t t = c0 + threadIdx.x + i * kBlock;
             dst[i] = nullptr;
             if (t >= N) continue;
@@ -341,14 +414,14 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < kExcPerLane; ++i) {
+        for (uint32_t i = 0; i < kExcPerLane; ++i) {
             if (dst[i] == nullptr) continue;
             const uint32_t t = c0 + threadIdx.x + i * kBlock;
             const uint32_t *exc = t >= N0 ? a.st[1].exc : a.st[0].exc;
             word[i] = exc[word[i]];
         }
 #pragma unroll
-        for (int i = 0; i < kExcPerLane; ++i) {
+        for (uint32_t i = 0; i < kExcPerLane; ++i) {
             if (dst[i] == nullptr) continue;
             const uint32_t t = c0 + threadIdx.x + i * kBlock;
             const uint32_t P = t >= N0 ? a.st[1].P : a.st[0].P;
@@ -358,25 +431,67 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     }
 }
 
-}  // namespace
-
-size_t fixed_lds_bytes(const DecodeArgs &a) {
-    if (a.expert_start == nullptr) return 0;
-    return ((2u * a.E + 15u) & ~15u) + 4u * (a.E + 1u);
+// ---------------------------------------------------------------------------
+// Per-tile exception index: thread i < E*NT handles tile j = i % NT of expert
+// e = i / NT and writes prefix[e] + #{entries of e with position < j*kIndexTile}
+// (a binary search over the expert's ascending positions); the last thread
+// writes prefix[E].  Prefix values are clamped to [0, n_exc].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void csf_index_kernel(StackArgs s, uint32_t E, int32_t *out) {
+    const uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t total = (uint64_t)E * s.index_tiles;
+    if (i > total) return;
+    auto clampn = [&](int32_t v) -> uint32_t { return v < 0 ? 0u : min((uint32_t)v, s.n_exc); };
+    if (i == total) {
+        out[i] = (int32_t)clampn(s.prefix[E]);
+        return;
+    }
+    const uint32_t e = (uint32_t)(i / s.index_tiles);
+    const uint32_t j = (uint32_t)(i - (uint64_t)e * s.index_tiles);
+    uint32_t lo = clampn(s.prefix[e]);
+    uint32_t hi = clampn(s.prefix[e + 1]);
+    if (hi < lo) hi = lo;
+    const uint32_t bound = j * kIndexTile;
+    while (lo < hi) {  // first entry with position >= bound
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if ((s.exc[mid] >> 8) < bound) lo = mid + 1; else hi = mid;
+    }
+    out[i] = (int32_t)lo;
 }
 
-size_t exc_lds_bytes(const DecodeArgs &a) {
+}  // namespace
+
+size_t tile_lds_bytes(const DecodeArgs &a) {
+    size_t n = a.bases_stage;
+    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + 4u * (a.E + 1u);
+    return n;
+}
+
+static size_t exc_lds_bytes(const DecodeArgs &a) {
     const size_t words = (a.E + 1u + 3u) & ~3u;
     return 5u * 4u * words + 2u * a.E;
 }
 
 hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL(csf_fixed_kernel, dim3(grid), dim3(kBlock), fixed_lds_bytes(a), stream, a);
+    hipLaunchKernelGGL(csf_fixed_kernel, dim3(grid), dim3(kBlock), tile_lds_bytes(a), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL(csf_fused_kernel, dim3(grid), dim3(kBlock), tile_lds_bytes(a), stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     hipLaunchKernelGGL(csf_exc_kernel, dim3(grid), dim3(kBlock), exc_lds_bytes(a), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_index(const StackArgs &s, uint32_t E, int32_t *tile_index,
+                              hipStream_t stream) {
+    const uint64_t n = (uint64_t)E * s.index_tiles + 1;
+    const uint32_t grid = (uint32_t)((n + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(csf_index_kernel, dim3(grid), dim3(kBlock), 0, stream, s, E, tile_index);
     return hipGetLastError();
 }
 

@@ -7,11 +7,14 @@
 
 namespace csf {
 
-constexpr int kBlock = 256;          // threads per workgroup (4 wave64)
-constexpr int kFixedMaxSlots = 4;    // offset groups per lane per fixed-stream unit
-constexpr int kBasesLds = 4096;      // bytes of row bases staged per fixed-stream unit
-constexpr int kBasesLdsSlack = 32;   // rows read past a unit's last row by edge runs
-constexpr int kExcPerLane = 8;       // exception entries per lane per exception chunk
+constexpr uint32_t kBlock = 256;                    // threads per workgroup (4 wave64)
+constexpr uint32_t kTile = 8192;                    // plane positions per tile (one workgroup pass)
+constexpr uint32_t kRunsPerLane = kTile / 16 / kBlock;  // 16-byte output runs per lane per tile
+constexpr uint32_t kIndexTile = 2048;               // positions per exception-index tile
+constexpr uint32_t kIndexPerTile = kTile / kIndexTile;
+constexpr uint32_t kExcRegs = 8;                    // entries per lane prefetched per tile
+constexpr uint32_t kExcPerLane = 8;                 // entries per lane per scatter chunk
+constexpr uint32_t kBasesSlack = 32;                // rows read past a tile's last row by edge runs
 
 // How a 16-byte output run finds its row bases.
 enum RowMode : uint32_t {
@@ -22,23 +25,22 @@ enum RowMode : uint32_t {
 
 // One compressed stack plus its dense destination, as the kernels see it.
 struct StackArgs {
-    const uint8_t *bases;     // [E * R]
-    const uint8_t *offsets;   // [E * stride], 16-byte aligned
-    const uint32_t *exc;      // [n_exc] (never dereferenced when n_exc == 0)
-    const int32_t *prefix;    // [E + 1]
-    uint8_t *ws;              // [E * P], any alignment
-    int64_t stride;           // offset bytes per expert (multiple of 16)
-    double rcp_cols;          // 1.0 / C, for exact row = pos / C with pos < 2^24
-    uint32_t n_exc;           // total entries (< 2^31)
-    uint32_t P;               // R * C  (< 2^24)
+    const uint8_t *bases;       // [E * R]
+    const uint8_t *offsets;     // [E * stride], 16-byte aligned
+    const uint32_t *exc;        // [n_exc] (never dereferenced when n_exc == 0)
+    const int32_t *prefix;      // [E + 1]
+    const int32_t *tile_index;  // [E * index_tiles + 1] or nullptr
+    uint8_t *ws;                // [E * P], any alignment
+    int64_t stride;             // offset bytes per expert (multiple of 16)
+    double rcp_cols;            // 1.0 / C, for exact row = pos / C with pos < 2^24
+    uint32_t n_exc;             // total entries (< 2^31)
+    uint32_t P;                 // R * C  (< 2^24)
     uint32_t R;
     uint32_t C;
-    uint32_t groups;          // 16-byte offset groups per expert: ceil(P / G)
-    uint32_t unit_groups;     // groups per fixed-stream unit (<= kBlock * kFixedMaxSlots)
-    uint32_t units;           // fixed-stream units per expert: ceil(groups / unit_groups)
-    uint32_t wbits;           // 4 (NVFP4) or 1 (MXFP4)
-    uint32_t row_mode;        // RowMode
-    uint32_t pad_;
+    uint32_t tiles;             // ceil(P / kTile)
+    uint32_t index_tiles;       // ceil(P / kIndexTile)
+    uint32_t wbits;             // 4 (NVFP4) or 1 (MXFP4)
+    uint32_t row_mode;          // RowMode
 };
 
 struct DecodeArgs {
@@ -46,11 +48,20 @@ struct DecodeArgs {
     const int32_t *expert_start;  // nullptr: every expert is active
     uint32_t nstacks;             // 1 or 2
     uint32_t E;                   // experts (same for both stacks)
+    uint32_t bases_stage;         // bytes of dynamic LDS for one tile's row bases
+    uint32_t pad_;
 };
 
-// Enqueue the fixed-stream expansion (every position = base + offset field).
+// Dynamic LDS bytes a tile kernel needs for these arguments.
+size_t tile_lds_bytes(const DecodeArgs &a);
+
+// Fixed stream alone: every position = base + offset field.
 hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
-// Enqueue the exception scatter (entries overwrite their positions).
+// Exception scatter alone (after the fixed stream): entries overwrite their positions.
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
+// Both in one pass, exceptions patched on chip before the stores (needs tile_index).
+hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
+// Per-tile exception index of one stack from its entries and prefix.
+hipError_t launch_build_index(const StackArgs &s, uint32_t E, int32_t *tile_index, hipStream_t stream);
 
 }  // namespace csf

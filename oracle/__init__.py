@@ -47,6 +47,10 @@ class Oracle:
         lib.oracle_encode_streams.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_int] * 4 + [_u8p, _u8p, _u32p, _i32p, _i32p, _u8p]
         lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_index_tiles.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.oracle_index_tiles.restype = ctypes.c_int64
+        lib.oracle_build_index.argtypes = [ctypes.c_int] * 3 + [_u32p, _i32p, _i32p]
+        lib.oracle_build_index.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -84,11 +88,30 @@ class Oracle:
                                             _ptr(prefix, _i32p))
         if rc != 0:
             raise ValueError("oracle_encode_streams failed")
-        return dict(fmt=fmt, E=E, R=R, C=C, stride=S, bases=bases.reshape(-1).copy(),
-                    offsets=offsets, exceptions=exc[:n].copy(), prefix=prefix)
+        st = dict(fmt=fmt, E=E, R=R, C=C, stride=S, bases=bases.reshape(-1).copy(),
+                  offsets=offsets, exceptions=exc[:n].copy(), prefix=prefix)
+        st["tile_index"] = self.build_index(st)
+        return st
 
     def encode(self, fmt: int, x: np.ndarray) -> dict:
         return self.encode_with_bases(fmt, x, self.choose_bases(fmt, x))
+
+    def index_tiles(self, R: int, C: int) -> int:
+        return int(self.lib.oracle_index_tiles(R, C))
+
+    def build_index(self, stack: dict) -> np.ndarray:
+        """Per-tile exception index of a stack (int32[E * tiles + 1])."""
+        E, R, C = stack["E"], stack["R"], stack["C"]
+        exc = np.ascontiguousarray(stack["exceptions"], dtype=np.uint32)
+        if exc.size == 0:
+            exc = np.zeros(1, dtype=np.uint32)
+        out = np.empty(E * self.index_tiles(R, C) + 1, dtype=np.int32)
+        rc = self.lib.oracle_build_index(E, R, C, _ptr(exc, _u32p),
+                                         _ptr(np.ascontiguousarray(stack["prefix"], dtype=np.int32), _i32p),
+                                         _ptr(out, _i32p))
+        if rc != 0:
+            raise ValueError("oracle_build_index rejected its arguments")
+        return out
 
     # -- decoder ------------------------------------------------------------
     def decode(self, stack: dict, expert_start: np.ndarray | None = None,

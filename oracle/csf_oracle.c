@@ -192,6 +192,43 @@ int oracle_encode(int fmt, int E, int R, int C, const uint8_t *x,
 }
 
 /*
+ * Exception index (PR 964, "Load native FP4 experts with optional lossless CSF
+ * scales", paragraphs on preparation: encoding is followed by an index built
+ * on the GPU; PR 478 commit messages: indexed reconstruction with exception
+ * lookup).  The pages do not give its form; this build's reading: every plane
+ * is cut into tiles of 2048 positions, NT = ceil(P / 2048) per expert, and
+ *   tile_index[e*NT + j] = prefix[e] + #{entries of expert e with p < 2048*j}
+ *   tile_index[E*NT]     = prefix[E]
+ * so the entries of tile j of expert e are tile_index[e*NT + j] ..
+ * tile_index[e*NT + j + 1] - 1 (the last tile of an expert ends where the next
+ * expert's first tile starts).  tile_index holds E*NT + 1 ints.
+ */
+#define ORACLE_INDEX_TILE 2048
+
+int64_t oracle_index_tiles(int R, int C)
+{
+    int64_t P = (int64_t)R * C;
+    return (P + ORACLE_INDEX_TILE - 1) / ORACLE_INDEX_TILE;
+}
+
+int oracle_build_index(int E, int R, int C, const uint32_t *exc,
+                       const int32_t *prefix, int32_t *tile_index)
+{
+    if (E <= 0 || R <= 0 || C <= 0) return ORACLE_BAD_ARGS;
+    int64_t NT = oracle_index_tiles(R, C);
+    for (int e = 0; e < E; e++) {
+        for (int64_t j = 0; j < NT; j++) {
+            int64_t below = 0;
+            for (int64_t k = prefix[e]; k < prefix[e + 1]; k++)
+                if ((int64_t)(exc[k] >> 8) < ORACLE_INDEX_TILE * j) below++;
+            tile_index[e * NT + j] = (int32_t)(prefix[e] + below);
+        }
+    }
+    tile_index[(int64_t)E * NT] = prefix[E];
+    return ORACLE_OK;
+}
+
+/*
  * Decoder (PR 1236, API paragraph).  expert_start may be NULL: then every
  * expert is expanded.  Otherwise expert e is expanded iff
  * expert_start[e+1] > expert_start[e], and the planes of all other experts are

@@ -290,7 +290,43 @@ def pin_out_of_plane_entries(orc):
     assert np.array_equal(ws[0], want[0]) and np.all(ws[1] == POISON)
 
 
+def pin_index_hand_worked(orc):
+    # Two experts, one row of 5000 columns: tiles [0, 2048), [2048, 4096), [4096, 5000).
+    # Expert 0 outliers at 5, 2047, 2048, 4999; expert 1 outliers at 100, 4096.
+    x = np.full((2, 1, 5000), 0x30, dtype=np.uint8)
+    for p in (5, 2047, 2048, 4999):
+        x[0, 0, p] = 0x90
+    for p in (100, 4096):
+        x[1, 0, p] = 0x90
+    st = orc.encode(workloads.NVFP4, x)
+    assert st["prefix"].tolist() == [0, 4, 6]
+    assert orc.index_tiles(1, 5000) == 3
+    assert st["tile_index"].tolist() == [0, 2, 3, 4, 5, 5, 6]
+    # exactly one tile per plane, and a plane of exactly two tiles
+    assert orc.index_tiles(1, 2048) == 1 and orc.index_tiles(2, 2048) == 2
+
+
+def pin_index_covers_entries(orc):
+    for fmt, x in ((workloads.NVFP4, workloads.nvfp4_stack(3, 300, 50, 9, 0.10, hot_row_frac=0.02)),
+                   (workloads.MXFP4, workloads.mxfp4_stack(2, 100, 160, 8, 0.15)),
+                   (workloads.NVFP4, workloads.uniform_bytes(2, 3, 7, 1))):
+        E, R, C = x.shape
+        st = orc.encode(fmt, x)
+        ti, pfx = st["tile_index"], st["prefix"]
+        NT = orc.index_tiles(R, C)
+        assert ti.size == E * NT + 1 and ti[-1] == pfx[-1]
+        assert np.all(np.diff(ti) >= 0)
+        pos = (st["exceptions"] >> 8).astype(np.int64)
+        for e in range(E):
+            assert ti[e * NT] == pfx[e]
+            for j in range(NT):
+                lo, hi = ti[e * NT + j], ti[e * NT + j + 1]
+                assert np.all((pos[lo:hi] >= 2048 * j) & (pos[lo:hi] < 2048 * (j + 1)))
+
+
 ALL_PINS = [
+    pin_index_hand_worked,
+    pin_index_covers_entries,
     pin_two_column_closed_form,
     pin_base_optimal,
     pin_nvfp4_layout_bytes,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csf_abi_version() == 1
+    assert lib.csf_abi_version() == 2
     for s in range(9):
         assert lib.csf_status_str(s)
     assert lib.csf_status_str(99) == b"unknown status"
@@ -44,7 +44,7 @@ def test_abi_version_and_status_strings(lib):
 def _same_stack(a: dict, b: dict):
     for k in ("fmt", "E", "R", "C", "stride"):
         assert a[k] == b[k], k
-    for k in ("bases", "offsets", "exceptions", "prefix"):
+    for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
         assert np.array_equal(np.asarray(a[k]).ravel(), np.asarray(b[k]).ravel()), k
 
 
@@ -79,7 +79,10 @@ def test_prepare_sizes_closed_form():
     st = mwd.prepare(x, workloads.NVFP4)
     assert st.stride == 256 and st.offsets.numel() == 4 * 256
     assert st.dense_bytes == 2048
-    assert st.compressed_bytes == 4 * 64 + 4 * 256 + 4 * st.num_exceptions + 4 * 5
+    # 512 positions per plane: one index tile per expert
+    assert st.tile_index.numel() == 4 * 1 + 1
+    assert st.compressed_bytes == 4 * 64 + 4 * 256 + 4 * st.num_exceptions + 4 * 5 + 4 * 5
+    assert mwd.prepare(x, workloads.NVFP4, index=False).tile_index is None
 
 
 def test_validate_accepts_encoded_stacks():
@@ -106,6 +109,10 @@ def _corrupt(st, what):
         p = int(exc[0] >> 8)
         base = int(st.bases[p // st.C])
         exc[0] = np.uint32((p << 8) | base)
+    elif what == "index_shifted":
+        st.tile_index[1] += 1
+    elif what == "index_end":
+        st.tile_index[-1] -= 1
     elif what == "field_at_exception":
         p = int(exc[0] >> 8)
         st.offsets[16 * (p // 32) + p % 16] |= np.uint8(1 << (4 * ((p % 32) // 16)))
@@ -113,7 +120,8 @@ def _corrupt(st, what):
 
 
 @pytest.mark.parametrize("what", ["prefix_start", "prefix_decreasing", "prefix_end", "unsorted",
-                                  "duplicate", "out_of_plane", "fits_window", "field_at_exception"])
+                                  "duplicate", "out_of_plane", "fits_window", "field_at_exception",
+                                  "index_shifted", "index_end"])
 def test_validate_rejects_corruption(what):
     x = workloads.TINY.generate()
     st = mwd.prepare(x, workloads.NVFP4)
@@ -142,11 +150,12 @@ def test_validate_rejects_wrapping_field():
 # --- decode argument errors: rejected on the host, before any HIP call -------
 
 def _fake(fmt=0, E=4, R=64, C=8, stride=256, n=10, bases=0x1000, offsets=0x2000, exc=0x3000,
-          prefix=0x4000):
+          prefix=0x4000, tile_index=None):
     d = mwd.csf_stack()
     d.format, d.num_experts, d.rows, d.cols = fmt, E, R, C
     d.offsets_stride, d.num_exceptions = stride, n
     d.bases, d.offsets, d.exceptions, d.exc_prefix = bases, offsets, exc, prefix
+    d.tile_index = tile_index
     return d
 
 
@@ -166,6 +175,7 @@ DECODE_ERRORS = [
     ("misaligned_offsets", _fake(offsets=0x2008), 0x5000, "CSF_E_ALIGN"),
     ("misaligned_prefix", _fake(prefix=0x4002), 0x5000, "CSF_E_ALIGN"),
     ("misaligned_exc", _fake(exc=0x3001), 0x5000, "CSF_E_ALIGN"),
+    ("misaligned_index", _fake(tile_index=0x8002), 0x5000, "CSF_E_ALIGN"),
 ]
 
 
@@ -188,17 +198,24 @@ def test_paired_and_passes_errors(lib):
         assert mwd.STATUS[lib.csf_decode_passes(ctypes.byref(a), 0x5000, None, None, None, passes,
                                                 None)] == "CSF_E_SIZE"
     assert mwd.STATUS[lib.csf_decode(ctypes.byref(a), 0x5000, 0x7002, None)] == "CSF_E_ALIGN"
+    assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), None, None)] == "CSF_E_NULL"
+    assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), 0x9002, None)] == "CSF_E_ALIGN"
+    assert mwd.STATUS[lib.csf_build_index(ctypes.byref(_fake(E=0)), 0x9000, None)] == "CSF_E_SHAPE"
 
 
 def test_prepare_errors(lib):
     sz = mwd.csf_sizes()
     x = np.zeros((2, 3, 4), dtype=np.uint8)
-    st = lib.csf_prepare(9, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None)
+    st = lib.csf_prepare(9, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None, None)
     assert mwd.STATUS[st] == "CSF_E_FORMAT"
-    st = lib.csf_prepare(0, 2, 0, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None)
+    st = lib.csf_prepare(0, 2, 0, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None, None)
     assert mwd.STATUS[st] == "CSF_E_SHAPE"
-    st = lib.csf_prepare(0, 2, 3, 4, None, ctypes.byref(sz), None, None, None, None)
+    st = lib.csf_prepare(0, 2, 3, 4, None, ctypes.byref(sz), None, None, None, None, None)
     assert mwd.STATUS[st] == "CSF_E_NULL"
     buf = np.zeros(64, dtype=np.uint8)
-    st = lib.csf_prepare(0, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), buf.ctypes.data, None, None, None)
+    st = lib.csf_prepare(0, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), buf.ctypes.data, None, None, None,
+                         None)
+    assert mwd.STATUS[st] == "CSF_E_NULL"
+    st = lib.csf_prepare(0, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None,
+                         buf.ctypes.data)
     assert mwd.STATUS[st] == "CSF_E_NULL"

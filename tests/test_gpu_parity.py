@@ -4,6 +4,10 @@ Every comparison is byte-exact over whole planes.  Inputs come from the seeded
 generators; the compressed streams fed to the GPU are the oracle's encodings
 (and, separately, the library encoder's), and the expected bytes are the
 oracle's decode of the same stream (which the oracle pins tie to the input x).
+
+Decode tests run twice: "fused" (stacks carry the tile index: one kernel
+patches exceptions on chip) and "two_pass" (no index: fixed-stream kernel,
+then the exception kernel).
 """
 import numpy as np
 import pytest
@@ -27,8 +31,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def upload(st: dict, dev) -> "mwd.CompressedStack":
-    return mwd.from_numpy(st, dev)
+MODES = ["fused", "two_pass"]
+
+
+def upload(st: dict, dev, mode="fused") -> "mwd.CompressedStack":
+    stack = mwd.from_numpy(st, dev)
+    return stack.without_index() if mode == "two_pass" else stack
 
 
 def run_decode(stack, dev, es=None, fill=POISON, offset=0):
@@ -73,11 +81,12 @@ def stack_case(name, orc):
     return _cache[name]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name", ["tiny_nvfp4", "gate_nvfp4", "down_nvfp4", "mxfp4"])
-def test_full_decode_matches_oracle(orc, dev, name):
+def test_full_decode_matches_oracle(orc, dev, name, mode):
     spec, x, st = stack_case(name, orc)
-    print(f"[parity] full decode {name} {x.shape} entries={st['exceptions'].size}", flush=True)
-    got = run_decode(upload(st, dev), dev)
+    print(f"[parity] full decode {name} {mode} {x.shape} entries={st['exceptions'].size}", flush=True)
+    got = run_decode(upload(st, dev, mode), dev)
     want = oracle_expect(orc, st)
     assert_bytes_equal(got, want, name)
     assert_bytes_equal(got, x, name + " vs input")
@@ -88,8 +97,18 @@ def test_library_encoded_stream_decodes(orc, dev, name):
     spec, x, st = stack_case(name, orc)
     lib_stack = mwd.prepare(torch.from_numpy(x).to(dev), spec.fmt)
     assert lib_stack.device.type == "cuda"  # preparation keeps the input's device
-    got = run_decode(lib_stack, dev)
-    assert_bytes_equal(got, x, name)
+    for mode_stack in (lib_stack, lib_stack.without_index()):
+        assert_bytes_equal(run_decode(mode_stack, dev), x, name)
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "gate_nvfp4", "down_nvfp4", "mxfp4"])
+def test_gpu_index_matches_oracle(orc, dev, name):
+    spec, x, st = stack_case(name, orc)
+    stack = upload(st, dev).without_index()
+    idx = mwd.build_index(stack)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), st["tile_index"])
+    assert_bytes_equal(run_decode(stack, dev), x, name + " with the GPU-built index")
 
 
 RAGGED = [
@@ -110,61 +129,68 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("fmt,E,R,C", RAGGED, ids=[f"f{c[0]}_{c[1]}x{c[2]}x{c[3]}" for c in RAGGED])
-def test_ragged_uniform_bytes(orc, dev, fmt, E, R, C):
+def test_ragged_uniform_bytes(orc, dev, fmt, E, R, C, mode):
     x = workloads.uniform_bytes(E, R, C, seed=E * 1000 + R * 10 + C)
     st = orc.encode(fmt, x)
-    got = run_decode(upload(st, dev), dev)
+    got = run_decode(upload(st, dev, mode), dev)
     assert_bytes_equal(got, oracle_expect(orc, st), "uniform")
     assert_bytes_equal(got, x, "uniform vs input")
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("fmt,E,R,C", [(workloads.NVFP4, 3, 1000, 50), (workloads.MXFP4, 3, 800, 160),
                                        (workloads.NVFP4, 2, 64, 8), (workloads.NVFP4, 2, 250, 130)])
-def test_generated_distributions_small(orc, dev, fmt, E, R, C):
+def test_generated_distributions_small(orc, dev, fmt, E, R, C, mode):
     if fmt == workloads.NVFP4:
         x = workloads.nvfp4_stack(E, R, C, 21, 0.10, hot_row_frac=0.02)
     else:
         x = workloads.mxfp4_stack(E, R, C, 22, 0.15)
     st = orc.encode(fmt, x)
-    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "generated")
+    assert_bytes_equal(run_decode(upload(st, dev, mode), dev), x, "generated")
 
 
-def test_largest_plane(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_largest_plane(orc, dev, mode):
     # R*C = 2^24 - 16: the largest plane an entry's 24-bit position can address
     R, C = 1048575, 16
     x = workloads.nvfp4_stack(1, R, C, 31, 0.05)
     st = orc.encode(workloads.NVFP4, x)
-    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "largest plane")
+    assert_bytes_equal(run_decode(upload(st, dev, mode), dev), x, "largest plane")
 
 
-def test_most_experts(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_most_experts(orc, dev, mode):
     x = workloads.nvfp4_stack(mwd.MAX_EXPERTS, 4, 24, 32, 0.2)
     st = orc.encode(workloads.NVFP4, x)
-    assert_bytes_equal(run_decode(upload(st, dev), dev), x, "2048 experts")
+    assert_bytes_equal(run_decode(upload(st, dev, mode), dev), x, "2048 experts")
     es = workloads.routing(mwd.MAX_EXPERTS, 300, 5, seed=33)
-    got = run_decode(upload(st, dev), dev, es=es)
+    got = run_decode(upload(st, dev, mode), dev, es=es)
     assert_bytes_equal(got, oracle_expect(orc, st, es), "2048 experts routed")
 
 
-def test_no_exceptions(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_no_exceptions(orc, dev, mode):
     x = workloads.nvfp4_stack(4, 64, 128, 5, 0.0)
     st = orc.encode(workloads.NVFP4, x)
     assert st["exceptions"].size == 0
-    stack = upload(st, dev)
+    stack = upload(st, dev, mode)
     assert stack.num_exceptions == 0 and stack.descriptor().exceptions is None
     assert_bytes_equal(run_decode(stack, dev), x, "no exceptions")
 
 
-def test_alternative_bases(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_alternative_bases(orc, dev, mode):
     rng = np.random.default_rng(41)
     for fmt in (workloads.NVFP4, workloads.MXFP4):
         x = workloads.uniform_bytes(3, 50, 50, 42 + fmt)
         st = orc.encode_with_bases(fmt, x, rng.integers(0, 256, (3, 50), dtype=np.uint8))
-        assert_bytes_equal(run_decode(upload(st, dev), dev), x, "random bases")
+        assert_bytes_equal(run_decode(upload(st, dev, mode), dev), x, "random bases")
 
 
-def test_arbitrary_offset_fields(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_arbitrary_offset_fields(orc, dev, mode):
     """Streams the encoder never writes (random fields everywhere, wrapping
     sums, fields past the plane) still decode exactly as the oracle does."""
     rng = np.random.default_rng(43)
@@ -173,25 +199,28 @@ def test_arbitrary_offset_fields(orc, dev):
         st = dict(st)
         st["offsets"] = rng.integers(0, 256, st["offsets"].size, dtype=np.uint8)
         st["bases"] = rng.integers(0, 256, st["bases"].size, dtype=np.uint8)
-        assert_bytes_equal(run_decode(upload(st, dev), dev), oracle_expect(orc, st), "random fields")
+        assert_bytes_equal(run_decode(upload(st, dev, mode), dev), oracle_expect(orc, st), "random fields")
 
 
-def test_entries_outside_plane_are_dropped(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_entries_outside_plane_are_dropped(orc, dev, mode):
     x = np.full((3, 2, 8), 0x40, dtype=np.uint8)
     st = dict(orc.encode(workloads.NVFP4, x))
     st["exceptions"] = np.array([(3 << 8) | 0x99, (16 << 8) | 0x77, (20 << 8) | 0x11,
                                  (15 << 8) | 0x33, (1 << 23 | 5) << 8 | 0x44], dtype=np.uint32)
     st["prefix"] = np.array([0, 3, 4, 5], dtype=np.int32)
+    st["tile_index"] = orc.build_index(st)
     for es in (None, np.array([0, 1, 1, 2], dtype=np.int32)):
-        got = run_decode(upload(st, dev), dev, es=es)
+        got = run_decode(upload(st, dev, mode), dev, es=es)
         assert_bytes_equal(got, oracle_expect(orc, st, es), "out-of-plane entries")
 
 
 # -- routing -------------------------------------------------------------------
 
-def test_tiny_every_routed_subset(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_every_routed_subset(orc, dev, mode):
     spec, x, st = stack_case("tiny_nvfp4", orc)
-    stack = upload(st, dev)
+    stack = upload(st, dev, mode)
     for m in range(1 << spec.E):
         mask = np.array([(m >> e) & 1 for e in range(spec.E)])
         es = workloads.expert_start_from_mask(mask, tokens=2)
@@ -199,17 +228,18 @@ def test_tiny_every_routed_subset(orc, dev):
         assert_bytes_equal(got, oracle_expect(orc, st, es), f"subset {mask}")
 
 
-def test_routed_garbage_expert_start(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_routed_garbage_expert_start(orc, dev, mode):
     spec, x, st = stack_case("tiny_nvfp4", orc)
     es = np.array([0, 5, 5, 3, -7], dtype=np.int32)  # only expert 0 has tokens
-    got = run_decode(upload(st, dev), dev, es=es)
+    got = run_decode(upload(st, dev, mode), dev, es=es)
     assert_bytes_equal(got, oracle_expect(orc, st, es), "garbage expert_start")
 
 
-def _paired(orc, dev, es, fill=POISON):
+def _paired(orc, dev, es, mode, fill=POISON):
     _, xg, sg = stack_case("gate_nvfp4", orc)
     _, xd, sd = stack_case("down_nvfp4", orc)
-    g, d = upload(sg, dev), upload(sd, dev)
+    g, d = upload(sg, dev, mode), upload(sd, dev, mode)
     wg = torch.full((g.dense_bytes,), fill, dtype=torch.uint8, device=dev)
     wd = torch.full((d.dense_bytes,), fill, dtype=torch.uint8, device=dev)
     es_t = None if es is None else torch.from_numpy(es).to(dev)
@@ -219,39 +249,44 @@ def _paired(orc, dev, es, fill=POISON):
             oracle_expect(orc, sg, es, fill), oracle_expect(orc, sd, es, fill))
 
 
-def test_routed_paired_gate_down(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_routed_paired_gate_down(orc, dev, mode):
     es = workloads.ROUTED.expert_start()
-    print(f"[parity] routed paired, active experts {np.nonzero(np.diff(es))[0].tolist()}", flush=True)
-    gg, gd, wg, wd = _paired(orc, dev, es)
+    print(f"[parity] routed paired {mode}, active experts {np.nonzero(np.diff(es))[0].tolist()}", flush=True)
+    gg, gd, wg, wd = _paired(orc, dev, es, mode)
     assert_bytes_equal(gg, wg, "routed gate")
     assert_bytes_equal(gd, wd, "routed down")
     inactive = np.diff(es) <= 0
     assert np.all(gg[inactive] == POISON) and np.all(gd[inactive] == POISON)
 
 
-def test_paired_full_and_all_inactive(orc, dev):
-    gg, gd, wg, wd = _paired(orc, dev, None)
+@pytest.mark.parametrize("mode", MODES)
+def test_paired_full_and_all_inactive(orc, dev, mode):
+    gg, gd, wg, wd = _paired(orc, dev, None, mode)
     assert_bytes_equal(gg, wg, "paired gate")
     assert_bytes_equal(gd, wd, "paired down")
     es = np.zeros(513, dtype=np.int32)
-    gg, gd, _, _ = _paired(orc, dev, es)
+    gg, gd, _, _ = _paired(orc, dev, es, mode)
     assert np.all(gg == POISON) and np.all(gd == POISON), "no expert routed: nothing written"
 
 
-def test_paired_all_active_equals_full(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_paired_all_active_equals_full(orc, dev, mode):
     es = workloads.expert_start_from_mask(np.ones(512, dtype=np.int64), tokens=1)
-    gg, gd, wg, wd = _paired(orc, dev, es)
+    gg, gd, wg, wd = _paired(orc, dev, es, mode)
     _, xg, _ = stack_case("gate_nvfp4", orc)
     _, xd, _ = stack_case("down_nvfp4", orc)
     assert_bytes_equal(gg, xg, "all active gate")
     assert_bytes_equal(gd, xd, "all active down")
 
 
-def test_paired_mixed_formats(orc, dev):
+@pytest.mark.parametrize("mode", MODES + ["one_indexed"])
+def test_paired_mixed_formats(orc, dev, mode):
     xa = workloads.nvfp4_stack(16, 100, 50, 51, 0.1)
     xb = workloads.mxfp4_stack(16, 60, 160, 52, 0.15)
     sa, sb = orc.encode(workloads.NVFP4, xa), orc.encode(workloads.MXFP4, xb)
-    a, b = upload(sa, dev), upload(sb, dev)
+    a = upload(sa, dev, "two_pass" if mode == "two_pass" else "fused")
+    b = upload(sb, dev, "fused" if mode == "fused" else "two_pass")
     es = workloads.routing(16, 5, 9, seed=53)
     wa = torch.full((a.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
     wb = torch.full((b.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
@@ -263,15 +298,16 @@ def test_paired_mixed_formats(orc, dev):
 
 # -- workspace, passes, streams, graphs -----------------------------------------
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("offset", [1, 3, 7, 15])
-def test_odd_offset_workspace(orc, dev, offset):
+def test_odd_offset_workspace(orc, dev, offset, mode):
     for name in ("tiny_nvfp4", "mxfp4"):
         spec, x, st = stack_case(name, orc)
-        got = run_decode(upload(st, dev), dev, offset=offset)
+        got = run_decode(upload(st, dev, mode), dev, offset=offset)
         assert_bytes_equal(got, x, f"{name} at offset {offset}")
     es = workloads.expert_start_from_mask(np.array([1, 0, 1, 1]), tokens=1)
     spec, x, st = stack_case("tiny_nvfp4", orc)
-    got = run_decode(upload(st, dev), dev, es=es, offset=offset)
+    got = run_decode(upload(st, dev, mode), dev, es=es, offset=offset)
     assert_bytes_equal(got, oracle_expect(orc, st, es), "routed odd offset")
 
 
@@ -292,9 +328,10 @@ def test_passes_one_at_a_time(orc, dev):
     assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), x, "fixed then exceptions")
 
 
-def test_repeat_is_deterministic(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_repeat_is_deterministic(orc, dev, mode):
     spec, x, st = stack_case("mxfp4", orc)
-    stack = upload(st, dev)
+    stack = upload(st, dev, mode)
     ws = torch.empty(stack.dense_bytes, dtype=torch.uint8, device=dev)
     ref = torch.from_numpy(x.reshape(-1)).to(dev)
     for i in range(20):
@@ -318,12 +355,13 @@ def test_side_stream_ordering(orc, dev):
     assert torch.equal(ws, ref)
 
 
-def test_graph_replay_follows_routing(orc, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_graph_replay_follows_routing(orc, dev, mode):
     """One captured paired decode replayed with three routings, poisoned
     workspaces in between; the library allocates nothing during capture."""
     _, xg, sg = stack_case("gate_nvfp4", orc)
     _, xd, sd = stack_case("down_nvfp4", orc)
-    g, d = upload(sg, dev), upload(sd, dev)
+    g, d = upload(sg, dev, mode), upload(sd, dev, mode)
     wg = torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev)
     wd = torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)
     es_t = torch.zeros(513, dtype=torch.int32, device=dev)
