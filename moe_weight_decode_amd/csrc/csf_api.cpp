@@ -20,15 +20,35 @@ using csf::StackArgs;
 
 constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of an entry
 
-// Workgroups per CU the grids aim for (persistent tile loops).
-#ifndef CSF_TILE_WG_PER_CU
-#define CSF_TILE_WG_PER_CU 8
+// Launch plan of the tile kernels (measured on MI355X with HBM-resident
+// stacks): NVFP4 stacks with few exceptions stream best in 16384-position
+// tiles at 6 workgroups per CU; stacks with more exceptions, and MXFP4, in
+// 8192-position tiles at 7 per CU; routed decodes of a few experts in
+// 4096-position tiles, which spread the little work over more CUs.
+#ifndef CSF_SPARSE_RUNS
+#define CSF_SPARSE_RUNS 4
 #endif
-#ifndef CSF_EXC_WG_PER_CU
-#define CSF_EXC_WG_PER_CU 8
+#ifndef CSF_SPARSE_WG_PER_CU
+#define CSF_SPARSE_WG_PER_CU 6
+#endif
+#ifndef CSF_DENSE_RUNS
+#define CSF_DENSE_RUNS 2
+#endif
+#ifndef CSF_DENSE_WG_PER_CU
+#define CSF_DENSE_WG_PER_CU 7
+#endif
+#ifndef CSF_ROUTED_RUNS
+#define CSF_ROUTED_RUNS 1
 #endif
 #ifndef CSF_ROUTED_WG_PER_CU
 #define CSF_ROUTED_WG_PER_CU 2
+#endif
+// "Few exceptions": at most this many entries per million dense positions.
+#ifndef CSF_SPARSE_PPM
+#define CSF_SPARSE_PPM 50000
+#endif
+#ifndef CSF_EXC_WG_PER_CU
+#define CSF_EXC_WG_PER_CU 8
 #endif
 
 int offset_bits(int32_t format) {
@@ -74,7 +94,7 @@ int64_t index_tiles(int32_t R, int32_t C) {
 
 static_assert(CSF_INDEX_TILE == csf::kIndexTile, "index tile of the ABI and the kernels");
 
-void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws) {
+void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t tile) {
     const uint32_t P = uint32_t(s.rows) * uint32_t(s.cols);
     const uint32_t C = uint32_t(s.cols);
     a.bases = s.bases;
@@ -89,17 +109,37 @@ void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws) {
     a.P = P;
     a.R = uint32_t(s.rows);
     a.C = C;
-    a.tiles = (P + csf::kTile - 1) / csf::kTile;
+    a.tiles = (P + tile - 1) / tile;
     a.index_tiles = uint32_t(index_tiles(s.rows, s.cols));
     a.wbits = uint32_t(offset_bits(s.format));
     a.row_mode = (C % 16 == 0) ? csf::kRowSplat : (C >= 16 ? csf::kRowTwo : csf::kRowBytes);
 }
 
-// LDS for one tile's row bases: a tile of kTile positions touches at most
-// (kTile - 1) / C + 2 rows; edge runs read up to kBasesSlack rows further.
-uint32_t bases_stage_bytes(uint32_t C) {
-    const uint32_t rows = (csf::kTile - 1) / C + 2 + csf::kBasesSlack;
+// LDS for one tile's row bases: a tile of `tile` positions touches at most
+// (tile - 1) / C + 2 rows; edge runs read up to kBasesSlack rows further.
+uint32_t bases_stage_bytes(uint32_t C, uint32_t tile) {
+    const uint32_t rows = (tile - 1) / C + 2 + csf::kBasesSlack;
     return (rows + 15u) & ~15u;
+}
+
+struct Plan {
+    uint32_t runs;
+    uint32_t wg_per_cu;
+};
+
+// Tile size and grid of the tile kernels for one call (host data only).
+Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
+    if (routed) return {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU};
+    int64_t entries = s0->num_exceptions, dense = int64_t(s0->num_experts) * s0->rows * s0->cols;
+    bool nvfp4 = s0->format == CSF_NVFP4_E4M3;
+    if (s1 != nullptr) {
+        entries += s1->num_exceptions;
+        dense += int64_t(s1->num_experts) * s1->rows * s1->cols;
+        nvfp4 = nvfp4 && s1->format == CSF_NVFP4_E4M3;
+    }
+    if (nvfp4 && entries * 1000000 <= dense * int64_t(CSF_SPARSE_PPM))
+        return {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU};
+    return {CSF_DENSE_RUNS, CSF_DENSE_WG_PER_CU};
 }
 
 uint32_t cu_count(hipStream_t stream) {
@@ -129,16 +169,19 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     const bool routed = expert_start != nullptr;
     if (routed && !aligned(expert_start, 4)) return CSF_E_ALIGN;
 
+    const Plan plan = plan_tiles(s0, s1, routed);
+    const uint32_t tile = csf::tile_positions(plan.runs);
     DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.expert_start = expert_start;
     a.nstacks = s1 ? 2u : 1u;
     a.E = uint32_t(s0->num_experts);
-    fill_stack(a.st[0], *s0, ws0);
-    a.bases_stage = bases_stage_bytes(a.st[0].C);
+    a.runs = plan.runs;
+    fill_stack(a.st[0], *s0, ws0, tile);
+    a.bases_stage = bases_stage_bytes(a.st[0].C, tile);
     if (s1) {
-        fill_stack(a.st[1], *s1, ws1);
-        a.bases_stage = std::max(a.bases_stage, bases_stage_bytes(a.st[1].C));
+        fill_stack(a.st[1], *s1, ws1, tile);
+        a.bases_stage = std::max(a.bases_stage, bases_stage_bytes(a.st[1].C, tile));
     } else {
         a.st[1] = a.st[0];  // never read: nstacks == 1
     }
@@ -146,7 +189,7 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const uint32_t cus = cu_count(stream);
     const uint64_t tile_units = uint64_t(a.E) * a.st[0].tiles + (s1 ? uint64_t(a.E) * a.st[1].tiles : 0);
-    const uint64_t tile_cap = uint64_t(cus) * (routed ? CSF_ROUTED_WG_PER_CU : CSF_TILE_WG_PER_CU);
+    const uint64_t tile_cap = uint64_t(cus) * plan.wg_per_cu;
     const uint32_t tile_grid = uint32_t(std::max<uint64_t>(1, std::min(tile_units, tile_cap)));
 
     const bool indexed = s0->tile_index != nullptr && (s1 == nullptr || s1->tile_index != nullptr);
@@ -176,7 +219,7 @@ csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_s
     if (st != CSF_OK) return st;
     if (!aligned(tile_index, 4)) return CSF_E_ALIGN;
     StackArgs a;
-    fill_stack(a, *s, nullptr);
+    fill_stack(a, *s, nullptr, csf::kIndexTile);
     if (a.n_exc == 0) a.exc = nullptr;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (csf::launch_build_index(a, uint32_t(s->num_experts), tile_index, stream) != hipSuccess)

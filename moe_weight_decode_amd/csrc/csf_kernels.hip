@@ -23,7 +23,8 @@
 // The work is a byte expansion bound by HBM bandwidth: no matrix cores, a few
 // integer ops per output byte.  Lane l of a workgroup owns the 16-byte output
 // runs l, l + 256, ... of a tile, so every store instruction of a wave covers
-// 1 KiB of contiguous output.
+// 1 KiB of contiguous output.  A tile is 4096, 8192 or 16384 positions (1, 2
+// or 4 runs per lane); the host picks one per launch.
 #include "csf_launch.h"
 
 namespace csf {
@@ -94,10 +95,15 @@ __device__ __forceinline__ u32x4 run_bases(const uint8_t *lds, uint32_t pos, uin
 }
 
 // Store up to 16 bytes of v at dst.  Full, 16-byte aligned runs (every run of
-// an aligned plane whose size is a multiple of 16) take one 128-bit store.
+// an aligned plane whose size is a multiple of 16) take one 128-bit store;
+// STREAM marks it non-temporal (the decoder never reads its output back).
+template <bool STREAM>
 __device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t nvalid) {
     if (nvalid >= 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-        *reinterpret_cast<u32x4 *>(dst) = v;
+        if constexpr (STREAM)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+        else
+            *reinterpret_cast<u32x4 *>(dst) = v;
         return;
     }
     const uint32_t n = nvalid < 16 ? nvalid : 16;
@@ -184,54 +190,59 @@ __device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, int32_t *
 // Expand this lane's runs of one tile: tile positions q0 .. q1-1, lds_bases
 // holding rows from r_lo.  FUSED writes the runs into the LDS tile; otherwise
 // they are stored to the plane directly.
-template <int WB, int MODE, bool FUSED>
+template <int WB, int MODE, bool FUSED, uint32_t RUNS>
 __device__ __forceinline__ void expand_tile(const StackArgs &st, const u32x4 *v, uint32_t q0,
                                             uint32_t q1, const uint8_t *lds_bases, uint32_t r_lo,
                                             uint8_t *tile, uint8_t *plane) {
     constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
     constexpr uint32_t FMASK = 8 / WB - 1;  // fields per group - 1
 #pragma unroll
-    for (uint32_t i = 0; i < kRunsPerLane; ++i) {
+    for (uint32_t i = 0; i < RUNS; ++i) {
         const uint32_t j = i * kBlock + threadIdx.x;
-        const uint32_t pos = q0 + 16u * j;
+        const uint32_t pos = q0 + kRunBytes * j;
         if (pos >= q1) break;
         const uint32_t f = (pos >> 4) & FMASK;
         const u32x4 field = (v[i] >> (uint32_t)(WB * f)) & MASK;
         const u32x4 out = add_bytes4(field, run_bases<MODE>(lds_bases, pos, r_lo, st.C, st.rcp_cols));
         if constexpr (FUSED) {
-            *reinterpret_cast<u32x4 *>(tile + 16u * j) = out;
+            *reinterpret_cast<u32x4 *>(tile + kRunBytes * j) = out;
         } else {
-            store_run(plane + pos, out, st.P - pos);
+            store_run<false>(plane + pos, out, st.P - pos);
         }
     }
 }
 
-template <bool FUSED>
+template <bool FUSED, uint32_t RUNS>
 __device__ __forceinline__ void expand_dispatch(const StackArgs &st, const u32x4 *v, uint32_t q0,
                                                 uint32_t q1, const uint8_t *lds_bases,
                                                 uint32_t r_lo, uint8_t *tile, uint8_t *plane) {
     switch ((st.wbits == 4 ? 0u : 3u) + st.row_mode) {
-        case 0: expand_tile<4, kRowSplat, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 1: expand_tile<4, kRowTwo, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 2: expand_tile<4, kRowBytes, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 3: expand_tile<1, kRowSplat, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 4: expand_tile<1, kRowTwo, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        default: expand_tile<1, kRowBytes, FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 0: expand_tile<4, kRowSplat, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 1: expand_tile<4, kRowTwo, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 2: expand_tile<4, kRowBytes, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 3: expand_tile<1, kRowSplat, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 4: expand_tile<1, kRowTwo, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        default: expand_tile<1, kRowBytes, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Tile loop shared by the fused and the fixed-stream kernels.
 //
-// Work unit = (stack, active expert, tile of kTile positions).  Per tile the
-// workgroup loads each lane's 16-byte offset groups with 128-bit loads (lanes
-// reading fields of the same group share one load), stages the tile's row
-// bases in LDS, widens each lane's field to 16 bytes and adds the row bases
-// byte-wise.  FUSED then patches the tile's exception entries into the LDS
-// tile and stores the finished tile.
+// Work unit = (stack, active expert, tile of TILE = 4096 * RUNS positions).
+// Per tile the workgroup loads each lane's 16-byte offset groups with 128-bit
+// loads (lanes reading fields of the same group share one load), stages the
+// tile's row bases in LDS, widens each lane's field to 16 bytes and adds the
+// row bases byte-wise.  FUSED then patches the tile's exception entries into
+// the LDS tile and stores the finished tile with non-temporal stores.
 // ---------------------------------------------------------------------------
-template <bool FUSED>
+template <bool FUSED, uint32_t RUNS>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+    constexpr uint32_t TILE = tile_positions(RUNS);
+    constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
+    // Entries prefetched per lane: 16384-position tiles serve sparse stacks
+    // only (a few entries per lane), so they keep fewer registers for them.
+    constexpr uint32_t EXC = RUNS >= 4 ? kExcRegs / 2 : kExcRegs;
     uint8_t *lds_bases = dyn;
     uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
     int32_t *es = reinterpret_cast<int32_t *>(dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u));
@@ -248,31 +259,31 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
         const uint32_t k = uu / st.tiles;
         const uint32_t t = uu - k * st.tiles;
         const uint32_t e = routed ? (uint32_t)act[k] : k;
-        const uint32_t q0 = t * kTile;
-        const uint32_t q1 = min(q0 + kTile, st.P);
+        const uint32_t q0 = t * TILE;
+        const uint32_t q1 = min(q0 + TILE, st.P);
 
         // Offset groups: run q (positions 16q .. 16q+15) is field q % F of
         // group q / F, F = 8 / w fields per group.
         const u32x4 *seg = reinterpret_cast<const u32x4 *>(st.offsets + (uint64_t)e * st.stride);
         const uint32_t gshift = st.wbits == 4 ? 1u : 3u;
-        u32x4 v[kRunsPerLane];
+        u32x4 v[RUNS];
 #pragma unroll
-        for (uint32_t i = 0; i < kRunsPerLane; ++i) {
-            const uint32_t pos = q0 + 16u * (i * kBlock + threadIdx.x);
+        for (uint32_t i = 0; i < RUNS; ++i) {
+            const uint32_t pos = q0 + kRunBytes * (i * kBlock + threadIdx.x);
             v[i] = pos < q1 ? seg[(pos >> 4) >> gshift] : (u32x4){0u, 0u, 0u, 0u};
         }
 
         // The tile's exception entries, prefetched into registers.
         uint32_t lo = 0, hi = 0;
-        uint32_t w[kExcRegs];
+        uint32_t w[EXC];
         if constexpr (FUSED) {
-            const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles + t * kIndexPerTile;
-            const uint32_t last = min(kIndexPerTile, st.index_tiles - t * kIndexPerTile);
+            const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles + t * INDEX_PER_TILE;
+            const uint32_t last = min(INDEX_PER_TILE, st.index_tiles - t * INDEX_PER_TILE);
             const int32_t l0 = ti[0], h0 = ti[last];
             hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
             lo = l0 < 0 ? 0u : min((uint32_t)l0, hi);
 #pragma unroll
-            for (uint32_t i = 0; i < kExcRegs; ++i) {
+            for (uint32_t i = 0; i < EXC; ++i) {
                 const uint32_t kk = lo + i * kBlock + threadIdx.x;
                 w[i] = kk < hi ? st.exc[kk] : 0xffffffffu;  // position 2^24 - 1: never in a tile
             }
@@ -287,27 +298,28 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
         __syncthreads();
 
         uint8_t *plane = st.ws + (uint64_t)e * st.P;
-        expand_dispatch<FUSED>(st, v, q0, q1, lds_bases, r_lo, tile, plane);
+        expand_dispatch<FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane);
 
         if constexpr (FUSED) {
             __syncthreads();  // tile expanded
 #pragma unroll
-            for (uint32_t i = 0; i < kExcRegs; ++i) {
+            for (uint32_t i = 0; i < EXC; ++i) {
                 const uint32_t pos = w[i] >> 8;
                 if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(w[i] & 0xffu);
             }
-            for (uint32_t kk = lo + kExcRegs * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
+            for (uint32_t kk = lo + EXC * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
                 const uint32_t x = st.exc[kk];
                 const uint32_t pos = x >> 8;
                 if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
             }
             __syncthreads();  // tile patched
 #pragma unroll
-            for (uint32_t i = 0; i < kRunsPerLane; ++i) {
+            for (uint32_t i = 0; i < RUNS; ++i) {
                 const uint32_t j = i * kBlock + threadIdx.x;
-                const uint32_t pos = q0 + 16u * j;
+                const uint32_t pos = q0 + kRunBytes * j;
                 if (pos >= q1) break;
-                store_run(plane + pos, *reinterpret_cast<const u32x4 *>(tile + 16u * j), st.P - pos);
+                store_run<true>(plane + pos, *reinterpret_cast<const u32x4 *>(tile + kRunBytes * j),
+                                st.P - pos);
             }
             // The next tile's first barrier orders these LDS reads before the
             // next expansion overwrites the tile.
@@ -315,15 +327,21 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
     }
 }
 
-__global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
+#ifndef CSF_MIN_WAVES_PER_SIMD
+#define CSF_MIN_WAVES_PER_SIMD 1
+#endif
+
+template <uint32_t RUNS>
+__global__ __launch_bounds__(kBlock, CSF_MIN_WAVES_PER_SIMD) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    __shared__ __align__(16) uint8_t tile[kTile];
-    tile_loop<true>(a, dyn_lds, tile);
+    __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
+    tile_loop<true, RUNS>(a, dyn_lds, tile);
 }
 
-__global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
+template <uint32_t RUNS>
+__global__ __launch_bounds__(kBlock, CSF_MIN_WAVES_PER_SIMD) void csf_fixed_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    tile_loop<false>(a, dyn_lds, nullptr);
+    tile_loop<false, RUNS>(a, dyn_lds, nullptr);
 }
 
 // Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
@@ -473,12 +491,24 @@ static size_t exc_lds_bytes(const DecodeArgs &a) {
 }
 
 hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL(csf_fixed_kernel, dim3(grid), dim3(kBlock), tile_lds_bytes(a), stream, a);
+    const size_t lds = tile_lds_bytes(a);
+    switch (a.runs) {
+        case 1: hipLaunchKernelGGL(csf_fixed_kernel<1>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(csf_fixed_kernel<2>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(csf_fixed_kernel<4>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL(csf_fused_kernel, dim3(grid), dim3(kBlock), tile_lds_bytes(a), stream, a);
+    const size_t lds = tile_lds_bytes(a);
+    switch (a.runs) {
+        case 1: hipLaunchKernelGGL(csf_fused_kernel<1>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(csf_fused_kernel<2>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(csf_fused_kernel<4>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -8,11 +8,12 @@
 namespace csf {
 
 constexpr uint32_t kBlock = 256;                    // threads per workgroup (4 wave64)
-constexpr uint32_t kTile = 8192;                    // plane positions per tile (one workgroup pass)
-constexpr uint32_t kRunsPerLane = kTile / 16 / kBlock;  // 16-byte output runs per lane per tile
+constexpr uint32_t kRunBytes = 16;                  // output bytes per lane per run
 constexpr uint32_t kIndexTile = 2048;               // positions per exception-index tile
-constexpr uint32_t kIndexPerTile = kTile / kIndexTile;
 constexpr uint32_t kExcRegs = 8;                    // entries per lane prefetched per tile
+
+// Tile = kBlock * kRunBytes * runs positions, runs (per lane) in {1, 2, 4}.
+constexpr uint32_t tile_positions(uint32_t runs) { return kBlock * kRunBytes * runs; }
 constexpr uint32_t kExcPerLane = 8;                 // entries per lane per scatter chunk
 constexpr uint32_t kBasesSlack = 32;                // rows read past a tile's last row by edge runs
 
@@ -37,7 +38,7 @@ struct StackArgs {
     uint32_t P;                 // R * C  (< 2^24)
     uint32_t R;
     uint32_t C;
-    uint32_t tiles;             // ceil(P / kTile)
+    uint32_t tiles;             // ceil(P / tile positions of the launch)
     uint32_t index_tiles;       // ceil(P / kIndexTile)
     uint32_t wbits;             // 4 (NVFP4) or 1 (MXFP4)
     uint32_t row_mode;          // RowMode
@@ -49,13 +50,13 @@ struct DecodeArgs {
     uint32_t nstacks;             // 1 or 2
     uint32_t E;                   // experts (same for both stacks)
     uint32_t bases_stage;         // bytes of dynamic LDS for one tile's row bases
-    uint32_t pad_;
+    uint32_t runs;                // 16-byte runs per lane per tile (1, 2 or 4)
 };
 
 // Dynamic LDS bytes a tile kernel needs for these arguments.
 size_t tile_lds_bytes(const DecodeArgs &a);
 
-// Fixed stream alone: every position = base + offset field.
+// Fixed stream alone: every position = base + offset field (a.runs picks the tile).
 hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 // Exception scatter alone (after the fixed stream): entries overwrite their positions.
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
