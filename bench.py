@@ -17,7 +17,10 @@ Prints ONE JSON line on stdout:
               HBM3E peak (8 TB/s)
   cpu_baseline the CPU oracle decoding the same stack on one host core
 
-  python bench.py [--steps K] [--warmup W] [--sets N] [--all] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--sets N] [--workload NAME] [--all] [--no-cpu]
+
+--workload picks another timed workload (down_nvfp4, mxfp4, tiny_nvfp4,
+routed_paired) for profiling; the default is the gate-like stack.
 
 --all also measures the other workloads (down-like, MXFP4, routed paired,
 tiny), the two-pass decode of each (fixed-stream kernel, then exception
@@ -199,6 +202,16 @@ def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
     return out
 
 
+def _repeat(fn, budget_s):
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t)
+    return statistics.median(times), len(times)
+
+
 def cpu_baseline(spec, x, budget_s=10.0):
     """The oracle (plain C, one thread) decoding the whole stack, repeated for
     about `budget_s` seconds; GB/s on the same byte formula as the GPU."""
@@ -208,22 +221,60 @@ def cpu_baseline(spec, x, budget_s=10.0):
     ws = orc.decode(st)
     if not (ws == x).all():
         raise SystemExit("oracle round trip failed")
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while time.perf_counter() < t_end or len(times) < 3:
-        t = time.perf_counter()
-        orc.decode(st, None, ws)
-        times.append(time.perf_counter() - t)
+    sec, n = _repeat(lambda: orc.decode(st, None, ws), budget_s)
     E = spec.E
     comp = E * spec.R + E * st["stride"] + 4 * st["exceptions"].size + 4 * (E + 1)
-    sec = statistics.median(times)
     return dict(value=round((comp + x.size) / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 us_per_stack=round(sec * 1e6, 1),
-                sample=f"whole {spec.name} stack ({spec.E}x{spec.R}x{spec.C}), decoded {len(times)} "
+                sample=f"whole {spec.name} stack ({spec.E}x{spec.R}x{spec.C}), decoded {n} "
                        f"times on one host core, median")
 
 
-def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True):
+def cpu_baseline_routed(workloads, budget_s=10.0):
+    """The oracle's routed decode of the gate and down stacks (8 of 512
+    experts), one host core; GB/s on the GPU's byte formula."""
+    import numpy as np
+    import oracle
+    orc = oracle.load()
+    gspec, dspec = workloads.ROUTED.stacks
+    es = workloads.ROUTED.expert_start()
+    act = np.diff(es) > 0
+    sts, wss, nbytes = [], [], 4 * len(es)
+    for spec in (gspec, dspec):
+        x = spec.generate()
+        st = orc.encode(spec.fmt, x)
+        sts.append(st)
+        wss.append(np.zeros(x.shape, dtype=np.uint8))
+        ent = int(np.diff(st["prefix"])[act].sum())
+        nbytes += int(act.sum()) * (spec.R + st["stride"] + spec.R * spec.C) + 4 * ent + 4 * (spec.E + 1)
+    sec, n = _repeat(lambda: [orc.decode(st, es, ws) for st, ws in zip(sts, wss)], budget_s)
+    return dict(value=round(nbytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                us_per_stack=round(sec * 1e6, 1),
+                sample=f"routed paired decode (8 of 512 experts) of the gate and down stacks, "
+                       f"{n} times on one host core, median")
+
+
+def routed_sets(workloads, E, n_active, max_tokens, seed, count):
+    """`count` routings whose active experts are disjoint groups of a seeded
+    permutation (each expert routed in turn), U{1..max_tokens} tokens each."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(E)
+    out = []
+    for i in range(count):
+        act = perm[(i * n_active) % E:(i * n_active) % E + n_active]
+        counts = np.zeros(E, dtype=np.int64)
+        counts[act] = rng.integers(1, max_tokens, n_active, endpoint=True)
+        out.append(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    return out
+
+
+def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, copies=2, routings=64):
+    """Paired gate + down decode of 8 routed experts.  Checks the configured
+    routing first.  Then times graph replays (no per-launch CPU cost) of
+    `copies` device copies of both stacks x `routings` disjoint routings, so
+    consecutive steps touch different planes, and of the configured routing
+    alone (warm)."""
     import numpy as np
     gspec, dspec = workloads.ROUTED.stacks
     xg, xd = gspec.generate(), dspec.generate()
@@ -233,8 +284,7 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True):
     es_t = torch.from_numpy(es).to(dev)
     wg = torch.full((g.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
     wd = torch.full((d.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
-    L = mwd.Launch(g, wg, d, wd, es_t)
-    L()
+    mwd.decode_paired(g, wg, d, wd, es_t)
     torch.cuda.synchronize()
     active = np.diff(es) > 0
     hg = wg.cpu().numpy().reshape(xg.shape)
@@ -242,10 +292,53 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True):
     if not (np.array_equal(hg[active], xg[active]) and np.all(hg[~active] == 0xA5)
             and np.array_equal(hd[active], xd[active]) and np.all(hd[~active] == 0xA5)):
         raise SystemExit("routed paired decode is wrong")
-    wall, evt = timed_loop(torch, ev, [L], steps, warmup)
+    spec = workloads.ROUTED
+    rs = routed_sets(workloads, gspec.E, spec.n_active, spec.max_tokens, spec.seed + 100, routings)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    calls, nbytes, keep = [], [], []
+    with torch.cuda.stream(side):
+        for c in range(copies):
+            gc, dc = (g, d) if c == 0 else (g.clone(), d.clone())
+            wgc = torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev)
+            wdc = torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)
+            for r in rs:
+                rt = torch.from_numpy(r).to(dev)
+                calls.append(mwd.Launch(gc, wgc, dc, wdc, rt))
+                act = np.diff(r) > 0
+                nbytes.append(sum(sum(stack_bytes(s, act)) for s in (gc, dc)) + 4 * len(r))
+        warm = [mwd.Launch(g, wg, d, wd, es_t)] * len(calls)
+        for L in calls + warm:  # warm the launch path outside capture
+            L()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for seq in (calls, warm):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            for L in seq:
+                L()
+        graphs.append(gr)
+    torch.cuda.synchronize()
+
+    class Replay:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def __init__(self, gr):
+            self.gr = gr
+
+        def __call__(self):
+            self.gr.replay()
+
+    reps = max(1, steps // len(calls))
+    wall, evt = timed_loop(torch, ev, [Replay(graphs[0])], reps, max(1, warmup // len(calls)))
+    wwall, wevt = timed_loop(torch, ev, [Replay(graphs[1])], reps, max(1, warmup // len(calls)))
+    n = len(calls)
     b = [stack_bytes(s, active) for s in (g, d)]
-    total = sum(f + e + dn for f, e, dn in b) + 4 * len(es)
-    return dict(step_ms=max(wall, evt), bytes=total, active=int(active.sum()))
+    return dict(step_ms=max(wall, evt) / n, event_ms=evt / n, wall_ms=wall / n,
+                bytes=sum(nbytes) / len(nbytes), warm_ms=max(wwall, wevt) / n,
+                warm_bytes=sum(sum(x) for x in b) + 4 * len(es), active=int(active.sum()),
+                sets=n, steps=reps * n)
 
 
 def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
@@ -271,6 +364,12 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other workloads on stderr")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="N",
+                    help="after the timed run, N plain 256 MiB device copies (reference for "
+                         "hardware byte counters)")
+    ap.add_argument("--workload", default="gate_nvfp4",
+                    choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired"],
+                    help="timed workload (default: the 512-expert gate-like stack)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the CSF decode path is rank-local and has no "
@@ -285,17 +384,50 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     ev = HipEvents()
-    spec = workloads.GATE
-    log(f"[bench] {spec.name}: generating and encoding {spec.E}x{spec.R}x{spec.C}")
-    r = bench_stack(mwd, torch, ev, spec, args.steps, args.warmup, args.sets, dev)
-    stack = r["stack"]
-    step_bytes = r["fixed_bytes"] + r["exc_bytes"] + r["dense_bytes"]
+    if args.workload == "routed_paired":
+        rr = bench_routed(mwd, torch, ev, workloads, args.steps, args.warmup, dev)
+        gs, ds = workloads.ROUTED.stacks
+        step_bytes = rr["bytes"]
+        r = dict(step_ms=rr["step_ms"], event_ms=rr["event_ms"], wall_ms=rr["wall_ms"])
+        config = {
+            "workload": f"routed_paired: one paired decode of the {gs.name} ({gs.E}x{gs.R}x{gs.C}) and "
+                        f"{ds.name} ({ds.E}x{ds.R}x{ds.C}) stacks with {rr['active']} of {gs.E} experts "
+                        f"routed (1..64 tokens each), int32 expert_start read on the device",
+            "decode": "single pass (fused kernel, tile index), routed; steps replayed from a "
+                      "HIP graph of all rotating sets",
+            "bytes_per_step": round(step_bytes),
+            "rotating_sets": rr["sets"],
+            "timed_steps": rr["steps"],
+            "warm_us_same_routing": round(rr["warm_ms"] * 1e3, 3),
+        }
+        x_head = None
+    else:
+        spec = workloads.STACKS[args.workload]
+        log(f"[bench] {spec.name}: generating and encoding {spec.E}x{spec.R}x{spec.C}")
+        r = bench_stack(mwd, torch, ev, spec, args.steps, args.warmup,
+                        args.sets if spec.E > 4 else 2, dev)
+        stack = r["stack"]
+        step_bytes = r["fixed_bytes"] + r["exc_bytes"] + r["dense_bytes"]
+        fmt = "NVFP4 (E4M3 scales)" if spec.fmt == workloads.NVFP4 else "MXFP4 (UE8M0 scales)"
+        config = {
+            "workload": f"{spec.name}: full-stack CSF decode of {spec.E} experts x {spec.R} rows x "
+                        f"{spec.C} scale columns (K={spec.K}), {spec.desc.split(', ', 1)[-1]}, "
+                        f"seed {spec.seed}",
+            "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": fmt,
+            "decode": "single pass (fused kernel, tile index)",
+            "exception_entries": stack.num_exceptions,
+            "compressed_bytes": r["fixed_bytes"] + r["exc_bytes"],
+            "dense_bytes": r["dense_bytes"],
+            "bytes_per_step": step_bytes,
+            "rotating_sets": args.sets if spec.E > 4 else 2,
+        }
+        x_head = r["x"]
     gbps = step_bytes / (r["step_ms"] * 1e-3) / 1e9
     launch_us = r["event_ms"] * 1e3
     achieved = step_bytes / (r["event_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
-    traffic = pmc_traffic("csf_fused_kernel", spec.name)
+    traffic = pmc_traffic("csf_fused_kernel", args.workload)
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -310,17 +442,7 @@ def main():
         "vs_baseline": None,
         "dtype": "u8",
         "data": "synthetic",
-        "config": {
-            "workload": f"{spec.name}: full-stack CSF decode of {spec.E} experts x {spec.R} rows x "
-                        f"{spec.C} E4M3 scale columns (K={spec.K}), 3% outliers, seed {spec.seed}",
-            "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": "NVFP4 (E4M3 scales)",
-            "decode": "single pass (fused kernel, tile index)",
-            "exception_entries": stack.num_exceptions,
-            "compressed_bytes": r["fixed_bytes"] + r["exc_bytes"],
-            "dense_bytes": r["dense_bytes"],
-            "bytes_per_step": step_bytes,
-            "rotating_sets": args.sets,
-        },
+        "config": config,
         "roofline": {
             "kernel": "csf_fused_kernel",
             "bound": "hbm",
@@ -329,7 +451,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": step_bytes,
+            "algorithmic_bytes_per_launch": round(step_bytes),
             "mean_launch_us": round(launch_us, 3),
         },
     }
@@ -356,19 +478,30 @@ def main():
             rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed)
             extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2),
                               gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                              bytes=rr["bytes"], active=rr["active"])
+                              warm_us=round(rr["warm_ms"] * 1e3, 2), bytes=round(rr["bytes"]),
+                              active=rr["active"], sets=rr["sets"])
             log(f"[bench] {key}: {extra[key]}")
         cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
         extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
         log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
         os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
         json.dump(extra, open(os.path.join(ROOT, "gpurun_out", "bench_all.json"), "w"), indent=1)
-        x_head = spec.generate()
-    else:
-        x_head = r["x"]
+    if args.calibrate_copy:
+        # an elementwise kernel (a large device-to-device copy_ may go to a DMA
+        # engine, which the counters do not see): 256 MiB read, 256 MiB written
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.calibrate_copy):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.calibrate_copy} calibration kernels reading and writing 268435456 bytes")
+        del src, dst
     if not args.no_cpu:
         log(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(spec, x_head, args.cpu_seconds)
+        if args.workload == "routed_paired":
+            out["cpu_baseline"] = cpu_baseline_routed(workloads, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(spec, x_head, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
