@@ -24,7 +24,10 @@ constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of
 // stacks): NVFP4 stacks with few exceptions stream best in 16384-position
 // tiles at 6 workgroups per CU; stacks with more exceptions, and MXFP4, in
 // 8192-position tiles at 7 per CU; routed decodes of a few experts in
-// 4096-position tiles, which spread the little work over more CUs.
+// 4096-position tiles, which spread the little work over more CUs, with
+// non-temporal loads (their planes are read once and rarely cache-resident).
+// Each lane loads 4 of its tile's exception entries with its offsets, 8 when
+// the stack's exception density would average more than 3.5 per lane.
 #ifndef CSF_SPARSE_RUNS
 #define CSF_SPARSE_RUNS 4
 #endif
@@ -46,6 +49,10 @@ constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of
 // "Few exceptions": at most this many entries per million dense positions.
 #ifndef CSF_SPARSE_PPM
 #define CSF_SPARSE_PPM 50000
+#endif
+// Mean entries per lane and tile above which a lane loads 8 instead of 4.
+#ifndef CSF_EXC_LANE_MILLI
+#define CSF_EXC_LANE_MILLI 3500
 #endif
 #ifndef CSF_EXC_WG_PER_CU
 #define CSF_EXC_WG_PER_CU 8
@@ -125,11 +132,13 @@ uint32_t bases_stage_bytes(uint32_t C, uint32_t tile) {
 struct Plan {
     uint32_t runs;
     uint32_t wg_per_cu;
+    bool stream_loads;
+    uint32_t exc_regs;
 };
 
-// Tile size and grid of the tile kernels for one call (host data only).
+// Tile size, grid and entry prefetch of the tile kernels for one call, from
+// host data only (formats, shapes, entry counts).
 Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
-    if (routed) return {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU};
     int64_t entries = s0->num_exceptions, dense = int64_t(s0->num_experts) * s0->rows * s0->cols;
     bool nvfp4 = s0->format == CSF_NVFP4_E4M3;
     if (s1 != nullptr) {
@@ -137,9 +146,18 @@ Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
         dense += int64_t(s1->num_experts) * s1->rows * s1->cols;
         nvfp4 = nvfp4 && s1->format == CSF_NVFP4_E4M3;
     }
-    if (nvfp4 && entries * 1000000 <= dense * int64_t(CSF_SPARSE_PPM))
-        return {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU};
-    return {CSF_DENSE_RUNS, CSF_DENSE_WG_PER_CU};
+    Plan p;
+    if (routed)
+        p = {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU, CSF_ROUTED_RUNS == 1, 4};
+    else if (nvfp4 && entries * 1000000 <= dense * int64_t(CSF_SPARSE_PPM))
+        p = {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU, false, 4};
+    else
+        p = {CSF_DENSE_RUNS, CSF_DENSE_WG_PER_CU, false, 4};
+    // mean entries per lane and tile = density * tile / kBlock
+    const int64_t tile = csf::tile_positions(p.runs);
+    if (p.runs == 2 && entries * tile * 1000 > dense * int64_t(csf::kBlock) * CSF_EXC_LANE_MILLI)
+        p.exc_regs = 8;
+    return p;
 }
 
 uint32_t cu_count(hipStream_t stream) {
@@ -177,6 +195,8 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     a.nstacks = s1 ? 2u : 1u;
     a.E = uint32_t(s0->num_experts);
     a.runs = plan.runs;
+    a.stream_loads = plan.stream_loads ? 1u : 0u;
+    a.exc_regs = plan.exc_regs;
     fill_stack(a.st[0], *s0, ws0, tile);
     a.bases_stage = bases_stage_bytes(a.st[0].C, tile);
     if (s1) {

@@ -235,14 +235,15 @@ __device__ __forceinline__ void expand_dispatch(const StackArgs &st, const u32x4
 // tile's row bases in LDS, widens each lane's field to 16 bytes and adds the
 // row bases byte-wise.  FUSED then patches the tile's exception entries into
 // the LDS tile and stores the finished tile with non-temporal stores.
+// EXC entries per lane are loaded together with the offsets (more, if the
+// tile holds them, are read after the expansion); STREAM_LOADS marks the
+// offset and entry loads non-temporal (routed decodes, whose few planes are
+// read once and are rarely cache-resident).
 // ---------------------------------------------------------------------------
-template <bool FUSED, uint32_t RUNS>
+template <bool FUSED, uint32_t RUNS, uint32_t EXC, bool STREAM_LOADS>
 __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
-    // Entries prefetched per lane: 16384-position tiles serve sparse stacks
-    // only (a few entries per lane), so they keep fewer registers for them.
-    constexpr uint32_t EXC = RUNS >= 4 ? kExcRegs / 2 : kExcRegs;
     uint8_t *lds_bases = dyn;
     uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
     int32_t *es = reinterpret_cast<int32_t *>(dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u));
@@ -270,7 +271,13 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
 #pragma unroll
         for (uint32_t i = 0; i < RUNS; ++i) {
             const uint32_t pos = q0 + kRunBytes * (i * kBlock + threadIdx.x);
-            v[i] = pos < q1 ? seg[(pos >> 4) >> gshift] : (u32x4){0u, 0u, 0u, 0u};
+            const u32x4 *src = seg + ((pos >> 4) >> gshift);
+            if (pos >= q1)
+                v[i] = (u32x4){0u, 0u, 0u, 0u};
+            else if constexpr (STREAM_LOADS)
+                v[i] = __builtin_nontemporal_load(src);
+            else
+                v[i] = *src;
         }
 
         // The tile's exception entries, prefetched into registers.
@@ -285,7 +292,12 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
 #pragma unroll
             for (uint32_t i = 0; i < EXC; ++i) {
                 const uint32_t kk = lo + i * kBlock + threadIdx.x;
-                w[i] = kk < hi ? st.exc[kk] : 0xffffffffu;  // position 2^24 - 1: never in a tile
+                if (kk >= hi)
+                    w[i] = 0xffffffffu;  // position 2^24 - 1: never in a tile
+                else if constexpr (STREAM_LOADS)
+                    w[i] = __builtin_nontemporal_load(st.exc + kk);
+                else
+                    w[i] = st.exc[kk];
             }
         }
 
@@ -327,21 +339,17 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
     }
 }
 
-#ifndef CSF_MIN_WAVES_PER_SIMD
-#define CSF_MIN_WAVES_PER_SIMD 1
-#endif
-
-template <uint32_t RUNS>
-__global__ __launch_bounds__(kBlock, CSF_MIN_WAVES_PER_SIMD) void csf_fused_kernel(DecodeArgs a) {
+template <uint32_t RUNS, uint32_t EXC, bool STREAM_LOADS>
+__global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
-    tile_loop<true, RUNS>(a, dyn_lds, tile);
+    tile_loop<true, RUNS, EXC, STREAM_LOADS>(a, dyn_lds, tile);
 }
 
 template <uint32_t RUNS>
-__global__ __launch_bounds__(kBlock, CSF_MIN_WAVES_PER_SIMD) void csf_fixed_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    tile_loop<false, RUNS>(a, dyn_lds, nullptr);
+    tile_loop<false, RUNS, 1, false>(a, dyn_lds, nullptr);
 }
 
 // Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
@@ -503,12 +511,18 @@ hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) 
 
 hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = tile_lds_bytes(a);
-    switch (a.runs) {
-        case 1: hipLaunchKernelGGL(csf_fused_kernel<1>, dim3(grid), dim3(kBlock), lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(csf_fused_kernel<2>, dim3(grid), dim3(kBlock), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(csf_fused_kernel<4>, dim3(grid), dim3(kBlock), lds, stream, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    const dim3 g(grid), b(kBlock);
+    // (runs, entries per lane, streaming loads) combinations the host plans
+    if (a.runs == 1 && a.exc_regs == 4 && a.stream_loads)
+        hipLaunchKernelGGL((csf_fused_kernel<1, 4, true>), g, b, lds, stream, a);
+    else if (a.runs == 2 && a.exc_regs == 4 && !a.stream_loads)
+        hipLaunchKernelGGL((csf_fused_kernel<2, 4, false>), g, b, lds, stream, a);
+    else if (a.runs == 2 && a.exc_regs == 8 && !a.stream_loads)
+        hipLaunchKernelGGL((csf_fused_kernel<2, 8, false>), g, b, lds, stream, a);
+    else if (a.runs == 4 && a.exc_regs == 4 && !a.stream_loads)
+        hipLaunchKernelGGL((csf_fused_kernel<4, 4, false>), g, b, lds, stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -10,7 +10,6 @@ namespace csf {
 constexpr uint32_t kBlock = 256;                    // threads per workgroup (4 wave64)
 constexpr uint32_t kRunBytes = 16;                  // output bytes per lane per run
 constexpr uint32_t kIndexTile = 2048;               // positions per exception-index tile
-constexpr uint32_t kExcRegs = 8;                    // entries per lane prefetched per tile
 
 // Tile = kBlock * kRunBytes * runs positions, runs (per lane) in {1, 2, 4}.
 constexpr uint32_t tile_positions(uint32_t runs) { return kBlock * kRunBytes * runs; }
@@ -51,6 +50,8 @@ struct DecodeArgs {
     uint32_t E;                   // experts (same for both stacks)
     uint32_t bases_stage;         // bytes of dynamic LDS for one tile's row bases
     uint32_t runs;                // 16-byte runs per lane per tile (1, 2 or 4)
+    uint32_t stream_loads;        // non-temporal offset/entry loads (fused, runs == 1 only)
+    uint32_t exc_regs;            // entries per lane loaded with the offsets (fused: 4 or 8)
 };
 
 // Dynamic LDS bytes a tile kernel needs for these arguments.
