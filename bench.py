@@ -469,8 +469,17 @@ def main():
                                two_pass_us=round(rr["two_pass_ms"] * 1e3, 2),
                                fixed_only_us=round(rr["fixed_only_ms"] * 1e3, 2),
                                bytes=b, entries=rr["stack"].num_exceptions)
+            xd = torch.from_numpy(rr["x"]).to(dev)
+            enc = []
+            for i in range(12):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                mwd.prepare(xd, s.fmt)  # device encode; reads back the entry count once
+                torch.cuda.synchronize()
+                enc.append(time.perf_counter() - t0)
+            extra[name]["gpu_encode_us"] = round(statistics.median(enc[2:]) * 1e6, 1)
             log(f"[bench] {name}: {extra[name]}")
-            del rr
+            del rr, xd
             torch.cuda.empty_cache()
         for indexed in (True, False):
             key = "routed_paired" + ("" if indexed else "_two_pass")

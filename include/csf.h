@@ -125,6 +125,32 @@ csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_
                        uint8_t *offsets, uint32_t *exceptions, int32_t *exc_prefix,
                        int32_t *tile_index);
 
+/* Phases of csf_encode_device. */
+#define CSF_ENCODE_STREAMS 1u /* bases, offsets, exc_prefix, tile_index */
+#define CSF_ENCODE_ENTRIES 2u /* exceptions */
+
+/*
+ * Encode a dense stack that is already in device memory, on the GPU ("Load
+ * native FP4 experts with optional lossless CSF scales", vLLM PR 964,
+ * preparation paragraphs: encoding and its index built on the GPU).  Same
+ * bytes as csf_prepare for every input.  All pointers are device pointers;
+ * dense is u8[E][R][C].  Two phases, so the caller can size the exception
+ * buffer in between (the library allocates nothing):
+ *   CSF_ENCODE_STREAMS writes bases (E*R), offsets (E*stride, 16-byte
+ *     aligned, stride = 16*ceil(R*C/G)), exc_prefix (E+1) and tile_index
+ *     (E*NT+1); exceptions is ignored.  Once the stream has run it,
+ *     exc_prefix[E] is the entry count n.
+ *   CSF_ENCODE_ENTRIES then writes the n entries to exceptions (u32[n]),
+ *     reading dense, bases and tile_index from the first phase.
+ * Both phases are enqueued on hip_stream and return without synchronising.
+ * Errors: CSF_E_NULL, CSF_E_FORMAT, CSF_E_SHAPE, CSF_E_SIZE (E*R*C >= 2^31, or
+ * a phase other than the two above), CSF_E_ALIGN, CSF_E_HIP.
+ */
+csf_status csf_encode_device(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
+                             const uint8_t *dense, uint8_t *bases, uint8_t *offsets,
+                             uint32_t *exceptions, int32_t *exc_prefix, int32_t *tile_index,
+                             uint32_t phase, void *hip_stream);
+
 /*
  * Build the tile index of a stack on the GPU from its exceptions and prefix
  * (device buffers, as in the descriptor; compressed->tile_index is ignored),

@@ -11,7 +11,8 @@ The functions mirror the C ABI in ``include/csf.h``:
 * ``prepare(dense, fmt)`` -> ``CompressedStack`` on ``dense``'s device
   (the preparation helper of "finegrained-kernels: decode losslessly
   compressed NVFP4 scales (CSF)", kernels-community PR 1236, API paragraph,
-  which keeps the input's device);
+  which keeps the input's device): a GPU tensor is encoded on the GPU
+  (``csf_encode_device``), host data by the host encoder (``csf_prepare``);
 * ``decode(stack, workspace, expert_start=None, stream=None)``;
 * ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``;
 * ``decode_passes(...)`` to enqueue the fixed-stream or exception pass alone;
@@ -36,6 +37,8 @@ MXFP4 = 1
 PASS_FIXED = 1
 PASS_EXCEPTIONS = 2
 PASS_ALL = 3
+ENCODE_STREAMS = 1
+ENCODE_ENTRIES = 2
 MAX_EXPERTS = 2048
 INDEX_TILE = 2048
 
@@ -44,8 +47,8 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsf.so")
 STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: "CSF_E_SIZE",
           5: "CSF_E_ALIGN", 6: "CSF_E_CORRUPT", 7: "CSF_E_MISMATCH", 8: "CSF_E_HIP"}
 
-EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_build_index", "csf_decode",
-           "csf_decode_paired", "csf_decode_passes", "csf_validate")
+EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_encode_device", "csf_build_index",
+           "csf_decode", "csf_decode_paired", "csf_decode_passes", "csf_validate")
 
 
 class CsfError(RuntimeError):
@@ -89,6 +92,8 @@ def _lib():
         lib.csf_status_str.argtypes = [ctypes.c_int]
         lib.csf_prepare.restype = ctypes.c_int
         lib.csf_prepare.argtypes = [i32, i32, i32, i32, vp, ctypes.POINTER(csf_sizes), vp, vp, vp, vp, vp]
+        lib.csf_encode_device.restype = ctypes.c_int
+        lib.csf_encode_device.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp]
         lib.csf_build_index.restype = ctypes.c_int
         lib.csf_build_index.argtypes = [ctypes.POINTER(csf_stack), vp, vp]
         lib.csf_decode.restype = ctypes.c_int
@@ -208,10 +213,45 @@ def _check(status: int, where: str):
         raise CsfError(status, where)
 
 
-def prepare(dense, fmt: int, index: bool = True) -> CompressedStack:
-    """Encode ``dense`` (uint8 [E, R, C], tensor or array) with the library's
-    encoder, with the tile index unless ``index`` is False; the result lives on
-    ``dense``'s device."""
+def offsets_stride(fmt: int, R: int, C: int) -> int:
+    """Offset bytes per expert: 16 per group of 128 / w positions."""
+    G = 32 if fmt == NVFP4 else 128
+    return 16 * ((R * C + G - 1) // G)
+
+
+def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> CompressedStack:
+    lib = _lib()
+    if x.dtype != torch.uint8 or x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("dense must be a contiguous uint8 [E, R, C] tensor")
+    E, R, C = (int(v) for v in x.shape)
+    dev = x.device
+    S = offsets_stride(fmt, R, C)
+    NT = (R * C + INDEX_TILE - 1) // INDEX_TILE
+    bases = torch.empty(E * R, dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E * S, dtype=torch.uint8, device=dev)
+    prefix = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tidx = torch.empty(E * NT + 1, dtype=torch.int32, device=dev)
+    h = _stream_handle(stream, dev)
+    _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), offsets.data_ptr(), None,
+                                 prefix.data_ptr(), tidx.data_ptr(), ENCODE_STREAMS, h),
+           "csf_encode_device(streams)")
+    if stream is not None:
+        stream.synchronize()
+    n = int(prefix[E].item())  # the one read-back: sizes the entry buffer
+    exc = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if n > 0:
+        _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), None, exc.data_ptr(),
+                                     None, tidx.data_ptr(), ENCODE_ENTRIES, h), "csf_encode_device(entries)")
+    return CompressedStack(fmt, E, R, C, S, n, bases, offsets, exc, prefix, tidx if index else None)
+
+
+def prepare(dense, fmt: int, index: bool = True, stream=None) -> CompressedStack:
+    """Encode ``dense`` (uint8 [E, R, C], tensor or array), with the tile index
+    unless ``index`` is False; the result lives on ``dense``'s device.  A GPU
+    tensor is encoded on the GPU (the count of exception entries is read back
+    once, to size their buffer); host data by the host encoder."""
+    if isinstance(dense, torch.Tensor) and dense.device.type == "cuda":
+        return _prepare_device(dense, fmt, index, stream)
     lib = _lib()
     device = dense.device if isinstance(dense, torch.Tensor) else torch.device("cpu")
     x = dense.detach().cpu().numpy() if isinstance(dense, torch.Tensor) else np.asarray(dense)

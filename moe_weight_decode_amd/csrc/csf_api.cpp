@@ -247,6 +247,45 @@ csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_s
     return CSF_OK;
 }
 
+csf_status encode_device_impl(int32_t format, int32_t E, int32_t R, int32_t C, const uint8_t *dense,
+                              uint8_t *bases, uint8_t *offsets, uint32_t *exceptions,
+                              int32_t *exc_prefix, int32_t *tile_index, uint32_t phase,
+                              void *hip_stream) {
+    csf_status st = check_shape(format, E, R, C);
+    if (st != CSF_OK) return st;
+    if (phase != CSF_ENCODE_STREAMS && phase != CSF_ENCODE_ENTRIES) return CSF_E_SIZE;
+    if (int64_t(E) * R * C >= (int64_t(1) << 31)) return CSF_E_SIZE;
+    if (dense == nullptr || bases == nullptr || tile_index == nullptr) return CSF_E_NULL;
+    if (phase == CSF_ENCODE_STREAMS && (offsets == nullptr || exc_prefix == nullptr)) return CSF_E_NULL;
+    if (phase == CSF_ENCODE_ENTRIES && exceptions == nullptr) return CSF_E_NULL;
+    if (!aligned(tile_index, 4)) return CSF_E_ALIGN;
+    if (phase == CSF_ENCODE_STREAMS && (!aligned(offsets, 16) || !aligned(exc_prefix, 4))) return CSF_E_ALIGN;
+    if (phase == CSF_ENCODE_ENTRIES && !aligned(exceptions, 4)) return CSF_E_ALIGN;
+
+    csf::EncodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.dense = dense;
+    a.bases = bases;
+    a.offsets = offsets;
+    a.exc = exceptions;
+    a.prefix = exc_prefix;
+    a.tile_index = tile_index;
+    a.stride = min_stride(format, R, C);
+    a.rcp_cols = 1.0 / double(C);
+    a.E = uint32_t(E);
+    a.R = uint32_t(R);
+    a.C = uint32_t(C);
+    a.P = uint32_t(R) * uint32_t(C);
+    a.groups = uint32_t(a.stride / 16);
+    a.index_tiles = uint32_t(index_tiles(R, C));
+    a.wbits = uint32_t(offset_bits(format));
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const uint32_t cus = cu_count(stream);
+    const hipError_t err = phase == CSF_ENCODE_STREAMS ? csf::launch_encode_streams(a, cus, stream)
+                                                       : csf::launch_encode_entries(a, cus, stream);
+    return err == hipSuccess ? CSF_OK : CSF_E_HIP;
+}
+
 // ---------------------------------------------------------------------------
 // Host encoder.  Same definition as the format in csf.h; written as a
 // sliding-window base search, a per-position field pass and a group packing
@@ -495,6 +534,18 @@ csf_status csf_prepare(int32_t format, int32_t num_experts, int32_t rows, int32_
                             exceptions, exc_prefix, tile_index);
     } catch (...) {
         return CSF_E_SIZE;  // allocation failure in the host encoder
+    }
+}
+
+csf_status csf_encode_device(int32_t format, int32_t num_experts, int32_t rows, int32_t cols,
+                             const uint8_t *dense, uint8_t *bases, uint8_t *offsets,
+                             uint32_t *exceptions, int32_t *exc_prefix, int32_t *tile_index,
+                             uint32_t phase, void *hip_stream) {
+    try {
+        return encode_device_impl(format, num_experts, rows, cols, dense, bases, offsets, exceptions,
+                                  exc_prefix, tile_index, phase, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
     }
 }
 

@@ -1,0 +1,237 @@
+// CSF encoder on gfx950: the preparation step run on the GPU, as the pages'
+// preparation does ("Load native FP4 experts with optional lossless CSF
+// scales", vLLM PR 964, preparation paragraphs: encoding plus the index on the
+// GPU).  Output is byte-identical to the host encoder for every input: the
+// base of a row is the row value v with the most row values in
+// [v, v + 2^w - 1], ties to the smallest v; offsets, exception entries,
+// prefix and tile index follow the layout in include/csf.h.
+//
+// Four kernels, all byte streams bound by HBM bandwidth:
+//   csf_enc_bases_kernel    one wave per row: 256-bin histogram in LDS,
+//                           window counts, arg-max by a wave reduction.
+//   csf_enc_pack_kernel     one lane per 16-byte offset group: fields packed
+//                           in the contiguous-decoding order; each index
+//                           tile's out-of-window count reduced across lanes.
+//   csf_enc_scan_kernel     one workgroup: exclusive scan of the per-tile
+//                           counts, in place, into tile_index and prefix.
+//   csf_enc_entries_kernel  one wave per index tile: out-of-window positions
+//                           ranked by a wave prefix and written in ascending
+//                           order at the tile's index.
+#include "csf_launch.h"
+
+namespace csf {
+namespace {
+
+constexpr uint32_t kWave = 64;
+constexpr uint32_t kScanThreads = 1024;
+
+__device__ __forceinline__ uint32_t div_exact(uint32_t n, double rcp) {
+    return (uint32_t)(((double)n + 0.5) * rcp);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (uint32_t d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, kWave));
+    return v;
+}
+
+// Orders this wave's LDS traffic (a wave works on its own histogram).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kBlock) void csf_enc_bases_kernel(EncodeArgs a) {
+    constexpr uint32_t kWaves = kBlock / kWave;
+    __shared__ uint32_t hist[kWaves][256 + 16];  // 16 zero bins past 255 for window sums
+    const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    uint32_t *h = hist[wave];
+    const uint32_t W = 1u << a.wbits;
+    const uint64_t rows = (uint64_t)a.E * a.R;
+    for (uint64_t row = (uint64_t)blockIdx.x * kWaves + wave; row < rows;
+         row += (uint64_t)gridDim.x * kWaves) {
+        for (uint32_t i = lane; i < 256 + 16; i += kWave) h[i] = 0;
+        wave_lds_sync();
+        const uint8_t *xr = a.dense + row * a.C;
+        for (uint32_t c = lane; c < a.C; c += kWave) atomicAdd(&h[xr[c]], 1u);
+        wave_lds_sync();
+        // key = (count in window << 8) | (255 - v) over present values v: the
+        // largest key has the largest count, then the smallest v.
+        uint32_t best = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            const uint32_t v = lane + kWave * i;
+            if (h[v] != 0) {
+                uint32_t win = 0;
+                for (uint32_t u = 0; u < W; ++u) win += h[v + u];
+                best = max(best, (win << 8) | (255u - v));
+            }
+        }
+        best = wave_max(best);
+        if (lane == 0) a.bases[row] = (uint8_t)(255u - (best & 0xffu));
+        wave_lds_sync();
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
+    const uint32_t lane = threadIdx.x % kWave;
+    const uint32_t waves_per_expert = (a.groups + kWave - 1) / kWave;
+    const uint64_t total_waves = (uint64_t)a.E * waves_per_expert;
+    const uint32_t W = 1u << a.wbits;
+    const uint32_t G = 128u / a.wbits;
+    const uint32_t F = 8u / a.wbits;
+    const uint32_t seg = kIndexTile / G;  // lanes (groups) per index tile: 64 or 16
+    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
+         wv += (uint64_t)gridDim.x * kBlock / kWave) {
+        const uint32_t e = (uint32_t)(wv / waves_per_expert);
+        const uint32_t g = (uint32_t)(wv - (uint64_t)e * waves_per_expert) * kWave + lane;
+        const uint8_t *plane = a.dense + (uint64_t)e * a.P;
+        const uint8_t *brow = a.bases + (uint64_t)e * a.R;
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
+        uint32_t outside = 0;
+        if (g < a.groups) {
+            for (uint32_t f = 0; f < F; ++f) {
+                const uint32_t p0 = g * G + 16u * f;
+                if (p0 >= a.P) break;
+                uint32_t r = div_exact(p0, a.rcp_cols);
+                uint32_t next = (r + 1u) * a.C;
+                uint32_t b = brow[r];
+                for (uint32_t j = 0; j < 16; ++j) {
+                    const uint32_t p = p0 + j;
+                    if (p >= a.P) break;
+                    if (p == next) {
+                        ++r;
+                        next += a.C;
+                        b = brow[r];
+                    }
+                    // unsigned 32-bit difference: the window [b, b + W - 1] does
+                    // not wrap past 255, so a value below b is never inside it
+                    const uint32_t d = (uint32_t)plane[p] - b;
+                    const bool in = d < W;
+                    outside += in ? 0u : 1u;
+                    word[j >> 2] |= (in ? d : 0u) << (8u * (j & 3u) + a.wbits * f);
+                }
+            }
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.offsets + (uint64_t)e * a.stride + 16u * g);
+            dst[0] = word[0];
+            dst[1] = word[1];
+            dst[2] = word[2];
+            dst[3] = word[3];
+        }
+        // Sum the counts of each index tile's lanes (seg consecutive lanes).
+        for (uint32_t d = 1; d < seg; d <<= 1) outside += __shfl_xor(outside, d, kWave);
+        const uint32_t tile = g / seg;
+        if (lane % seg == 0 && tile < a.index_tiles && g < a.groups)
+            a.tile_index[(uint64_t)e * a.index_tiles + tile] = (int32_t)outside;
+    }
+}
+
+// One workgroup: tile_index[0 .. N) holds per-tile counts; replace them by
+// their exclusive prefix, set tile_index[N] = total, prefix[e] =
+// tile_index[e * NT] and prefix[E] = total.  The host keeps E * P < 2^31.
+__global__ __launch_bounds__(kScanThreads) void csf_enc_scan_kernel(EncodeArgs a) {
+    __shared__ uint32_t part[kScanThreads];
+    const uint32_t N = a.E * a.index_tiles;
+    const uint32_t chunk = (N + kScanThreads - 1) / kScanThreads;
+    const uint32_t t = threadIdx.x;
+    const uint32_t lo = min(t * chunk, N), hi = min(lo + chunk, N);
+    uint32_t sum = 0;
+    for (uint32_t i = lo; i < hi; ++i) sum += (uint32_t)a.tile_index[i];
+    part[t] = sum;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the partial sums.
+    for (uint32_t d = 1; d < kScanThreads; d <<= 1) {
+        const uint32_t v = t >= d ? part[t - d] : 0u;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint32_t run = part[t] - sum;  // exclusive
+    for (uint32_t i = lo; i < hi; ++i) {
+        const uint32_t c = (uint32_t)a.tile_index[i];
+        a.tile_index[i] = (int32_t)run;
+        run += c;
+    }
+    const uint32_t total = part[kScanThreads - 1];
+    if (t == 0) {
+        a.tile_index[N] = (int32_t)total;
+        a.prefix[a.E] = (int32_t)total;
+    }
+    __syncthreads();  // every thread's tile_index writes are visible in the workgroup
+    for (uint32_t e = t; e < a.E; e += kScanThreads)
+        a.prefix[e] = a.tile_index[(uint64_t)e * a.index_tiles];
+}
+
+// One wave per index tile of kIndexTile positions; lane l takes positions
+// 32l .. 32l+31 of the tile, so lane order is position order.
+__global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
+    constexpr uint32_t kPerLane = kIndexTile / kWave;  // 32
+    const uint32_t lane = threadIdx.x % kWave;
+    const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
+    const uint32_t W = 1u << a.wbits;
+    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
+         wv += (uint64_t)gridDim.x * kBlock / kWave) {
+        const uint32_t e = (uint32_t)(wv / a.index_tiles);
+        const uint32_t it = (uint32_t)(wv - (uint64_t)e * a.index_tiles);
+        const uint8_t *plane = a.dense + (uint64_t)e * a.P;
+        const uint8_t *brow = a.bases + (uint64_t)e * a.R;
+        const uint32_t p0 = it * kIndexTile + lane * kPerLane;
+        uint32_t flags = 0;
+        if (p0 < a.P) {
+            uint32_t r = div_exact(p0, a.rcp_cols);
+            uint32_t next = (r + 1u) * a.C;
+            uint32_t b = brow[r];
+            for (uint32_t k = 0; k < kPerLane; ++k) {
+                const uint32_t p = p0 + k;
+                if (p >= a.P) break;
+                if (p == next) {
+                    ++r;
+                    next += a.C;
+                    b = brow[r];
+                }
+                if ((uint32_t)plane[p] - b >= W) flags |= 1u << k;  // no wrap past 255
+            }
+        }
+        const uint32_t cnt = __popc(flags);
+        uint32_t incl = cnt;
+#pragma unroll
+        for (uint32_t d = 1; d < kWave; d <<= 1) {
+            const uint32_t y = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += y;
+        }
+        uint32_t k_out = (uint32_t)a.tile_index[wv] + (incl - cnt);
+        while (flags != 0) {
+            const uint32_t k = __ffs(flags) - 1;
+            flags &= flags - 1;
+            a.exc[k_out++] = ((p0 + k) << 8) | plane[p0 + k];
+        }
+    }
+}
+
+}  // namespace
+
+static uint32_t grid_for(uint64_t waves_needed, uint32_t cus) {
+    const uint64_t wgs = (waves_needed + kBlock / kWave - 1) / (kBlock / kWave);
+    const uint64_t cap = (uint64_t)cus * 16;
+    return (uint32_t)(wgs < cap ? (wgs > 0 ? wgs : 1) : cap);
+}
+
+hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t stream) {
+    uint32_t grid = grid_for((uint64_t)a.E * a.R, cus);
+    hipLaunchKernelGGL(csf_enc_bases_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    grid = grid_for((uint64_t)a.E * ((a.groups + kWave - 1) / kWave), cus);
+    hipLaunchKernelGGL(csf_enc_pack_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(csf_enc_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_entries(const EncodeArgs &a, uint32_t cus, hipStream_t stream) {
+    const uint32_t grid = grid_for((uint64_t)a.E * a.index_tiles, cus);
+    hipLaunchKernelGGL(csf_enc_entries_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace csf

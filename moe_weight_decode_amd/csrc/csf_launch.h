@@ -66,4 +66,27 @@ hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 // Per-tile exception index of one stack from its entries and prefix.
 hipError_t launch_build_index(const StackArgs &s, uint32_t E, int32_t *tile_index, hipStream_t stream);
 
+// Encoder on the device (csf_encode.hip).
+struct EncodeArgs {
+    const uint8_t *dense;   // [E * P]
+    uint8_t *bases;         // [E * R]
+    uint8_t *offsets;       // [E * stride]
+    uint32_t *exc;          // [n]
+    int32_t *prefix;        // [E + 1]
+    int32_t *tile_index;    // [E * index_tiles + 1]
+    int64_t stride;         // 16 * groups
+    double rcp_cols;        // 1.0 / C
+    uint32_t E, R, C, P;
+    uint32_t groups;        // 16-byte offset groups per expert
+    uint32_t index_tiles;   // ceil(P / kIndexTile)
+    uint32_t wbits;         // 4 or 1
+    uint32_t pad_;
+};
+
+// Row bases, offset stream, per-tile entry counts scanned into tile_index
+// and prefix.
+hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t stream);
+// Exception entries (after launch_encode_streams, in stream order).
+hipError_t launch_encode_entries(const EncodeArgs &a, uint32_t cus, hipStream_t stream);
+
 }  // namespace csf

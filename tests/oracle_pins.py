@@ -18,6 +18,8 @@ What pins what:
   * pin_window_invariant: every stored offset is x - base < W; every exception
     byte lies outside its row's window; entries ascend within each expert.
   * pin_special_cases: one-column rows, constant rows, widely spaced rows.
+  * pin_window_does_not_wrap: a base above 240 keeps values below it out of
+    the window.
   * pin_routed_subsets: every subset of routed experts leaves inactive planes
     byte-identical to the poison and active planes equal to x.
   * pin_alternative_bases: any per-row base decodes back to x.
@@ -242,6 +244,20 @@ def pin_special_cases(orc):
     assert st["offsets"][:5].tolist() == [1, 0, 0, 1, 1]
 
 
+def pin_window_does_not_wrap(orc):
+    # Base 250: the window is 250..255 only; 0..9 lie below the base and are
+    # exceptions, not offsets 6..15 of a window wrapping past 255.
+    x = np.array([[[250, 250, 250, 0, 1, 9, 255, 252]]], dtype=np.uint8)
+    st = orc.encode(workloads.NVFP4, x)
+    assert st["bases"].tolist() == [250]
+    assert st["exceptions"].tolist() == [(3 << 8) | 0, (4 << 8) | 1, (5 << 8) | 9]
+    assert st["offsets"][:8].tolist() == [0, 0, 0, 0, 0, 0, 5, 2]
+    x = np.array([[[255, 255, 255, 0, 0]]], dtype=np.uint8)
+    st = orc.encode(workloads.MXFP4, x)
+    assert st["bases"].tolist() == [255]
+    assert st["exceptions"].tolist() == [(3 << 8) | 0, (4 << 8) | 0]
+
+
 def pin_routed_subsets(orc):
     x = workloads.TINY.generate()
     E = x.shape[0]
@@ -325,6 +341,7 @@ def pin_index_covers_entries(orc):
 
 
 ALL_PINS = [
+    pin_window_does_not_wrap,
     pin_index_hand_worked,
     pin_index_covers_entries,
     pin_two_column_closed_form,

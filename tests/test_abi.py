@@ -203,6 +203,27 @@ def test_paired_and_passes_errors(lib):
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(_fake(E=0)), 0x9000, None)] == "CSF_E_SHAPE"
 
 
+def test_encode_device_errors(lib):
+    f = lib.csf_encode_device
+    ok = dict(dense=0x1000, bases=0x2000, offsets=0x3000, exc=0x4000, prefix=0x5000, tidx=0x6000)
+
+    def call(fmt=0, E=2, R=3, C=4, phase=1, **kw):
+        p = dict(ok, **kw)
+        return mwd.STATUS[f(fmt, E, R, C, p["dense"], p["bases"], p["offsets"], p["exc"], p["prefix"],
+                            p["tidx"], phase, None)]
+    assert call(fmt=3) == "CSF_E_FORMAT"
+    assert call(R=0) == "CSF_E_SHAPE"
+    assert call(phase=0) == "CSF_E_SIZE" and call(phase=3) == "CSF_E_SIZE"
+    assert call(E=2048, R=1024, C=1024) == "CSF_E_SIZE"  # E*R*C >= 2^31
+    assert call(dense=None) == "CSF_E_NULL"
+    assert call(tidx=None) == "CSF_E_NULL"
+    assert call(offsets=None) == "CSF_E_NULL"
+    assert call(phase=2, exc=None) == "CSF_E_NULL"
+    assert call(offsets=0x3004) == "CSF_E_ALIGN"
+    assert call(prefix=0x5001) == "CSF_E_ALIGN"
+    assert call(phase=2, exc=0x4002) == "CSF_E_ALIGN"
+
+
 def test_prepare_errors(lib):
     sz = mwd.csf_sizes()
     x = np.zeros((2, 3, 4), dtype=np.uint8)

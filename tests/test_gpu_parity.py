@@ -393,3 +393,78 @@ def test_graph_replay_follows_routing(orc, dev, mode):
                                f"replay {rnd}.{i} gate")
             assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), oracle_expect(orc, sd, es),
                                f"replay {rnd}.{i} down")
+
+
+# -- the GPU encoder ------------------------------------------------------------
+
+def _same_streams(got: dict, want: dict, what: str):
+    for k in ("fmt", "E", "R", "C", "stride"):
+        assert got[k] == want[k], f"{what}: {k}"
+    for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
+        g, w = np.asarray(got[k]).ravel(), np.asarray(want[k]).ravel()
+        if not np.array_equal(g, w):
+            bad = np.nonzero(g[:min(g.size, w.size)] != w[:min(g.size, w.size)])[0]
+            raise AssertionError(f"{what}: {k} differs (sizes {g.size} vs {w.size}; first at {bad[:5]})")
+
+
+@pytest.mark.parametrize("name", ["tiny_nvfp4", "gate_nvfp4", "down_nvfp4", "mxfp4"])
+def test_gpu_encoder_matches_oracle(orc, dev, name):
+    spec, x, st = stack_case(name, orc)
+    print(f"[parity] gpu encode {name}", flush=True)
+    got = mwd.prepare(torch.from_numpy(x).to(dev), spec.fmt)
+    torch.cuda.synchronize()
+    _same_streams(got.numpy(), st, name)
+    assert_bytes_equal(run_decode(got, dev), x, name + " decoded")
+
+
+ENCODE_SHAPES = RAGGED + [(workloads.NVFP4, 2, 3000, 50), (workloads.MXFP4, 2, 1500, 160),
+                          (workloads.NVFP4, 1, 1048575, 16)]
+
+
+@pytest.mark.parametrize("fmt,E,R,C", ENCODE_SHAPES, ids=[f"f{c[0]}_{c[1]}x{c[2]}x{c[3]}" for c in ENCODE_SHAPES])
+def test_gpu_encoder_ragged(orc, dev, fmt, E, R, C):
+    if R * C > 1 << 20:
+        x = workloads.nvfp4_stack(E, R, C, 71, 0.05)
+    else:
+        x = workloads.uniform_bytes(E, R, C, seed=E * 7 + R * 3 + C)
+    got = mwd.prepare(torch.from_numpy(x).to(dev), fmt)
+    torch.cuda.synchronize()
+    _same_streams(got.numpy(), orc.encode(fmt, x), f"{fmt} {E}x{R}x{C}")
+
+
+def test_gpu_encoder_two_column_exhaustive(orc, dev):
+    a, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
+    x = np.stack([a.ravel(), b.ravel()], axis=1).astype(np.uint8).reshape(4, 16384, 2)
+    for fmt in (workloads.NVFP4, workloads.MXFP4):
+        got = mwd.prepare(torch.from_numpy(x).to(dev), fmt)
+        torch.cuda.synchronize()
+        _same_streams(got.numpy(), orc.encode(fmt, x), f"two-column {fmt}")
+
+
+def test_gpu_encoder_no_exceptions_and_side_stream(orc, dev):
+    x = workloads.nvfp4_stack(3, 64, 128, 5, 0.0)
+    side = torch.cuda.Stream(device=dev)
+    xt = torch.from_numpy(x).to(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        got = mwd.prepare(xt, workloads.NVFP4, stream=side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    assert got.num_exceptions == 0
+    _same_streams(got.numpy(), orc.encode(workloads.NVFP4, x), "no exceptions")
+
+
+def test_gpu_encoder_high_bases(orc, dev):
+    """Rows whose base is above 240 next to small values: the window does not
+    wrap past 255, so the small values are exceptions."""
+    rng = np.random.default_rng(81)
+    for fmt, W in ((workloads.NVFP4, 16), (workloads.MXFP4, 2)):
+        base = rng.integers(241, 256, (3, 200), dtype=np.int64)
+        off = rng.integers(0, W, (3, 200, 40))
+        x = np.minimum(base[:, :, None] + off, 255)
+        low = rng.random((3, 200, 40)) < 0.2
+        x = np.where(low, rng.integers(0, 16, (3, 200, 40)), x).astype(np.uint8)
+        want = orc.encode(fmt, x)
+        got = mwd.prepare(torch.from_numpy(x).to(dev), fmt)
+        torch.cuda.synchronize()
+        _same_streams(got.numpy(), want, f"high bases {fmt}")
+        assert_bytes_equal(run_decode(got, dev), x, "high bases decoded")

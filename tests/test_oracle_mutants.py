@@ -16,6 +16,7 @@ MUTANTS = [
     ("ties go to the largest base", "if (count > best_count) {", "if (count >= best_count) {", False),
     ("window check admits W", "return d >= 0 && d < W;", "return d >= 0 && d <= W;", False),
     ("window check below base", "return d >= 0 && d < W;", "return d >= -1 && d < W;", False),
+    ("window wraps past 255", "int d = value - base;", "int d = (value - base) & 255;", False),
     ("field and byte index swapped in both coder halves",
      "int64_t byte_in_group = p % 16;\n                int64_t field_index = (p % G) / 16;",
      "int64_t byte_in_group = (p % G) / 16;\n                int64_t field_index = p % 16;", False),
