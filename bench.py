@@ -108,10 +108,16 @@ def stack_bytes(stack, active=None):
 
 
 def source_hash() -> str:
+    """Fingerprint of the decode sources' code: comments and whitespace are
+    dropped, so only a change to the code itself invalidates counter records."""
+    import re
     h = hashlib.sha256()
     for rel in ("moe_weight_decode_amd/csrc/csf_kernels.hip", "moe_weight_decode_amd/csrc/csf_launch.h",
                 "moe_weight_decode_amd/csrc/csf_api.cpp"):
-        h.update(open(os.path.join(ROOT, rel), "rb").read())
+        text = open(os.path.join(ROOT, rel)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -195,6 +195,15 @@ csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up,
                              const csf_stack *down, uint8_t *ws_down,
                              const int32_t *expert_start, void *hip_stream);
 
+/*
+ * csf_decode / csf_decode_paired with an int64 expert_start (int64[E + 1],
+ * 8-byte aligned): the pages keep the paired decode for both routing integer
+ * types (PR 478, commit messages).  second may be NULL for a single stack;
+ * expert_start may be NULL (full decode).  Otherwise as csf_decode_paired.
+ */
+csf_status csf_decode_i64(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
+                          uint8_t *ws_second, const int64_t *expert_start, void *hip_stream);
+
 /* Pass selection for csf_decode_passes. */
 #define CSF_PASS_FIXED 1u      /* base + offset expansion of every position */
 #define CSF_PASS_EXCEPTIONS 2u /* exception entries overwrite their positions */

@@ -14,7 +14,8 @@ The functions mirror the C ABI in ``include/csf.h``:
   which keeps the input's device): a GPU tensor is encoded on the GPU
   (``csf_encode_device``), host data by the host encoder (``csf_prepare``);
 * ``decode(stack, workspace, expert_start=None, stream=None)``;
-* ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``;
+* ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``
+  (``expert_start`` int32 or int64; int64 goes through ``csf_decode_i64``);
 * ``decode_passes(...)`` to enqueue the fixed-stream or exception pass alone;
 * ``build_index(stack)`` (the per-tile exception index, built on the GPU);
 * ``validate(stack)`` (host-side layout check).
@@ -48,7 +49,7 @@ STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: 
           5: "CSF_E_ALIGN", 6: "CSF_E_CORRUPT", 7: "CSF_E_MISMATCH", 8: "CSF_E_HIP"}
 
 EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_encode_device", "csf_build_index",
-           "csf_decode", "csf_decode_paired", "csf_decode_passes", "csf_validate")
+           "csf_decode", "csf_decode_paired", "csf_decode_i64", "csf_decode_passes", "csf_validate")
 
 
 class CsfError(RuntimeError):
@@ -101,6 +102,8 @@ def _lib():
         lib.csf_decode_paired.restype = ctypes.c_int
         lib.csf_decode_paired.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp,
                                           vp, vp]
+        lib.csf_decode_i64.restype = ctypes.c_int
+        lib.csf_decode_i64.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp, vp, vp]
         lib.csf_decode_passes.restype = ctypes.c_int
         lib.csf_decode_passes.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp,
                                           vp, ctypes.c_uint32, vp]
@@ -301,19 +304,30 @@ def _check_device(stack: CompressedStack, ws: torch.Tensor, name: str):
 def _es_ptr(expert_start, stack: CompressedStack):
     if expert_start is None:
         return None
-    if (not isinstance(expert_start, torch.Tensor) or expert_start.dtype != torch.int32
+    if (not isinstance(expert_start, torch.Tensor) or expert_start.dtype not in (torch.int32, torch.int64)
             or expert_start.device != stack.device or expert_start.numel() != stack.E + 1
             or not expert_start.is_contiguous()):
-        raise ValueError(f"expert_start must be a contiguous int32[{stack.E + 1}] tensor on {stack.device}")
+        raise ValueError(f"expert_start must be a contiguous int32 or int64 [{stack.E + 1}] tensor "
+                         f"on {stack.device}")
     return expert_start.data_ptr()
 
 
+def _is_wide(expert_start) -> bool:
+    return expert_start is not None and expert_start.dtype == torch.int64
+
+
 def decode(stack: CompressedStack, workspace: torch.Tensor, expert_start=None, stream=None):
-    """Enqueue the full decode of ``stack`` into ``workspace`` on ``stream``."""
+    """Enqueue the full decode of ``stack`` into ``workspace`` on ``stream``;
+    ``expert_start`` (int32 or int64 [E+1], on the device) limits it to the
+    experts with routed tokens."""
     _check_device(stack, workspace, "decode")
     d = stack.descriptor()
-    _check(_lib().csf_decode(ctypes.byref(d), workspace.data_ptr(), _es_ptr(expert_start, stack),
-                             _stream_handle(stream, stack.device)), "csf_decode")
+    es, h = _es_ptr(expert_start, stack), _stream_handle(stream, stack.device)
+    if _is_wide(expert_start):
+        _check(_lib().csf_decode_i64(ctypes.byref(d), workspace.data_ptr(), None, None, es, h),
+               "csf_decode_i64")
+    else:
+        _check(_lib().csf_decode(ctypes.byref(d), workspace.data_ptr(), es, h), "csf_decode")
 
 
 def decode_paired(gate_up: CompressedStack, ws_gate_up: torch.Tensor, down: CompressedStack,
@@ -322,9 +336,13 @@ def decode_paired(gate_up: CompressedStack, ws_gate_up: torch.Tensor, down: Comp
     _check_device(gate_up, ws_gate_up, "decode_paired")
     _check_device(down, ws_down, "decode_paired")
     a, b = gate_up.descriptor(), down.descriptor()
-    _check(_lib().csf_decode_paired(ctypes.byref(a), ws_gate_up.data_ptr(), ctypes.byref(b),
-                                    ws_down.data_ptr(), _es_ptr(expert_start, gate_up),
-                                    _stream_handle(stream, gate_up.device)), "csf_decode_paired")
+    es, h = _es_ptr(expert_start, gate_up), _stream_handle(stream, gate_up.device)
+    if _is_wide(expert_start):
+        _check(_lib().csf_decode_i64(ctypes.byref(a), ws_gate_up.data_ptr(), ctypes.byref(b),
+                                     ws_down.data_ptr(), es, h), "csf_decode_i64")
+    else:
+        _check(_lib().csf_decode_paired(ctypes.byref(a), ws_gate_up.data_ptr(), ctypes.byref(b),
+                                        ws_down.data_ptr(), es, h), "csf_decode_paired")
 
 
 def decode_passes(first: CompressedStack, ws_first: torch.Tensor, second=None, ws_second=None,
@@ -357,17 +375,25 @@ class Launch:
         self._b = second.descriptor() if second is not None else None
         self._args_ws = (ws_first.data_ptr(), ws_second.data_ptr() if second is not None else None)
         self._es = _es_ptr(expert_start, first)
+        self._wide = _is_wide(expert_start)
         self._stream = _stream_handle(stream, first.device)
         self._fn = _lib().csf_decode_passes
+        self._fn64 = _lib().csf_decode_i64
 
     @property
     def stream(self) -> int:
         return self._stream
 
     def __call__(self, passes: int = PASS_ALL):
-        st = self._fn(ctypes.byref(self._a), self._args_ws[0],
-                      ctypes.byref(self._b) if self._b is not None else None, self._args_ws[1],
-                      self._es, passes, self._stream)
+        b = ctypes.byref(self._b) if self._b is not None else None
+        if self._wide:
+            if passes != PASS_ALL:
+                raise ValueError("an int64 expert_start decodes all passes together")
+            st = self._fn64(ctypes.byref(self._a), self._args_ws[0], b, self._args_ws[1], self._es,
+                            self._stream)
+        else:
+            st = self._fn(ctypes.byref(self._a), self._args_ws[0], b, self._args_ws[1], self._es, passes,
+                          self._stream)
         if st != 0:
             raise CsfError(st, "csf_decode_passes")
 

@@ -175,7 +175,7 @@ uint32_t cu_count(hipStream_t stream) {
 }
 
 csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8_t *ws1,
-                   const int32_t *expert_start, uint32_t passes, void *hip_stream) {
+                   const void *expert_start, bool es_wide, uint32_t passes, void *hip_stream) {
     if (passes == 0 || (passes & ~CSF_PASS_ALL) != 0) return CSF_E_SIZE;
     csf_status st = check_stack(s0, ws0);
     if (st != CSF_OK) return st;
@@ -185,13 +185,14 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
         if (s1->num_experts != s0->num_experts) return CSF_E_MISMATCH;
     }
     const bool routed = expert_start != nullptr;
-    if (routed && !aligned(expert_start, 4)) return CSF_E_ALIGN;
+    if (routed && !aligned(expert_start, es_wide ? 8 : 4)) return CSF_E_ALIGN;
 
     const Plan plan = plan_tiles(s0, s1, routed);
     const uint32_t tile = csf::tile_positions(plan.runs);
     DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.expert_start = expert_start;
+    a.es_wide = es_wide ? 1u : 0u;
     a.nstacks = s1 ? 2u : 1u;
     a.E = uint32_t(s0->num_experts);
     a.runs = plan.runs;
@@ -517,7 +518,7 @@ const char *csf_status_str(csf_status s) {
         case CSF_E_SHAPE: return "bad shape (E, R, C must be positive, R*C < 2^24, E <= CSF_MAX_EXPERTS)";
         case CSF_E_FORMAT: return "unknown format";
         case CSF_E_SIZE: return "stride, exception count or pass selection inconsistent";
-        case CSF_E_ALIGN: return "misaligned buffer (offsets need 16 bytes, exceptions/prefix/expert_start 4)";
+        case CSF_E_ALIGN: return "misaligned buffer (offsets need 16 bytes, exceptions/prefix/index 4, expert_start its element size)";
         case CSF_E_CORRUPT: return "compressed stream breaks the layout";
         case CSF_E_MISMATCH: return "paired stacks have different expert counts";
         case CSF_E_HIP: return "HIP runtime refused the launch";
@@ -560,7 +561,8 @@ csf_status csf_build_index(const csf_stack *compressed, int32_t *tile_index, voi
 csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace, const int32_t *expert_start,
                       void *hip_stream) {
     try {
-        return enqueue(compressed, workspace, nullptr, nullptr, expert_start, CSF_PASS_ALL, hip_stream);
+        return enqueue(compressed, workspace, nullptr, nullptr, expert_start, false, CSF_PASS_ALL,
+                       hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }
@@ -570,7 +572,7 @@ csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up, cons
                              uint8_t *ws_down, const int32_t *expert_start, void *hip_stream) {
     if (down == nullptr) return CSF_E_NULL;
     try {
-        return enqueue(gate_up, ws_gate_up, down, ws_down, expert_start, CSF_PASS_ALL, hip_stream);
+        return enqueue(gate_up, ws_gate_up, down, ws_down, expert_start, false, CSF_PASS_ALL, hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }
@@ -580,8 +582,18 @@ csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first, const cs
                              uint8_t *ws_second, const int32_t *expert_start, uint32_t passes,
                              void *hip_stream) {
     try {
-        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, passes,
+        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, false, passes,
                        hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_decode_i64(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
+                          uint8_t *ws_second, const int64_t *expert_start, void *hip_stream) {
+    try {
+        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, true,
+                       CSF_PASS_ALL, hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }

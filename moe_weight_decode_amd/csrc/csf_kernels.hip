@@ -117,13 +117,29 @@ __device__ __forceinline__ StackArgs pick(const DecodeArgs &a, uint32_t s) {
     return s ? a.st[1] : a.st[0];
 }
 
-// Wave 0 of the workgroup: list the active experts (expert_start[e+1] >
-// expert_start[e], or all when es is null) in increasing order into act[];
+// flags[e] = 1 iff expert e has routed tokens, expert_start[e + 1] >
+// expert_start[e], for e in [first, E) with stride step; the routing tensor is
+// int32 or int64 (the grouped routing comes in both widths).
+template <typename T>
+__device__ __forceinline__ void stage_flags(const T *es, uint32_t E, uint32_t first, uint32_t step,
+                                            uint8_t *flags) {
+    for (uint32_t i = first; i < E; i += step) flags[i] = es[i + 1] > es[i] ? 1 : 0;
+}
+
+__device__ __forceinline__ void routed_flags(const DecodeArgs &a, uint8_t *flags) {
+    if (a.es_wide)
+        stage_flags(static_cast<const int64_t *>(a.expert_start), a.E, threadIdx.x, kBlock, flags);
+    else
+        stage_flags(static_cast<const int32_t *>(a.expert_start), a.E, threadIdx.x, kBlock, flags);
+}
+
+// Wave 0 of the workgroup: list the active experts (flags[e] != 0, or all
+// when flags is null) in increasing order into act[];
 // for each stack s < ns also the exclusive prefix M_s over the listed experts
 // of their entry counts (prefix[e+1] - prefix[e], clamped to [0, n_exc]),
 // capped at n_exc.  Returns the number of active experts.  A wave-level
 // prefix: ballot + popcount for the positions, a shuffle scan for the counts.
-__device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uint32_t ns,
+__device__ uint32_t build_maps(const uint8_t *flags, uint32_t E, uint16_t *act, uint32_t ns,
                                const int32_t *pfx0, const int32_t *pfx1, uint32_t n0,
                                uint32_t n1, uint32_t *M0, uint32_t *M1) {
     const uint32_t lane = threadIdx.x;
@@ -135,7 +151,7 @@ __device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uin
     }
     for (uint32_t base = 0; base < E; base += kWave) {
         const uint32_t e = base + lane;
-        const bool on = e < E && (es == nullptr || es[e + 1] > es[e]);
+        const bool on = e < E && (flags == nullptr || flags[e] != 0);
         const uint64_t mask = __ballot(on);
         const uint32_t slot = n + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
         if (on) act[slot] = (uint16_t)e;
@@ -175,12 +191,12 @@ __device__ uint32_t build_maps(const int32_t *es, uint32_t E, uint16_t *act, uin
 }
 
 // Routed mode: the active-expert list in LDS (all threads take part).
-__device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, int32_t *es) {
+__device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, uint8_t *flags) {
     __shared__ uint32_t s_nact;
-    for (uint32_t i = threadIdx.x; i <= a.E; i += kBlock) es[i] = a.expert_start[i];
+    routed_flags(a, flags);
     __syncthreads();
     if (threadIdx.x < kWave) {
-        const uint32_t n = build_maps(es, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
+        const uint32_t n = build_maps(flags, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
         if (threadIdx.x == 0) s_nact = n;
     }
     __syncthreads();
@@ -246,10 +262,10 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
     uint8_t *lds_bases = dyn;
     uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
-    int32_t *es = reinterpret_cast<int32_t *>(dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u));
+    uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
 
     const bool routed = a.expert_start != nullptr;
-    const uint32_t nact = routed ? active_experts(a, act, es) : a.E;
+    const uint32_t nact = routed ? active_experts(a, act, flags) : a.E;
     const uint32_t u0 = nact * a.st[0].tiles;
     const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
 
@@ -386,22 +402,22 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     const uint32_t E = a.E;
     const uint32_t ns = a.nstacks;
     const uint32_t words = (E + 1u + 3u) & ~3u;  // one int32[E+1] map, padded to 16 B
-    int32_t *es = reinterpret_cast<int32_t *>(dyn_lds);
-    int32_t *p0 = es + words;
+    uint8_t *flags = dyn_lds;
+    int32_t *p0 = reinterpret_cast<int32_t *>(dyn_lds + ((E + 15u) & ~15u));
     int32_t *p1 = p0 + words;
     uint32_t *M0 = reinterpret_cast<uint32_t *>(p1 + words);
     uint32_t *M1 = M0 + words;
     uint16_t *act = reinterpret_cast<uint16_t *>(M1 + words);
 
     const bool routed = a.expert_start != nullptr;
+    if (routed) routed_flags(a, flags);
     for (uint32_t i = threadIdx.x; i <= E; i += kBlock) {
-        if (routed) es[i] = a.expert_start[i];
         p0[i] = a.st[0].prefix[i];
         if (ns > 1) p1[i] = a.st[1].prefix[i];
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
-        const uint32_t n = build_maps(routed ? es : nullptr, E, act, ns, p0, p1, a.st[0].n_exc,
+        const uint32_t n = build_maps(routed ? flags : nullptr, E, act, ns, p0, p1, a.st[0].n_exc,
                                       ns > 1 ? a.st[1].n_exc : 0u, M0, M1);
         if (threadIdx.x == 0) s_nact = n;
     }
@@ -489,13 +505,13 @@ __global__ __launch_bounds__(kBlock) void csf_index_kernel(StackArgs s, uint32_t
 
 size_t tile_lds_bytes(const DecodeArgs &a) {
     size_t n = a.bases_stage;
-    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + 4u * (a.E + 1u);
+    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + a.E;
     return n;
 }
 
 static size_t exc_lds_bytes(const DecodeArgs &a) {
     const size_t words = (a.E + 1u + 3u) & ~3u;
-    return 5u * 4u * words + 2u * a.E;
+    return ((a.E + 15u) & ~15u) + 4u * 4u * words + 2u * a.E;
 }
 
 hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {

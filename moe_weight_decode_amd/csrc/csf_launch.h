@@ -45,13 +45,15 @@ struct StackArgs {
 
 struct DecodeArgs {
     StackArgs st[2];
-    const int32_t *expert_start;  // nullptr: every expert is active
+    const void *expert_start;     // int32 or int64 [E + 1]; nullptr: every expert is active
     uint32_t nstacks;             // 1 or 2
     uint32_t E;                   // experts (same for both stacks)
     uint32_t bases_stage;         // bytes of dynamic LDS for one tile's row bases
     uint32_t runs;                // 16-byte runs per lane per tile (1, 2 or 4)
     uint32_t stream_loads;        // non-temporal offset/entry loads (fused, runs == 1 only)
     uint32_t exc_regs;            // entries per lane loaded with the offsets (fused: 4 or 8)
+    uint32_t es_wide;             // expert_start holds int64 (else int32)
+    uint32_t pad_;
 };
 
 // Dynamic LDS bytes a tile kernel needs for these arguments.

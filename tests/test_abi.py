@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csf_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csf_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -198,6 +198,10 @@ def test_paired_and_passes_errors(lib):
         assert mwd.STATUS[lib.csf_decode_passes(ctypes.byref(a), 0x5000, None, None, None, passes,
                                                 None)] == "CSF_E_SIZE"
     assert mwd.STATUS[lib.csf_decode(ctypes.byref(a), 0x5000, 0x7002, None)] == "CSF_E_ALIGN"
+    assert mwd.STATUS[lib.csf_decode_i64(ctypes.byref(a), 0x5000, None, None, 0x7004, None)] == "CSF_E_ALIGN"
+    assert mwd.STATUS[lib.csf_decode_i64(ctypes.byref(a), 0x5000, ctypes.byref(b), 0x6000, 0x7000,
+                                         None)] == "CSF_E_MISMATCH"
+    assert mwd.STATUS[lib.csf_decode_i64(None, 0x5000, None, None, 0x7000, None)] == "CSF_E_NULL"
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), None, None)] == "CSF_E_NULL"
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), 0x9002, None)] == "CSF_E_ALIGN"
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(_fake(E=0)), 0x9000, None)] == "CSF_E_SHAPE"

@@ -468,3 +468,30 @@ def test_gpu_encoder_high_bases(orc, dev):
         torch.cuda.synchronize()
         _same_streams(got.numpy(), want, f"high bases {fmt}")
         assert_bytes_equal(run_decode(got, dev), x, "high bases decoded")
+
+
+# -- int64 routing ----------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES)
+def test_routed_int64_expert_start(orc, dev, mode):
+    """int64 expert_start with offsets beyond 2^32: the same planes as the
+    int32 routing with the same token counts."""
+    es32 = workloads.ROUTED.expert_start()
+    es64 = es32.astype(np.int64) + (np.int64(5) << 40)
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev, mode), upload(sd, dev, mode)
+    wg = torch.full((g.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    wd = torch.full((d.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode_paired(g, wg, d, wd, torch.from_numpy(es64).to(dev))
+    torch.cuda.synchronize()
+    assert_bytes_equal(wg.cpu().numpy().reshape(xg.shape), oracle_expect(orc, sg, es32), "int64 gate")
+    assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), oracle_expect(orc, sd, es32), "int64 down")
+    # single stack; the low 32 bits alone would say "no tokens" for expert 1
+    spec, x, st = stack_case("tiny_nvfp4", orc)
+    es = np.array([0, 1 << 33, (1 << 33) + 1, (1 << 33) + 1, (1 << 34)], dtype=np.int64)
+    ws = torch.full((x.size,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode(upload(st, dev, mode), ws, torch.from_numpy(es).to(dev))
+    torch.cuda.synchronize()
+    want = oracle_expect(orc, st, np.array([0, 1, 2, 2, 3], dtype=np.int32))
+    assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), want, "int64 single")
