@@ -22,12 +22,15 @@ constexpr int64_t kMaxPlane = int64_t(1) << 24;  // positions ride in 24 bits of
 
 // Launch plan of the tile kernels (measured on MI355X with HBM-resident
 // stacks): NVFP4 stacks with few exceptions stream best in 16384-position
-// tiles at 6 workgroups per CU; stacks with more exceptions, and MXFP4, in
-// 8192-position tiles at 7 per CU; routed decodes of a few experts in
-// 4096-position tiles, which spread the little work over more CUs, with
-// non-temporal loads (their planes are read once and rarely cache-resident).
-// Each lane loads 4 of its tile's exception entries with its offsets, 8 when
-// the stack's exception density would average more than 3.5 per lane.
+// tiles at 6 workgroups per CU with the pipelined schedule (the next tile's
+// loads before this tile's stores, entries read 16 bytes per lane); stacks
+// with more exceptions, and MXFP4, in 8192-position tiles at 7 per CU, one
+// tile's loads at a time, with non-temporal entry loads; routed decodes of a
+// few experts in 4096-position tiles, which spread the little work over more
+// CUs, with non-temporal offset and entry loads (their planes are read once
+// and rarely cache-resident).  Each lane prefetches 4 of its tile's
+// exception entries, 8 when the stack's exception density would average more
+// than 3.5 per lane.
 #ifndef CSF_SPARSE_RUNS
 #define CSF_SPARSE_RUNS 4
 #endif
@@ -132,7 +135,7 @@ uint32_t bases_stage_bytes(uint32_t C, uint32_t tile) {
 struct Plan {
     uint32_t runs;
     uint32_t wg_per_cu;
-    bool stream_loads;
+    uint32_t sched;
     uint32_t exc_regs;
 };
 
@@ -148,11 +151,11 @@ Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
     }
     Plan p;
     if (routed)
-        p = {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU, CSF_ROUTED_RUNS == 1, 4};
+        p = {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU, csf::kSchedStreamAll, 4};
     else if (nvfp4 && entries * 1000000 <= dense * int64_t(CSF_SPARSE_PPM))
-        p = {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU, false, 4};
+        p = {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU, csf::kSchedPipelined, 4};
     else
-        p = {CSF_DENSE_RUNS, CSF_DENSE_WG_PER_CU, false, 4};
+        p = {CSF_DENSE_RUNS, CSF_DENSE_WG_PER_CU, csf::kSchedStreamEntries, 4};
     // mean entries per lane and tile = density * tile / kBlock
     const int64_t tile = csf::tile_positions(p.runs);
     if (p.runs == 2 && entries * tile * 1000 > dense * int64_t(csf::kBlock) * CSF_EXC_LANE_MILLI)
@@ -196,7 +199,7 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     a.nstacks = s1 ? 2u : 1u;
     a.E = uint32_t(s0->num_experts);
     a.runs = plan.runs;
-    a.stream_loads = plan.stream_loads ? 1u : 0u;
+    a.sched = plan.sched;
     a.exc_regs = plan.exc_regs;
     fill_stack(a.st[0], *s0, ws0, tile);
     a.bases_stage = bases_stage_bytes(a.st[0].C, tile);

@@ -31,6 +31,7 @@ namespace csf {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kWave = 64;
 
@@ -43,6 +44,21 @@ __device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b) {
 __device__ __forceinline__ u32x4 add_bytes4(u32x4 a, u32x4 b) {
     return (u32x4){add_bytes(a.x, b.x), add_bytes(a.y, b.y), add_bytes(a.z, b.z),
                    add_bytes(a.w, b.w)};
+}
+
+// Buffer resources: a 128-bit descriptor of a byte range [base, base+bytes).
+// A buffer load outside the range returns 0 and a buffer store outside it is
+// dropped by the hardware, so the tile loop issues every load and store
+// unconditionally: the number of memory operations between a load and its
+// use is then fixed, and each wait covers exactly the loads it needs (never
+// the stores issued after them).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw byte buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;         // cache policy bit NT (streaming access)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
 }
 
 // floor(n / d) for n, d < 2^24 with rcp = 1.0 / d.  (n + 0.5) / d lies at least
@@ -242,22 +258,42 @@ __device__ __forceinline__ void expand_dispatch(const StackArgs &st, const u32x4
     }
 }
 
+// Work unit u of a launch: stack s, expert e, tile t of e's plane.  Units
+// run over stack 0's active experts' tiles, then stack 1's.
+struct Unit {
+    uint32_t s, e, t;
+};
+
+template <bool UNIFORM>
+__device__ __forceinline__ Unit locate(const DecodeArgs &a, uint32_t u, uint32_t u0,
+                                       const uint16_t *act, bool routed) {
+    const uint32_t s = u >= u0 ? 1u : 0u;
+    const uint32_t uu = u - (s ? u0 : 0u);
+    const uint32_t tiles = s ? a.st[1].tiles : a.st[0].tiles;
+    const uint32_t k = uu / tiles;
+    uint32_t e = k;
+    if (routed) e = UNIFORM ? (uint32_t)__builtin_amdgcn_readfirstlane(act[k]) : (uint32_t)act[k];
+    return {s, e, uu - k * tiles};
+}
+
 // ---------------------------------------------------------------------------
-// Tile loop shared by the fused and the fixed-stream kernels.
+// Serial tile loop (the fixed-stream kernel, and the fused kernel on dense
+// exception streams).
 //
-// Work unit = (stack, active expert, tile of TILE = 4096 * RUNS positions).
-// Per tile the workgroup loads each lane's 16-byte offset groups with 128-bit
-// loads (lanes reading fields of the same group share one load), stages the
-// tile's row bases in LDS, widens each lane's field to 16 bytes and adds the
-// row bases byte-wise.  FUSED then patches the tile's exception entries into
-// the LDS tile and stores the finished tile with non-temporal stores.
-// EXC entries per lane are loaded together with the offsets (more, if the
-// tile holds them, are read after the expansion); STREAM_LOADS marks the
-// offset and entry loads non-temporal (routed decodes, whose few planes are
-// read once and are rarely cache-resident).
+// Work unit = (stack, active expert, tile of TILE = 4096 * RUNS positions);
+// workgroups take units grid-stride, so the units in flight at any moment
+// are neighbours in memory.  Per tile the workgroup loads each lane's 16-byte
+// offset groups with 128-bit loads (lanes reading fields of the same group
+// share one load), the tile's index bounds and then its first EXC * kBlock
+// exception entries, and its row bases into LDS; it widens each lane's field
+// to 16 bytes and adds the row bases byte-wise.  FUSED then patches the
+// tile's entries into the LDS tile and stores the finished tile with
+// non-temporal stores; otherwise the runs are stored straight from
+// registers.  OFFSET_NT / ENTRY_NT mark the offset / entry loads
+// non-temporal.
 // ---------------------------------------------------------------------------
-template <bool FUSED, uint32_t RUNS, uint32_t EXC, bool STREAM_LOADS>
-__device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+template <bool FUSED, uint32_t RUNS, uint32_t EXC, bool OFFSET_NT, bool ENTRY_NT>
+__device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
     uint8_t *lds_bases = dyn;
@@ -290,7 +326,7 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
             const u32x4 *src = seg + ((pos >> 4) >> gshift);
             if (pos >= q1)
                 v[i] = (u32x4){0u, 0u, 0u, 0u};
-            else if constexpr (STREAM_LOADS)
+            else if constexpr (OFFSET_NT)
                 v[i] = __builtin_nontemporal_load(src);
             else
                 v[i] = *src;
@@ -310,7 +346,7 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
                 const uint32_t kk = lo + i * kBlock + threadIdx.x;
                 if (kk >= hi)
                     w[i] = 0xffffffffu;  // position 2^24 - 1: never in a tile
-                else if constexpr (STREAM_LOADS)
+                else if constexpr (ENTRY_NT)
                     w[i] = __builtin_nontemporal_load(st.exc + kk);
                 else
                     w[i] = st.exc[kk];
@@ -355,17 +391,233 @@ __device__ __forceinline__ void tile_loop(const DecodeArgs &a, uint8_t *dyn, uin
     }
 }
 
-template <uint32_t RUNS, uint32_t EXC, bool STREAM_LOADS>
+// Load schedule of the fused kernel (the host picks one per call).
+//   kPipelined      pipelined loop, cached loads (stacks with few exceptions)
+//   kStreamEntries  serial loop, non-temporal entry loads (dense exception
+//                   streams)
+//   kStreamAll      pipelined loop, non-temporal offset and entry loads
+//                   (routed decodes: their planes are read once and are
+//                   rarely cache-resident)
+// Which loop suits which stream was measured on MI355X: on dense exception
+// streams the serial loop with non-temporal entries is the fastest.
+enum Sched : uint32_t {
+    kPipelined = kSchedPipelined,
+    kStreamEntries = kSchedStreamEntries,
+    kStreamAll = kSchedStreamAll
+};
+
+// Everything a tile needs from memory, loaded ahead of its decode: the
+// lane's offset groups, two row bases, EXC exception entries (slot i holds
+// entry entry_of(first, i)) and the tile's entry range [lo, hi).
+template <uint32_t RUNS, uint32_t EXC>
+struct TileLoads {
+    u32x4 v[RUNS];
+    uint32_t w[EXC];
+    uint8_t b0, b1;
+    uint32_t lo, hi, first;
+};
+
+// Stream index of slot i of a lane's prefetched entries: each 16-byte load
+// of a workgroup covers 4 * kBlock consecutive entries.
+__device__ __forceinline__ uint32_t entry_of(uint32_t first, uint32_t i) {
+    return first + 4u * ((i / 4u) * kBlock + threadIdx.x) + (i % 4u);
+}
+
+// Issue the loads of unit w (tile positions from q0); l0/h0 are its tile
+// index bounds.  Every load is issued, whatever the tile holds: loads past the
+// expert's offset segment or bases, or past the tile's entries, read 0.
+template <uint32_t RUNS, uint32_t EXC, int POLICY>
+__device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, uint32_t q0,
+                                            int32_t l0, int32_t h0, TileLoads<RUNS, EXC> &L) {
+    // Offset groups: run q (positions 16q .. 16q+15) is field q % F of
+    // group q / F, F = 8 / w fields per group.
+    const rsrc_t seg = make_rsrc(st.offsets + (uint64_t)w.e * st.stride, (uint32_t)st.stride);
+    const uint32_t gshift = st.wbits == 4 ? 1u : 3u;
+#pragma unroll
+    for (uint32_t i = 0; i < RUNS; ++i) {
+        const uint32_t run = (q0 >> 4) + i * kBlock + threadIdx.x;
+        L.v[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg, (int)((run >> gshift) << 4), 0, POLICY));
+    }
+    // Row bases of the tile's first 2 * kBlock rows.
+    const uint32_t r_lo = div_exact(q0, st.rcp_cols);
+    const rsrc_t rb = make_rsrc(st.bases + (uint64_t)w.e * st.R, st.R);
+    L.b0 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(r_lo + threadIdx.x), 0, 0);
+    L.b1 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(r_lo + kBlock + threadIdx.x), 0, 0);
+    // Entries from `first` (lo rounded down to a multiple of 4) in 16-byte
+    // loads; the resource ends at hi.
+    L.hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
+    L.lo = l0 < 0 ? 0u : min((uint32_t)l0, L.hi);
+    L.first = L.lo & ~3u;
+    const rsrc_t rx = make_rsrc(st.exc + L.first, 4u * (L.hi - L.first));
+#pragma unroll
+    for (uint32_t i = 0; i < EXC / 4; ++i) {
+        const u32x4 q = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(16u * (i * kBlock + threadIdx.x)), 0,
+                                                         POLICY));
+        L.w[4 * i] = q.x;
+        L.w[4 * i + 1] = q.y;
+        L.w[4 * i + 2] = q.z;
+        L.w[4 * i + 3] = q.w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined tile loop of the fused kernel.
+//
+// Work unit = (stack, active expert, tile of TILE = 4096 * RUNS positions);
+// workgroups take units grid-stride, so the units in flight at any moment
+// are neighbours in memory.  A tile's loads are its lanes' 16-byte offset
+// groups (128-bit loads; lanes reading fields of the same group share one
+// load), its row bases and its first EXC * kBlock exception entries.  The
+// entry ranges come from the tile index, read for 64 units at a time (lane j
+// of every wave holds unit j's range), so no load of a tile waits on another
+// load.  Per tile the workgroup stages the row bases in LDS, widens each
+// lane's field to 16 bytes and adds the row bases byte-wise into an LDS tile,
+// patches the tile's entries into it and stores the finished tile with
+// non-temporal stores.  The next tile's loads go out before this tile's
+// stores, so no wait on a tile's data also waits for the stores before it.
+// POLICY is the cache policy of the offset and entry loads.
+// ---------------------------------------------------------------------------
+template <uint32_t RUNS, uint32_t EXC, int POLICY>
+__device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+    constexpr uint32_t TILE = tile_positions(RUNS);
+    constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
+    static_assert(EXC % 4 == 0, "entries are prefetched in 16-byte loads");
+    uint8_t *lds_bases = dyn;
+    uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
+    uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
+
+    const bool routed = a.expert_start != nullptr;
+    const uint32_t nact = routed ? active_experts(a, act, flags) : a.E;
+    const uint32_t u0 = nact * a.st[0].tiles;
+    const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
+    if (blockIdx.x >= total) return;
+    const uint32_t G = gridDim.x;
+    const uint32_t lane = threadIdx.x & (kWave - 1u);
+
+    // Tile index bounds of units ub + j*G, j < 64, in lane j.
+    int32_t blo = 0, bhi = 0;
+    auto load_batch = [&](uint32_t ub) {
+        const uint32_t uj = ub + lane * G;
+        if (uj < total) {
+            const Unit w = locate<false>(a, uj, u0, act, routed);
+            const StackArgs &st = w.s ? a.st[1] : a.st[0];
+            const int32_t *ti = st.tile_index + (uint64_t)w.e * st.index_tiles + w.t * INDEX_PER_TILE;
+            blo = ti[0];
+            bhi = ti[min(INDEX_PER_TILE, st.index_tiles - w.t * INDEX_PER_TILE)];
+        }
+    };
+
+    uint32_t u = blockIdx.x;
+    uint32_t j = 0;
+    load_batch(u);
+    Unit cur = locate<true>(a, u, u0, act, routed);
+    TileLoads<RUNS, EXC> L;
+    {
+        const StackArgs st = pick(a, cur.s);
+        issue_loads<RUNS, EXC, POLICY>(st, cur, cur.t * TILE, __builtin_amdgcn_readlane(blo, 0),
+                                       __builtin_amdgcn_readlane(bhi, 0), L);
+        // As many stores as a tile's store phase, into an empty range (the
+        // hardware drops them): the loop is then entered with the same memory
+        // operations in flight from here as from its own end, and its waits
+        // need not cover the previous tile's stores.
+        const rsrc_t none = make_rsrc(st.ws, 0u);
+#pragma unroll
+        for (uint32_t i = 0; i < RUNS; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128((int32x4_t){0, 0, 0, 0}, none,
+                                                   (int)(kRunBytes * (i * kBlock + threadIdx.x)), 0,
+                                                   kNonTemporal);
+    }
+    while (true) {
+        const StackArgs st = pick(a, cur.s);
+        const uint32_t e = cur.e;
+        const uint32_t q0 = cur.t * TILE;
+        const uint32_t q1 = min(q0 + TILE, st.P);
+        const uint32_t r_lo = div_exact(q0, st.rcp_cols);
+        const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
+
+        // Row bases into LDS (the barrier also ends the previous tile's LDS reads).
+        if (threadIdx.x < nrows) lds_bases[threadIdx.x] = L.b0;
+        if (threadIdx.x + kBlock < nrows) lds_bases[threadIdx.x + kBlock] = L.b1;
+        const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
+        for (uint32_t r = threadIdx.x + 2u * kBlock; r < nrows; r += kBlock) lds_bases[r] = brow[r];
+        __syncthreads();
+
+        uint8_t *plane = st.ws + (uint64_t)e * st.P;
+        expand_dispatch<true, RUNS>(st, L.v, q0, q1, lds_bases, r_lo, tile, plane);
+        __syncthreads();  // tile expanded
+
+#pragma unroll
+        for (uint32_t i = 0; i < EXC; ++i) {
+            const uint32_t k = entry_of(L.first, i);
+            const uint32_t pos = L.w[i] >> 8;
+            if (k >= L.lo && k < L.hi && pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(L.w[i] & 0xffu);
+        }
+        for (uint32_t kk = L.first + EXC * kBlock + threadIdx.x; kk < L.hi; kk += kBlock) {
+            const uint32_t x = st.exc[kk];
+            const uint32_t pos = x >> 8;
+            if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
+        }
+        __syncthreads();  // tile patched
+
+        const uint32_t un = u + G;
+        const bool more = un < total;
+        if (more) {
+            // Each branch reads its bounds itself, so no later wait covers the
+            // batch load.
+            int32_t nl, nh;
+            if (++j == kWave) {
+                load_batch(un);
+                j = 0;
+                nl = __builtin_amdgcn_readlane(blo, 0);
+                nh = __builtin_amdgcn_readlane(bhi, 0);
+            } else {
+                nl = __builtin_amdgcn_readlane(blo, j);
+                nh = __builtin_amdgcn_readlane(bhi, j);
+            }
+            cur = locate<true>(a, un, u0, act, routed);
+            // The next unit's loads go out before this tile's stores.
+            issue_loads<RUNS, EXC, POLICY>(pick(a, cur.s), cur, cur.t * TILE, nl, nh, L);
+        }
+
+        // Whole 16-byte runs of an aligned tile: one non-temporal 128-bit
+        // store per run, issued for every run (those past the tile's whole
+        // runs are dropped).  A ragged plane end or a misaligned workspace
+        // leaves bytes for the byte loop.
+        uint8_t *dst = plane + q0;
+        const uint32_t n = q1 - q0;
+        const uint32_t whole = (reinterpret_cast<uintptr_t>(dst) & 15u) ? 0u : (n & ~15u);
+        const rsrc_t rw = make_rsrc(dst, whole);
+#pragma unroll
+        for (uint32_t i = 0; i < RUNS; ++i) {
+            const uint32_t off = kRunBytes * (i * kBlock + threadIdx.x);
+            const u32x4 out = *reinterpret_cast<const u32x4 *>(tile + off);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)off, 0,
+                                                   kNonTemporal);
+        }
+        for (uint32_t b = whole + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
+        // The next tile's first barrier orders these LDS reads before the
+        // next expansion overwrites the tile.
+        if (!more) break;
+        u = un;
+    }
+}
+
+template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED>
 __global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
-    tile_loop<true, RUNS, EXC, STREAM_LOADS>(a, dyn_lds, tile);
+    if constexpr (SCHED == kStreamEntries)
+        tile_loop_serial<true, RUNS, EXC, false, true>(a, dyn_lds, tile);
+    else
+        tile_loop_pipelined<RUNS, EXC, SCHED == kStreamAll ? kNonTemporal : 0>(a, dyn_lds, tile);
 }
 
 template <uint32_t RUNS>
 __global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    tile_loop<false, RUNS, 1, false>(a, dyn_lds, nullptr);
+    tile_loop_serial<false, RUNS, 1, false, false>(a, dyn_lds, nullptr);
 }
 
 // Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
@@ -528,15 +780,15 @@ hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) 
 hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = tile_lds_bytes(a);
     const dim3 g(grid), b(kBlock);
-    // (runs, entries per lane, streaming loads) combinations the host plans
-    if (a.runs == 1 && a.exc_regs == 4 && a.stream_loads)
-        hipLaunchKernelGGL((csf_fused_kernel<1, 4, true>), g, b, lds, stream, a);
-    else if (a.runs == 2 && a.exc_regs == 4 && !a.stream_loads)
-        hipLaunchKernelGGL((csf_fused_kernel<2, 4, false>), g, b, lds, stream, a);
-    else if (a.runs == 2 && a.exc_regs == 8 && !a.stream_loads)
-        hipLaunchKernelGGL((csf_fused_kernel<2, 8, false>), g, b, lds, stream, a);
-    else if (a.runs == 4 && a.exc_regs == 4 && !a.stream_loads)
-        hipLaunchKernelGGL((csf_fused_kernel<4, 4, false>), g, b, lds, stream, a);
+    // (runs, entries per lane, load schedule) combinations the host plans
+    if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedStreamAll)
+        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kStreamAll>), g, b, lds, stream, a);
+    else if (a.runs == 2 && a.exc_regs == 4 && a.sched == kSchedStreamEntries)
+        hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries>), g, b, lds, stream, a);
+    else if (a.runs == 2 && a.exc_regs == 8 && a.sched == kSchedStreamEntries)
+        hipLaunchKernelGGL((csf_fused_kernel<2, 8, kStreamEntries>), g, b, lds, stream, a);
+    else if (a.runs == 4 && a.exc_regs == 4 && a.sched == kSchedPipelined)
+        hipLaunchKernelGGL((csf_fused_kernel<4, 4, kPipelined>), g, b, lds, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -16,6 +16,11 @@ constexpr uint32_t tile_positions(uint32_t runs) { return kBlock * kRunBytes * r
 constexpr uint32_t kExcPerLane = 8;                 // entries per lane per scatter chunk
 constexpr uint32_t kBasesSlack = 32;                // rows read past a tile's last row by edge runs
 
+// Load schedules of the fused kernel (csf_kernels.hip describes them).
+constexpr uint32_t kSchedPipelined = 0;
+constexpr uint32_t kSchedStreamEntries = 1;
+constexpr uint32_t kSchedStreamAll = 2;
+
 // How a 16-byte output run finds its row bases.
 enum RowMode : uint32_t {
     kRowSplat = 0,  // C % 16 == 0: a run never crosses a row
@@ -50,7 +55,7 @@ struct DecodeArgs {
     uint32_t E;                   // experts (same for both stacks)
     uint32_t bases_stage;         // bytes of dynamic LDS for one tile's row bases
     uint32_t runs;                // 16-byte runs per lane per tile (1, 2 or 4)
-    uint32_t stream_loads;        // non-temporal offset/entry loads (fused, runs == 1 only)
+    uint32_t sched;               // load schedule of the fused kernel (kSched*)
     uint32_t exc_regs;            // entries per lane loaded with the offsets (fused: 4 or 8)
     uint32_t es_wide;             // expert_start holds int64 (else int32)
     uint32_t pad_;
