@@ -439,11 +439,13 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
         L.v[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg, (int)((run >> gshift) << 4), 0, POLICY));
     }
-    // Row bases of the tile's first 2 * kBlock rows.
+    // Row bases of the tile's first 2 * kBlock rows; the resource covers the
+    // tile's rows only, so lanes past them read nothing from memory.
     const uint32_t r_lo = div_exact(q0, st.rcp_cols);
-    const rsrc_t rb = make_rsrc(st.bases + (uint64_t)w.e * st.R, st.R);
-    L.b0 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(r_lo + threadIdx.x), 0, 0);
-    L.b1 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(r_lo + kBlock + threadIdx.x), 0, 0);
+    const uint32_t r_hi = div_exact(min(q0 + tile_positions(RUNS), st.P) - 1u, st.rcp_cols) + 1u;
+    const rsrc_t rb = make_rsrc(st.bases + (uint64_t)w.e * st.R + r_lo, r_hi - r_lo);
+    L.b0 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)threadIdx.x, 0, 0);
+    L.b1 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(kBlock + threadIdx.x), 0, 0);
     // Entries from `first` (lo rounded down to a multiple of 4) in 16-byte
     // loads; the resource ends at hi.
     L.hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
