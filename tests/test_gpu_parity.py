@@ -170,6 +170,29 @@ def test_most_experts(orc, dev, mode):
     assert_bytes_equal(got, oracle_expect(orc, st, es), "2048 experts routed")
 
 
+def test_many_tiles_per_workgroup(orc, dev):
+    # A routed call decodes 4096-position tiles on 2 workgroups per CU with the
+    # pipelined loop, which reads the tile index bounds of 64 tiles at a time.
+    # With all 2048 experts routed in a paired call and enough tiles per plane,
+    # every workgroup decodes more than 64 tiles and reads bounds in batches.
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    E, C = mwd.MAX_EXPERTS, 128
+    tiles = -(-64 * 2 * cus // (2 * E)) + 1
+    R = tiles * 4096 // C
+    assert 2 * E * tiles > 64 * 2 * cus
+    xg = workloads.nvfp4_stack(E, R, C, 41, 0.03)
+    xd = workloads.nvfp4_stack(E, R, C, 42, 0.10)
+    g = upload(orc.encode(workloads.NVFP4, xg), dev)
+    d = upload(orc.encode(workloads.NVFP4, xd), dev)
+    es = torch.from_numpy(workloads.expert_start_from_mask(np.ones(E, dtype=bool), tokens=2)).to(dev)
+    wg = torch.full((g.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    wd = torch.full((d.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode_paired(g, wg, d, wd, es)
+    torch.cuda.synchronize()
+    assert_bytes_equal(wg.cpu().numpy().reshape(xg.shape), xg, "gate half, every expert routed")
+    assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), xd, "down half, every expert routed")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_no_exceptions(orc, dev, mode):
     x = workloads.nvfp4_stack(4, 64, 128, 5, 0.0)
