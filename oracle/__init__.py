@@ -47,6 +47,9 @@ class Oracle:
         lib.oracle_encode_streams.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_int] * 4 + [_u8p, _u8p, _u32p, _i32p, _i32p, _u8p]
         lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_decode_rows.argtypes = ([ctypes.c_int] * 4 + [_u8p, _u8p, _u32p, _i32p, _i32p]
+                                           + [ctypes.c_int] * 2 + [_u8p])
+        lib.oracle_decode_rows.restype = ctypes.c_int
         lib.oracle_index_tiles.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.oracle_index_tiles.restype = ctypes.c_int64
         lib.oracle_build_index.argtypes = [ctypes.c_int] * 3 + [_u32p, _i32p, _i32p]
@@ -139,6 +142,31 @@ class Oracle:
                                     _ptr(es, _i32p), _ptr(ws, _u8p))
         if rc != 0:
             raise ValueError("oracle_decode rejected its arguments")
+        return ws
+
+
+    def decode_rows(self, stack: dict, row_begin: int, row_end: int,
+                    expert_start: np.ndarray | None = None, ws: np.ndarray | None = None) -> np.ndarray:
+        """Expand rows ``row_begin .. row_end-1`` of every (routed) plane into
+        ``ws`` (uint8[E, R, C]); every other byte of ``ws`` keeps its value."""
+        fmt, E, R, C = stack["fmt"], stack["E"], stack["R"], stack["C"]
+        if ws is None:
+            ws = np.zeros((E, R, C), dtype=np.uint8)
+        assert ws.shape == (E, R, C) and ws.dtype == np.uint8 and ws.flags["C_CONTIGUOUS"]
+        exc = np.ascontiguousarray(stack["exceptions"], dtype=np.uint32)
+        if exc.size == 0:
+            exc = np.zeros(1, dtype=np.uint32)
+        es = None if expert_start is None else np.ascontiguousarray(expert_start, dtype=np.int32)
+        if es is not None:
+            assert es.shape == (E + 1,)
+        rc = self.lib.oracle_decode_rows(fmt, E, R, C,
+                                         _ptr(np.ascontiguousarray(stack["bases"], dtype=np.uint8), _u8p),
+                                         _ptr(np.ascontiguousarray(stack["offsets"], dtype=np.uint8), _u8p),
+                                         _ptr(exc, _u32p),
+                                         _ptr(np.ascontiguousarray(stack["prefix"], dtype=np.int32), _i32p),
+                                         _ptr(es, _i32p), int(row_begin), int(row_end), _ptr(ws, _u8p))
+        if rc != 0:
+            raise ValueError("oracle_decode_rows rejected its arguments")
         return ws
 
 

@@ -269,3 +269,51 @@ int oracle_decode(int fmt, int E, int R, int C, const uint8_t *bases,
     }
     return ORACLE_OK;
 }
+
+/*
+ * Row-window decoder ("NVFP4-CSF: expand_scales() ..." b12x PR 478, commit
+ * messages: decode only the gate halves a consumer reads).  Reading: the
+ * consumer reads rows row_begin .. row_end-1 of every plane; exactly those
+ * rows of each expanded plane are written, in the usual dense layout, and
+ * every other byte of the workspace keeps its value, as the planes of
+ * unrouted experts do.  Routing as oracle_decode.  The fixed stream writes
+ * base[row] + field for the positions of those rows; an exception entry is
+ * applied when its position lies in one of those rows.
+ */
+int oracle_decode_rows(int fmt, int E, int R, int C, const uint8_t *bases,
+                       const uint8_t *offsets, const uint32_t *exc,
+                       const int32_t *prefix, const int32_t *expert_start,
+                       int row_begin, int row_end, uint8_t *ws)
+{
+    if (!shape_ok(fmt, E, R, C)) return ORACLE_BAD_ARGS;
+    if (row_begin < 0 || row_begin > row_end || row_end > R) return ORACLE_BAD_ARGS;
+    int w = offset_bits(fmt);
+    int W = 1 << w;
+    int64_t G = 128 / w;
+    int64_t P = (int64_t)R * C;
+    int64_t S = oracle_segment_bytes(fmt, R, C);
+    for (int e = 0; e < E; e++) {
+        if (expert_start != NULL && !(expert_start[e + 1] > expert_start[e]))
+            continue;
+        /* fixed stream, rows of the window */
+        for (int64_t r = row_begin; r < row_end; r++) {
+            for (int64_t c = 0; c < C; c++) {
+                int64_t p = r * C + c;
+                int64_t group = p / G;
+                int64_t byte_in_group = p % 16;
+                int64_t field_index = (p % G) / 16;
+                int byte = offsets[(int64_t)e * S + 16 * group + byte_in_group];
+                int field = (byte >> (w * field_index)) & (W - 1);
+                ws[(int64_t)e * P + p] = (uint8_t)(bases[(int64_t)e * R + r] + field);
+            }
+        }
+        /* exception pass, entries of the window's rows */
+        for (int64_t k = prefix[e]; k < prefix[e + 1]; k++) {
+            int64_t pos = exc[k] >> 8;
+            int64_t row = pos / C;
+            if (pos < P && row >= row_begin && row < row_end)
+                ws[(int64_t)e * P + pos] = (uint8_t)(exc[k] & 0xFF);
+        }
+    }
+    return ORACLE_OK;
+}

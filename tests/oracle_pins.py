@@ -306,6 +306,37 @@ def pin_out_of_plane_entries(orc):
     assert np.array_equal(ws[0], want[0]) and np.all(ws[1] == POISON)
 
 
+def pin_row_window(orc):
+    # Rows begin .. end-1 of every routed plane equal the input x; every other
+    # byte keeps the poison (the round trip, restricted to the window).
+    cases = [(workloads.NVFP4, workloads.nvfp4_stack(3, 40, 50, 5, 0.10, hot_row_frac=0.05)),
+             (workloads.MXFP4, workloads.mxfp4_stack(2, 24, 160, 6, 0.15)),
+             (workloads.NVFP4, workloads.uniform_bytes(2, 9, 7, 12))]
+    rng = np.random.default_rng(5)
+    for fmt, x in cases:
+        E, R, C = x.shape
+        st = orc.encode(fmt, x)
+        windows = [(0, R), (0, R // 2), (R // 2, R), (0, 0), (R, R), (0, 1), (R - 1, R)]
+        windows += [tuple(sorted(rng.integers(0, R + 1, 2))) for _ in range(4)]
+        for b, e in windows:
+            for es in (None, workloads.expert_start_from_mask(np.arange(E) % 2 == 0, tokens=1)):
+                ws = np.full(x.shape, POISON, dtype=np.uint8)
+                orc.decode_rows(st, b, e, es, ws)
+                for k in range(E):
+                    if es is not None and not es[k + 1] > es[k]:
+                        assert np.all(ws[k] == POISON)
+                        continue
+                    assert np.array_equal(ws[k, b:e], x[k, b:e]), (b, e)
+                    assert np.all(ws[k, :b] == POISON) and np.all(ws[k, e:] == POISON), (b, e)
+        # a window outside the plane is refused
+        for b, e in ((-1, 2), (3, 2), (0, R + 1)):
+            try:
+                orc.decode_rows(st, b, e)
+            except ValueError:
+                continue
+            raise AssertionError(f"window {(b, e)} accepted")
+
+
 def pin_index_hand_worked(orc):
     # Two experts, one row of 5000 columns: tiles [0, 2048), [2048, 4096), [4096, 5000).
     # Expert 0 outliers at 5, 2047, 2048, 4999; expert 1 outliers at 100, 4096.
@@ -356,4 +387,5 @@ ALL_PINS = [
     pin_routed_subsets,
     pin_alternative_bases,
     pin_out_of_plane_entries,
+    pin_row_window,
 ]

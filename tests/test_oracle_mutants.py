@@ -33,6 +33,12 @@ MUTANTS = [
     ("index counts entries at the tile start", "< ORACLE_INDEX_TILE * j) below++;",
      "<= ORACLE_INDEX_TILE * j) below++;", False),
     ("index tile of 1024 positions", "#define ORACLE_INDEX_TILE 2048", "#define ORACLE_INDEX_TILE 1024", False),
+    ("row window end inclusive", "for (int64_t r = row_begin; r < row_end; r++) {",
+     "for (int64_t r = row_begin; r <= row_end && r < R; r++) {", False),
+    ("row window begins a row early", "for (int64_t r = row_begin; r < row_end; r++) {",
+     "for (int64_t r = row_begin > 0 ? row_begin - 1 : 0; r < row_end; r++) {", False),
+    ("windowed exception pass ignores the window", "if (pos < P && row >= row_begin && row < row_end)",
+     "if (pos < P)", False),
     ("index tiles rounded down", "return (P + ORACLE_INDEX_TILE - 1) / ORACLE_INDEX_TILE;",
      "return P / ORACLE_INDEX_TILE + 1;", False),
 ]
