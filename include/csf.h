@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSF_ABI_VERSION 2
+#define CSF_ABI_VERSION 3
 
 /* Positions per exception-index tile. */
 #define CSF_INDEX_TILE 2048
@@ -222,6 +222,30 @@ csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first,
                              const csf_stack *second, uint8_t *ws_second,
                              const int32_t *expert_start, uint32_t passes,
                              void *hip_stream);
+
+/* A window of rows [begin, end) of every plane of a stack, 0 <= begin <= end <= rows. */
+typedef struct csf_rows {
+    int32_t begin;
+    int32_t end;
+} csf_rows;
+
+/*
+ * csf_decode_passes restricted to a window of rows of each stack (PR 478,
+ * commit messages: decode only the gate halves a consumer reads).  Rows
+ * rows_first->begin .. rows_first->end - 1 of every expanded plane of first
+ * (likewise for second) are written, in the usual dense layout; every other
+ * workspace byte keeps its value, as the planes of unrouted experts do.  For
+ * a gate/up stack whose planes hold the gate rows before the up rows, the
+ * gate half is {0, rows / 2}.  rows_first / rows_second may be NULL (every
+ * row); an empty window writes nothing for that stack.  expert_start is int32
+ * [E + 1] or NULL; passes as csf_decode_passes (CSF_PASS_ALL decodes in one
+ * kernel when every stack carries a tile index).
+ * Errors: CSF_E_SHAPE for a window outside [0, rows]; otherwise as
+ *   csf_decode_passes.
+ */
+csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_rows *rows_first,
+                           const csf_stack *second, uint8_t *ws_second, const csf_rows *rows_second,
+                           const int32_t *expert_start, uint32_t passes, void *hip_stream);
 
 /*
  * Full host-side check of a stack whose buffers are in HOST memory: prefix

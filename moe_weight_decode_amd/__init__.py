@@ -49,7 +49,8 @@ STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: 
           5: "CSF_E_ALIGN", 6: "CSF_E_CORRUPT", 7: "CSF_E_MISMATCH", 8: "CSF_E_HIP"}
 
 EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_encode_device", "csf_build_index",
-           "csf_decode", "csf_decode_paired", "csf_decode_i64", "csf_decode_passes", "csf_validate")
+           "csf_decode", "csf_decode_paired", "csf_decode_i64", "csf_decode_passes", "csf_decode_rows",
+           "csf_validate")
 
 
 class CsfError(RuntimeError):
@@ -66,6 +67,10 @@ class csf_sizes(ctypes.Structure):
                 ("num_exceptions", ctypes.c_int64), ("exceptions_bytes", ctypes.c_int64),
                 ("prefix_bytes", ctypes.c_int64), ("index_tiles", ctypes.c_int64),
                 ("index_bytes", ctypes.c_int64), ("compressed_bytes", ctypes.c_int64)]
+
+
+class csf_rows(ctypes.Structure):
+    _fields_ = [("begin", ctypes.c_int32), ("end", ctypes.c_int32)]
 
 
 class csf_stack(ctypes.Structure):
@@ -107,6 +112,10 @@ def _lib():
         lib.csf_decode_passes.restype = ctypes.c_int
         lib.csf_decode_passes.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp,
                                           vp, ctypes.c_uint32, vp]
+        lib.csf_decode_rows.restype = ctypes.c_int
+        lib.csf_decode_rows.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_rows),
+                                        ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_rows), vp,
+                                        ctypes.c_uint32, vp]
         lib.csf_validate.restype = ctypes.c_int
         lib.csf_validate.argtypes = [ctypes.POINTER(csf_stack)]
         _LIB = lib
@@ -358,6 +367,28 @@ def decode_passes(first: CompressedStack, ws_first: torch.Tensor, second=None, w
     _check(_lib().csf_decode_passes(ctypes.byref(a), ws_first.data_ptr(), b_ref, ws_b,
                                     _es_ptr(expert_start, first), passes,
                                     _stream_handle(stream, first.device)), "csf_decode_passes")
+
+
+def decode_rows(first: CompressedStack, ws_first: torch.Tensor, rows_first=None, second=None,
+                ws_second=None, rows_second=None, expert_start=None, passes: int = PASS_ALL, stream=None):
+    """Enqueue the decode of a window of rows of every plane (see
+    ``csf_decode_rows``): ``rows_*`` is ``(begin, end)`` or None for every row;
+    ``expert_start`` is int32 [E+1] or None."""
+    _check_device(first, ws_first, "decode_rows")
+    if expert_start is not None and _is_wide(expert_start):
+        raise ValueError("decode_rows takes an int32 expert_start")
+    a = first.descriptor()
+    ra = None if rows_first is None else csf_rows(*rows_first)
+    b_ref, ws_b, rb = None, None, None
+    if second is not None:
+        _check_device(second, ws_second, "decode_rows")
+        b = second.descriptor()
+        b_ref, ws_b = ctypes.byref(b), ws_second.data_ptr()
+        rb = None if rows_second is None else csf_rows(*rows_second)
+    _check(_lib().csf_decode_rows(ctypes.byref(a), ws_first.data_ptr(), None if ra is None else ctypes.byref(ra),
+                                  b_ref, ws_b, None if rb is None else ctypes.byref(rb),
+                                  _es_ptr(expert_start, first), passes,
+                                  _stream_handle(stream, first.device)), "csf_decode_rows")
 
 
 class Launch:

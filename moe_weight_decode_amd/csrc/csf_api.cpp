@@ -104,7 +104,8 @@ int64_t index_tiles(int32_t R, int32_t C) {
 
 static_assert(CSF_INDEX_TILE == csf::kIndexTile, "index tile of the ABI and the kernels");
 
-void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t tile) {
+// Rows [rb, re) of every plane are decoded (0 <= rb <= re <= R).
+void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t tile, int32_t rb, int32_t re) {
     const uint32_t P = uint32_t(s.rows) * uint32_t(s.cols);
     const uint32_t C = uint32_t(s.cols);
     a.bases = s.bases;
@@ -119,7 +120,10 @@ void fill_stack(StackArgs &a, const csf_stack &s, uint8_t *ws, uint32_t tile) {
     a.P = P;
     a.R = uint32_t(s.rows);
     a.C = C;
-    a.tiles = (P + tile - 1) / tile;
+    a.pbeg = uint32_t(rb) * C;
+    a.pend = uint32_t(re) * C;
+    a.tile0 = a.pbeg / tile;
+    a.tiles = a.pend > a.pbeg ? (a.pend + tile - 1) / tile - a.tile0 : 0u;
     a.index_tiles = uint32_t(index_tiles(s.rows, s.cols));
     a.wbits = uint32_t(offset_bits(s.format));
     a.row_mode = (C % 16 == 0) ? csf::kRowSplat : (C >= 16 ? csf::kRowTwo : csf::kRowBytes);
@@ -177,8 +181,16 @@ uint32_t cu_count(hipStream_t stream) {
     return uint32_t(n);
 }
 
-csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8_t *ws1,
-                   const void *expert_start, bool es_wide, uint32_t passes, void *hip_stream) {
+// Row window of a stack: rows, or every row when rows is NULL.
+bool window(const csf_stack *s, const csf_rows *rows, int32_t &rb, int32_t &re) {
+    rb = rows ? rows->begin : 0;
+    re = rows ? rows->end : s->rows;
+    return 0 <= rb && rb <= re && re <= s->rows;
+}
+
+csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, const csf_stack *s1,
+                   uint8_t *ws1, const csf_rows *rows1, const void *expert_start, bool es_wide,
+                   uint32_t passes, void *hip_stream) {
     if (passes == 0 || (passes & ~CSF_PASS_ALL) != 0) return CSF_E_SIZE;
     csf_status st = check_stack(s0, ws0);
     if (st != CSF_OK) return st;
@@ -189,6 +201,16 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     }
     const bool routed = expert_start != nullptr;
     if (routed && !aligned(expert_start, es_wide ? 8 : 4)) return CSF_E_ALIGN;
+    int32_t rb0 = 0, re0 = 0, rb1 = 0, re1 = 0;
+    if (!window(s0, rows0, rb0, re0)) return CSF_E_SHAPE;
+    if (s1 != nullptr && !window(s1, rows1, rb1, re1)) return CSF_E_SHAPE;
+    // A stack with an empty window is left out of the launch.
+    if (s1 != nullptr && rb1 == re1) s1 = nullptr;
+    if (rb0 == re0) {
+        if (s1 == nullptr) return CSF_OK;
+        s0 = s1, ws0 = ws1, rb0 = rb1, re0 = re1;
+        s1 = nullptr;
+    }
 
     const Plan plan = plan_tiles(s0, s1, routed);
     const uint32_t tile = csf::tile_positions(plan.runs);
@@ -201,14 +223,15 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_stack *s1, uint8
     a.runs = plan.runs;
     a.sched = plan.sched;
     a.exc_regs = plan.exc_regs;
-    fill_stack(a.st[0], *s0, ws0, tile);
+    fill_stack(a.st[0], *s0, ws0, tile, rb0, re0);
     a.bases_stage = bases_stage_bytes(a.st[0].C, tile);
     if (s1) {
-        fill_stack(a.st[1], *s1, ws1, tile);
+        fill_stack(a.st[1], *s1, ws1, tile, rb1, re1);
         a.bases_stage = std::max(a.bases_stage, bases_stage_bytes(a.st[1].C, tile));
     } else {
         a.st[1] = a.st[0];  // never read: nstacks == 1
     }
+    a.windowed = (rb0 != 0 || re0 != s0->rows || (s1 && (rb1 != 0 || re1 != s1->rows))) ? 1u : 0u;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const uint32_t cus = cu_count(stream);
@@ -243,7 +266,7 @@ csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_s
     if (st != CSF_OK) return st;
     if (!aligned(tile_index, 4)) return CSF_E_ALIGN;
     StackArgs a;
-    fill_stack(a, *s, nullptr, csf::kIndexTile);
+    fill_stack(a, *s, nullptr, csf::kIndexTile, 0, s->rows);
     if (a.n_exc == 0) a.exc = nullptr;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (csf::launch_build_index(a, uint32_t(s->num_experts), tile_index, stream) != hipSuccess)
@@ -564,7 +587,7 @@ csf_status csf_build_index(const csf_stack *compressed, int32_t *tile_index, voi
 csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace, const int32_t *expert_start,
                       void *hip_stream) {
     try {
-        return enqueue(compressed, workspace, nullptr, nullptr, expert_start, false, CSF_PASS_ALL,
+        return enqueue(compressed, workspace, nullptr, nullptr, nullptr, nullptr, expert_start, false, CSF_PASS_ALL,
                        hip_stream);
     } catch (...) {
         return CSF_E_HIP;
@@ -575,7 +598,8 @@ csf_status csf_decode_paired(const csf_stack *gate_up, uint8_t *ws_gate_up, cons
                              uint8_t *ws_down, const int32_t *expert_start, void *hip_stream) {
     if (down == nullptr) return CSF_E_NULL;
     try {
-        return enqueue(gate_up, ws_gate_up, down, ws_down, expert_start, false, CSF_PASS_ALL, hip_stream);
+        return enqueue(gate_up, ws_gate_up, nullptr, down, ws_down, nullptr, expert_start, false, CSF_PASS_ALL,
+                       hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }
@@ -585,7 +609,8 @@ csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first, const cs
                              uint8_t *ws_second, const int32_t *expert_start, uint32_t passes,
                              void *hip_stream) {
     try {
-        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, false, passes,
+        return enqueue(first, ws_first, nullptr, second, second ? ws_second : nullptr, nullptr, expert_start,
+                       false, passes,
                        hip_stream);
     } catch (...) {
         return CSF_E_HIP;
@@ -595,8 +620,20 @@ csf_status csf_decode_passes(const csf_stack *first, uint8_t *ws_first, const cs
 csf_status csf_decode_i64(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
                           uint8_t *ws_second, const int64_t *expert_start, void *hip_stream) {
     try {
-        return enqueue(first, ws_first, second, second ? ws_second : nullptr, expert_start, true,
+        return enqueue(first, ws_first, nullptr, second, second ? ws_second : nullptr, nullptr, expert_start,
+                       true,
                        CSF_PASS_ALL, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_rows *rows_first,
+                           const csf_stack *second, uint8_t *ws_second, const csf_rows *rows_second,
+                           const int32_t *expert_start, uint32_t passes, void *hip_stream) {
+    try {
+        return enqueue(first, ws_first, rows_first, second, second ? ws_second : nullptr,
+                       second ? rows_second : nullptr, expert_start, false, passes, hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }

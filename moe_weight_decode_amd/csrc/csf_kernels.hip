@@ -110,12 +110,13 @@ __device__ __forceinline__ u32x4 run_bases(const uint8_t *lds, uint32_t pos, uin
     }
 }
 
-// Store up to 16 bytes of v at dst.  Full, 16-byte aligned runs (every run of
-// an aligned plane whose size is a multiple of 16) take one 128-bit store;
-// STREAM marks it non-temporal (the decoder never reads its output back).
+// Store bytes first .. nvalid-1 (nvalid clamped to 16) of the 16-byte run v
+// at dst.  Whole, 16-byte aligned runs (every run of an aligned plane whose
+// size is a multiple of 16) take one 128-bit store; STREAM marks it
+// non-temporal (the decoder never reads its output back).
 template <bool STREAM>
-__device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t nvalid) {
-    if (nvalid >= 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+__device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t first, uint32_t nvalid) {
+    if (first == 0 && nvalid >= 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
         if constexpr (STREAM)
             __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
         else
@@ -126,7 +127,7 @@ __device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t nvalid
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (uint32_t j = 0; j < 16; ++j)
-        if (j < n) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+        if (j >= first && j < n) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
 }
 
 __device__ __forceinline__ StackArgs pick(const DecodeArgs &a, uint32_t s) {
@@ -221,11 +222,12 @@ __device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, uint8_t *
 
 // Expand this lane's runs of one tile: tile positions q0 .. q1-1, lds_bases
 // holding rows from r_lo.  FUSED writes the runs into the LDS tile; otherwise
-// they are stored to the plane directly.
-template <int WB, int MODE, bool FUSED, uint32_t RUNS>
+// positions sb .. q1-1 are stored to the plane directly (sb > q0 only in a
+// WINDOW launch, whose row window may start inside the tile).
+template <int WB, int MODE, bool FUSED, uint32_t RUNS, bool WINDOW>
 __device__ __forceinline__ void expand_tile(const StackArgs &st, const u32x4 *v, uint32_t q0,
-                                            uint32_t q1, const uint8_t *lds_bases, uint32_t r_lo,
-                                            uint8_t *tile, uint8_t *plane) {
+                                            uint32_t q1, uint32_t sb, const uint8_t *lds_bases,
+                                            uint32_t r_lo, uint8_t *tile, uint8_t *plane) {
     constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
     constexpr uint32_t FMASK = 8 / WB - 1;  // fields per group - 1
 #pragma unroll
@@ -239,27 +241,34 @@ __device__ __forceinline__ void expand_tile(const StackArgs &st, const u32x4 *v,
         if constexpr (FUSED) {
             *reinterpret_cast<u32x4 *>(tile + kRunBytes * j) = out;
         } else {
-            store_run<false>(plane + pos, out, st.P - pos);
+            if constexpr (WINDOW) {
+                if (pos + kRunBytes > sb)
+                    store_run<false>(plane + pos, out, sb > pos ? sb - pos : 0u, q1 - pos);
+            } else {
+                store_run<false>(plane + pos, out, 0u, q1 - pos);
+            }
         }
     }
 }
 
-template <bool FUSED, uint32_t RUNS>
+template <bool FUSED, uint32_t RUNS, bool WINDOW>
 __device__ __forceinline__ void expand_dispatch(const StackArgs &st, const u32x4 *v, uint32_t q0,
-                                                uint32_t q1, const uint8_t *lds_bases,
+                                                uint32_t q1, uint32_t sb, const uint8_t *lds_bases,
                                                 uint32_t r_lo, uint8_t *tile, uint8_t *plane) {
     switch ((st.wbits == 4 ? 0u : 3u) + st.row_mode) {
-        case 0: expand_tile<4, kRowSplat, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 1: expand_tile<4, kRowTwo, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 2: expand_tile<4, kRowBytes, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 3: expand_tile<1, kRowSplat, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        case 4: expand_tile<1, kRowTwo, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
-        default: expand_tile<1, kRowBytes, FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane); break;
+        case 0: expand_tile<4, kRowSplat, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
+        case 1: expand_tile<4, kRowTwo, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
+        case 2: expand_tile<4, kRowBytes, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
+        case 3: expand_tile<1, kRowSplat, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
+        case 4: expand_tile<1, kRowTwo, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
+        default: expand_tile<1, kRowBytes, FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane); break;
     }
 }
 
-// Work unit u of a launch: stack s, expert e, tile t of e's plane.  Units
-// run over stack 0's active experts' tiles, then stack 1's.
+// Work unit u of a launch: stack s, expert e, tile t of e's plane (tiles are
+// counted from the plane's start; a decode covers tiles tile0 .. tile0 +
+// tiles - 1 of every plane).  Units run over stack 0's active experts'
+// tiles, then stack 1's.
 struct Unit {
     uint32_t s, e, t;
 };
@@ -273,7 +282,7 @@ __device__ __forceinline__ Unit locate(const DecodeArgs &a, uint32_t u, uint32_t
     const uint32_t k = uu / tiles;
     uint32_t e = k;
     if (routed) e = UNIFORM ? (uint32_t)__builtin_amdgcn_readfirstlane(act[k]) : (uint32_t)act[k];
-    return {s, e, uu - k * tiles};
+    return {s, e, (s ? a.st[1].tile0 : a.st[0].tile0) + uu - k * tiles};
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +301,7 @@ __device__ __forceinline__ Unit locate(const DecodeArgs &a, uint32_t u, uint32_t
 // registers.  OFFSET_NT / ENTRY_NT mark the offset / entry loads
 // non-temporal.
 // ---------------------------------------------------------------------------
-template <bool FUSED, uint32_t RUNS, uint32_t EXC, bool OFFSET_NT, bool ENTRY_NT>
+template <bool FUSED, uint32_t RUNS, uint32_t EXC, bool OFFSET_NT, bool ENTRY_NT, bool WINDOW>
 __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
@@ -310,10 +319,11 @@ __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *d
         const StackArgs st = pick(a, s);
         const uint32_t uu = u - (s ? u0 : 0u);
         const uint32_t k = uu / st.tiles;
-        const uint32_t t = uu - k * st.tiles;
+        const uint32_t t = st.tile0 + uu - k * st.tiles;
         const uint32_t e = routed ? (uint32_t)act[k] : k;
         const uint32_t q0 = t * TILE;
-        const uint32_t q1 = min(q0 + TILE, st.P);
+        const uint32_t q1 = min(q0 + TILE, st.pend);
+        const uint32_t sb = WINDOW ? max(q0, st.pbeg) : q0;  // first position stored
 
         // Offset groups: run q (positions 16q .. 16q+15) is field q % F of
         // group q / F, F = 8 / w fields per group.
@@ -362,7 +372,7 @@ __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *d
         __syncthreads();
 
         uint8_t *plane = st.ws + (uint64_t)e * st.P;
-        expand_dispatch<FUSED, RUNS>(st, v, q0, q1, lds_bases, r_lo, tile, plane);
+        expand_dispatch<FUSED, RUNS, WINDOW>(st, v, q0, q1, sb, lds_bases, r_lo, tile, plane);
 
         if constexpr (FUSED) {
             __syncthreads();  // tile expanded
@@ -382,8 +392,13 @@ __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *d
                 const uint32_t j = i * kBlock + threadIdx.x;
                 const uint32_t pos = q0 + kRunBytes * j;
                 if (pos >= q1) break;
-                store_run<true>(plane + pos, *reinterpret_cast<const u32x4 *>(tile + kRunBytes * j),
-                                st.P - pos);
+                const u32x4 out = *reinterpret_cast<const u32x4 *>(tile + kRunBytes * j);
+                if constexpr (WINDOW) {
+                    if (pos + kRunBytes > sb)
+                        store_run<true>(plane + pos, out, sb > pos ? sb - pos : 0u, q1 - pos);
+                } else {
+                    store_run<true>(plane + pos, out, 0u, q1 - pos);
+                }
             }
             // The next tile's first barrier orders these LDS reads before the
             // next expansion overwrites the tile.
@@ -442,7 +457,7 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
     // Row bases of the tile's first 2 * kBlock rows; the resource covers the
     // tile's rows only, so lanes past them read nothing from memory.
     const uint32_t r_lo = div_exact(q0, st.rcp_cols);
-    const uint32_t r_hi = div_exact(min(q0 + tile_positions(RUNS), st.P) - 1u, st.rcp_cols) + 1u;
+    const uint32_t r_hi = div_exact(min(q0 + tile_positions(RUNS), st.pend) - 1u, st.rcp_cols) + 1u;
     const rsrc_t rb = make_rsrc(st.bases + (uint64_t)w.e * st.R + r_lo, r_hi - r_lo);
     L.b0 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)threadIdx.x, 0, 0);
     L.b1 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(kBlock + threadIdx.x), 0, 0);
@@ -481,7 +496,7 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
 // stores, so no wait on a tile's data also waits for the stores before it.
 // POLICY is the cache policy of the offset and entry loads.
 // ---------------------------------------------------------------------------
-template <uint32_t RUNS, uint32_t EXC, int POLICY>
+template <uint32_t RUNS, uint32_t EXC, int POLICY, bool WINDOW>
 __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
@@ -535,7 +550,7 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
         const StackArgs st = pick(a, cur.s);
         const uint32_t e = cur.e;
         const uint32_t q0 = cur.t * TILE;
-        const uint32_t q1 = min(q0 + TILE, st.P);
+        const uint32_t q1 = min(q0 + TILE, st.pend);
         const uint32_t r_lo = div_exact(q0, st.rcp_cols);
         const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
 
@@ -547,7 +562,7 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
         __syncthreads();
 
         uint8_t *plane = st.ws + (uint64_t)e * st.P;
-        expand_dispatch<true, RUNS>(st, L.v, q0, q1, lds_bases, r_lo, tile, plane);
+        expand_dispatch<true, RUNS, false>(st, L.v, q0, q1, q0, lds_bases, r_lo, tile, plane);
         __syncthreads();  // tile expanded
 
 #pragma unroll
@@ -583,22 +598,31 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
             issue_loads<RUNS, EXC, POLICY>(pick(a, cur.s), cur, cur.t * TILE, nl, nh, L);
         }
 
-        // Whole 16-byte runs of an aligned tile: one non-temporal 128-bit
-        // store per run, issued for every run (those past the tile's whole
-        // runs are dropped).  A ragged plane end or a misaligned workspace
-        // leaves bytes for the byte loop.
+        // Tile bytes s0 .. n-1 are stored (s0 > 0 only where a row window
+        // starts inside the tile).  Whole 16-byte runs of an aligned tile
+        // from the first run boundary at or after s0, h .. wend-1, take one
+        // non-temporal 128-bit store each, issued for every run: the resource
+        // starts at h, so runs before it have offsets that wrap past the
+        // resource and runs past wend lie beyond it; the hardware drops both.
+        // A ragged window edge or a misaligned workspace leaves bytes for the
+        // byte loop.
         uint8_t *dst = plane + q0;
         const uint32_t n = q1 - q0;
-        const uint32_t whole = (reinterpret_cast<uintptr_t>(dst) & 15u) ? 0u : (n & ~15u);
-        const rsrc_t rw = make_rsrc(dst, whole);
+        const uint32_t s0 = WINDOW && st.pbeg > q0 ? st.pbeg - q0 : 0u;
+        const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+        const uint32_t h = aligned ? (WINDOW ? min((s0 + 15u) & ~15u, n) : 0u) : n;
+        const uint32_t wend = max(h, n & ~15u);
+        const rsrc_t rw = make_rsrc(dst + h, wend - h);
 #pragma unroll
         for (uint32_t i = 0; i < RUNS; ++i) {
             const uint32_t off = kRunBytes * (i * kBlock + threadIdx.x);
             const u32x4 out = *reinterpret_cast<const u32x4 *>(tile + off);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)off, 0,
-                                                   kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)(off - h),
+                                                   0, kNonTemporal);
         }
-        for (uint32_t b = whole + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
+        if (WINDOW || !aligned)
+            for (uint32_t b = s0 + threadIdx.x; b < h; b += kBlock) dst[b] = tile[b];
+        for (uint32_t b = wend + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
         // The next tile's first barrier orders these LDS reads before the
         // next expansion overwrites the tile.
         if (!more) break;
@@ -606,20 +630,21 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
     }
 }
 
-template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED>
+// WINDOW: some stack's row window does not cover its whole plane (csf_decode_rows).
+template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED, bool WINDOW>
 __global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
     if constexpr (SCHED == kStreamEntries)
-        tile_loop_serial<true, RUNS, EXC, false, true>(a, dyn_lds, tile);
+        tile_loop_serial<true, RUNS, EXC, false, true, WINDOW>(a, dyn_lds, tile);
     else
-        tile_loop_pipelined<RUNS, EXC, SCHED == kStreamAll ? kNonTemporal : 0>(a, dyn_lds, tile);
+        tile_loop_pipelined<RUNS, EXC, SCHED == kStreamAll ? kNonTemporal : 0, WINDOW>(a, dyn_lds, tile);
 }
 
-template <uint32_t RUNS>
+template <uint32_t RUNS, bool WINDOW>
 __global__ __launch_bounds__(kBlock) void csf_fixed_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    tile_loop_serial<false, RUNS, 1, false, false>(a, dyn_lds, nullptr);
+    tile_loop_serial<false, RUNS, 1, false, false, WINDOW>(a, dyn_lds, nullptr);
 }
 
 // Largest k in [k, n) with M[k] <= t, given M[k] <= t < M[n]: gallop, then bisect.
@@ -720,9 +745,9 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
         for (uint32_t i = 0; i < kExcPerLane; ++i) {
             if (dst[i] == nullptr) continue;
             const uint32_t t = c0 + threadIdx.x + i * kBlock;
-            const uint32_t P = t >= N0 ? a.st[1].P : a.st[0].P;
+            const StackArgs &st = t >= N0 ? a.st[1] : a.st[0];
             const uint32_t pos = word[i] >> 8;
-            if (pos < P) dst[i][pos] = (uint8_t)(word[i] & 0xffu);
+            if (pos >= st.pbeg && pos < st.pend) dst[i][pos] = (uint8_t)(word[i] & 0xffu);
         }
     }
 }
@@ -768,32 +793,42 @@ static size_t exc_lds_bytes(const DecodeArgs &a) {
     return ((a.E + 15u) & ~15u) + 4u * 4u * words + 2u * a.E;
 }
 
-hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+template <bool WINDOW>
+hipError_t launch_fixed_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = tile_lds_bytes(a);
     switch (a.runs) {
-        case 1: hipLaunchKernelGGL(csf_fixed_kernel<1>, dim3(grid), dim3(kBlock), lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(csf_fixed_kernel<2>, dim3(grid), dim3(kBlock), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(csf_fixed_kernel<4>, dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((csf_fixed_kernel<1, WINDOW>), dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((csf_fixed_kernel<2, WINDOW>), dim3(grid), dim3(kBlock), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((csf_fixed_kernel<4, WINDOW>), dim3(grid), dim3(kBlock), lds, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    return a.windowed ? launch_fixed_t<true>(a, grid, stream) : launch_fixed_t<false>(a, grid, stream);
+}
+
+template <bool WINDOW>
+hipError_t launch_fused_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = tile_lds_bytes(a);
     const dim3 g(grid), b(kBlock);
     // (runs, entries per lane, load schedule) combinations the host plans
     if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedStreamAll)
-        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kStreamAll>), g, b, lds, stream, a);
+        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kStreamAll, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 4 && a.sched == kSchedStreamEntries)
-        hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries>), g, b, lds, stream, a);
+        hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 8 && a.sched == kSchedStreamEntries)
-        hipLaunchKernelGGL((csf_fused_kernel<2, 8, kStreamEntries>), g, b, lds, stream, a);
+        hipLaunchKernelGGL((csf_fused_kernel<2, 8, kStreamEntries, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 4 && a.exc_regs == 4 && a.sched == kSchedPipelined)
-        hipLaunchKernelGGL((csf_fused_kernel<4, 4, kPipelined>), g, b, lds, stream, a);
+        hipLaunchKernelGGL((csf_fused_kernel<4, 4, kPipelined, WINDOW>), g, b, lds, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    return a.windowed ? launch_fused_t<true>(a, grid, stream) : launch_fused_t<false>(a, grid, stream);
 }
 
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {

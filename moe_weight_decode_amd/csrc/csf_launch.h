@@ -42,7 +42,9 @@ struct StackArgs {
     uint32_t P;                 // R * C  (< 2^24)
     uint32_t R;
     uint32_t C;
-    uint32_t tiles;             // ceil(P / tile positions of the launch)
+    uint32_t pbeg, pend;        // positions decoded: rows begin .. end-1 (0, P: every row)
+    uint32_t tile0;             // first tile decoded: pbeg / tile positions of the launch
+    uint32_t tiles;             // tiles decoded per plane: tile0 .. ceil(pend / tile) - 1
     uint32_t index_tiles;       // ceil(P / kIndexTile)
     uint32_t wbits;             // 4 (NVFP4) or 1 (MXFP4)
     uint32_t row_mode;          // RowMode
@@ -58,7 +60,7 @@ struct DecodeArgs {
     uint32_t sched;               // load schedule of the fused kernel (kSched*)
     uint32_t exc_regs;            // entries per lane loaded with the offsets (fused: 4 or 8)
     uint32_t es_wide;             // expert_start holds int64 (else int32)
-    uint32_t pad_;
+    uint32_t windowed;            // some stack decodes a row window short of its whole plane
 };
 
 // Dynamic LDS bytes a tile kernel needs for these arguments.

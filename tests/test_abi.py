@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csf_abi_version() == 2
+    assert lib.csf_abi_version() == 3
     for s in range(9):
         assert lib.csf_status_str(s)
     assert lib.csf_status_str(99) == b"unknown status"
@@ -205,6 +205,30 @@ def test_paired_and_passes_errors(lib):
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), None, None)] == "CSF_E_NULL"
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(a), 0x9002, None)] == "CSF_E_ALIGN"
     assert mwd.STATUS[lib.csf_build_index(ctypes.byref(_fake(E=0)), 0x9000, None)] == "CSF_E_SHAPE"
+
+
+def test_decode_rows_windows(lib):
+    a, b = _fake(R=64), _fake(R=32)
+    ws = 0x5000
+
+    def call(ra, rb=None, second=None, passes=3):
+        r1 = mwd.csf_rows(*ra) if ra is not None else None
+        r2 = mwd.csf_rows(*rb) if rb is not None else None
+        return mwd.STATUS[lib.csf_decode_rows(ctypes.byref(a), ws, None if r1 is None else ctypes.byref(r1),
+                                              None if second is None else ctypes.byref(second),
+                                              0x6000 if second is not None else None,
+                                              None if r2 is None else ctypes.byref(r2), None, passes, None)]
+
+    for bad in ((-1, 4), (5, 4), (0, 65), (64, 65)):
+        assert call(bad) == "CSF_E_SHAPE", bad
+        assert call((0, 0), bad, second=b) in ("CSF_E_SHAPE",), bad
+    assert call((0, 64), (0, 33), second=b) == "CSF_E_SHAPE"
+    assert call((0, 4), passes=0) == "CSF_E_SIZE"
+    # empty windows launch nothing (no HIP call on this GPU-less host)
+    assert call((0, 0)) == "CSF_OK"
+    assert call((64, 64)) == "CSF_OK"
+    assert call((7, 7), (32, 32), second=b) == "CSF_OK"
+    assert mwd.STATUS[lib.csf_decode_rows(None, ws, None, None, None, None, None, 3, None)] == "CSF_E_NULL"
 
 
 def test_encode_device_errors(lib):

@@ -518,3 +518,96 @@ def test_routed_int64_expert_start(orc, dev, mode):
     torch.cuda.synchronize()
     want = oracle_expect(orc, st, np.array([0, 1, 2, 2, 3], dtype=np.int32))
     assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), want, "int64 single")
+
+
+# -- row windows (decode only the rows a consumer reads) -----------------------
+
+def run_decode_rows(stack, dev, rows, es=None, offset=0, second=None, rows_second=None):
+    """csf_decode_rows into guarded, poisoned workspaces; returns the dense
+    bytes of each stack and asserts the guard bands are intact."""
+    stacks = [stack] + ([second] if second is not None else [])
+    bufs, wss = [], []
+    for s in stacks:
+        n = s.dense_bytes
+        buf = torch.full((GUARD_BYTES + offset + n + GUARD_BYTES,), GUARD, dtype=torch.uint8, device=dev)
+        ws = buf[GUARD_BYTES + offset: GUARD_BYTES + offset + n]
+        ws.fill_(POISON)
+        bufs.append(buf)
+        wss.append(ws)
+    es_t = None if es is None else torch.from_numpy(np.ascontiguousarray(es, dtype=np.int32)).to(dev)
+    mwd.decode_rows(stack, wss[0], rows, second, wss[1] if second is not None else None, rows_second, es_t)
+    torch.cuda.synchronize()
+    out = []
+    for s, buf in zip(stacks, bufs):
+        h = buf.cpu().numpy()
+        n = s.dense_bytes
+        assert np.all(h[:GUARD_BYTES + offset] == GUARD), "write before the workspace"
+        assert np.all(h[GUARD_BYTES + offset + n:] == GUARD), "write past the workspace"
+        out.append(h[GUARD_BYTES + offset: GUARD_BYTES + offset + n].reshape(s.E, s.R, s.C))
+    return out
+
+
+def oracle_rows(orc, st, rows, es=None):
+    b, e = rows if rows is not None else (0, st["R"])
+    return orc.decode_rows(st, b, e, es, np.full((st["E"], st["R"], st["C"]), POISON, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", ["gate_nvfp4", "down_nvfp4", "mxfp4"])
+def test_row_window_full_stacks(orc, dev, name, mode):
+    spec, x, st = stack_case(name, orc)
+    R = spec.R
+    stack = upload(st, dev, mode)
+    for rows in ((0, R // 2), (R // 2, R), (37, R - 101)):
+        got, = run_decode_rows(stack, dev, rows)
+        assert_bytes_equal(got, oracle_rows(orc, st, rows), f"{name} rows {rows}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmt,E,R,C", [(workloads.NVFP4, 5, 300, 50), (workloads.MXFP4, 3, 200, 160),
+                                       (workloads.NVFP4, 3, 2000, 7), (workloads.NVFP4, 4, 130, 128)],
+                         ids=["nv_c50", "mx_c160", "nv_c7", "nv_c128"])
+def test_row_window_small(orc, dev, fmt, E, R, C, mode):
+    if fmt == workloads.NVFP4:
+        x = workloads.nvfp4_stack(E, R, C, 61, 0.08, hot_row_frac=0.02)
+    else:
+        x = workloads.mxfp4_stack(E, R, C, 62, 0.15)
+    st = orc.encode(fmt, x)
+    stack = upload(st, dev, mode)
+    rng = np.random.default_rng(R)
+    windows = [(0, R), (0, R // 2), (R // 2, R), (0, 1), (R - 1, R), (0, 0), (R, R), (3, 4)]
+    windows += [tuple(int(v) for v in sorted(rng.integers(0, R + 1, 2))) for _ in range(6)]
+    es = workloads.expert_start_from_mask(np.arange(E) % 2 == 1, tokens=2)
+    for rows in windows:
+        got, = run_decode_rows(stack, dev, rows)
+        assert_bytes_equal(got, oracle_rows(orc, st, rows), f"rows {rows}")
+        got, = run_decode_rows(stack, dev, rows, es=es)
+        assert_bytes_equal(got, oracle_rows(orc, st, rows, es), f"rows {rows} routed")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("offset", [1, 7])
+def test_row_window_odd_offset_workspace(orc, dev, offset, mode):
+    x = workloads.nvfp4_stack(3, 500, 50, 63, 0.05)
+    st = orc.encode(workloads.NVFP4, x)
+    stack = upload(st, dev, mode)
+    for rows in ((0, 250), (123, 411)):
+        got, = run_decode_rows(stack, dev, rows, offset=offset)
+        assert_bytes_equal(got, oracle_rows(orc, st, rows), f"offset {offset} rows {rows}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_row_window_paired_gate_half(orc, dev, mode):
+    # the gate half of the gate/up stack and every row of the down stack, routed
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev, mode), upload(sd, dev, mode)
+    es = workloads.ROUTED.expert_start()
+    half = (0, xg.shape[1] // 2)
+    wg, wd = run_decode_rows(g, dev, half, es=es, second=d, rows_second=None)
+    assert_bytes_equal(wg, oracle_rows(orc, sg, half, es), "gate half")
+    assert_bytes_equal(wd, oracle_rows(orc, sd, None, es), "down, every row")
+    # an empty first window leaves only the second stack to decode
+    wg, wd = run_decode_rows(g, dev, (5, 5), es=es, second=d, rows_second=(100, 900))
+    assert np.all(wg == POISON)
+    assert_bytes_equal(wd, oracle_rows(orc, sd, (100, 900), es), "down rows 100..899")
