@@ -160,3 +160,39 @@ MX = StackSpec("mxfp4", MXFP4, 384, 1024, 160, seed=4, exc_rate=0.15,
                desc="384 experts x 1024 rows x 160 scale columns (K=5120), 15% outliers")
 
 STACKS = {s.name: s for s in (TINY, GATE, DOWN, MX)}
+
+
+# -- W4A16 MoE projection inputs (the consumer of the decoded scales) ----------
+
+@dataclass
+class W4A16Inputs:
+    x_bits: np.ndarray        # uint16 [T, K]: bfloat16 bit patterns of the routed tokens
+    w_packed: np.ndarray      # uint8 [E, N, K/2]: two E2M1 codes per byte (even k low nibble)
+    scales: np.ndarray        # uint8 [E, N, K/16]: E4M3 scale bytes
+    alpha: np.ndarray         # float32 [E]: per-expert tensor scale
+    expert_start: np.ndarray  # int32 [E + 1]: grouped routing (tokens sorted by expert)
+
+
+def bf16_bits(T: int, K: int, rng) -> np.ndarray:
+    """Random bfloat16 bit patterns: random sign and mantissa, exponent field
+    in [118, 130] (magnitudes ~2^-9 .. 2^4), no zeros, NaNs or infinities."""
+    sign = rng.integers(0, 2, (T, K), dtype=np.uint16) << 15
+    exp = rng.integers(118, 131, (T, K), dtype=np.uint16) << 7
+    man = rng.integers(0, 128, (T, K), dtype=np.uint16)
+    return (sign | exp | man).astype(np.uint16)
+
+
+def w4a16_inputs(E: int, N: int, K: int, expert_start: np.ndarray, seed: int,
+                 exc_rate: float = 0.03) -> W4A16Inputs:
+    """Seeded inputs of a routed NVFP4 projection: scales shaped like the
+    gate-like stack (nvfp4_stack with C = K / 16), uniform random E2M1 codes,
+    bfloat16 activations for the routed tokens, alpha uniform in [0.5, 2)."""
+    assert K % 32 == 0
+    es = np.ascontiguousarray(expert_start, dtype=np.int32)
+    T = int(es[-1])
+    scales = nvfp4_stack(E, N, K // 16, seed, exc_rate)
+    rng = np.random.default_rng(seed + 1000)
+    w = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    x = bf16_bits(T, K, rng)
+    alpha = rng.uniform(0.5, 2.0, E).astype(np.float32)
+    return W4A16Inputs(x, w, scales, alpha, es)
