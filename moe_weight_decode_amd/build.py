@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "csf_api.cpp"), os.path.join(CSRC, "csf_kernels.hip"),
            os.path.join(CSRC, "csf_encode.hip")]
-HEADERS = [os.path.join(ROOT, "include", "csf.h"), os.path.join(CSRC, "csf_launch.h")]
+HEADERS = [os.path.join(ROOT, "include", "csf.h"), os.path.join(CSRC, "csf_launch.h"),
+           os.path.join(CSRC, "csf_device.h")]
 LIBRARY = os.path.join(PKG, "libcsf.so")
 ARCH = "gfx950"
 
