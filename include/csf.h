@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSF_ABI_VERSION 3
+#define CSF_ABI_VERSION 4
 
 /* Positions per exception-index tile. */
 #define CSF_INDEX_TILE 2048
@@ -246,6 +246,37 @@ typedef struct csf_rows {
 csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_rows *rows_first,
                            const csf_stack *second, uint8_t *ws_second, const csf_rows *rows_second,
                            const int32_t *expert_start, uint32_t passes, void *hip_stream);
+
+/*
+ * W4A16 MoE projection whose NVFP4 block scales stay compressed: the consumer
+ * the pages pair with the compressed scales ("NVFP4-CSF: expand_scales() ...",
+ * b12x PR 478, last commit message: each W4A16 pipeline stage rebuilds its
+ * E4M3 K16 scales in shared memory from the compressed storage, so small calls
+ * need no dense scale scratch).  For every expert e with tokens t in
+ * [expert_start[e], expert_start[e+1]):
+ *     y[t][n] = alpha[e] * sum_k x[t][k] * e2m1(W[e][n][k]) * e4m3(S[e][n][k/16])
+ *
+ * scales: the NVFP4 stack of the projection's scales (E experts, rows = N output
+ *   features, cols = K/16; K a multiple of 32, at most 4096), device buffers.
+ *   With dense_scales NULL each workgroup expands the scales of its 16 rows
+ *   straight into LDS from the CSF streams (needs the tile index); otherwise
+ *   the scales are read from dense_scales, u8[E][N][K/16] (for example a
+ *   csf_decode workspace) and the CSF streams are not read.
+ * weights: u8[E][N][K/2], two E2M1 codes per byte, code k of row n in the low
+ *   nibble of byte k/2 for even k, the high nibble for odd k; 16-byte aligned.
+ * x: bfloat16 [num_tokens][K], tokens sorted by expert (the grouped routing).
+ * alpha: float32 [E].  expert_start: int32 [E + 1] on the device; token
+ *   indices are clamped to [0, num_tokens].  y: float32 [num_tokens][N]; rows
+ *   of tokens outside every expert's range are not written.
+ * Enqueued on hip_stream; allocates nothing; no host synchronisation.
+ * Errors: CSF_E_NULL (a required pointer, or the tile index when dense_scales is
+ *   NULL), CSF_E_FORMAT (not NVFP4), CSF_E_SHAPE (K not a multiple of 32 or
+ *   above 4096, or the stack's own shape checks), CSF_E_SIZE (num_tokens < 0),
+ *   CSF_E_ALIGN, CSF_E_HIP.
+ */
+csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, const uint8_t *weights,
+                         const uint16_t *x, int32_t num_tokens, const float *alpha,
+                         const int32_t *expert_start, float *y, void *hip_stream);
 
 /*
  * Full host-side check of a stack whose buffers are in HOST memory: prefix

@@ -50,7 +50,7 @@ STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: 
 
 EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_encode_device", "csf_build_index",
            "csf_decode", "csf_decode_paired", "csf_decode_i64", "csf_decode_passes", "csf_decode_rows",
-           "csf_validate")
+           "csf_moe_w4a16", "csf_validate")
 
 
 class CsfError(RuntimeError):
@@ -116,6 +116,8 @@ def _lib():
         lib.csf_decode_rows.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_rows),
                                         ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_rows), vp,
                                         ctypes.c_uint32, vp]
+        lib.csf_moe_w4a16.restype = ctypes.c_int
+        lib.csf_moe_w4a16.argtypes = [ctypes.POINTER(csf_stack), vp, vp, vp, i32, vp, vp, vp, vp]
         lib.csf_validate.restype = ctypes.c_int
         lib.csf_validate.argtypes = [ctypes.POINTER(csf_stack)]
         _LIB = lib
@@ -389,6 +391,40 @@ def decode_rows(first: CompressedStack, ws_first: torch.Tensor, rows_first=None,
                                   b_ref, ws_b, None if rb is None else ctypes.byref(rb),
                                   _es_ptr(expert_start, first), passes,
                                   _stream_handle(stream, first.device)), "csf_decode_rows")
+
+
+def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, alpha: torch.Tensor,
+              expert_start: torch.Tensor, out: torch.Tensor | None = None, dense_scales=None, stream=None):
+    """Enqueue the routed W4A16 projection (see ``csf_moe_w4a16``); returns y
+    (float32 [T, N]).  ``x`` is bfloat16 (or int16/uint16 bit patterns)
+    [T, K]; ``weights`` uint8 [E, N, K/2]; ``alpha`` float32 [E]; with
+    ``dense_scales`` (uint8, E*N*K/16 bytes) the scales come from it instead
+    of the compressed stack."""
+    dev = scales.device
+    if dev.type != "cuda":
+        raise ValueError("moe_w4a16: compressed stack must be on a GPU")
+    T = x.shape[0]
+    for name, t, dt in (("weights", weights, (torch.uint8,)), ("x", x, (torch.bfloat16, torch.int16, torch.uint16)),
+                        ("alpha", alpha, (torch.float32,)), ("expert_start", expert_start, (torch.int32,))):
+        if t.device != dev or t.dtype not in dt or not t.is_contiguous():
+            raise ValueError(f"moe_w4a16: {name} must be a contiguous {dt} tensor on {dev}")
+    if weights.numel() != scales.E * scales.R * scales.C * 8 or x.numel() != T * scales.C * 16:
+        raise ValueError("moe_w4a16: weights / x sizes do not match the scale stack")
+    if alpha.numel() != scales.E or expert_start.numel() != scales.E + 1:
+        raise ValueError("moe_w4a16: alpha must be [E] and expert_start [E+1]")
+    if out is None:
+        out = torch.empty(T, scales.R, dtype=torch.float32, device=dev)
+    elif out.device != dev or out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != T * scales.R:
+        raise ValueError("moe_w4a16: out must be a contiguous float32 [T, N] tensor")
+    if dense_scales is not None and (dense_scales.device != dev or dense_scales.dtype != torch.uint8
+                                     or dense_scales.numel() < scales.dense_bytes):
+        raise ValueError("moe_w4a16: dense_scales must be uint8 with the stack's dense size")
+    d = scales.descriptor()
+    _check(_lib().csf_moe_w4a16(ctypes.byref(d), None if dense_scales is None else dense_scales.data_ptr(),
+                                weights.data_ptr(), x.data_ptr() if T > 0 else None, T, alpha.data_ptr(),
+                                expert_start.data_ptr(), out.data_ptr(), _stream_handle(stream, dev)),
+           "csf_moe_w4a16")
+    return out
 
 
 class Launch:

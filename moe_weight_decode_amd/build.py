@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "csf_api.cpp"), os.path.join(CSRC, "csf_kernels.hip"),
-           os.path.join(CSRC, "csf_encode.hip")]
+           os.path.join(CSRC, "csf_encode.hip"), os.path.join(CSRC, "csf_moe.hip")]
 HEADERS = [os.path.join(ROOT, "include", "csf.h"), os.path.join(CSRC, "csf_launch.h"),
            os.path.join(CSRC, "csf_device.h")]
 LIBRARY = os.path.join(PKG, "libcsf.so")

@@ -260,6 +260,52 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, con
     return CSF_OK;
 }
 
+// Workgroups per CU of the W4A16 consumer (its VGPR count allows 3).
+#ifndef CSF_MOE_WG_PER_CU
+#define CSF_MOE_WG_PER_CU 3
+#endif
+
+csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t *weights,
+                    const uint16_t *x, int32_t num_tokens, const float *alpha,
+                    const int32_t *expert_start, float *y, void *hip_stream) {
+    csf_status st = check_stack(scales, weights);
+    if (st != CSF_OK) return st;
+    if (scales->format != CSF_NVFP4_E4M3) return CSF_E_FORMAT;
+    const int64_t C = scales->cols, K = 16 * C;
+    if (C % 2 != 0 || C > 256) return CSF_E_SHAPE;  // K a multiple of 32, at most 4096
+    if (num_tokens < 0) return CSF_E_SIZE;
+    if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
+    if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;
+    if (dense == nullptr && scales->tile_index == nullptr) return CSF_E_NULL;
+    if (!aligned(weights, 16) || (x && !aligned(x, 4)) || !aligned(alpha, 4) || !aligned(expert_start, 4) ||
+        !aligned(y, 4))
+        return CSF_E_ALIGN;
+    if (num_tokens == 0) return CSF_OK;
+
+    csf::MoeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    fill_stack(a.st, *scales, nullptr, csf::kIndexTile, 0, scales->rows);
+    a.dense = dense;
+    a.w = weights;
+    a.x = x;
+    a.alpha = alpha;
+    a.expert_start = expert_start;
+    a.y = y;
+    a.E = uint32_t(scales->num_experts);
+    a.N = uint32_t(scales->rows);
+    a.K = uint32_t(K);
+    a.C = uint32_t(C);
+    a.T = uint32_t(num_tokens);
+    a.ntiles = (a.N + 15u) / 16u;
+    a.bases_stage = bases_stage_bytes(a.C, 16u * a.C);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const uint64_t units = uint64_t(a.E) * a.ntiles;
+    const uint64_t cap = uint64_t(cu_count(stream)) * CSF_MOE_WG_PER_CU;
+    const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(units, cap)));
+    if (csf::launch_moe_w4a16(a, grid, stream) != hipSuccess) return CSF_E_HIP;
+    return CSF_OK;
+}
+
 csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_stream) {
     if (tile_index == nullptr) return CSF_E_NULL;
     csf_status st = check_stack(s, reinterpret_cast<const uint8_t *>(tile_index));
@@ -634,6 +680,16 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
     try {
         return enqueue(first, ws_first, rows_first, second, second ? ws_second : nullptr,
                        second ? rows_second : nullptr, expert_start, false, passes, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, const uint8_t *weights,
+                         const uint16_t *x, int32_t num_tokens, const float *alpha,
+                         const int32_t *expert_start, float *y, void *hip_stream) {
+    try {
+        return moe_impl(scales, dense_scales, weights, x, num_tokens, alpha, expert_start, y, hip_stream);
     } catch (...) {
         return CSF_E_HIP;
     }

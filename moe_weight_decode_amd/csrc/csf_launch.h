@@ -75,6 +75,24 @@ hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 // Per-tile exception index of one stack from its entries and prefix.
 hipError_t launch_build_index(const StackArgs &s, uint32_t E, int32_t *tile_index, hipStream_t stream);
 
+// W4A16 MoE projection consuming the compressed scales (csf_moe.hip).
+struct MoeArgs {
+    StackArgs st;                  // scale stack: shape, and the CSF streams when dense is nullptr
+    const uint8_t *dense;          // dense scales [E][N][C], or nullptr: scales decoded into LDS
+    const uint8_t *w;              // E2M1 codes [E][N][K/2], even k in the low nibble
+    const uint16_t *x;             // bfloat16 activations [T][K], tokens grouped by expert
+    const float *alpha;            // per-expert tensor scale [E]
+    const int32_t *expert_start;   // [E + 1]
+    float *y;                      // [T][N]
+    uint32_t E, N, K, C, T;        // C = K / 16
+    uint32_t ntiles;               // ceil(N / 16) work units per routed expert
+    uint32_t bases_stage;          // dynamic LDS bytes for one unit's row bases
+    uint32_t pad_;
+};
+
+size_t moe_lds_bytes(const MoeArgs &a);
+hipError_t launch_moe_w4a16(const MoeArgs &a, uint32_t grid, hipStream_t stream);
+
 // Encoder on the device (csf_encode.hip).
 struct EncodeArgs {
     const uint8_t *dense;   // [E * P]

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.csf_abi_version() == 3
+    assert lib.csf_abi_version() == 4
     for s in range(9):
         assert lib.csf_status_str(s)
     assert lib.csf_status_str(99) == b"unknown status"
@@ -229,6 +229,25 @@ def test_decode_rows_windows(lib):
     assert call((64, 64)) == "CSF_OK"
     assert call((7, 7), (32, 32), second=b) == "CSF_OK"
     assert mwd.STATUS[lib.csf_decode_rows(None, ws, None, None, None, None, None, 3, None)] == "CSF_E_NULL"
+
+
+def test_moe_w4a16_errors(lib):
+    def call(desc, dense=None, w=0x10000, x=0x20000, T=4, alpha=0x30000, es=0x40000, y=0x50000):
+        return mwd.STATUS[lib.csf_moe_w4a16(ctypes.byref(desc) if desc is not None else None, dense, w, x, T,
+                                            alpha, es, y, None)]
+    ok = _fake(R=32, C=16, stride=16 * 16, tile_index=0x8000)
+    assert call(_fake(fmt=1, R=32, C=16, stride=16 * 64, tile_index=0x8000)) == "CSF_E_FORMAT"
+    assert call(_fake(R=32, C=15, stride=16 * 15, tile_index=0x8000)) == "CSF_E_SHAPE"   # K = 240
+    assert call(_fake(R=32, C=258, stride=16 * 258, tile_index=0x8000)) == "CSF_E_SHAPE"  # K > 4096
+    assert call(_fake(R=32, C=16, stride=16 * 16)) == "CSF_E_NULL"        # no tile index, no dense scales
+    assert call(ok, w=None) == "CSF_E_NULL"
+    assert call(ok, alpha=None) == "CSF_E_NULL"
+    assert call(ok, x=None) == "CSF_E_NULL"
+    assert call(ok, T=-1) == "CSF_E_SIZE"
+    assert call(ok, w=0x10008) == "CSF_E_ALIGN"
+    assert call(ok, y=0x50002) == "CSF_E_ALIGN"
+    assert call(None) == "CSF_E_NULL"
+    assert call(ok, T=0, x=None) == "CSF_OK"                              # nothing to do, nothing launched
 
 
 def test_encode_device_errors(lib):

@@ -36,7 +36,7 @@ def _kernel_resources(source):
     return out
 
 
-@pytest.mark.parametrize("source", ["csf_kernels.hip", "csf_encode.hip"])
+@pytest.mark.parametrize("source", ["csf_kernels.hip", "csf_encode.hip", "csf_moe.hip"])
 def test_no_scratch_and_plan_occupancy(source):
     res = _kernel_resources(os.path.join(CSRC, source))
     assert res, "no kernels found"
