@@ -20,7 +20,10 @@ Prints ONE JSON line on stdout:
   python bench.py [--steps K] [--warmup W] [--sets N] [--workload NAME] [--all] [--no-cpu]
 
 --workload picks another timed workload (down_nvfp4, mxfp4, tiny_nvfp4,
-routed_paired) for profiling; the default is the gate-like stack.
+routed_paired, routed_moe) for profiling; the default is the gate-like stack.
+routed_moe times the W4A16 consumer that expands its scales in LDS from the
+CSF streams (csf_moe_w4a16) on the gate-like projection with 8 of 512 experts
+routed, next to a routed decode followed by the same GEMM on dense scales.
 
 --all also measures the other workloads (down-like, MXFP4, routed paired,
 tiny), the two-pass decode of each (fixed-stream kernel, then exception
@@ -107,14 +110,21 @@ def stack_bytes(stack, active=None):
     return fixed, exc, dense
 
 
-def source_hash() -> str:
-    """Fingerprint of the decode sources' code: comments and whitespace are
-    dropped, so only a change to the code itself invalidates counter records."""
+_KERNEL_SOURCES = {
+    "csf_fused_kernel": ("csf_kernels.hip",),
+    "csf_moe_w4a16_kernel": ("csf_moe.hip",),
+}
+
+
+def source_hash(kernel: str = "csf_fused_kernel") -> str:
+    """Fingerprint of the code a kernel is built and launched from (its own
+    source plus the shared device helpers, launch structs and host planner):
+    comments and whitespace are dropped, so only a change to the code itself
+    invalidates that kernel's counter records."""
     import re
     h = hashlib.sha256()
-    for rel in ("moe_weight_decode_amd/csrc/csf_kernels.hip", "moe_weight_decode_amd/csrc/csf_launch.h",
-                "moe_weight_decode_amd/csrc/csf_api.cpp"):
-        text = open(os.path.join(ROOT, rel)).read()
+    for name in _KERNEL_SOURCES[kernel] + ("csf_launch.h", "csf_api.cpp", "csf_device.h"):
+        text = open(os.path.join(ROOT, "moe_weight_decode_amd", "csrc", name)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
@@ -129,7 +139,7 @@ def pmc_traffic(kernel: str, workload: str):
         return None
     data = json.load(open(path))
     rec = data.get(f"{kernel}/{workload}")
-    if not rec or rec.get("source_hash") != source_hash():
+    if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -347,6 +357,127 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
                 sets=n, steps=reps * n)
 
 
+def bench_moe(mwd, torch, ev, workloads, steps, warmup, dev, routings=64):
+    """Routed W4A16 projection of the gate-like shape (512 experts x 800 rows x
+    K = 2048, scales of the gate-like stack), 8 experts routed per call with
+    1..64 tokens each; `routings` disjoint routings cover every expert once, so
+    each replay of the call sequence reads every expert's weights from HBM.
+    Times, from HIP-graph replays: the stage-local consumer (scales expanded in
+    LDS from the CSF streams), a routed decode into a dense workspace followed
+    by the same GEMM on the dense scales, and the GEMM alone on scales decoded
+    beforehand.  Checks the first routing against the oracle first."""
+    import numpy as np
+    from oracle import w4a16 as ref
+    spec = workloads.GATE
+    E, N, C = spec.E, spec.R, spec.C
+    K = 16 * C
+    xs = spec.generate()
+    stack = mwd.prepare(xs, spec.fmt).to(dev)
+    rng = np.random.default_rng(77)
+    w_host = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    w = torch.from_numpy(w_host).to(dev)
+    alpha_host = rng.uniform(0.5, 2.0, E).astype(np.float32)
+    alpha = torch.from_numpy(alpha_host).to(dev)
+    full = torch.empty(stack.dense_bytes, dtype=torch.uint8, device=dev)
+    mwd.decode(stack, full)
+    ws = torch.empty(stack.dense_bytes, dtype=torch.uint8, device=dev)
+    rs = routed_sets(workloads, E, workloads.ROUTED.n_active, workloads.ROUTED.max_tokens, 177, routings)
+    cases, nbytes, extra_bytes = [], [], []
+    pfx = stack.prefix.cpu().numpy()
+    for i, es in enumerate(rs):
+        T = int(es[-1])
+        xb = workloads.bf16_bits(T, K, rng)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev)
+        y = torch.empty(T, N, dtype=torch.float32, device=dev)
+        es_t = torch.from_numpy(es).to(dev)
+        act = np.flatnonzero(np.diff(es) > 0)
+        entries = int(sum(pfx[e + 1] - pfx[e] for e in act))
+        scales = len(act) * (stack.R + stack.stride) + 4 * entries + 4 * len(act) * (stack.index_tiles + 1)
+        nbytes.append(len(act) * N * K // 2 + scales + T * K * 2 + T * N * 4 + 4 * (E + 1) + 4 * len(act))
+        extra_bytes.append(2 * len(act) * stack.P)
+        cases.append((x, y, es_t))
+        if i == 0:
+            y0 = mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)
+            torch.cuda.synchronize()
+            got = y0.cpu().numpy()
+            yr, mag = ref.moe_w4a16(xb, w_host, xs, alpha_host, es, experts=act)
+            if not np.all(np.abs(got - yr) <= (K + 8) * 2.0 ** -24 * mag):
+                raise SystemExit("routed W4A16 projection differs from the oracle")
+            y1 = torch.empty_like(y)
+            mwd.decode(stack, ws, es_t)
+            mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y1, dense_scales=ws)
+            torch.cuda.synchronize()
+            if not torch.equal(y0, y1):
+                raise SystemExit("stage-local and dense-scale projections differ")
+            first = (xb, es, act)
+
+    def seq(kind):
+        for x, y, es_t in cases:
+            if kind == "stage":
+                mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)
+            elif kind == "decode_then_gemm":
+                mwd.decode(stack, ws, es_t)
+                mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y, dense_scales=ws)
+            else:
+                mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y, dense_scales=full)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    graphs = {}
+    with torch.cuda.stream(side):
+        for kind in ("stage", "decode_then_gemm", "dense_gemm"):
+            seq(kind)  # warm the launch path outside capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for kind in ("stage", "decode_then_gemm", "dense_gemm"):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=side):
+            seq(kind)
+        graphs[kind] = gr
+    torch.cuda.synchronize()
+
+    class Replay:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def __init__(self, gr):
+            self.gr = gr
+
+        def __call__(self):
+            self.gr.replay()
+
+    n = len(cases)
+    reps = max(1, steps // n)
+    out = dict(bytes=sum(nbytes) / n, extra_bytes=sum(extra_bytes) / n, calls=n, steps=reps * n,
+               tokens=sum(int(c[2][-1]) for c in cases) / n, first=first, w_host=w_host, xs=xs,
+               alpha_host=alpha_host, first_bytes=nbytes[0])
+    for kind, gr in graphs.items():
+        wall, evt = timed_loop(torch, ev, [Replay(gr)], reps, max(1, warmup // n))
+        out[kind + "_ms"] = max(wall, evt) / n
+        out[kind + "_event_ms"] = evt / n
+    return out
+
+
+def cpu_baseline_moe(mr, budget_s=10.0):
+    """The W4A16 oracle (numpy float64) computing the first routing's projection."""
+    from oracle import w4a16 as ref
+    xb, es, act = mr["first"]
+    sec, n = _repeat(lambda: ref.moe_w4a16(xb, mr["w_host"], mr["xs"], mr["alpha_host"], es, experts=act),
+                     budget_s)
+    return dict(value=round(mr["first_bytes"] / sec / 1e9, 4), unit="GB/s", cores=_blas_threads(),
+                kind="oracle", us_per_call=round(sec * 1e6, 1),
+                sample=f"one routed call ({len(act)} experts, {int(es[-1])} tokens) of the W4A16 "
+                       f"oracle, repeated {n} times, median")
+
+
+def _blas_threads() -> int:
+    """Threads numpy's BLAS may use (the float64 matmuls of the W4A16 oracle)."""
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+        v = os.environ.get(var)
+        if v and v.isdigit():
+            return int(v)
+    return len(os.sched_getaffinity(0))
+
+
 def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
     srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
     dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
@@ -374,7 +505,7 @@ def main():
                     help="after the timed run, N plain 256 MiB device copies (reference for "
                          "hardware byte counters)")
     ap.add_argument("--workload", default="gate_nvfp4",
-                    choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired"],
+                    choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe"],
                     help="timed workload (default: the 512-expert gate-like stack)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -390,7 +521,26 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     ev = HipEvents()
-    if args.workload == "routed_paired":
+    if args.workload == "routed_moe":
+        mr = bench_moe(mwd, torch, ev, workloads, args.steps, args.warmup, dev)
+        step_bytes = mr["bytes"]
+        r = dict(step_ms=mr["stage_ms"], event_ms=mr["stage_event_ms"], wall_ms=mr["stage_ms"])
+        config = {
+            "workload": "routed_moe: W4A16 projection of the gate-like shape (512 experts x 800 rows x "
+                        "K=2048, NVFP4 weights, CSF scales of the gate-like stack) with 8 of 512 experts "
+                        "routed (1..64 tokens each); scales expanded in LDS from the CSF streams",
+            "decode": "stage-local (csf_moe_w4a16 reading the CSF streams); steps replayed from a HIP "
+                      "graph of all rotating routings",
+            "bytes_per_step": round(step_bytes),
+            "mean_tokens": mr["tokens"],
+            "rotating_sets": mr["calls"],
+            "timed_steps": mr["steps"],
+            "decode_then_gemm_us": round(mr["decode_then_gemm_ms"] * 1e3, 3),
+            "dense_scale_gemm_us": round(mr["dense_gemm_ms"] * 1e3, 3),
+            "decode_then_gemm_extra_bytes": round(mr["extra_bytes"]),
+        }
+        x_head = None
+    elif args.workload == "routed_paired":
         rr = bench_routed(mwd, torch, ev, workloads, args.steps, args.warmup, dev)
         gs, ds = workloads.ROUTED.stacks
         step_bytes = rr["bytes"]
@@ -433,7 +583,8 @@ def main():
     achieved = step_bytes / (r["event_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
-    traffic = pmc_traffic("csf_fused_kernel", args.workload)
+    kernel = "csf_moe_w4a16_kernel" if args.workload == "routed_moe" else "csf_fused_kernel"
+    traffic = pmc_traffic(kernel, args.workload)
     out = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -446,11 +597,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": "bf16" if args.workload == "routed_moe" else "u8",
         "data": "synthetic",
         "config": config,
         "roofline": {
-            "kernel": "csf_fused_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -515,6 +666,8 @@ def main():
         log(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
         if args.workload == "routed_paired":
             out["cpu_baseline"] = cpu_baseline_routed(workloads, args.cpu_seconds)
+        elif args.workload == "routed_moe":
+            out["cpu_baseline"] = cpu_baseline_moe(mr, args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline(spec, x_head, args.cpu_seconds)
     else:

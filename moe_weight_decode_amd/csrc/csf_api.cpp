@@ -260,9 +260,9 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, con
     return CSF_OK;
 }
 
-// Workgroups per CU of the W4A16 consumer (its VGPR count allows 3).
+// Workgroups per CU of the W4A16 consumer (16 waves of at most 128 VGPRs: one).
 #ifndef CSF_MOE_WG_PER_CU
-#define CSF_MOE_WG_PER_CU 3
+#define CSF_MOE_WG_PER_CU 1
 #endif
 
 csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t *weights,
@@ -272,7 +272,7 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     if (st != CSF_OK) return st;
     if (scales->format != CSF_NVFP4_E4M3) return CSF_E_FORMAT;
     const int64_t C = scales->cols, K = 16 * C;
-    if (C % 2 != 0 || C > 256) return CSF_E_SHAPE;  // K a multiple of 32, at most 4096
+    if (C % 2 != 0 || C > 128) return CSF_E_SHAPE;  // K a multiple of 32, at most 2048
     if (num_tokens < 0) return CSF_E_SIZE;
     if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
     if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;
@@ -296,8 +296,8 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     a.K = uint32_t(K);
     a.C = uint32_t(C);
     a.T = uint32_t(num_tokens);
-    a.ntiles = (a.N + 15u) / 16u;
-    a.bases_stage = bases_stage_bytes(a.C, 16u * a.C);
+    a.ntiles = (a.N + 31u) / 32u;
+    a.bases_stage = bases_stage_bytes(a.C, 32u * a.C);
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const uint64_t units = uint64_t(a.E) * a.ntiles;
     const uint64_t cap = uint64_t(cu_count(stream)) * CSF_MOE_WG_PER_CU;

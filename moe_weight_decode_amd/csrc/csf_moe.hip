@@ -16,230 +16,340 @@
 // x bfloat16 [T][K], W two E2M1 codes per byte [E][N][K/2] (even k in the low
 // nibble), y float32 [T][N].
 //
-// Work unit = (routed expert, 16 consecutive weight rows).  The workgroup
-// first brings the 16 x K/16 scale bytes of its rows into LDS: straight from
-// the CSF streams (the rows are one contiguous span of scale positions,
-// expanded with the decoder's tile code and patched with the span's
-// exception entries found through the tile index), or, for comparison, from a
-// dense scale workspace.  Its 4 waves then split K in 128-wide chunks: per
-// chunk a lane loads 32 E2M1 codes of one row (16 bytes) and the matching 32
-// bfloat16 activations of one token (64 bytes), turns the codes into bfloat16
-// weights (code value x scale is exact in bfloat16) and issues 8 MFMA
-// 16x16x16 bf16 steps per 16-token block.  K is permuted consistently in
-// both operands (lane group q of an MFMA step holds k = chunk + 32q + 4s ..
-// +3), which leaves the sums unchanged and lets every load be 16 contiguous
-// bytes.  The four waves' partial sums meet in LDS and wave 0 writes y.
+// Work unit = (routed expert, 32 consecutive weight rows).  A workgroup of
+// 8 waves issues every load of the unit at once, in a fixed order: the
+// tile-index bounds of the rows' scale span, the expert's alpha, the span's
+// offset runs and row bases (or its dense scale bytes), 32 weight bytes per
+// lane and the activations of up to 64 tokens; once the index bounds are in,
+// it issues the span's exception entries, so their round trip overlaps the
+// bulk loads.  The scale bytes are expanded into LDS with the decoder's tile
+// code and patched with the entries.  Wave w owns K in [256w, 256w + 256), two
+// 128-wide chunks: per 16-row block and chunk a lane turns 32 E2M1 codes of
+// one row into bfloat16 weights (hardware E2M1 -> f32 conversion, one exact
+// multiply by the E4M3 scale, top halves packed) and issues 4 MFMA 16x16x32
+// bf16 steps per 16-token block.  K is permuted consistently in both operands
+// (lane group q of step s holds k = chunk + 32q + 8s .. +7), which leaves the sums
+// unchanged and makes every operand one 16-byte load.  The waves' partial
+// sums meet in LDS and are added in wave order, so the result does not depend
+// on timing.
 #include "csf_device.h"
+
+#include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 namespace csf {
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kMoeRowBlocks = 2;   // 16-row MFMA row blocks per work unit
+constexpr uint32_t kMoeRows = 16 * kMoeRowBlocks;
+constexpr uint32_t kMoeChunk = 128;     // K per chunk (4 lane groups x 32)
+constexpr uint32_t kMoeChunks = 2;      // chunks per wave
+constexpr uint32_t kMoeWaveK = kMoeChunk * kMoeChunks;
+constexpr uint32_t kMoeWaves = 8;       // waves per workgroup
+constexpr uint32_t kMoeThreads = kMoeWaves * kWave;
+constexpr uint32_t kMoeBlocks = 4;      // 16-token MFMA column blocks per pass
+constexpr uint32_t kMoePass = 16 * kMoeBlocks;
+constexpr uint32_t kMoeSteps = 4;       // MFMA 16x16x32 steps per 128-wide chunk
+constexpr uint32_t kMoeMaxCols = kMoeWaves * kMoeWaveK / 16;  // scale columns per row: K <= 2048
+constexpr uint32_t kXcds = 8;           // MI355X: workgroups go round-robin to 8 XCDs
+
+typedef float v2f32 __attribute__((ext_vector_type(2)));
 typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 
-constexpr uint32_t kMoeRows = 16;      // weight rows per work unit (one MFMA row block)
-constexpr uint32_t kMoeTokens = 64;    // tokens per pass (four 16-token MFMA column blocks)
-constexpr uint32_t kMoeChunk = 128;    // K per wave step (4 lane groups x 32)
-constexpr uint32_t kMoeMaxCols = 256;  // scale columns per row (K <= 4096)
-
-// E4M3 ("E4M3FN") byte -> float: sign, 4-bit exponent with bias 7, 3-bit
-// mantissa; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t em = b & 0x7fu;
-    float mag = em >= 0x08u ? __uint_as_float((((em >> 3) + 120u) << 23) | ((em & 7u) << 20))
-                            : (float)em * 0x1p-9f;
-    if (em == 0x7fu) mag = __uint_as_float(0x7fc00000u);
-    return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
+// E4M3 "E4M3FN" scale byte (bit 7 sign, bits 6..3 exponent with bias 7,
+// bits 2..0 mantissa; exponent 0 subnormal; S.1111.111 NaN, no infinities)
+// -> its float value, without branches: bits 6..0 placed at half-precision
+// bits 13..7 give the value times 2^-8 (subnormals included), which the
+// half -> float conversion and a multiply by 2^8 make exact.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+    const float v = __half2float(__ushort_as_half((unsigned short)(((b & 0x7fu) << 7) | ((b & 0x80u) << 8)))) * 256.0f;
+    return (b & 0x7fu) == 0x7fu ? __uint_as_float(0x7fc00000u) : v;
 }
 
-// E2M1 code -> float: sign bit 3, 2-bit exponent with bias 1, 1-bit mantissa;
-// exponent 0 is subnormal (m * 0.5).  Values 0, 0.5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-    const uint32_t mag = c & 7u;
-    const float v = mag < 2u ? 0.5f * (float)mag
-                             : __uint_as_float((((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22));
-    return (c & 8u) ? -v : v;
+// bfloat16 weights of one MFMA step: the 8 E2M1 codes of a 32-bit word (byte
+// j holds codes 2j in the low and 2j + 1 in the high nibble) times the scale.
+// The hardware conversion gives each code's exact value (its scale operand,
+// 1.0 here, acts through its exponent only, so it cannot carry an E4M3
+// scale); code value x scale has at most 6 significant bits and lies in
+// bfloat16's range, so the float product is exact and its top 16 bits are
+// the bfloat16 weight.
+__device__ __forceinline__ uint32_t pack_hi(v2f32 f, float scale) {
+    return __builtin_amdgcn_perm(__float_as_uint(f.y * scale), __float_as_uint(f.x * scale), 0x07060302u);
 }
 
-// bfloat16 pattern of code * scale (the product has at most 6 significant
-// bits and lies in bfloat16's range, so dropping the low 16 bits is exact).
-__device__ __forceinline__ uint32_t dequant_bf16(uint32_t code, float scale) {
-    return __float_as_uint(e2m1_to_f32(code) * scale) >> 16;
+__device__ __forceinline__ v8bf16 dequant8(uint32_t codes, float scale) {
+    const u32x4 w = {pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0), scale),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), scale),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), scale),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), scale)};
+    return __builtin_bit_cast(v8bf16, w);
 }
 
-// The scale bytes of rows n0 .. n0+nrows-1 of expert e (positions q0 .. q1-1
-// of its plane) into LDS, expanded from the CSF streams: one 16-position run
-// per lane, row bases staged in LDS, then the span's exception entries.
-__device__ void span_scales_from_csf(const StackArgs &st, uint32_t e, uint32_t q0, uint32_t q1,
-                                     uint8_t *lds_bases, uint8_t *tile) {
-    const u32x4 *seg = reinterpret_cast<const u32x4 *>(st.offsets + (uint64_t)e * st.stride);
-    const uint32_t pos = q0 + kRunBytes * threadIdx.x;
-    u32x4 v[1];
-    v[0] = pos < q1 ? seg[pos >> 5] : (u32x4){0u, 0u, 0u, 0u};  // NVFP4: 32 positions per group
-    const uint32_t r_lo = div_exact(q0, st.rcp_cols);
-    const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
-    const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
-    for (uint32_t r = threadIdx.x; r < nrows; r += kBlock) lds_bases[r] = brow[r];
-    // entry range of the span from the tile index
-    const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles;
-    const uint32_t i1 = min((q1 + kIndexTile - 1u) / kIndexTile, st.index_tiles);
-    const int32_t l0 = ti[q0 / kIndexTile], h0 = ti[i1];
-    const uint32_t hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
-    const uint32_t lo = l0 < 0 ? 0u : min((uint32_t)l0, hi);
-    __syncthreads();
-    expand_dispatch<true, 1, false>(st, v, q0, q1, q0, lds_bases, r_lo, tile, nullptr);
-    __syncthreads();
-    for (uint32_t k = lo + threadIdx.x; k < hi; k += kBlock) {
-        const uint32_t x = st.exc[k];
-        const uint32_t p = x >> 8;
-        if (p >= q0 && p < q1) tile[p - q0] = (uint8_t)(x & 0xffu);
-    }
+__device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+
+__device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every range used here: reads 0
 
 template <bool DENSE>
-__global__ __launch_bounds__(kBlock) void csf_moe_w4a16_kernel(MoeArgs a) {
+__global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t s_scales[kMoeRows * kMoeMaxCols];
-    __shared__ __align__(16) v4f32 s_red[3][kMoeTokens / 16][kWave];
+    __shared__ __align__(16) v4f32 s_part[kMoeWaves][kMoeRowBlocks][kMoeBlocks][kWave];
     __shared__ uint32_t s_nact;
+    // dynamic LDS: row bases | expert_start copy | active list | flags
     uint8_t *lds_bases = dyn_lds;
-    uint16_t *act = reinterpret_cast<uint16_t *>(dyn_lds + a.bases_stage);
-    uint8_t *flags = dyn_lds + a.bases_stage + ((2u * a.E + 15u) & ~15u);
+    int32_t *s_es = reinterpret_cast<int32_t *>(dyn_lds + a.bases_stage);
+    uint16_t *act = reinterpret_cast<uint16_t *>(s_es + ((a.E + 1u + 3u) & ~3u));
+    uint8_t *flags = reinterpret_cast<uint8_t *>(act) + ((2u * a.E + 15u) & ~15u);
+    const uint32_t tid = threadIdx.x;
 
-    // Routed experts, listed in LDS by wave 0.
-    stage_flags(a.expert_start, a.E, threadIdx.x, kBlock, flags);
+    // Routing: expert_start into LDS (token ranges later cost no round trip),
+    // routed experts listed by wave 0.
+    for (uint32_t i = tid; i <= a.E; i += kMoeThreads) s_es[i] = a.expert_start[i];
     __syncthreads();
-    if (threadIdx.x < kWave) {
+    stage_flags(s_es, a.E, tid, kMoeThreads, flags);
+    __syncthreads();
+    if (tid < kWave) {
         const uint32_t n = build_maps(flags, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
-        if (threadIdx.x == 0) s_nact = n;
+        if (tid == 0) s_nact = n;
     }
     __syncthreads();
-    const uint32_t nact = s_nact;
-    const uint32_t total = nact * a.ntiles;
+    const uint32_t total = s_nact * a.ntiles;
 
-    const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const uint32_t row = lane & 15u;  // weight row within the unit (A) / token within a block (B)
+    const uint32_t wave = tid / kWave, lane = tid % kWave;
+    const uint32_t row = lane & 15u;  // row within a row block (A) / token within a block (B)
     const uint32_t kq = lane >> 4;    // lane group: k = chunk + 32 * kq ..
     const uint32_t C = a.C, K = a.K, half_k = K / 2;
-    const uint32_t nchunks = (K + kMoeChunk - 1) / kMoeChunk;
+    uint32_t k0[kMoeChunks];          // this lane's 32 k of each of the wave's chunks
+    bool lvalid[kMoeChunks];          // K is a multiple of 32: whole lane groups
+#pragma unroll
+    for (uint32_t c = 0; c < kMoeChunks; ++c) {
+        k0[c] = wave * kMoeWaveK + c * kMoeChunk + 32u * kq;
+        lvalid[c] = k0[c] < K;
+    }
+    // lane-constant buffer offsets of the weight and activation loads (past
+    // every range where the lane has no k, so those loads read 0)
+    uint32_t woff[kMoeChunks], xoff[kMoeChunks];
+#pragma unroll
+    for (uint32_t c = 0; c < kMoeChunks; ++c) {
+        woff[c] = lvalid[c] ? row * half_k + k0[c] / 2u : kOutOfRange;
+        xoff[c] = lvalid[c] ? (row * K + k0[c]) * 2u : kOutOfRange;
+    }
+    const uint32_t nwaves = (K + kMoeWaveK - 1u) / kMoeWaveK;  // waves with some K
+    const bool kvalid = wave < nwaves;
     const uint64_t plane = (uint64_t)a.N * C;
 
-    for (uint32_t u = blockIdx.x; u < total; u += gridDim.x) {
+    // Units in XCD order: workgroup b runs on XCD b % 8, so each XCD takes a
+    // contiguous range of units (the rows of few experts), and an expert's
+    // activations are fetched into few L2 caches.  Any grid size stays
+    // correct: without 8 | grid the units go round-robin.
+    uint32_t u = blockIdx.x, ustep = gridDim.x, uend = total;
+    if ((gridDim.x & (kXcds - 1u)) == 0) {
+        const uint32_t per = (total + kXcds - 1u) / kXcds, x = blockIdx.x & (kXcds - 1u);
+        u = x * per + blockIdx.x / kXcds;
+        ustep = gridDim.x / kXcds;
+        uend = min(total, (x + 1u) * per);
+    }
+
+    for (; u < uend; u += ustep) {
         const uint32_t kx = u / a.ntiles;
         const uint32_t e = __builtin_amdgcn_readfirstlane(act[kx]);
         const uint32_t n0 = (u - kx * a.ntiles) * kMoeRows;
         const uint32_t nrows = min(kMoeRows, a.N - n0);
-        const int32_t s0 = a.expert_start[e], s1 = a.expert_start[e + 1];
+        const int32_t s0 = s_es[e], s1 = s_es[e + 1];
         const uint32_t t0 = (uint32_t)min(max(s0, 0), (int32_t)a.T);
         const uint32_t t1 = (uint32_t)min(max(s1, (int32_t)t0), (int32_t)a.T);
         const uint32_t m = t1 - t0;
-
-        // 1. this unit's 16 x C scale bytes into LDS
         const uint32_t q0 = n0 * C, q1 = (n0 + nrows) * C;
-        if constexpr (DENSE) {
-            const uint8_t *src = a.dense + (uint64_t)e * plane + q0;
-            for (uint32_t b = threadIdx.x; b < q1 - q0; b += kBlock) s_scales[b] = src[b];
-        } else {
-            span_scales_from_csf(a.st, e, q0, q1, lds_bases, s_scales);
-        }
-        __syncthreads();
 
-        const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0) * half_k, nrows * half_k);
-        const float alpha = a.alpha[e];
-        for (uint32_t tb0 = 0; tb0 < m; tb0 += kMoeTokens) {
-            const uint32_t mt = min(kMoeTokens, m - tb0);
-            const uint32_t nblk = (mt + 15u) / 16u;
-            const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + tb0) * K, mt * K * 2u);
-            v4f32 acc[kMoeTokens / 16];
-#pragma unroll
-            for (uint32_t b = 0; b < kMoeTokens / 16; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
-
-            for (uint32_t ch = wave; ch < nchunks; ch += kBlock / kWave) {
-                const uint32_t k0 = ch * kMoeChunk + 32u * kq;
-                const bool valid = k0 < K && row < nrows;
-                // 32 codes of weight row `row`, k0 .. k0+31, and their two scales
-                u32x4 wa = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(row * half_k + k0 / 2u), 0, 0));
-                float sc0 = 0.f, sc1 = 0.f;
-                if (valid) {
-                    sc0 = e4m3_to_f32(s_scales[row * C + k0 / 16u]);
-                    sc1 = e4m3_to_f32(s_scales[row * C + k0 / 16u + 1u]);
-                } else {
-                    wa = (u32x4){0u, 0u, 0u, 0u};
-                }
-                // bfloat16 weights: step s takes codes 4s .. 4s+3 (bytes 2s, 2s+1)
-                v4i16 aw[8];
-                const uint32_t wd[4] = {wa.x, wa.y, wa.z, wa.w};
-#pragma unroll
-                for (uint32_t s = 0; s < 8; ++s) {
-                    const uint32_t bits = wd[s >> 1] >> (16u * (s & 1u));  // 4 codes of step s
-                    const float sc = s < 4 ? sc0 : sc1;
-                    aw[s] = (v4i16){(short)dequant_bf16(bits & 15u, sc), (short)dequant_bf16((bits >> 4) & 15u, sc),
-                                    (short)dequant_bf16((bits >> 8) & 15u, sc),
-                                    (short)dequant_bf16((bits >> 12) & 15u, sc)};
-                }
-#pragma unroll
-                for (uint32_t b = 0; b < kMoeTokens / 16; ++b) {
-                    if (b >= nblk) break;
-                    // 32 activations of token b*16 + row, k0 .. k0+31 (64 bytes)
-                    const uint32_t off = ((b * 16u + row) * K + k0) * 2u;
-                    u32x4 xa[4];
-#pragma unroll
-                    for (uint32_t q = 0; q < 4; ++q) {
-                        xa[q] = __builtin_bit_cast(
-                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16u * q), 0, 0));
-                        if (!(k0 < K)) xa[q] = (u32x4){0u, 0u, 0u, 0u};
-                    }
-#pragma unroll
-                    for (uint32_t s = 0; s < 8; ++s) {
-                        const u32x4 q = xa[s >> 1];
-                        const uint32_t lo = (s & 1u) ? q.z : q.x, hi = (s & 1u) ? q.w : q.y;
-                        const v4i16 bx = (v4i16){(short)(lo & 0xffffu), (short)(lo >> 16), (short)(hi & 0xffffu),
-                                                 (short)(hi >> 16)};
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aw[s], bx, acc[b], 0, 0, 0);
-                    }
-                }
+        // One unit with NB 16-token blocks in its first pass (more passes
+        // only when m > 64, with NB = 4).  Straight-line loads per NB keep
+        // every wait exact.
+        auto unit = [&](auto nbc) {
+            constexpr uint32_t NB = decltype(nbc)::value;
+            // ---- loads, in order
+            uint32_t l0 = 0, h0 = 0;
+            if constexpr (!DENSE) {
+                const rsrc_t rt = make_rsrc(a.st.tile_index + (uint64_t)e * a.st.index_tiles,
+                                            (a.st.index_tiles + 1u) * 4u);
+                l0 = load_b32(rt, 4u * (q0 / kIndexTile));
+                h0 = load_b32(rt, 4u * min((q1 + kIndexTile - 1u) / kIndexTile, a.st.index_tiles));
             }
-
-            // 2. sum the four waves' partial sums; wave 0 writes y
-            if (wave > 0) {
+            const float alpha = __uint_as_float(load_b32(make_rsrc(a.alpha + e, 4u), 0u));
+            u32x4 runs = {0u, 0u, 0u, 0u};
+            constexpr uint32_t kDense16 = kMoeRows * kMoeMaxCols / 2u / kMoeThreads;  // 16-bit loads per lane
+            uint32_t base_byte = 0u, dense2[kDense16] = {};
+            if constexpr (DENSE) {
+                const rsrc_t rd = make_rsrc(a.dense + (uint64_t)e * plane + q0, q1 - q0);
 #pragma unroll
-                for (uint32_t b = 0; b < kMoeTokens / 16; ++b) s_red[wave - 1][b][lane] = acc[b];
+                for (uint32_t i = 0; i < kDense16; ++i)
+                    dense2[i] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(2u * (tid + i * kMoeThreads)), 0, 0);
+            } else {
+                // NVFP4: 32 positions per 16-byte offset group
+                const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + 31u) / 32u) * 16u);
+                runs = load_b128(rs, ((q0 + kRunBytes * tid) / 32u) * 16u);
+                base_byte = __builtin_amdgcn_raw_buffer_load_b8(
+                    make_rsrc(a.st.bases + (uint64_t)e * a.st.R + n0, nrows), (int)tid, 0, 0);
+            }
+            // One buffer resource per 16-row block and per 16-token block:
+            // every load is then a lane-constant offset plus an immediate.
+            // 32 codes of row rb*16 + row at k0[c] (rows past the unit's and
+            // k past K read 0)
+            u32x4 wa[kMoeRowBlocks][kMoeChunks];
+#pragma unroll
+            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
+                const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
+#pragma unroll
+                for (uint32_t c = 0; c < kMoeChunks; ++c) wa[rb][c] = load_b128(rw, woff[c]);
+            }
+            // 32 activations of token tb + b*16 + row at k0[c] (tokens past
+            // the expert's read 0)
+            u32x4 xa[NB][kMoeChunks][kMoeSteps];
+            auto load_pass = [&](uint32_t tb) {
+#pragma unroll
+                for (uint32_t b = 0; b < NB; ++b) {
+                    const uint32_t t = tb + b * 16u;
+                    const uint32_t toks = m > t ? min(16u, m - t) : 0u;
+                    const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + t) * K, toks * K * 2u);
+#pragma unroll
+                    for (uint32_t c = 0; c < kMoeChunks; ++c)
+#pragma unroll
+                        for (uint32_t s = 0; s < kMoeSteps; ++s) xa[b][c][s] = load_b128(rx, xoff[c] + 16u * s);
+                }
+            };
+            load_pass(0);
+            // every load above is issued before the first wait below
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- scale bytes of the unit's rows into LDS
+            if constexpr (DENSE) {
+#pragma unroll
+                for (uint32_t i = 0; i < kDense16; ++i)
+                    if (2u * (tid + i * kMoeThreads) < q1 - q0)
+                        *reinterpret_cast<uint16_t *>(s_scales + 2u * (tid + i * kMoeThreads)) = (uint16_t)dense2[i];
+            } else {
+                // the span's exception entries, once the index bounds are in
+                const int32_t l = (int32_t)__builtin_amdgcn_readfirstlane(l0);
+                const int32_t h = (int32_t)__builtin_amdgcn_readfirstlane(h0);
+                const uint32_t hi = h < 0 ? 0u : min((uint32_t)h, a.st.n_exc);
+                const uint32_t lo = l < 0 ? 0u : min((uint32_t)l, hi);
+                const uint32_t cnt = hi - lo;
+                const uint32_t entry = load_b32(make_rsrc(a.st.exc + lo, min(cnt, kMoeThreads) * 4u), 4u * tid);
+                if (tid < nrows) lds_bases[tid] = (uint8_t)base_byte;
+                __syncthreads();
+                switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
+                    case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                    case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                    default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                }
+                __syncthreads();
+                if (tid < cnt) {
+                    const uint32_t p = entry >> 8;
+                    if (p >= q0 && p < q1) s_scales[p - q0] = (uint8_t)(entry & 0xffu);
+                }
+                for (uint32_t k = kMoeThreads + tid; k < cnt; k += kMoeThreads) {  // dense spans only
+                    const uint32_t x = a.st.exc[lo + k];
+                    const uint32_t p = x >> 8;
+                    if (p >= q0 && p < q1) s_scales[p - q0] = (uint8_t)(x & 0xffu);
+                }
             }
             __syncthreads();
-            if (wave == 0) {
-                const uint32_t nq = n0 + 4u * kq;  // output rows nq .. nq+3 of token b*16 + row
+
+            // the scales of the lane's codes: blocks k0[c]/16 and k0[c]/16 + 1
+            // (0 past the rows or past K, where the codes read 0)
+            float sc[kMoeRowBlocks][kMoeChunks][2];
 #pragma unroll
-                for (uint32_t b = 0; b < kMoeTokens / 16; ++b) {
-                    const uint32_t tok = b * 16u + row;
-                    if (tok >= mt) continue;
-                    v4f32 r = acc[b] + s_red[0][b][lane] + s_red[1][b][lane] + s_red[2][b][lane];
-                    r *= alpha;
-                    float *dst = a.y + (uint64_t)(t0 + tb0 + tok) * a.N + nq;
-                    if (nq + 4u <= a.N && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-                        *reinterpret_cast<v4f32 *>(dst) = r;
-                    } else {
+            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
+#pragma unroll
+                for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                    const uint32_t r = rb * 16u + row;
+                    const bool valid = lvalid[c] && r < nrows;
+                    sc[rb][c][0] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u]) : 0.f;
+                    sc[rb][c][1] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u + 1u]) : 0.f;
+                }
+
+            for (uint32_t tb = 0; tb < m; tb += kMoePass) {
+                if (tb > 0) {
+                    __syncthreads();  // the previous pass's partial sums are read
+                    load_pass(tb);
+                }
+                if (kvalid) {
+#pragma unroll
+                    for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                        v4f32 acc[NB];
+#pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                            const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
+#pragma unroll
+                            for (uint32_t s = 0; s < kMoeSteps; ++s) {
+                                // one step at a time: converted ahead, the weights of every
+                                // step would hold their float intermediates at once
+                                const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
+#pragma unroll
+                                for (uint32_t b = 0; b < NB; ++b)
+                                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+#pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
+                    }
+                }
+                __syncthreads();
+                // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
+                // of its 16 x 16 block: one thread per such 4-row vector adds
+                // the waves' vectors in wave order and writes 4 outputs.
+                if (tid < kMoeRowBlocks * NB * kWave) {
+                    const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
+                    v4f32 r = s_part[0][rb][b][l];
+                    for (uint32_t w = 1; w < nwaves; ++w) r += s_part[w][rb][b][l];
+                    const uint32_t t = tb + b * 16u + l % 16u, nn = rb * 16u + 4u * (l / 16u);
+                    if (t < m) {
+                        float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
                         const float rr[4] = {r.x, r.y, r.z, r.w};
-                        for (uint32_t i = 0; i < 4; ++i)
-                            if (nq + i < a.N) dst[i] = rr[i];
+#pragma unroll
+                        for (uint32_t c = 0; c < 4; ++c)
+                            if (nn + c < nrows) dst[c] = rr[c] * alpha;
                     }
                 }
             }
-            __syncthreads();  // s_red and s_scales are reused
+        };
+        // The next unit's first LDS writes (row bases, scale bytes) touch
+        // nothing the reduction reads, and its partial sums are written only
+        // after a barrier every wave passes once its reduction is done.
+        switch ((m + 15u) / 16u) {
+            case 0: break;
+            case 1: unit(std::integral_constant<uint32_t, 1>{}); break;
+            case 2: unit(std::integral_constant<uint32_t, 2>{}); break;
+            case 3: unit(std::integral_constant<uint32_t, 3>{}); break;
+            default: unit(std::integral_constant<uint32_t, 4>{}); break;
         }
     }
 }
 
 }  // namespace
 
-size_t moe_lds_bytes(const MoeArgs &a) { return a.bases_stage + ((2u * a.E + 15u) & ~15u) + a.E; }
+size_t moe_lds_bytes(const MoeArgs &a) {
+    return a.bases_stage + 4u * ((a.E + 1u + 3u) & ~3u) + ((2u * a.E + 15u) & ~15u) + a.E;
+}
 
 hipError_t launch_moe_w4a16(const MoeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = moe_lds_bytes(a);
     if (a.dense != nullptr)
-        hipLaunchKernelGGL(csf_moe_w4a16_kernel<true>, dim3(grid), dim3(kBlock), lds, stream, a);
+        hipLaunchKernelGGL(csf_moe_w4a16_kernel<true>, dim3(grid), dim3(kMoeThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL(csf_moe_w4a16_kernel<false>, dim3(grid), dim3(kBlock), lds, stream, a);
+        hipLaunchKernelGGL(csf_moe_w4a16_kernel<false>, dim3(grid), dim3(kMoeThreads), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -63,9 +63,10 @@ def check(inp, got, what):
 @pytest.mark.parametrize("E,N,K,counts", [
     (4, 48, 256, [0, 1, 17, 70]),
     (3, 40, 96, [5, 0, 64]),
-    (2, 16, 4096, [3, 33]),
+    (2, 16, 2048, [3, 33]),
     (5, 7, 32, [1, 2, 0, 16, 15]),
-], ids=["mixed_counts", "ragged_rows", "k4096", "tiny"])
+    (3, 70, 160, [40, 1, 7]),
+], ids=["mixed_counts", "ragged_rows", "k2048", "tiny", "k160_rows70"])
 def test_small_shapes(orc, dev, E, N, K, counts):
     es = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     inp = workloads.w4a16_inputs(E, N, K, es, seed=E * 100 + N, exc_rate=0.08)
