@@ -260,7 +260,7 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, con
     return CSF_OK;
 }
 
-// Workgroups per CU of the W4A16 consumer (16 waves of at most 128 VGPRs: one).
+// Workgroups per CU of the W4A16 consumer (8 waves of up to 256 VGPRs: one).
 #ifndef CSF_MOE_WG_PER_CU
 #define CSF_MOE_WG_PER_CU 1
 #endif
