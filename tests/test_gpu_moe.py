@@ -96,3 +96,81 @@ def test_unit_weights_give_activation_sums(orc, dev):
     inp.scales[:] = 0x38
     got = run(orc, dev, inp, dense=False)
     check(inp, got, "unit weights")
+
+
+def _routing(counts, T):
+    es = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    assert es[-1] <= T
+    return es
+
+
+def test_graph_replay_follows_routing_and_activations(orc, dev):
+    """One captured call replayed with three routings and fresh activations:
+    the library allocates nothing during capture, every replay equals an
+    eager call bit for bit and the oracle within the bound, and the outputs
+    of tokens a routing leaves out stay untouched."""
+    E, N, K, T = 24, 80, 512, 160
+    routings = [_routing([0, 9, 0, 33, 1, 0, 64, 5] + [0] * 16, T),      # 112 of 160 tokens routed
+                _routing([0] * 10 + [150] + [0] * 13, T),                 # one expert, several passes
+                _routing([T // E + (i < T % E) for i in range(E)], T)]    # every expert, every token
+    inp = workloads.w4a16_inputs(E, N, K, routings[0], seed=91, exc_rate=0.08)
+    stack = mwd.from_numpy(orc.encode(workloads.NVFP4, inp.scales), dev)
+    w = torch.from_numpy(inp.w_packed).to(dev)
+    alpha = torch.from_numpy(inp.alpha).to(dev)
+    x = torch.zeros((T, K), dtype=torch.int16, device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    es_t = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):  # warm the launch path outside capture
+        mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        allocated, reserved = torch.cuda.memory_allocated(dev), torch.cuda.memory_reserved(dev)
+        mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)
+        assert torch.cuda.memory_allocated(dev) == allocated
+        assert torch.cuda.memory_reserved(dev) == reserved
+    rng = np.random.default_rng(92)
+    for rnd in range(2):
+        for i, es in enumerate(routings):
+            xb = workloads.bf16_bits(T, K, rng)
+            x.copy_(torch.from_numpy(xb.view(np.int16)))
+            es_t.copy_(torch.from_numpy(es))
+            y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            eager = mwd.moe_w4a16(stack, w, x, alpha, es_t).cpu().numpy()
+            routed = int(es[-1])
+            assert np.array_equal(got[:routed], eager[:routed]), f"replay {rnd}/{i} differs from an eager call"
+            assert np.isnan(got[routed:]).all(), f"replay {rnd}/{i} wrote outputs of unrouted tokens"
+            if rnd == 0:
+                ref, mag = ref_moe(xb, inp, es)
+                err = np.abs(got[:routed].astype(np.float64) - ref[:routed])
+                assert np.all(err <= (K + 8) * 2.0 ** -24 * mag[:routed]), f"replay {i} outside the bound"
+
+
+def ref_moe(x_bits, inp, es):
+    return ref.moe_w4a16(x_bits, inp.w_packed, inp.scales, inp.alpha, es)
+
+
+def test_side_stream_ordering(orc, dev):
+    es = _routing([3, 0, 40, 17], 60)
+    inp = workloads.w4a16_inputs(4, 48, 256, es, seed=93)
+    stack = mwd.from_numpy(orc.encode(workloads.NVFP4, inp.scales), dev)
+    w = torch.from_numpy(inp.w_packed).to(dev)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev)
+    alpha = torch.from_numpy(inp.alpha).to(dev)
+    es_t = torch.from_numpy(inp.expert_start).to(dev)
+    y = torch.full((60, 48), float("nan"), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)  # the current stream is the side stream
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.current_stream(dev).wait_event(done)
+    check(inp, y.cpu().numpy(), "side stream")
