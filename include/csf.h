@@ -160,11 +160,13 @@ csf_status csf_encode_device(int32_t format, int32_t num_experts, int32_t rows, 
 csf_status csf_build_index(const csf_stack *compressed, int32_t *tile_index, void *hip_stream);
 
 /*
- * Expand a compressed stack into the dense workspace (PR 1236, API paragraph:
- * decoding on the GPU into reusable, caller-owned workspace; fixed stream then
- * exception pass; with the grouped-routing expert_start tensor only experts
- * with routed tokens are expanded and every other plane is left untouched; no
- * selection buffer and no CPU synchronisation; without it the whole stack).
+ * Expand a compressed stack into the dense workspace (PR 1236, API paragraph).
+ * The decode runs on the GPU, into a workspace the caller owns and may reuse:
+ * a fixed-stream pass, then an exception pass.  When the device-side token
+ * offsets per expert (expert_start) are given, an expert without tokens is
+ * skipped by both passes and its plane keeps its previous bytes; the call
+ * needs no host read-back and no list of selected experts.  With expert_start
+ * NULL every plane is expanded.
  *
  * workspace: device u8[E*R*C], any byte alignment (PR 1236, validation
  *   paragraph: odd-offset workspace).
@@ -184,8 +186,9 @@ csf_status csf_decode(const csf_stack *compressed, uint8_t *workspace,
 
 /*
  * Gate/up and down stacks of the same experts in one call: each pass is a
- * single launch covering both stacks (PR 478, commit messages: decode only
- * routed experts and pair gate/up and down scales without adding streams).
+ * single launch covering both stacks (PR 478, commit messages: the gate/up
+ * and the down scales of the routed experts are expanded together, with no
+ * extra streams, and unrouted experts are skipped).
  * Formats and shapes may differ between the stacks; expert counts must match
  * (CSF_E_MISMATCH).  expert_start is shared and may be NULL.  The single-pass
  * kernel is used when both stacks carry a tile index.  Otherwise as
@@ -250,9 +253,10 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
 /*
  * W4A16 MoE projection whose NVFP4 block scales stay compressed: the consumer
  * the pages pair with the compressed scales ("NVFP4-CSF: expand_scales() ...",
- * b12x PR 478, last commit message: each W4A16 pipeline stage rebuilds its
- * E4M3 K16 scales in shared memory from the compressed storage, so small calls
- * need no dense scale scratch).  For every expert e with tokens t in
+ * b12x PR 478, last commit message: the MoE kernel keeps the E4M3 block
+ * scales, one per 16 weights, compressed and expands only those a pipeline
+ * step is about to use, in on-chip shared memory, so a small call needs no
+ * separate dense expansion).  For every expert e with tokens t in
  * [expert_start[e], expert_start[e+1]):
  *     y[t][n] = alpha[e] * sum_k x[t][k] * e2m1(W[e][n][k]) * e4m3(S[e][n][k/16])
  *

@@ -2,11 +2,12 @@
 // CSF-compressed block scales.
 //
 // "NVFP4-CSF: expand_scales() for ahead-of-call scale expansion (canonical
-// twin of #477)" (b12x PR 478), last commit message: packed W4A16 experts keep
-// their E4M3 scales (one per 16 weights) as compressed storage and each
-// pipeline stage of the MoE GEMM rebuilds the scales it needs in shared memory
-// from that storage, so small calls no longer expand every routed expert's
-// scales into a dense scratch before the MoE.  "finegrained-kernels: decode
+// twin of #477)" (b12x PR 478), last commit message: the W4A16 MoE kernel
+// reads its experts' E4M3 block scales (one per 16 weights) in compressed
+// form; the scales a step of its software pipeline consumes are turned back
+// into plain bytes in on-chip shared memory right before use, which spares
+// small calls the separate expansion of all routed experts' scales into a
+// dense buffer.  "finegrained-kernels: decode
 // losslessly compressed NVFP4 scales (CSF)" (kernels-community PR 1236),
 // format paragraph: NVFP4 = 4-bit (E2M1) weights and one E4M3 scale per 16
 // weights.

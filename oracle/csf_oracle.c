@@ -9,10 +9,11 @@
  * What the method computes (all integer, byte exact):
  *
  *   "finegrained-kernels: decode losslessly compressed NVFP4 scales (CSF)"
- *   (kernels-community PR 1236), paragraph on the format: NVFP4 keeps one 8-bit
- *   scale per 16 weights; CSF stores one base byte per row, most scales as 4-bit
- *   offsets from that base, and the values outside that range in an exception
- *   stream; decoding gives back the original scale bytes exactly.
+ *   (kernels-community PR 1236), paragraph on the format: an NVFP4 tensor has
+ *   one 8-bit scale for each group of 16 weights.  The lossless CSF form keeps,
+ *   per row, a single base byte; a scale within the 4-bit reach above the base
+ *   is kept as its offset, any other scale goes to a separate list of
+ *   (position, byte) exceptions; the decoder restores every byte unchanged.
  *
  *   "NVFP4-CSF: expand_scales() for ahead-of-call scale expansion (canonical
  *   twin of #477)" (b12x PR 478), commit messages: offsets are one bit wide for

@@ -12,10 +12,10 @@ What is computed (float64 throughout):
   weights and one 8-bit (E4M3) scale for every 16 weights.
 
   "NVFP4-CSF: expand_scales() for ahead-of-call scale expansion (canonical
-  twin of #477)" (b12x PR 478), last commit message: packed W4A16 experts
-  (4-bit weights, 16-bit activations) whose E4M3 scales per 16 weights stay
-  compressed; each pipeline stage of the MoE GEMM rebuilds the scales it
-  needs in shared memory from the compressed storage.
+  twin of #477)" (b12x PR 478), last commit message: a W4A16 MoE kernel
+  (4-bit weights, 16-bit activations) that keeps the E4M3 block scales (one
+  per 16 weights) compressed and turns the ones it is about to use back into
+  plain bytes in on-chip shared memory.
 
   For every expert e with routed tokens t in [expert_start[e], expert_start[e+1])
   (the grouped routing: tokens sorted by expert):
