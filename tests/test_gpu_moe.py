@@ -174,3 +174,38 @@ def test_side_stream_ordering(orc, dev):
         done.record(side)
     torch.cuda.current_stream(dev).wait_event(done)
     check(inp, y.cpu().numpy(), "side stream")
+
+
+def check_non_finite(inp, got, what):
+    """Like check(), where the oracle's output is NaN or infinite: the GPU
+    output must be NaN at exactly the same places and the same infinity
+    elsewhere; finite outputs keep the float32 bound."""
+    K = inp.x_bits.shape[1]
+    with np.errstate(invalid="ignore"):  # inf * 0 in the oracle is meant to give NaN
+        y, mag = ref.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start)
+    got = got.astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(y)), f"{what}: NaN pattern differs"
+    inf = np.isinf(y)
+    assert np.array_equal(got[inf], y[inf]), f"{what}: infinities differ"
+    fin = np.isfinite(y)
+    assert np.isfinite(got[fin]).all(), f"{what}: non-finite output where the oracle's is finite"
+    assert np.all(np.abs(got[fin] - y[fin]) <= (K + 8) * 2.0 ** -24 * mag[fin]), f"{what}: outside the bound"
+    return y
+
+
+@pytest.mark.parametrize("K", [160, 2048])
+def test_non_finite_values_stay_in_their_outputs(orc, dev, K):
+    """A NaN scale byte (E4M3 S.1111.111) makes exactly its row's outputs NaN
+    for the expert's tokens; an infinite or NaN activation reaches only its own
+    token's outputs (K = 160 leaves part of a chunk past K: no lane may read
+    the next token's row there)."""
+    es = _routing([5, 6], 11)
+    inp = workloads.w4a16_inputs(2, 40, K, es, seed=94 + K, exc_rate=0.05)
+    inp.scales[1, 33, 3] = 0x7F                          # expert 1 (tokens 5..10), row 33
+    inp.x_bits[2, K - 1] = 0x7F80                        # +inf, last k of token 2
+    inp.x_bits[3, 0] = 0x7FC0                            # NaN, first k of token 3
+    inp.x_bits[8, K // 2] = 0xFF80                       # -inf, token 8 (expert 1)
+    for dense in (False, True):
+        got = run(orc, dev, inp, dense=dense)
+        y = check_non_finite(inp, got, f"non-finite inputs, {'dense' if dense else 'CSF'} scales")
+    assert np.isnan(y[5:11, 33]).all() and np.isfinite(y[[0, 1, 4]]).all()
