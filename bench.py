@@ -501,6 +501,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--sets", type=int, default=8, help="rotating device copies (HBM, not cache)")
     ap.add_argument("--all", action="store_true", help="also time the other workloads on stderr")
+    ap.add_argument("--all-json", default=None, metavar="PATH", help="with --all: also write those timings as JSON")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="N",
@@ -652,8 +653,9 @@ def main():
         cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
         extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
         log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
-        os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-        json.dump(extra, open(os.path.join(ROOT, "gpurun_out", "bench_all.json"), "w"), indent=1)
+        if args.all_json:
+            os.makedirs(os.path.dirname(os.path.abspath(args.all_json)), exist_ok=True)
+            json.dump(extra, open(args.all_json, "w"), indent=1)
     if args.calibrate_copy:
         # an elementwise kernel (a large device-to-device copy_ may go to a DMA
         # engine, which the counters do not see): 256 MiB read, 256 MiB written
