@@ -261,7 +261,7 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
  *     y[t][n] = alpha[e] * sum_k x[t][k] * e2m1(W[e][n][k]) * e4m3(S[e][n][k/16])
  *
  * scales: the NVFP4 stack of the projection's scales (E experts, rows = N output
- *   features, cols = K/16; K a multiple of 32, at most 2048), device buffers.
+ *   features, cols = K/16; K a multiple of 32, at most 8192), device buffers.
  *   With dense_scales NULL each workgroup expands the scales of its 32 rows
  *   straight into LDS from the CSF streams (needs the tile index); otherwise
  *   the scales are read from dense_scales, u8[E][N][K/16] (for example a
@@ -275,7 +275,7 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
  * Enqueued on hip_stream; allocates nothing; no host synchronisation.
  * Errors: CSF_E_NULL (a required pointer, or the tile index when dense_scales is
  *   NULL), CSF_E_FORMAT (not NVFP4), CSF_E_SHAPE (K not a multiple of 32 or
- *   above 2048, or the stack's own shape checks), CSF_E_SIZE (num_tokens < 0),
+ *   above 8192, or the stack's own shape checks), CSF_E_SIZE (num_tokens < 0),
  *   CSF_E_ALIGN, CSF_E_HIP.
  */
 csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, const uint8_t *weights,

@@ -272,7 +272,7 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     if (st != CSF_OK) return st;
     if (scales->format != CSF_NVFP4_E4M3) return CSF_E_FORMAT;
     const int64_t C = scales->cols, K = 16 * C;
-    if (C % 2 != 0 || C > 128) return CSF_E_SHAPE;  // K a multiple of 32, at most 2048
+    if (C % 2 != 0 || C > 512) return CSF_E_SHAPE;  // K a multiple of 32, at most 8192
     if (num_tokens < 0) return CSF_E_SIZE;
     if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
     if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;

@@ -32,7 +32,10 @@
 // (lane group q of step s holds k = chunk + 32q + 8s .. +7), which leaves the sums
 // unchanged and makes every operand one 16-byte load.  The waves' partial
 // sums meet in LDS and are added in wave order, so the result does not depend
-// on timing.
+// on timing.  K above 2048 runs in K-tiles of 2048 (every wave one 256-wide
+// slice of each): the unit's whole scale span is expanded into LDS once, each
+// K-tile loads its codes and activations, and the reduction threads add the
+// K-tiles' wave sums in K order into running sums before the one store.
 #include "csf_device.h"
 
 #include <hip/hip_fp16.h>
@@ -52,7 +55,9 @@ constexpr uint32_t kMoeThreads = kMoeWaves * kWave;
 constexpr uint32_t kMoeBlocks = 4;      // 16-token MFMA column blocks per pass
 constexpr uint32_t kMoePass = 16 * kMoeBlocks;
 constexpr uint32_t kMoeSteps = 4;       // MFMA 16x16x32 steps per 128-wide chunk
-constexpr uint32_t kMoeMaxCols = kMoeWaves * kMoeWaveK / 16;  // scale columns per row: K <= 2048
+constexpr uint32_t kMoeKTile = kMoeWaves * kMoeWaveK;  // K per K-tile: one 256-wide slice per wave
+constexpr uint32_t kMoeMaxCols = 512;   // scale columns per row: K <= 8192
+constexpr uint32_t kMoeStage = 4096;    // scale bytes read with the unit's first loads (K <= 2048)
 constexpr uint32_t kXcds = 8;           // MI355X: workgroups go round-robin to 8 XCDs
 
 typedef float v2f32 __attribute__((ext_vector_type(2)));
@@ -98,7 +103,9 @@ __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every range used here: reads 0
 
-template <bool DENSE>
+// MULTI: K > 2048, several K-tiles per unit (a separate instantiation, so the
+// single K-tile code keeps its own register allocation).
+template <bool DENSE, bool MULTI>
 __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t s_scales[kMoeRows * kMoeMaxCols];
@@ -128,8 +135,8 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
     const uint32_t row = lane & 15u;  // row within a row block (A) / token within a block (B)
     const uint32_t kq = lane >> 4;    // lane group: k = chunk + 32 * kq ..
     const uint32_t C = a.C, K = a.K, half_k = K / 2;
-    uint32_t k0[kMoeChunks];          // this lane's 32 k of each of the wave's chunks
-    bool lvalid[kMoeChunks];          // K is a multiple of 32: whole lane groups
+    uint32_t k0[kMoeChunks];          // this lane's 32 k of each of the wave's chunks, in a K-tile
+    bool lvalid[kMoeChunks];          // (first K-tile) K is a multiple of 32: whole lane groups
 #pragma unroll
     for (uint32_t c = 0; c < kMoeChunks; ++c) {
         k0[c] = wave * kMoeWaveK + c * kMoeChunk + 32u * kq;
@@ -143,8 +150,8 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
         woff[c] = lvalid[c] ? row * half_k + k0[c] / 2u : kOutOfRange;
         xoff[c] = lvalid[c] ? (row * K + k0[c]) * 2u : kOutOfRange;
     }
-    const uint32_t nwaves = (K + kMoeWaveK - 1u) / kMoeWaveK;  // waves with some K
-    const bool kvalid = wave < nwaves;
+    const uint32_t nkt = (K + kMoeKTile - 1u) / kMoeKTile;  // K-tiles
+    const uint32_t nwaves1 = min(kMoeWaves, (K + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K (one K-tile)
     const uint64_t plane = (uint64_t)a.N * C;
 
     // Units in XCD order: workgroup b runs on XCD b % 8, so each XCD takes a
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
             }
             const float alpha = __uint_as_float(load_b32(make_rsrc(a.alpha + e, 4u), 0u));
             u32x4 runs = {0u, 0u, 0u, 0u};
-            constexpr uint32_t kDense16 = kMoeRows * kMoeMaxCols / 2u / kMoeThreads;  // 16-bit loads per lane
+            constexpr uint32_t kDense16 = kMoeStage / 2u / kMoeThreads;  // 16-bit loads per lane
             uint32_t base_byte = 0u, dense2[kDense16] = {};
             if constexpr (DENSE) {
                 const rsrc_t rd = make_rsrc(a.dense + (uint64_t)e * plane + q0, q1 - q0);
@@ -236,6 +243,11 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                 for (uint32_t i = 0; i < kDense16; ++i)
                     if (2u * (tid + i * kMoeThreads) < q1 - q0)
                         *reinterpret_cast<uint16_t *>(s_scales + 2u * (tid + i * kMoeThreads)) = (uint16_t)dense2[i];
+                if constexpr (MULTI) {  // K > 2048: the rest of the span
+                    const uint16_t *src = reinterpret_cast<const uint16_t *>(a.dense + (uint64_t)e * plane + q0);
+                    for (uint32_t b = kMoeStage / 2u + tid; 2u * b < q1 - q0; b += kMoeThreads)
+                        *reinterpret_cast<uint16_t *>(s_scales + 2u * b) = src[b];
+                }
             } else {
                 // the span's exception entries, once the index bounds are in
                 const int32_t l = (int32_t)__builtin_amdgcn_readfirstlane(l0);
@@ -246,10 +258,28 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                 const uint32_t entry = load_b32(make_rsrc(a.st.exc + lo, min(cnt, kMoeThreads) * 4u), 4u * tid);
                 if (tid < nrows) lds_bases[tid] = (uint8_t)base_byte;
                 __syncthreads();
-                switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
-                    case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
-                    case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
-                    default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                if constexpr (!MULTI) {
+                    switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
+                        case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                        case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                        default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                    }
+                } else {
+                    // one 16-position run per thread: 8192 positions per round, the
+                    // first round's offsets read with the unit's first loads
+                    for (uint32_t g = 0; g * kRunBytes * kMoeThreads < q1 - q0; ++g) {
+                        const uint32_t qg = q0 + g * kRunBytes * kMoeThreads;
+                        if (g > 0) {  // K > 4096
+                            const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + 31u) / 32u) * 16u);
+                            runs = load_b128(rs, ((qg + kRunBytes * tid) / 32u) * 16u);
+                        }
+                        uint8_t *dst = s_scales + (qg - q0);
+                        switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
+                            case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                            case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                            default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                        }
+                    }
                 }
                 __syncthreads();
                 if (tid < cnt) {
@@ -264,64 +294,162 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
             }
             __syncthreads();
 
-            // the scales of the lane's codes: blocks k0[c]/16 and k0[c]/16 + 1
-            // (0 past the rows or past K, where the codes read 0)
-            float sc[kMoeRowBlocks][kMoeChunks][2];
-#pragma unroll
-            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
-#pragma unroll
-                for (uint32_t c = 0; c < kMoeChunks; ++c) {
-                    const uint32_t r = rb * 16u + row;
-                    const bool valid = lvalid[c] && r < nrows;
-                    sc[rb][c][0] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u]) : 0.f;
-                    sc[rb][c][1] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u + 1u]) : 0.f;
-                }
+            if constexpr (!MULTI) {
+                // the scales of the lane's codes: blocks k0[c]/16 and k0[c]/16 + 1
+                // (0 past the rows or past K, where the codes read 0)
+                float sc[kMoeRowBlocks][kMoeChunks][2];
+    #pragma unroll
+                for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
+    #pragma unroll
+                    for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                        const uint32_t r = rb * 16u + row;
+                        const bool valid = lvalid[c] && r < nrows;
+                        sc[rb][c][0] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u]) : 0.f;
+                        sc[rb][c][1] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u + 1u]) : 0.f;
+                    }
 
-            for (uint32_t tb = 0; tb < m; tb += kMoePass) {
-                if (tb > 0) {
-                    __syncthreads();  // the previous pass's partial sums are read
-                    load_pass(tb);
-                }
-                if (kvalid) {
-#pragma unroll
-                    for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
-                        v4f32 acc[NB];
-#pragma unroll
-                        for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (uint32_t c = 0; c < kMoeChunks; ++c) {
-                            const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
-#pragma unroll
-                            for (uint32_t s = 0; s < kMoeSteps; ++s) {
-                                // one step at a time: converted ahead, the weights of every
-                                // step would hold their float intermediates at once
-                                const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
-#pragma unroll
-                                for (uint32_t b = 0; b < NB; ++b)
-                                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
-                                __builtin_amdgcn_sched_barrier(0);
+                for (uint32_t tb = 0; tb < m; tb += kMoePass) {
+                    if (tb > 0) {
+                        __syncthreads();  // the previous pass's partial sums are read
+                        load_pass(tb);
+                    }
+                    if (wave < nwaves1) {
+    #pragma unroll
+                        for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                            v4f32 acc[NB];
+    #pragma unroll
+                            for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                            for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                                const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
+    #pragma unroll
+                                for (uint32_t s = 0; s < kMoeSteps; ++s) {
+                                    // one step at a time: converted ahead, the weights of every
+                                    // step would hold their float intermediates at once
+                                    const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
+    #pragma unroll
+                                    for (uint32_t b = 0; b < NB; ++b)
+                                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                            aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
                             }
+    #pragma unroll
+                            for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
                         }
-#pragma unroll
-                        for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
+                    }
+                    __syncthreads();
+                    // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
+                    // of its 16 x 16 block: one thread per such 4-row vector adds
+                    // the waves' vectors in wave order and writes 4 outputs.
+                    if (tid < kMoeRowBlocks * NB * kWave) {
+                        const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
+                        v4f32 r = s_part[0][rb][b][l];
+                        for (uint32_t w = 1; w < nwaves1; ++w) r += s_part[w][rb][b][l];
+                        const uint32_t t = tb + b * 16u + l % 16u, nn = rb * 16u + 4u * (l / 16u);
+                        if (t < m) {
+                            float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
+                            const float rr[4] = {r.x, r.y, r.z, r.w};
+    #pragma unroll
+                            for (uint32_t c = 0; c < 4; ++c)
+                                if (nn + c < nrows) dst[c] = rr[c] * alpha;
+                        }
                     }
                 }
-                __syncthreads();
-                // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
-                // of its 16 x 16 block: one thread per such 4-row vector adds
-                // the waves' vectors in wave order and writes 4 outputs.
-                if (tid < kMoeRowBlocks * NB * kWave) {
-                    const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
-                    v4f32 r = s_part[0][rb][b][l];
-                    for (uint32_t w = 1; w < nwaves; ++w) r += s_part[w][rb][b][l];
-                    const uint32_t t = tb + b * 16u + l % 16u, nn = rb * 16u + 4u * (l / 16u);
-                    if (t < m) {
-                        float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
-                        const float rr[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-                        for (uint32_t c = 0; c < 4; ++c)
-                            if (nn + c < nrows) dst[c] = rr[c] * alpha;
+            } else {
+                for (uint32_t tb = 0; tb < m; tb += kMoePass) {
+                    // Running sums of the outputs a reduction thread owns (one
+                    // 4-row vector of one 16 x 16 block), over the K-tiles in order.
+                    v4f32 total = {0.f, 0.f, 0.f, 0.f};
+                    for (uint32_t kt = 0; kt < nkt; ++kt) {
+                        const uint32_t kb = kt * kMoeKTile;
+                        bool lv[kMoeChunks];
+    #pragma unroll
+                        for (uint32_t c = 0; c < kMoeChunks; ++c) lv[c] = kb + k0[c] < K;
+                        if (tb > 0 || kt > 0) {
+                            __syncthreads();  // the previous partial sums are read
+                            // this K-tile's codes and activations (the first K-tile's
+                            // first pass came with the unit's first loads)
+    #pragma unroll
+                            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                                const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
+                                const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
+    #pragma unroll
+                                for (uint32_t c = 0; c < kMoeChunks; ++c)
+                                    wa[rb][c] = load_b128(rw, lv[c] ? row * half_k + (kb + k0[c]) / 2u : kOutOfRange);
+                            }
+    #pragma unroll
+                            for (uint32_t b = 0; b < NB; ++b) {
+                                const uint32_t t = tb + b * 16u;
+                                const uint32_t toks = m > t ? min(16u, m - t) : 0u;
+                                const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + t) * K, toks * K * 2u);
+    #pragma unroll
+                                for (uint32_t c = 0; c < kMoeChunks; ++c)
+    #pragma unroll
+                                    for (uint32_t s = 0; s < kMoeSteps; ++s)
+                                        xa[b][c][s] = load_b128(rx, lv[c] ? (row * K + kb + k0[c]) * 2u + 16u * s : kOutOfRange);
+                            }
+                        }
+                        const uint32_t nwaves = min(kMoeWaves, (K - kb + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K
+                        // the scales of the lane's codes: blocks (kb + k0[c])/16 and
+                        // the next (0 past the rows or past K, where the codes read 0)
+                        float sc[kMoeRowBlocks][kMoeChunks][2];
+    #pragma unroll
+                        for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
+    #pragma unroll
+                            for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                                const uint32_t r = rb * 16u + row;
+                                const bool valid = lv[c] && r < nrows;
+                                const uint32_t i = valid ? r * C + (kb + k0[c]) / 16u : 0u;
+                                sc[rb][c][0] = valid ? e4m3_value(s_scales[i]) : 0.f;
+                                sc[rb][c][1] = valid ? e4m3_value(s_scales[i + 1u]) : 0.f;
+                            }
+                        if (wave < nwaves) {
+    #pragma unroll
+                            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                                v4f32 acc[NB];
+    #pragma unroll
+                                for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                                for (uint32_t c = 0; c < kMoeChunks; ++c) {
+                                    const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
+    #pragma unroll
+                                    for (uint32_t s = 0; s < kMoeSteps; ++s) {
+                                        // one step at a time: converted ahead, the weights of every
+                                        // step would hold their float intermediates at once
+                                        const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
+    #pragma unroll
+                                        for (uint32_t b = 0; b < NB; ++b)
+                                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                                aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
+                                        __builtin_amdgcn_sched_barrier(0);
+                                    }
+                                }
+    #pragma unroll
+                                for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
+                            }
+                        }
+                        __syncthreads();
+                        // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
+                        // of its 16 x 16 block: one thread per such 4-row vector adds
+                        // the waves' vectors in wave order to its running sums.
+                        if (tid < kMoeRowBlocks * NB * kWave) {
+                            const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
+                            v4f32 r = s_part[0][rb][b][l];
+                            for (uint32_t w = 1; w < nwaves; ++w) r += s_part[w][rb][b][l];
+                            total += r;
+                        }
+                    }
+                    if (tid < kMoeRowBlocks * NB * kWave) {
+                        const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
+                        const uint32_t t = tb + b * 16u + l % 16u, nn = rb * 16u + 4u * (l / 16u);
+                        if (t < m) {
+                            float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
+                            const float rr[4] = {total.x, total.y, total.z, total.w};
+    #pragma unroll
+                            for (uint32_t c = 0; c < 4; ++c)
+                                if (nn + c < nrows) dst[c] = rr[c] * alpha;
+                        }
                     }
                 }
             }
@@ -347,10 +475,18 @@ size_t moe_lds_bytes(const MoeArgs &a) {
 
 hipError_t launch_moe_w4a16(const MoeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = moe_lds_bytes(a);
-    if (a.dense != nullptr)
-        hipLaunchKernelGGL(csf_moe_w4a16_kernel<true>, dim3(grid), dim3(kMoeThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL(csf_moe_w4a16_kernel<false>, dim3(grid), dim3(kMoeThreads), lds, stream, a);
+    const bool multi = a.K > kMoeKTile;
+    if (a.dense != nullptr) {
+        if (multi)
+            hipLaunchKernelGGL((csf_moe_w4a16_kernel<true, true>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+        else
+            hipLaunchKernelGGL((csf_moe_w4a16_kernel<true, false>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+    } else {
+        if (multi)
+            hipLaunchKernelGGL((csf_moe_w4a16_kernel<false, true>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+        else
+            hipLaunchKernelGGL((csf_moe_w4a16_kernel<false, false>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ def test_moe_w4a16_errors(lib):
     ok = _fake(R=32, C=16, stride=16 * 16, tile_index=0x8000)
     assert call(_fake(fmt=1, R=32, C=16, stride=16 * 64, tile_index=0x8000)) == "CSF_E_FORMAT"
     assert call(_fake(R=32, C=15, stride=16 * 15, tile_index=0x8000)) == "CSF_E_SHAPE"   # K = 240
-    assert call(_fake(R=32, C=130, stride=16 * 130, tile_index=0x8000)) == "CSF_E_SHAPE"  # K > 2048
+    assert call(_fake(R=32, C=514, stride=16 * 514, tile_index=0x8000)) == "CSF_E_SHAPE"  # K > 8192
     assert call(_fake(R=32, C=16, stride=16 * 16)) == "CSF_E_NULL"        # no tile index, no dense scales
     assert call(ok, w=None) == "CSF_E_NULL"
     assert call(ok, alpha=None) == "CSF_E_NULL"
