@@ -251,32 +251,42 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
                            const int32_t *expert_start, uint32_t passes, void *hip_stream);
 
 /*
- * W4A16 MoE projection whose NVFP4 block scales stay compressed: the consumer
- * the pages pair with the compressed scales ("NVFP4-CSF: expand_scales() ...",
+ * W4A16 MoE projection whose block scales stay compressed: the consumer the
+ * pages pair with the compressed scales ("NVFP4-CSF: expand_scales() ...",
  * b12x PR 478, last commit message: the MoE kernel keeps the E4M3 block
  * scales, one per 16 weights, compressed and expands only those a pipeline
  * step is about to use, in on-chip shared memory, so a small call needs no
- * separate dense expansion).  For every expert e with tokens t in
- * [expert_start[e], expert_start[e+1]):
- *     y[t][n] = alpha[e] * sum_k x[t][k] * e2m1(W[e][n][k]) * e4m3(S[e][n][k/16])
+ * separate dense expansion).  The same holds for the MXFP4 stack (the pages'
+ * 1-bit layout: one UE8M0 scale per 32 weights).  For every expert e with
+ * tokens t in [expert_start[e], expert_start[e+1]):
+ *     y[t][n] = alpha[e] * sum_k x[t][k] * e2m1(W[e][n][k]) * scale(S[e][n][k/B])
+ * with B = 16 and scale = e4m3 for NVFP4, B = 32 and scale(b) = 2^(b - 127)
+ * (b = 255: NaN) for MXFP4.
  *
- * scales: the NVFP4 stack of the projection's scales (E experts, rows = N output
- *   features, cols = K/16; K a multiple of 32, at most 8192), device buffers.
- *   With dense_scales NULL each workgroup expands the scales of its 32 rows
- *   straight into LDS from the CSF streams (needs the tile index); otherwise
- *   the scales are read from dense_scales, u8[E][N][K/16] (for example a
- *   csf_decode workspace) and the CSF streams are not read.
+ * scales: the NVFP4 or MXFP4 stack of the projection's scales (E experts,
+ *   rows = N output features, cols = K/B; K a multiple of 32, at most 8192),
+ *   device buffers.  With dense_scales NULL each workgroup expands the scales
+ *   of its 32 rows straight into LDS from the CSF streams (needs the tile
+ *   index); otherwise the scales are read from dense_scales, u8[E][N][K/B]
+ *   (for example a csf_decode workspace) and the CSF streams are not read.
  * weights: u8[E][N][K/2], two E2M1 codes per byte, code k of row n in the low
  *   nibble of byte k/2 for even k, the high nibble for odd k; 16-byte aligned.
  * x: bfloat16 [num_tokens][K], tokens sorted by expert (the grouped routing).
  * alpha: float32 [E].  expert_start: int32 [E + 1] on the device; token
  *   indices are clamped to [0, num_tokens].  y: float32 [num_tokens][N]; rows
  *   of tokens outside every expert's range are not written.
+ * MXFP4 weights are widened to bfloat16 with their scale applied: exact for
+ *   scale bytes 2..252 and 255; with bytes 0, 1 (weights below bfloat16's
+ *   normal range) or 253, 254 (weights up to 6 * 2^127, beyond its largest
+ *   finite value) the result follows the hardware's conversion.  The E4M3
+ *   path widens every weight exactly.  Accumulation is in float32: for
+ *   exactly widened weights |y - y_exact| <= (K + 8) 2^-24 |alpha[e]|
+ *   sum_k |x[t][k] w[n][k]|.
  * Enqueued on hip_stream; allocates nothing; no host synchronisation.
  * Errors: CSF_E_NULL (a required pointer, or the tile index when dense_scales is
- *   NULL), CSF_E_FORMAT (not NVFP4), CSF_E_SHAPE (K not a multiple of 32 or
- *   above 8192, or the stack's own shape checks), CSF_E_SIZE (num_tokens < 0),
- *   CSF_E_ALIGN, CSF_E_HIP.
+ *   NULL), CSF_E_FORMAT (neither NVFP4 nor MXFP4), CSF_E_SHAPE (K not a
+ *   multiple of 32 or above 8192, or the stack's own shape checks),
+ *   CSF_E_SIZE (num_tokens < 0), CSF_E_ALIGN, CSF_E_HIP.
  */
 csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, const uint8_t *weights,
                          const uint16_t *x, int32_t num_tokens, const float *alpha,

@@ -397,9 +397,10 @@ def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, a
               expert_start: torch.Tensor, out: torch.Tensor | None = None, dense_scales=None, stream=None):
     """Enqueue the routed W4A16 projection (see ``csf_moe_w4a16``); returns y
     (float32 [T, N]).  ``x`` is bfloat16 (or int16/uint16 bit patterns)
-    [T, K]; ``weights`` uint8 [E, N, K/2]; ``alpha`` float32 [E]; with
-    ``dense_scales`` (uint8, E*N*K/16 bytes) the scales come from it instead
-    of the compressed stack."""
+    [T, K]; ``weights`` uint8 [E, N, K/2]; ``alpha`` float32 [E]; K is 16
+    (NVFP4) or 32 (MXFP4) times the stack's scale columns.  With
+    ``dense_scales`` (uint8, the stack's dense size) the scales come from it
+    instead of the compressed stack."""
     dev = scales.device
     if dev.type != "cuda":
         raise ValueError("moe_w4a16: compressed stack must be on a GPU")
@@ -408,7 +409,8 @@ def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, a
                         ("alpha", alpha, (torch.float32,)), ("expert_start", expert_start, (torch.int32,))):
         if t.device != dev or t.dtype not in dt or not t.is_contiguous():
             raise ValueError(f"moe_w4a16: {name} must be a contiguous {dt} tensor on {dev}")
-    if weights.numel() != scales.E * scales.R * scales.C * 8 or x.numel() != T * scales.C * 16:
+    K = scales.C * (16 if scales.fmt == NVFP4 else 32)  # weights per scale byte
+    if weights.numel() != scales.E * scales.R * K // 2 or x.numel() != T * K:
         raise ValueError("moe_w4a16: weights / x sizes do not match the scale stack")
     if alpha.numel() != scales.E or expert_start.numel() != scales.E + 1:
         raise ValueError("moe_w4a16: alpha must be [E] and expert_start [E+1]")

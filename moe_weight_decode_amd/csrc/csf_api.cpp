@@ -270,9 +270,10 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
                     const int32_t *expert_start, float *y, void *hip_stream) {
     csf_status st = check_stack(scales, weights);
     if (st != CSF_OK) return st;
-    if (scales->format != CSF_NVFP4_E4M3) return CSF_E_FORMAT;
-    const int64_t C = scales->cols, K = 16 * C;
-    if (C % 2 != 0 || C > 512) return CSF_E_SHAPE;  // K a multiple of 32, at most 8192
+    if (scales->format != CSF_NVFP4_E4M3 && scales->format != CSF_MXFP4_UE8M0) return CSF_E_FORMAT;
+    const bool mx = scales->format == CSF_MXFP4_UE8M0;
+    const int64_t C = scales->cols, K = (mx ? 32 : 16) * C;
+    if (K % 32 != 0 || K > 8192) return CSF_E_SHAPE;  // whole 32-wide MFMA lane groups, at most 4 K-tiles
     if (num_tokens < 0) return CSF_E_SIZE;
     if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
     if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;

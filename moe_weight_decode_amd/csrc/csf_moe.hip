@@ -93,6 +93,25 @@ __device__ __forceinline__ v8bf16 dequant8(uint32_t codes, float scale) {
     return __builtin_bit_cast(v8bf16, w);
 }
 
+// MXFP4: a UE8M0 scale byte b (value 2^(b - 127), 0xFF NaN; OCP Microscaling
+// Formats v1.0, E8M0) as the float whose exponent field is b: the hardware
+// conversion below reads only that field, so byte 0 (2^-127) is passed as 0.0.
+__device__ __forceinline__ float ue8m0_as_scale(uint32_t b) {
+    return b == 0xffu ? __uint_as_float(0x7fc00000u) : __uint_as_float(b << 23);
+}
+
+// MXFP4 weights of one MFMA step: 8 E2M1 codes times 2^(b - 127) straight to
+// bfloat16 pairs by the hardware conversion, whose scale acts through its
+// exponent, exactly the UE8M0 scale (code value x power of two is exact while
+// it stays in bfloat16's range).
+__device__ __forceinline__ v8bf16 dequant8_mx(uint32_t codes, float scale) {
+    const u32x4 w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3))};
+    return __builtin_bit_cast(v8bf16, w);
+}
+
 __device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
@@ -104,9 +123,14 @@ __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every range used here: reads 0
 
 // MULTI: K > 2048, several K-tiles per unit (a separate instantiation, so the
-// single K-tile code keeps its own register allocation).
-template <bool DENSE, bool MULTI>
+// single K-tile code keeps its own register allocation).  MX: MXFP4 weights
+// with UE8M0 scales per 32 (one-bit CSF offsets) instead of NVFP4 with E4M3
+// scales per 16 (four-bit offsets).
+template <bool DENSE, bool MULTI, bool MX>
 __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
+    constexpr uint32_t WB = MX ? 1u : 4u;       // CSF offset bits
+    constexpr uint32_t GROUP = 128u / WB;       // positions per 16-byte offset group
+    constexpr uint32_t BLOCK = MX ? 32u : 16u;  // weights per scale
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t s_scales[kMoeRows * kMoeMaxCols];
     __shared__ __align__(16) v4f32 s_part[kMoeWaves][kMoeRowBlocks][kMoeBlocks][kWave];
@@ -192,17 +216,24 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
             }
             const float alpha = __uint_as_float(load_b32(make_rsrc(a.alpha + e, 4u), 0u));
             u32x4 runs = {0u, 0u, 0u, 0u};
-            constexpr uint32_t kDense16 = kMoeStage / 2u / kMoeThreads;  // 16-bit loads per lane
-            uint32_t base_byte = 0u, dense2[kDense16] = {};
+            // dense scales: 16-bit loads for NVFP4 (C even: every span and its
+            // start are even), byte loads for MXFP4 (C = K/32 may be odd);
+            // either way kDenseLoads per lane cover a single-K-tile span
+            constexpr uint32_t kDenseLoads = kMoeStage / 2u / kMoeThreads;
+            constexpr uint32_t DW = MX ? 1u : 2u;
+            uint32_t base_byte = 0u, dense2[kDenseLoads] = {};
             if constexpr (DENSE) {
                 const rsrc_t rd = make_rsrc(a.dense + (uint64_t)e * plane + q0, q1 - q0);
 #pragma unroll
-                for (uint32_t i = 0; i < kDense16; ++i)
-                    dense2[i] = __builtin_amdgcn_raw_buffer_load_b16(rd, (int)(2u * (tid + i * kMoeThreads)), 0, 0);
+                for (uint32_t i = 0; i < kDenseLoads; ++i) {
+                    const int off = (int)(DW * (tid + i * kMoeThreads));
+                    dense2[i] = MX ? __builtin_amdgcn_raw_buffer_load_b8(rd, off, 0, 0)
+                                   : __builtin_amdgcn_raw_buffer_load_b16(rd, off, 0, 0);
+                }
             } else {
-                // NVFP4: 32 positions per 16-byte offset group
-                const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + 31u) / 32u) * 16u);
-                runs = load_b128(rs, ((q0 + kRunBytes * tid) / 32u) * 16u);
+                // GROUP positions per 16-byte offset group
+                const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + GROUP - 1u) / GROUP) * 16u);
+                runs = load_b128(rs, ((q0 + kRunBytes * tid) / GROUP) * 16u);
                 base_byte = __builtin_amdgcn_raw_buffer_load_b8(
                     make_rsrc(a.st.bases + (uint64_t)e * a.st.R + n0, nrows), (int)tid, 0, 0);
             }
@@ -240,13 +271,24 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
             // ---- scale bytes of the unit's rows into LDS
             if constexpr (DENSE) {
 #pragma unroll
-                for (uint32_t i = 0; i < kDense16; ++i)
-                    if (2u * (tid + i * kMoeThreads) < q1 - q0)
-                        *reinterpret_cast<uint16_t *>(s_scales + 2u * (tid + i * kMoeThreads)) = (uint16_t)dense2[i];
+                for (uint32_t i = 0; i < kDenseLoads; ++i) {
+                    const uint32_t off = DW * (tid + i * kMoeThreads);
+                    if (off < q1 - q0) {
+                        if constexpr (MX)
+                            s_scales[off] = (uint8_t)dense2[i];
+                        else
+                            *reinterpret_cast<uint16_t *>(s_scales + off) = (uint16_t)dense2[i];
+                    }
+                }
                 if constexpr (MULTI) {  // K > 2048: the rest of the span
-                    const uint16_t *src = reinterpret_cast<const uint16_t *>(a.dense + (uint64_t)e * plane + q0);
-                    for (uint32_t b = kMoeStage / 2u + tid; 2u * b < q1 - q0; b += kMoeThreads)
-                        *reinterpret_cast<uint16_t *>(s_scales + 2u * b) = src[b];
+                    const rsrc_t rd = make_rsrc(a.dense + (uint64_t)e * plane + q0, q1 - q0);
+                    for (uint32_t b = kDenseLoads * kMoeThreads + tid; DW * b < q1 - q0; b += kMoeThreads) {
+                        if constexpr (MX)
+                            s_scales[b] = (uint8_t)__builtin_amdgcn_raw_buffer_load_b8(rd, (int)b, 0, 0);
+                        else
+                            *reinterpret_cast<uint16_t *>(s_scales + 2u * b) =
+                                (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rd, (int)(2u * b), 0, 0);
+                    }
                 }
             } else {
                 // the span's exception entries, once the index bounds are in
@@ -259,10 +301,10 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                 if (tid < nrows) lds_bases[tid] = (uint8_t)base_byte;
                 __syncthreads();
                 if constexpr (!MULTI) {
-                    switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
-                        case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
-                        case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
-                        default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                    switch (a.st.row_mode) {
+                        case kRowSplat: expand_tile<WB, kRowSplat, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                        case kRowTwo: expand_tile<WB, kRowTwo, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
+                        default: expand_tile<WB, kRowBytes, true, 1, false>(a.st, &runs, q0, q1, q0, lds_bases, n0, s_scales, nullptr); break;
                     }
                 } else {
                     // one 16-position run per thread: 8192 positions per round, the
@@ -270,14 +312,14 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                     for (uint32_t g = 0; g * kRunBytes * kMoeThreads < q1 - q0; ++g) {
                         const uint32_t qg = q0 + g * kRunBytes * kMoeThreads;
                         if (g > 0) {  // K > 4096
-                            const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + 31u) / 32u) * 16u);
-                            runs = load_b128(rs, ((qg + kRunBytes * tid) / 32u) * 16u);
+                            const rsrc_t rs = make_rsrc(a.st.offsets + (uint64_t)e * a.st.stride, ((q1 + GROUP - 1u) / GROUP) * 16u);
+                            runs = load_b128(rs, ((qg + kRunBytes * tid) / GROUP) * 16u);
                         }
                         uint8_t *dst = s_scales + (qg - q0);
-                        switch (a.st.row_mode) {  // NVFP4 stacks only (4-bit offsets)
-                            case kRowSplat: expand_tile<4, kRowSplat, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
-                            case kRowTwo: expand_tile<4, kRowTwo, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
-                            default: expand_tile<4, kRowBytes, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                        switch (a.st.row_mode) {
+                            case kRowSplat: expand_tile<WB, kRowSplat, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                            case kRowTwo: expand_tile<WB, kRowTwo, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
+                            default: expand_tile<WB, kRowBytes, true, 1, false>(a.st, &runs, qg, q1, qg, lds_bases, n0, dst, nullptr); break;
                         }
                     }
                 }
@@ -298,14 +340,19 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                 // the scales of the lane's codes: blocks k0[c]/16 and k0[c]/16 + 1
                 // (0 past the rows or past K, where the codes read 0)
                 float sc[kMoeRowBlocks][kMoeChunks][2];
-    #pragma unroll
+#pragma unroll
                 for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
-    #pragma unroll
+#pragma unroll
                     for (uint32_t c = 0; c < kMoeChunks; ++c) {
                         const uint32_t r = rb * 16u + row;
                         const bool valid = lvalid[c] && r < nrows;
-                        sc[rb][c][0] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u]) : 0.f;
-                        sc[rb][c][1] = valid ? e4m3_value(s_scales[r * C + k0[c] / 16u + 1u]) : 0.f;
+                        if constexpr (MX) {  // one scale per 32 weights: the lane's 32
+                            sc[rb][c][0] = valid ? ue8m0_as_scale(s_scales[r * C + k0[c] / BLOCK]) : 0.f;
+                            sc[rb][c][1] = 0.f;
+                        } else {
+                            sc[rb][c][0] = valid ? e4m3_value(s_scales[r * C + k0[c] / BLOCK]) : 0.f;
+                            sc[rb][c][1] = valid ? e4m3_value(s_scales[r * C + k0[c] / BLOCK + 1u]) : 0.f;
+                        }
                     }
 
                 for (uint32_t tb = 0; tb < m; tb += kMoePass) {
@@ -314,27 +361,27 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                         load_pass(tb);
                     }
                     if (wave < nwaves1) {
-    #pragma unroll
+#pragma unroll
                         for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
                             v4f32 acc[NB];
-    #pragma unroll
+#pragma unroll
                             for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                             for (uint32_t c = 0; c < kMoeChunks; ++c) {
                                 const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t s = 0; s < kMoeSteps; ++s) {
                                     // one step at a time: converted ahead, the weights of every
                                     // step would hold their float intermediates at once
-                                    const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
-    #pragma unroll
+                                    const v8bf16 aw = MX ? dequant8_mx(wd[s], sc[rb][c][0]) : dequant8(wd[s], sc[rb][c][s >> 1]);
+#pragma unroll
                                     for (uint32_t b = 0; b < NB; ++b)
                                         acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                             aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
                                     __builtin_amdgcn_sched_barrier(0);
                                 }
                             }
-    #pragma unroll
+#pragma unroll
                             for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
                         }
                     }
@@ -350,7 +397,7 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                         if (t < m) {
                             float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
                             const float rr[4] = {r.x, r.y, r.z, r.w};
-    #pragma unroll
+#pragma unroll
                             for (uint32_t c = 0; c < 4; ++c)
                                 if (nn + c < nrows) dst[c] = rr[c] * alpha;
                         }
@@ -364,28 +411,28 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                     for (uint32_t kt = 0; kt < nkt; ++kt) {
                         const uint32_t kb = kt * kMoeKTile;
                         bool lv[kMoeChunks];
-    #pragma unroll
+#pragma unroll
                         for (uint32_t c = 0; c < kMoeChunks; ++c) lv[c] = kb + k0[c] < K;
                         if (tb > 0 || kt > 0) {
                             __syncthreads();  // the previous partial sums are read
                             // this K-tile's codes and activations (the first K-tile's
                             // first pass came with the unit's first loads)
-    #pragma unroll
+#pragma unroll
                             for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
                                 const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
                                 const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t c = 0; c < kMoeChunks; ++c)
                                     wa[rb][c] = load_b128(rw, lv[c] ? row * half_k + (kb + k0[c]) / 2u : kOutOfRange);
                             }
-    #pragma unroll
+#pragma unroll
                             for (uint32_t b = 0; b < NB; ++b) {
                                 const uint32_t t = tb + b * 16u;
                                 const uint32_t toks = m > t ? min(16u, m - t) : 0u;
                                 const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + t) * K, toks * K * 2u);
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t c = 0; c < kMoeChunks; ++c)
-    #pragma unroll
+#pragma unroll
                                     for (uint32_t s = 0; s < kMoeSteps; ++s)
                                         xa[b][c][s] = load_b128(rx, lv[c] ? (row * K + kb + k0[c]) * 2u + 16u * s : kOutOfRange);
                             }
@@ -394,38 +441,43 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                         // the scales of the lane's codes: blocks (kb + k0[c])/16 and
                         // the next (0 past the rows or past K, where the codes read 0)
                         float sc[kMoeRowBlocks][kMoeChunks][2];
-    #pragma unroll
+#pragma unroll
                         for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
-    #pragma unroll
+#pragma unroll
                             for (uint32_t c = 0; c < kMoeChunks; ++c) {
                                 const uint32_t r = rb * 16u + row;
                                 const bool valid = lv[c] && r < nrows;
-                                const uint32_t i = valid ? r * C + (kb + k0[c]) / 16u : 0u;
-                                sc[rb][c][0] = valid ? e4m3_value(s_scales[i]) : 0.f;
-                                sc[rb][c][1] = valid ? e4m3_value(s_scales[i + 1u]) : 0.f;
+                                const uint32_t i = valid ? r * C + (kb + k0[c]) / BLOCK : 0u;
+                                if constexpr (MX) {
+                                    sc[rb][c][0] = valid ? ue8m0_as_scale(s_scales[i]) : 0.f;
+                                    sc[rb][c][1] = 0.f;
+                                } else {
+                                    sc[rb][c][0] = valid ? e4m3_value(s_scales[i]) : 0.f;
+                                    sc[rb][c][1] = valid ? e4m3_value(s_scales[i + 1u]) : 0.f;
+                                }
                             }
                         if (wave < nwaves) {
-    #pragma unroll
+#pragma unroll
                             for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
                                 v4f32 acc[NB];
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t c = 0; c < kMoeChunks; ++c) {
                                     const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
-    #pragma unroll
+#pragma unroll
                                     for (uint32_t s = 0; s < kMoeSteps; ++s) {
                                         // one step at a time: converted ahead, the weights of every
                                         // step would hold their float intermediates at once
-                                        const v8bf16 aw = dequant8(wd[s], sc[rb][c][s >> 1]);
-    #pragma unroll
+                                        const v8bf16 aw = MX ? dequant8_mx(wd[s], sc[rb][c][0]) : dequant8(wd[s], sc[rb][c][s >> 1]);
+#pragma unroll
                                         for (uint32_t b = 0; b < NB; ++b)
                                             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                                 aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
                                         __builtin_amdgcn_sched_barrier(0);
                                     }
                                 }
-    #pragma unroll
+#pragma unroll
                                 for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
                             }
                         }
@@ -446,7 +498,7 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                         if (t < m) {
                             float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
                             const float rr[4] = {total.x, total.y, total.z, total.w};
-    #pragma unroll
+#pragma unroll
                             for (uint32_t c = 0; c < 4; ++c)
                                 if (nn + c < nrows) dst[c] = rr[c] * alpha;
                         }
@@ -473,19 +525,23 @@ size_t moe_lds_bytes(const MoeArgs &a) {
     return a.bases_stage + 4u * ((a.E + 1u + 3u) & ~3u) + ((2u * a.E + 15u) & ~15u) + a.E;
 }
 
+template <bool DENSE, bool MULTI, bool MX>
+static void launch_one(const MoeArgs &a, uint32_t grid, size_t lds, hipStream_t stream) {
+    hipLaunchKernelGGL((csf_moe_w4a16_kernel<DENSE, MULTI, MX>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+}
+
 hipError_t launch_moe_w4a16(const MoeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = moe_lds_bytes(a);
-    const bool multi = a.K > kMoeKTile;
-    if (a.dense != nullptr) {
-        if (multi)
-            hipLaunchKernelGGL((csf_moe_w4a16_kernel<true, true>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
-        else
-            hipLaunchKernelGGL((csf_moe_w4a16_kernel<true, false>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
-    } else {
-        if (multi)
-            hipLaunchKernelGGL((csf_moe_w4a16_kernel<false, true>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
-        else
-            hipLaunchKernelGGL((csf_moe_w4a16_kernel<false, false>), dim3(grid), dim3(kMoeThreads), lds, stream, a);
+    const bool dense = a.dense != nullptr, multi = a.K > kMoeKTile, mx = a.st.wbits == 1;
+    switch ((dense ? 4 : 0) + (multi ? 2 : 0) + (mx ? 1 : 0)) {
+        case 0: launch_one<false, false, false>(a, grid, lds, stream); break;
+        case 1: launch_one<false, false, true>(a, grid, lds, stream); break;
+        case 2: launch_one<false, true, false>(a, grid, lds, stream); break;
+        case 3: launch_one<false, true, true>(a, grid, lds, stream); break;
+        case 4: launch_one<true, false, false>(a, grid, lds, stream); break;
+        case 5: launch_one<true, false, true>(a, grid, lds, stream); break;
+        case 6: launch_one<true, true, false>(a, grid, lds, stream); break;
+        default: launch_one<true, true, true>(a, grid, lds, stream); break;
     }
     return hipGetLastError();
 }

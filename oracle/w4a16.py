@@ -26,6 +26,14 @@ What is computed (float64 throughout):
   scale bytes (the dense plane a CSF decode gives back), alpha[e] a float32
   per-expert tensor scale.
 
+  MXFP4 weights (fmt="mxfp4"): the same E2M1 codes with one UE8M0 scale byte
+  per 32 weights, y[t, n] = alpha[e] * sum_k x[t, k] * e2m1(W[e, n, k]) *
+  2^(S[e, n, k // 32] - 127) (OCP Microscaling Formats v1.0: MXFP4 blocks of
+  32 E2M1 elements sharing an E8M0 scale; E8M0 = 2^(byte - 127), 0xFF NaN).
+  The pages compress MXFP4 scale planes the same way, with one-bit offsets
+  ("NVFP4-CSF: expand_scales() ...", b12x PR 478, commit messages); they give
+  no MXFP4 consumer, so this is the plainest one.
+
 Readings fixed here (the pages give no consumer layout):
   * W is packed two codes per byte, row-major [E][N][K/2]: code k of row n is
     the low nibble of byte k // 2 for even k and the high nibble for odd k.
@@ -69,8 +77,18 @@ def e4m3_value(byte: int) -> float:
     return sign * mag
 
 
+def ue8m0_value(byte: int) -> float:
+    """Value of a UE8M0 (E8M0) scale byte: 2^(byte - 127); 0xFF is NaN."""
+    if byte == 0xFF:
+        return float("nan")
+    return 2.0 ** (byte - 127)
+
+
 E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 E4M3_TABLE = np.array([e4m3_value(b) for b in range(256)], dtype=np.float64)
+UE8M0_TABLE = np.array([ue8m0_value(b) for b in range(256)], dtype=np.float64)
+# weights per scale and scale byte table of each weight format
+FORMATS = {"nvfp4": (16, E4M3_TABLE), "mxfp4": (32, UE8M0_TABLE)}
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -88,23 +106,26 @@ def unpack_codes(w_packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_weights(w_packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Dense float64 weights [..., N, K] = e2m1(code) * e4m3(scale of its 16-block)."""
+def dequant_weights(w_packed: np.ndarray, scales: np.ndarray, fmt: str = "nvfp4") -> np.ndarray:
+    """Dense float64 weights [..., N, K] = e2m1(code) * value of the scale of
+    its block (16 weights, E4M3 for NVFP4; 32 weights, UE8M0 for MXFP4)."""
+    block, table = FORMATS[fmt]
     codes = unpack_codes(w_packed)
     K = codes.shape[-1]
-    s = E4M3_TABLE[np.asarray(scales, dtype=np.uint8)]          # [..., N, K/16]
-    return E2M1_TABLE[codes] * np.repeat(s, 16, axis=-1)[..., :K]
+    s = table[np.asarray(scales, dtype=np.uint8)]               # [..., N, K/block]
+    return E2M1_TABLE[codes] * np.repeat(s, block, axis=-1)[..., :K]
 
 
 def moe_w4a16(x_bits: np.ndarray, w_packed: np.ndarray, scales: np.ndarray, alpha: np.ndarray,
-              expert_start: np.ndarray, experts=None):
+              expert_start: np.ndarray, experts=None, fmt: str = "nvfp4"):
     """Reference output y (float64 [T, N]) and the bound sum |x * w| * |alpha|
     per output (float64 [T, N]) for the routed projection.  ``experts``
     limits the computation to those expert indices (rows of other tokens stay 0)."""
     x = bf16_to_f64(x_bits)
     T, K = x.shape
     E, N = w_packed.shape[0], w_packed.shape[1]
-    assert w_packed.shape[2] * 2 == K and scales.shape == (E, N, K // 16)
+    block = FORMATS[fmt][0]
+    assert w_packed.shape[2] * 2 == K and scales.shape == (E, N, K // block)
     es = np.asarray(expert_start, dtype=np.int64)
     y = np.zeros((T, N), dtype=np.float64)
     mag = np.zeros((T, N), dtype=np.float64)
@@ -112,7 +133,7 @@ def moe_w4a16(x_bits: np.ndarray, w_packed: np.ndarray, scales: np.ndarray, alph
         t0, t1 = es[e], es[e + 1]
         if t1 <= t0:
             continue
-        w = dequant_weights(w_packed[e], scales[e])              # [N, K]
+        w = dequant_weights(w_packed[e], scales[e], fmt)         # [N, K]
         a = float(np.float32(alpha[e]))
         y[t0:t1] = a * (x[t0:t1] @ w.T)
         mag[t0:t1] = abs(a) * (np.abs(x[t0:t1]) @ np.abs(w).T)

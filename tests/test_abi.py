@@ -236,7 +236,8 @@ def test_moe_w4a16_errors(lib):
         return mwd.STATUS[lib.csf_moe_w4a16(ctypes.byref(desc) if desc is not None else None, dense, w, x, T,
                                             alpha, es, y, None)]
     ok = _fake(R=32, C=16, stride=16 * 16, tile_index=0x8000)
-    assert call(_fake(fmt=1, R=32, C=16, stride=16 * 64, tile_index=0x8000)) == "CSF_E_FORMAT"
+    assert call(_fake(fmt=5, R=32, C=16, stride=16 * 64, tile_index=0x8000)) == "CSF_E_FORMAT"
+    assert call(_fake(fmt=1, R=32, C=257, stride=16 * 128, tile_index=0x8000)) == "CSF_E_SHAPE"  # MXFP4 K = 8224
     assert call(_fake(R=32, C=15, stride=16 * 15, tile_index=0x8000)) == "CSF_E_SHAPE"   # K = 240
     assert call(_fake(R=32, C=514, stride=16 * 514, tile_index=0x8000)) == "CSF_E_SHAPE"  # K > 8192
     assert call(_fake(R=32, C=16, stride=16 * 16)) == "CSF_E_NULL"        # no tile index, no dense scales

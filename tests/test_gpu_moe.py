@@ -1,7 +1,8 @@
 """GPU parity of the W4A16 consumer (csf_moe_w4a16) against its oracle.
 
-The kernel reads the E4M3 scales either straight from the CSF streams
-(expanded into LDS per 16-row unit) or from a dense scale workspace; both must
+The kernel reads the block scales (E4M3 per 16 weights for NVFP4, UE8M0 per 32
+for MXFP4) either straight from the CSF streams (expanded into LDS per unit of
+32 rows) or from a dense scale workspace; both must
 give the same float32 outputs bit for bit, and both must match the float64
 oracle within the fp32 accumulation bound
 
@@ -30,8 +31,11 @@ def dev():
     return torch.device("cuda:0")
 
 
+FMT_NAME = {workloads.NVFP4: "nvfp4", workloads.MXFP4: "mxfp4"}
+
+
 def run(orc, dev, inp: workloads.W4A16Inputs, dense: bool):
-    st = orc.encode(workloads.NVFP4, inp.scales)
+    st = orc.encode(inp.fmt, inp.scales)
     stack = mwd.from_numpy(st, dev)
     w = torch.from_numpy(inp.w_packed).to(dev)
     x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev)
@@ -49,7 +53,8 @@ def run(orc, dev, inp: workloads.W4A16Inputs, dense: bool):
 
 def check(inp, got, what):
     K = inp.x_bits.shape[1]
-    y, mag = ref.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start)
+    y, mag = ref.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start,
+                           fmt=FMT_NAME[inp.fmt])
     tol = (K + 8) * 2.0 ** -24 * mag
     err = np.abs(got.astype(np.float64) - y)
     bad = ~(err <= tol)
@@ -185,7 +190,8 @@ def check_non_finite(inp, got, what):
     elsewhere; finite outputs keep the float32 bound."""
     K = inp.x_bits.shape[1]
     with np.errstate(invalid="ignore"):  # inf * 0 in the oracle is meant to give NaN
-        y, mag = ref.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start)
+        y, mag = ref.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start,
+                               fmt=FMT_NAME[inp.fmt])
     got = got.astype(np.float64)
     assert np.array_equal(np.isnan(got), np.isnan(y)), f"{what}: NaN pattern differs"
     inf = np.isinf(y)
@@ -212,3 +218,50 @@ def test_non_finite_values_stay_in_their_outputs(orc, dev, K):
         got = run(orc, dev, inp, dense=dense)
         y = check_non_finite(inp, got, f"non-finite inputs, {'dense' if dense else 'CSF'} scales")
     assert np.isnan(y[5:11, 33]).all() and np.isfinite(y[[0, 1, 4]]).all()
+
+
+# -- MXFP4: UE8M0 scale per 32 weights, 1-bit CSF offsets ----------------------
+
+@pytest.mark.parametrize("E,N,K,counts", [
+    (3, 40, 96, [5, 0, 64]),
+    (5, 7, 32, [1, 2, 0, 16, 15]),
+    (3, 70, 160, [40, 1, 7]),
+    (2, 16, 2048, [3, 33]),
+    (2, 40, 2080, [17, 5]),
+    (2, 33, 5120, [1, 50]),
+    (2, 48, 8192, [70, 3]),
+], ids=["k96", "tiny", "k160_rows70", "k2048", "k2080", "k5120", "k8192_two_passes"])
+def test_mxfp4_small_shapes(orc, dev, E, N, K, counts):
+    es = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    inp = workloads.w4a16_inputs(E, N, K, es, seed=E * 100 + N + 1, exc_rate=0.15, fmt=workloads.MXFP4)
+    got_csf = run(orc, dev, inp, dense=False)
+    got_dense = run(orc, dev, inp, dense=True)
+    check(inp, got_csf, "MXFP4 scales from CSF")
+    assert np.array_equal(got_csf, got_dense)
+
+
+def test_mxfp4_routed_full_shape(orc, dev):
+    # the MXFP4 stack's shape (384 experts x 1024 rows, K = 5120), 8 experts routed
+    es = workloads.routing(384, 8, 64, 4)
+    inp = workloads.w4a16_inputs(384, 1024, 5120, es, seed=4, exc_rate=0.15, fmt=workloads.MXFP4)
+    got_csf = run(orc, dev, inp, dense=False)
+    got_dense = run(orc, dev, inp, dense=True)
+    check(inp, got_csf, "MXFP4 routed scales from CSF")
+    assert np.array_equal(got_csf, got_dense)
+
+
+def test_mxfp4_scale_extremes_and_nan(orc, dev):
+    """UE8M0 bytes far from 127 scale by their exponent alone (rows whose
+    blocks carry 20 and 230, products still inside float32's normal range,
+    stay within the bound), and byte 255 (NaN) makes
+    exactly its row's outputs NaN for the expert's tokens."""
+    es = _routing([6, 5], 11)
+    inp = workloads.w4a16_inputs(2, 40, 160, es, seed=95, exc_rate=0.05, fmt=workloads.MXFP4)
+    inp.scales[0, 3, :] = 20
+    inp.scales[0, 4, 1] = 230
+    inp.scales[1, 9, :] = np.array([20, 230, 127, 100, 200], dtype=np.uint8)
+    inp.scales[1, 21, 4] = 0xFF
+    for dense in (False, True):
+        got = run(orc, dev, inp, dense=dense)
+        y = check_non_finite(inp, got, f"MXFP4 extremes, {'dense' if dense else 'CSF'} scales")
+    assert np.isnan(y[6:11, 21]).all() and np.isfinite(y[:6]).all()

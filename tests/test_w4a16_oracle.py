@@ -2,8 +2,9 @@
 
 Each pin ties the oracle to something outside itself: the E2M1 value table of
 the OCP MX specification (tests/golden/e2m1_ocp_mx.json), torch's float8_e4m3fn
-conversion for every E4M3 byte, a scalar brute-force evaluation written
-independently of the vectorised reference, and closed-form special cases."""
+and float8_e8m0fnu conversions for every scale byte, a scalar brute-force
+evaluation written independently of the vectorised reference (both weight
+formats), and closed-form special cases."""
 import json
 import math
 import os
@@ -34,13 +35,20 @@ def test_e4m3_table_matches_torch_for_every_byte():
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 at 0x80
 
 
+def test_ue8m0_table_matches_torch_for_every_byte():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = w4a16.UE8M0_TABLE
+    assert np.isnan(got[255]) and np.isnan(ref[255]) and not np.isnan(got[:255]).any()
+    assert np.array_equal(got[:255], ref[:255])
+
+
 def test_bf16_bits_exact():
     bits = workloads.bf16_bits(7, 33, np.random.default_rng(3))
     ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(w4a16.bf16_to_f64(bits), ref)
 
 
-def _brute(inp: workloads.W4A16Inputs):
+def _brute(inp: workloads.W4A16Inputs, fmt: str = "nvfp4"):
     """Scalar evaluation with its own bit extraction (Python ints and floats)."""
     T, K = inp.x_bits.shape
     E, N = inp.w_packed.shape[:2]
@@ -57,6 +65,11 @@ def _brute(inp: workloads.W4A16Inputs):
         e, m = b >> 3, b & 7
         return s * (m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10))
 
+    def e8(b):
+        return float("nan") if b == 255 else math.ldexp(1.0, b - 127)
+
+    block, scale = (16, f8) if fmt == "nvfp4" else (32, e8)
+
     def bf(u):
         s = -1.0 if u >= 32768 else 1.0
         e, m = (u >> 7) & 255, u & 127
@@ -69,20 +82,23 @@ def _brute(inp: workloads.W4A16Inputs):
                 for k in range(K):
                     byte = int(inp.w_packed[e, n, k // 2])
                     code = (byte >> 4) if k % 2 else (byte & 15)
-                    acc += bf(int(inp.x_bits[t, k])) * f4(code) * f8(int(inp.scales[e, n, k // 16]))
+                    acc += bf(int(inp.x_bits[t, k])) * f4(code) * scale(int(inp.scales[e, n, k // block]))
                 y[t][n] = float(np.float32(inp.alpha[e])) * acc
     return np.array(y)
 
 
-def _tiny():
+def _tiny(fmt: str = "nvfp4"):
     es = np.array([0, 2, 2, 5], dtype=np.int32)   # expert 1 has no tokens
-    return workloads.w4a16_inputs(3, 3, 64, es, seed=11)
+    if fmt == "nvfp4":
+        return workloads.w4a16_inputs(3, 3, 64, es, seed=11)
+    return workloads.w4a16_inputs(3, 3, 96, es, seed=12, exc_rate=0.3, fmt=workloads.MXFP4)
 
 
-def test_reference_matches_brute_force():
-    inp = _tiny()
-    y, mag = w4a16.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start)
-    want = _brute(inp)
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_reference_matches_brute_force(fmt):
+    inp = _tiny(fmt)
+    y, mag = w4a16.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start, fmt=fmt)
+    want = _brute(inp, fmt)
     assert np.allclose(y, want, rtol=1e-12, atol=1e-300)
     assert np.all(mag >= np.abs(y) * (1 - 1e-12))
 
@@ -95,6 +111,18 @@ def test_unit_weights_sum_activations():
     y, _ = w4a16.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start)
     x = w4a16.bf16_to_f64(inp.x_bits)
     assert np.array_equal(y, np.repeat(x.sum(axis=1, keepdims=True), 3, axis=1))
+
+
+def test_mxfp4_unit_scales_equal_plain_e2m1():
+    # UE8M0 byte 127 is 1.0: y is the plain E2M1 product
+    inp = _tiny("mxfp4")
+    inp.scales[:] = 127
+    y, _ = w4a16.moe_w4a16(inp.x_bits, inp.w_packed, inp.scales, inp.alpha, inp.expert_start, fmt="mxfp4")
+    x = w4a16.bf16_to_f64(inp.x_bits)
+    codes = w4a16.E2M1_TABLE[w4a16.unpack_codes(inp.w_packed)]
+    for e in range(3):
+        t0, t1 = inp.expert_start[e], inp.expert_start[e + 1]
+        assert np.array_equal(y[t0:t1], float(inp.alpha[e]) * (x[t0:t1] @ codes[e].T))
 
 
 def test_sign_bit_negates():
@@ -126,3 +154,31 @@ def test_brute_force_catches_plausible_mistakes(mistake):
     else:
         y, _ = w4a16.moe_w4a16(inp.x_bits, w, s, inp.alpha, es)
     assert not np.allclose(y, _brute(inp), rtol=1e-9)
+
+
+@pytest.mark.parametrize("mistake", ["scale per 16 weights", "exponent bias 126", "nibbles swapped"])
+def test_brute_force_catches_plausible_mxfp4_mistakes(mistake):
+    """The MXFP4 brute-force pin is sensitive to each of these reference mistakes."""
+    inp = _tiny("mxfp4")
+    w, s = inp.w_packed, inp.scales
+    if mistake == "nibbles swapped":
+        w = ((w & 0x0F) << 4) | (w >> 4)
+    if mistake == "scale per 16 weights":
+        # the row's MX scale bytes read as one per 16 weights (the row's bytes twice over)
+        s16 = np.concatenate([s, s], axis=-1)
+        saved = w4a16.FORMATS["mxfp4"]
+        w4a16.FORMATS["mxfp4"] = (16, w4a16.UE8M0_TABLE)
+        try:
+            y, _ = w4a16.moe_w4a16(inp.x_bits, w, s16, inp.alpha, inp.expert_start, fmt="mxfp4")
+        finally:
+            w4a16.FORMATS["mxfp4"] = saved
+    elif mistake == "exponent bias 126":
+        saved = w4a16.UE8M0_TABLE.copy()
+        w4a16.UE8M0_TABLE[:255] *= 2.0
+        try:
+            y, _ = w4a16.moe_w4a16(inp.x_bits, w, s, inp.alpha, inp.expert_start, fmt="mxfp4")
+        finally:
+            w4a16.UE8M0_TABLE[:] = saved
+    else:
+        y, _ = w4a16.moe_w4a16(inp.x_bits, w, s, inp.alpha, inp.expert_start, fmt="mxfp4")
+    assert not np.allclose(y, _brute(inp, "mxfp4"), rtol=1e-9)

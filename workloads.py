@@ -168,9 +168,10 @@ STACKS = {s.name: s for s in (TINY, GATE, DOWN, MX)}
 class W4A16Inputs:
     x_bits: np.ndarray        # uint16 [T, K]: bfloat16 bit patterns of the routed tokens
     w_packed: np.ndarray      # uint8 [E, N, K/2]: two E2M1 codes per byte (even k low nibble)
-    scales: np.ndarray        # uint8 [E, N, K/16]: E4M3 scale bytes
+    scales: np.ndarray        # uint8 [E, N, K/16] E4M3 (NVFP4) or [E, N, K/32] UE8M0 (MXFP4) scale bytes
     alpha: np.ndarray         # float32 [E]: per-expert tensor scale
     expert_start: np.ndarray  # int32 [E + 1]: grouped routing (tokens sorted by expert)
+    fmt: int = NVFP4          # NVFP4 or MXFP4
 
 
 def bf16_bits(T: int, K: int, rng) -> np.ndarray:
@@ -183,16 +184,20 @@ def bf16_bits(T: int, K: int, rng) -> np.ndarray:
 
 
 def w4a16_inputs(E: int, N: int, K: int, expert_start: np.ndarray, seed: int,
-                 exc_rate: float = 0.03) -> W4A16Inputs:
-    """Seeded inputs of a routed NVFP4 projection: scales shaped like the
-    gate-like stack (nvfp4_stack with C = K / 16), uniform random E2M1 codes,
-    bfloat16 activations for the routed tokens, alpha uniform in [0.5, 2)."""
+                 exc_rate: float = 0.03, fmt: int = NVFP4) -> W4A16Inputs:
+    """Seeded inputs of a routed NVFP4 or MXFP4 projection: scales shaped like
+    the gate-like stack (nvfp4_stack with C = K / 16) or the MXFP4 stack
+    (mxfp4_stack with C = K / 32), uniform random E2M1 codes, bfloat16
+    activations for the routed tokens, alpha uniform in [0.5, 2)."""
     assert K % 32 == 0
     es = np.ascontiguousarray(expert_start, dtype=np.int32)
     T = int(es[-1])
-    scales = nvfp4_stack(E, N, K // 16, seed, exc_rate)
+    if fmt == NVFP4:
+        scales = nvfp4_stack(E, N, K // 16, seed, exc_rate)
+    else:
+        scales = mxfp4_stack(E, N, K // 32, seed, exc_rate)
     rng = np.random.default_rng(seed + 1000)
     w = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     x = bf16_bits(T, K, rng)
     alpha = rng.uniform(0.5, 2.0, E).astype(np.float32)
-    return W4A16Inputs(x, w, scales, alpha, es)
+    return W4A16Inputs(x, w, scales, alpha, es, fmt)
