@@ -20,14 +20,17 @@ Prints ONE JSON line on stdout:
   python bench.py [--steps K] [--warmup W] [--sets N] [--workload NAME] [--all] [--no-cpu]
 
 --workload picks another timed workload (down_nvfp4, mxfp4, tiny_nvfp4,
-routed_paired, routed_moe) for profiling; the default is the gate-like stack.
-routed_moe times the W4A16 consumer that expands its scales in LDS from the
-CSF streams (csf_moe_w4a16) on the gate-like projection with 8 of 512 experts
-routed, next to a routed decode followed by the same GEMM on dense scales.
+routed_paired, routed_moe, routed_moe_mx) for profiling; the default is the
+gate-like stack.  routed_moe times the W4A16 consumer that expands its scales
+in LDS from the CSF streams (csf_moe_w4a16) on the gate-like projection with 8
+of 512 experts routed, next to a routed decode followed by the same GEMM on
+dense scales; routed_moe_mx does the same on the MXFP4 stack's projection
+(384 x 1024, K = 5120, 8 of 384 experts routed).
 
 --all also measures the other workloads (down-like, MXFP4, routed paired,
 tiny), the two-pass decode of each (fixed-stream kernel, then exception
-kernel), and a plain copy; one line each on stderr.
+kernel), warm and cache-flushed single calls, the floor of two dependent tiny
+launches, and a plain copy; one line each on stderr.
 """
 from __future__ import annotations
 
@@ -178,6 +181,26 @@ def timed_loop(torch, ev, calls, steps, warmup):
     return wall_ms / steps, total_ms / steps
 
 
+def flushed_call_ms(torch, ev, launch, dev, reps=30, flush_bytes=1 << 30):
+    """Latency of one call on cold caches: a 1 GiB buffer (more than the MALL
+    and every L2 together) is written on the call's stream before each call,
+    and one event pair brackets the call alone.  Median over `reps` calls."""
+    if torch.cuda.current_stream(dev).cuda_stream != launch.stream:
+        raise RuntimeError("flushed_call_ms: the call must run on the current stream")
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    evs = ev.create(2 * reps)
+    for i in range(reps):
+        buf.fill_(i & 0xFF)
+        ev.record(evs[2 * i], launch.stream)
+        launch()
+        ev.record(evs[2 * i + 1], launch.stream)
+    torch.cuda.synchronize()
+    t = [ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(reps)]
+    ev.destroy(evs)
+    del buf
+    return statistics.median(t)
+
+
 class Passes:
     """A Launch restricted to some passes (for the two-pass split)."""
 
@@ -197,7 +220,9 @@ def check_equal(torch, ws, x, what):
 
 def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
     """Time the full decode of `spec` (fused, indexed stack); with `split`
-    also the two-pass decode of the same stack and its fixed pass alone."""
+    also the two-pass decode of the same stack and its fixed pass alone, one
+    stack decoded over and over (warm: its 85-109 MB stay in the MALL), and
+    single calls on flushed caches."""
     x = spec.generate()
     stack = mwd.prepare(x, spec.fmt).to(dev)
     sets = make_sets(mwd, torch, stack, nsets, dev)
@@ -216,7 +241,9 @@ def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
         check_equal(torch, sets[0][1], x, spec.name + " two-pass")
         w2, e2 = timed_loop(torch, ev, two, steps, warmup)
         wf, ef = timed_loop(torch, ev, [Passes(L, mwd.PASS_FIXED) for L in two], steps, warmup)
-        out.update(two_pass_ms=max(w2, e2), fixed_only_ms=max(wf, ef))
+        ww, we = timed_loop(torch, ev, [launches[0]], steps, warmup)
+        out.update(two_pass_ms=max(w2, e2), fixed_only_ms=max(wf, ef), warm_ms=max(ww, we),
+                   flushed_ms=flushed_call_ms(torch, ev, launches[0], dev))
     return out
 
 
@@ -351,28 +378,30 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
     reps = max(1, steps // len(calls))
     wall, evt = timed_loop(torch, ev, [Replay(graphs[0])], reps, max(1, warmup // len(calls)))
     wwall, wevt = timed_loop(torch, ev, [Replay(graphs[1])], reps, max(1, warmup // len(calls)))
+    flushed = flushed_call_ms(torch, ev, mwd.Launch(g, wg, d, wd, es_t), dev)
     n = len(calls)
     b = [stack_bytes(s, active) for s in (g, d)]
     return dict(step_ms=max(wall, evt) / n, event_ms=evt / n, wall_ms=wall / n,
                 bytes=sum(nbytes) / len(nbytes), warm_ms=max(wwall, wevt) / n,
-                warm_bytes=sum(sum(x) for x in b) + 4 * len(es), active=int(active.sum()),
+                warm_bytes=sum(sum(x) for x in b) + 4 * len(es), active=int(active.sum()), flushed_ms=flushed,
                 sets=n, steps=reps * n)
 
 
-def bench_moe(mwd, torch, ev, workloads, steps, warmup, dev, routings=64):
-    """Routed W4A16 projection of the gate-like shape (512 experts x 800 rows x
-    K = 2048, scales of the gate-like stack), 8 experts routed per call with
-    1..64 tokens each; `routings` disjoint routings cover every expert once, so
-    each replay of the call sequence reads every expert's weights from HBM.
+def bench_moe(mwd, torch, ev, workloads, steps, warmup, dev, routings=64, spec=None):
+    """Routed W4A16 projection of a stack's shape with its scales: the
+    gate-like NVFP4 stack (512 experts x 800 rows x K = 2048) by default, or
+    the MXFP4 stack (384 x 1024 x K = 5120); 8 experts routed per call with
+    1..64 tokens each; `routings` disjoint routings cover every expert at least
+    once, so each replay of the call sequence reads every expert's weights from HBM.
     Times, from HIP-graph replays: the stage-local consumer (scales expanded in
     LDS from the CSF streams), a routed decode into a dense workspace followed
     by the same GEMM on the dense scales, and the GEMM alone on scales decoded
     beforehand.  Checks the first routing against the oracle first."""
     import numpy as np
     from oracle import w4a16 as ref
-    spec = workloads.GATE
-    E, N, C = spec.E, spec.R, spec.C
-    K = 16 * C
+    spec = spec or workloads.GATE
+    E, N, K = spec.E, spec.R, spec.K
+    fmt = "nvfp4" if spec.fmt == workloads.NVFP4 else "mxfp4"
     xs = spec.generate()
     stack = mwd.prepare(xs, spec.fmt).to(dev)
     rng = np.random.default_rng(77)
@@ -402,7 +431,7 @@ def bench_moe(mwd, torch, ev, workloads, steps, warmup, dev, routings=64):
             y0 = mwd.moe_w4a16(stack, w, x, alpha, es_t, out=y)
             torch.cuda.synchronize()
             got = y0.cpu().numpy()
-            yr, mag = ref.moe_w4a16(xb, w_host, xs, alpha_host, es, experts=act)
+            yr, mag = ref.moe_w4a16(xb, w_host, xs, alpha_host, es, experts=act, fmt=fmt)
             if not np.all(np.abs(got - yr) <= (K + 8) * 2.0 ** -24 * mag):
                 raise SystemExit("routed W4A16 projection differs from the oracle")
             y1 = torch.empty_like(y)
@@ -451,7 +480,7 @@ def bench_moe(mwd, torch, ev, workloads, steps, warmup, dev, routings=64):
     reps = max(1, steps // n)
     out = dict(bytes=sum(nbytes) / n, extra_bytes=sum(extra_bytes) / n, calls=n, steps=reps * n,
                tokens=sum(int(c[2][-1]) for c in cases) / n, first=first, w_host=w_host, xs=xs,
-               alpha_host=alpha_host, first_bytes=nbytes[0])
+               alpha_host=alpha_host, first_bytes=nbytes[0], fmt=fmt)
     for kind, gr in graphs.items():
         wall, evt = timed_loop(torch, ev, [Replay(gr)], reps, max(1, warmup // n))
         out[kind + "_ms"] = max(wall, evt) / n
@@ -463,8 +492,8 @@ def cpu_baseline_moe(mr, budget_s=10.0):
     """The W4A16 oracle (numpy float64) computing the first routing's projection."""
     from oracle import w4a16 as ref
     xb, es, act = mr["first"]
-    sec, n = _repeat(lambda: ref.moe_w4a16(xb, mr["w_host"], mr["xs"], mr["alpha_host"], es, experts=act),
-                     budget_s)
+    sec, n = _repeat(lambda: ref.moe_w4a16(xb, mr["w_host"], mr["xs"], mr["alpha_host"], es, experts=act,
+                                           fmt=mr["fmt"]), budget_s)
     return dict(value=round(mr["first_bytes"] / sec / 1e9, 4), unit="GB/s", cores=_blas_threads(),
                 kind="oracle", us_per_call=round(sec * 1e6, 1),
                 sample=f"one routed call ({len(act)} experts, {int(es[-1])} tokens) of the W4A16 "
@@ -478,6 +507,41 @@ def _blas_threads() -> int:
         if v and v.isdigit():
             return int(v)
     return len(os.sched_getaffinity(0))
+
+
+def launch_floor(torch, ev, dev, steps=2000):
+    """The floor under a decode call of two dependent launches: two tiny
+    kernels (one-element adds) per step, launched directly and replayed from
+    a HIP graph of 64 steps; µs per step."""
+    t = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    class Pair:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def __call__(self):
+            t.add_(1)
+            t.add_(1)
+
+    wall, evt = timed_loop(torch, ev, [Pair()], steps, 100)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        Pair()()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=side):
+        for _ in range(64):
+            Pair()()
+
+    class Replay:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def __call__(self):
+            gr.replay()
+
+    gw, ge = timed_loop(torch, ev, [Replay()], max(1, steps // 64), 2)
+    return dict(direct_us=round(max(wall, evt) * 1e3, 2), graph_us=round(max(gw, ge) / 64 * 1e3, 2))
 
 
 def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
@@ -508,7 +572,8 @@ def main():
                     help="after the timed run, N plain 256 MiB device copies (reference for "
                          "hardware byte counters)")
     ap.add_argument("--workload", default="gate_nvfp4",
-                    choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe"],
+                    choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe",
+                             "routed_moe_mx"],
                     help="timed workload (default: the 512-expert gate-like stack)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -524,14 +589,20 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     ev = HipEvents()
-    if args.workload == "routed_moe":
-        mr = bench_moe(mwd, torch, ev, workloads, args.steps, args.warmup, dev)
+    moe = args.workload.startswith("routed_moe")
+    if moe:
+        mx = args.workload == "routed_moe_mx"
+        mr = bench_moe(mwd, torch, ev, workloads, args.steps, args.warmup, dev,
+                       spec=workloads.MX if mx else workloads.GATE)
         step_bytes = mr["bytes"]
         r = dict(step_ms=mr["stage_ms"], event_ms=mr["stage_event_ms"], wall_ms=mr["stage_ms"])
+        shape = ("the MXFP4 stack's shape (384 experts x 1024 rows x K=5120, MXFP4 weights, CSF scales of "
+                 "the MXFP4 stack) with 8 of 384 experts" if mx else
+                 "the gate-like shape (512 experts x 800 rows x K=2048, NVFP4 weights, CSF scales of the "
+                 "gate-like stack) with 8 of 512 experts")
         config = {
-            "workload": "routed_moe: W4A16 projection of the gate-like shape (512 experts x 800 rows x "
-                        "K=2048, NVFP4 weights, CSF scales of the gate-like stack) with 8 of 512 experts "
-                        "routed (1..64 tokens each); scales expanded in LDS from the CSF streams",
+            "workload": f"{args.workload}: W4A16 projection of {shape} routed (1..64 tokens each); scales "
+                        "expanded in LDS from the CSF streams",
             "decode": "stage-local (csf_moe_w4a16 reading the CSF streams); steps replayed from a HIP "
                       "graph of all rotating routings",
             "bytes_per_step": round(step_bytes),
@@ -586,10 +657,10 @@ def main():
     achieved = step_bytes / (r["event_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
-    kernel = "csf_moe_w4a16_kernel" if args.workload == "routed_moe" else "csf_fused_kernel"
+    kernel = "csf_moe_w4a16_kernel" if moe else "csf_fused_kernel"
     traffic = pmc_traffic(kernel, args.workload)
     out = {
-        "metric": MOE_METRIC if args.workload == "routed_moe" else METRIC,
+        "metric": MOE_METRIC if moe else METRIC,
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -600,7 +671,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.workload == "routed_moe" else "u8",
+        "dtype": "bf16" if moe else "u8",
         "data": "synthetic",
         "config": config,
         "roofline": {
@@ -628,6 +699,8 @@ def main():
                                gbps=round(b / (rr["step_ms"] * 1e-3) / 1e9, 1),
                                two_pass_us=round(rr["two_pass_ms"] * 1e3, 2),
                                fixed_only_us=round(rr["fixed_only_ms"] * 1e3, 2),
+                               warm_us=round(rr["warm_ms"] * 1e3, 2),
+                               flushed_us=round(rr["flushed_ms"] * 1e3, 2),
                                bytes=b, entries=rr["stack"].num_exceptions)
             xd = torch.from_numpy(rr["x"]).to(dev)
             enc = []
@@ -647,9 +720,12 @@ def main():
             rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed)
             extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2),
                               gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                              warm_us=round(rr["warm_ms"] * 1e3, 2), bytes=round(rr["bytes"]),
+                              warm_us=round(rr["warm_ms"] * 1e3, 2), flushed_us=round(rr["flushed_ms"] * 1e3, 2),
+                              bytes=round(rr["bytes"]),
                               active=rr["active"], sets=rr["sets"])
             log(f"[bench] {key}: {extra[key]}")
+        extra["launch_floor"] = launch_floor(torch, ev, dev)
+        log(f"[bench] launch floor: {extra['launch_floor']}")
         cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
         extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
         log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
@@ -670,7 +746,7 @@ def main():
         log(f"[bench] cpu oracle baseline (~{args.cpu_seconds:.0f} s)")
         if args.workload == "routed_paired":
             out["cpu_baseline"] = cpu_baseline_routed(workloads, args.cpu_seconds)
-        elif args.workload == "routed_moe":
+        elif moe:
             out["cpu_baseline"] = cpu_baseline_moe(mr, args.cpu_seconds)
         else:
             out["cpu_baseline"] = cpu_baseline(spec, x_head, args.cpu_seconds)
