@@ -1,5 +1,5 @@
-// W4A16 MoE projection with NVFP4 weights on gfx950: the consumer of the
-// CSF-compressed block scales.
+// W4A16 MoE projection with NVFP4 or MXFP4 weights on gfx950: the consumer
+// of the CSF-compressed block scales.
 //
 // "NVFP4-CSF: expand_scales() for ahead-of-call scale expansion (canonical
 // twin of #477)" (b12x PR 478), last commit message: the W4A16 MoE kernel
@@ -10,10 +10,13 @@
 // dense buffer.  "finegrained-kernels: decode
 // losslessly compressed NVFP4 scales (CSF)" (kernels-community PR 1236),
 // format paragraph: NVFP4 = 4-bit (E2M1) weights and one E4M3 scale per 16
-// weights.
+// weights.  The same pages compress MXFP4 scale planes (one UE8M0 scale per 32
+// E2M1 weights, OCP Microscaling Formats v1.0) with one-bit offsets; the MXFP4
+// instantiation is the same projection on those.
 //
 // For every expert e with routed tokens t in [expert_start[e], expert_start[e+1]):
-//     y[t, n] = alpha[e] * sum_k x[t, k] * e2m1(W[e, n, k]) * e4m3(S[e, n, k / 16])
+//     y[t, n] = alpha[e] * sum_k x[t, k] * e2m1(W[e, n, k]) * e4m3(S[e, n, k / 16])     (NVFP4)
+//     y[t, n] = alpha[e] * sum_k x[t, k] * e2m1(W[e, n, k]) * 2^(S[e, n, k / 32] - 127) (MXFP4)
 // x bfloat16 [T][K], W two E2M1 codes per byte [E][N][K/2] (even k in the low
 // nibble), y float32 [T][N].
 //
@@ -26,8 +29,9 @@
 // bulk loads.  The scale bytes are expanded into LDS with the decoder's tile
 // code and patched with the entries.  Wave w owns K in [256w, 256w + 256), two
 // 128-wide chunks: per 16-row block and chunk a lane turns 32 E2M1 codes of
-// one row into bfloat16 weights (hardware E2M1 -> f32 conversion, one exact
-// multiply by the E4M3 scale, top halves packed) and issues 4 MFMA 16x16x32
+// one row into bfloat16 weights (NVFP4: hardware E2M1 -> f32 conversion, one
+// exact multiply by the E4M3 scale, top halves packed; MXFP4: the hardware
+// E2M1 -> bf16 conversion with the UE8M0 scale applied) and issues 4 MFMA 16x16x32
 // bf16 steps per 16-token block.  K is permuted consistently in both operands
 // (lane group q of step s holds k = chunk + 32q + 8s .. +7), which leaves the sums
 // unchanged and makes every operand one 16-byte load.  The waves' partial
@@ -57,7 +61,7 @@ constexpr uint32_t kMoePass = 16 * kMoeBlocks;
 constexpr uint32_t kMoeSteps = 4;       // MFMA 16x16x32 steps per 128-wide chunk
 constexpr uint32_t kMoeKTile = kMoeWaves * kMoeWaveK;  // K per K-tile: one 256-wide slice per wave
 constexpr uint32_t kMoeMaxCols = 512;   // scale columns per row: K <= 8192
-constexpr uint32_t kMoeStage = 4096;    // scale bytes read with the unit's first loads (K <= 2048)
+constexpr uint32_t kMoeStage = 4096;    // dense-scale bytes read with the unit's first loads (K <= 2048 NVFP4)
 constexpr uint32_t kXcds = 8;           // MI355X: workgroups go round-robin to 8 XCDs
 
 typedef float v2f32 __attribute__((ext_vector_type(2)));
