@@ -17,6 +17,13 @@ The functions mirror the C ABI in ``include/csf.h``:
 * ``decode_paired(gate_up, ws_gate_up, down, ws_down, expert_start=None, stream=None)``
   (``expert_start`` int32 or int64; int64 goes through ``csf_decode_i64``);
 * ``decode_passes(...)`` to enqueue the fixed-stream or exception pass alone;
+* ``decode_rows(...)`` to decode a window of rows of every plane (for example
+  only the gate half of a gate/up stack);
+* ``moe_w4a16(scales, weights, x, alpha, expert_start, ...)``: the routed
+  W4A16 projection (NVFP4 or MXFP4 weights) that expands its scales in LDS
+  from the CSF streams, or reads them from a dense workspace;
+* ``Launch(...)``: a decode with its arguments marshalled once, for loops
+  and graph capture;
 * ``build_index(stack)`` (the per-tile exception index, built on the GPU);
 * ``validate(stack)`` (host-side layout check).
 
@@ -419,8 +426,9 @@ def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, a
     elif out.device != dev or out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != T * scales.R:
         raise ValueError("moe_w4a16: out must be a contiguous float32 [T, N] tensor")
     if dense_scales is not None and (dense_scales.device != dev or dense_scales.dtype != torch.uint8
+                                     or not dense_scales.is_contiguous()
                                      or dense_scales.numel() < scales.dense_bytes):
-        raise ValueError("moe_w4a16: dense_scales must be uint8 with the stack's dense size")
+        raise ValueError("moe_w4a16: dense_scales must be contiguous uint8 with the stack's dense size")
     d = scales.descriptor()
     _check(_lib().csf_moe_w4a16(ctypes.byref(d), None if dense_scales is None else dense_scales.data_ptr(),
                                 weights.data_ptr(), x.data_ptr() if T > 0 else None, T, alpha.data_ptr(),
