@@ -34,7 +34,13 @@
 // E2M1 -> bf16 conversion with the UE8M0 scale applied) and issues 4 MFMA 16x16x32
 // bf16 steps per 16-token block.  K is permuted consistently in both operands
 // (lane group q of step s holds k = chunk + 32q + 8s .. +7), which leaves the sums
-// unchanged and makes every operand one 16-byte load.  The waves' partial
+// unchanged and makes every operand 16 contiguous bytes.  The operand layout
+// puts 16 different tokens on every 16 consecutive lanes, so loading it
+// directly splits each load into 16-byte pieces of 16 rows (about 36 GB/s per
+// CU against 94 GB/s for quad-contiguous loads); instead each lane quad loads
+// 64 contiguous bytes of one token row (the four steps' pieces of one lane
+// group), and a 4 x 4 transpose inside the quad across the four step registers
+// (two rounds of DPP quad permutes) moves every piece to its operand lane.  The waves' partial
 // sums meet in LDS and are added in wave order, so the result does not depend
 // on timing.  K above 2048 runs in K-tiles of 2048 (every wave one 256-wide
 // slice of each): the unit's whole scale span is expanded into LDS once, each
@@ -97,6 +103,24 @@ __device__ __forceinline__ v8bf16 dequant8(uint32_t codes, float scale) {
     return __builtin_bit_cast(v8bf16, w);
 }
 
+// An E4M3 scale byte as the float16 bit pattern of its value / 256 (the
+// exponent fields differ in width by one bit and in bias by 8), NaN (S.1111.111)
+// as a float16 NaN: every E4M3 value is exact in float16.
+__device__ __forceinline__ uint32_t e4m3_half(uint32_t b) {
+    const uint32_t sign = (b & 0x80u) << 8;
+    return (b & 0x7fu) == 0x7fu ? (0x7e00u | sign) : (((b & 0x7fu) << 7) | sign);
+}
+
+// dequant8 with the scale given as value / 256: the codes are converted x 256
+// (a power of two, exact), so the products are the same exact values.
+__device__ __forceinline__ v8bf16 dequant8_h(uint32_t codes, float scale256) {
+    const u32x4 w = {pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 0), scale256),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 1), scale256),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 2), scale256),
+                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 3), scale256)};
+    return __builtin_bit_cast(v8bf16, w);
+}
+
 // MXFP4: a UE8M0 scale byte b (value 2^(b - 127), 0xFF NaN; OCP Microscaling
 // Formats v1.0, E8M0) as the float whose exponent field is b: the hardware
 // conversion below reads only that field, so byte 0 (2^-127) is passed as 0.0.
@@ -120,6 +144,31 @@ __device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
+// Lane j of every quad reads lane j ^ m of the same quad: quad_perm 0x4E is
+// [2, 3, 0, 1] (m = 2), 0xB1 is [1, 0, 3, 2] (m = 1).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+// Exchange across one bit m of the quad lane and of the register index:
+// a'[j] = hi ? b[j ^ m] : a[j], b'[j] = hi ? b[j] : a[j ^ m], hi = bit m of j.
+template <int CTRL>
+__device__ __forceinline__ void quad_swap(u32x4 &a, u32x4 &b, bool hi) {
+    // each lane sends what its partner (the lane with the other bit) keeps of
+    // the pair: a from a set lane, b from a clear one
+    u32x4 t = hi ? a : b;
+    t = (u32x4){quad_dpp<CTRL>(t.x), quad_dpp<CTRL>(t.y), quad_dpp<CTRL>(t.z), quad_dpp<CTRL>(t.w)};
+    a = hi ? t : a;
+    b = hi ? b : t;
+}
+// Register j of quad lane s <- register s of quad lane j (each bit of the
+// register index trades places with the same bit of the quad lane).
+__device__ __forceinline__ void quad_transpose(u32x4 (&r)[4], bool hi1, bool hi0) {
+    quad_swap<0x4E>(r[0], r[2], hi1);
+    quad_swap<0x4E>(r[1], r[3], hi1);
+    quad_swap<0xB1>(r[0], r[1], hi0);
+    quad_swap<0xB1>(r[2], r[3], hi0);
+}
 __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
@@ -171,12 +220,18 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
         lvalid[c] = k0[c] < K;
     }
     // lane-constant buffer offsets of the weight and activation loads (past
-    // every range where the lane has no k, so those loads read 0)
-    uint32_t woff[kMoeChunks], xoff[kMoeChunks];
+    // every range where the lane has no k, so those loads read 0: k0[c] < K
+    // holds for all four lanes of a quad alike)
+    uint32_t woff[kMoeChunks], xraw[kMoeChunks];
+    const bool qhi1 = (lane & 2u) != 0, qhi0 = (lane & 1u) != 0;  // quad lane bits
 #pragma unroll
     for (uint32_t c = 0; c < kMoeChunks; ++c) {
         woff[c] = lvalid[c] ? row * half_k + k0[c] / 2u : kOutOfRange;
-        xoff[c] = lvalid[c] ? (row * K + k0[c]) * 2u : kOutOfRange;
+        // activations, load s: quad (lane / 4) % 4 takes token 4 * that + s of
+        // the 16-token block, its lane j the 8 k at k0[c] + 8j (64 bytes per
+        // quad); after the quad transpose, register s of lane l holds token
+        // l % 16 at k0[c] + 8s, the operand layout
+        xraw[c] = ((4u * ((lane >> 2) & 3u)) * K + k0[c] + 8u * (lane & 3u)) * 2u;
     }
     const uint32_t nkt = (K + kMoeKTile - 1u) / kMoeKTile;  // K-tiles
     const uint32_t nwaves1 = min(kMoeWaves, (K + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K (one K-tile)
@@ -265,7 +320,7 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
 #pragma unroll
                     for (uint32_t c = 0; c < kMoeChunks; ++c)
 #pragma unroll
-                        for (uint32_t s = 0; s < kMoeSteps; ++s) xa[b][c][s] = load_b128(rx, xoff[c] + 16u * s);
+                        for (uint32_t s = 0; s < kMoeSteps; ++s) xa[b][c][s] = load_b128(rx, (lvalid[c] ? xraw[c] : kOutOfRange) + 2u * s * K);
                 }
             };
             load_pass(0);
@@ -366,6 +421,10 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                     }
                     if (wave < nwaves1) {
 #pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b)
+#pragma unroll
+                            for (uint32_t c = 0; c < kMoeChunks; ++c) quad_transpose(xa[b][c], qhi1, qhi0);
+#pragma unroll
                         for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
                             v4f32 acc[NB];
 #pragma unroll
@@ -438,13 +497,15 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                                 for (uint32_t c = 0; c < kMoeChunks; ++c)
 #pragma unroll
                                     for (uint32_t s = 0; s < kMoeSteps; ++s)
-                                        xa[b][c][s] = load_b128(rx, lv[c] ? (row * K + kb + k0[c]) * 2u + 16u * s : kOutOfRange);
+                                        xa[b][c][s] = load_b128(rx, lv[c] ? xraw[c] + 2u * kb + 2u * s * K : kOutOfRange);
                             }
                         }
                         const uint32_t nwaves = min(kMoeWaves, (K - kb + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K
                         // the scales of the lane's codes: blocks (kb + k0[c])/16 and
                         // the next (0 past the rows or past K, where the codes read 0)
-                        float sc[kMoeRowBlocks][kMoeChunks][2];
+                        // NVFP4: both scales as float16 patterns of value / 256 in one word
+                        float sc[kMoeRowBlocks][kMoeChunks];
+                        uint32_t scp[kMoeRowBlocks][kMoeChunks];
 #pragma unroll
                         for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
 #pragma unroll
@@ -453,14 +514,18 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                                 const bool valid = lv[c] && r < nrows;
                                 const uint32_t i = valid ? r * C + (kb + k0[c]) / BLOCK : 0u;
                                 if constexpr (MX) {
-                                    sc[rb][c][0] = valid ? ue8m0_as_scale(s_scales[i]) : 0.f;
-                                    sc[rb][c][1] = 0.f;
+                                    sc[rb][c] = valid ? ue8m0_as_scale(s_scales[i]) : 0.f;
+                                    scp[rb][c] = 0u;
                                 } else {
-                                    sc[rb][c][0] = valid ? e4m3_value(s_scales[i]) : 0.f;
-                                    sc[rb][c][1] = valid ? e4m3_value(s_scales[i + 1u]) : 0.f;
+                                    sc[rb][c] = 0.f;
+                                    scp[rb][c] = valid ? e4m3_half(s_scales[i]) | (e4m3_half(s_scales[i + 1u]) << 16) : 0u;
                                 }
                             }
                         if (wave < nwaves) {
+#pragma unroll
+                            for (uint32_t b = 0; b < NB; ++b)
+#pragma unroll
+                                for (uint32_t c = 0; c < kMoeChunks; ++c) quad_transpose(xa[b][c], qhi1, qhi0);
 #pragma unroll
                             for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
                                 v4f32 acc[NB];
@@ -473,7 +538,9 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                                     for (uint32_t s = 0; s < kMoeSteps; ++s) {
                                         // one step at a time: converted ahead, the weights of every
                                         // step would hold their float intermediates at once
-                                        const v8bf16 aw = MX ? dequant8_mx(wd[s], sc[rb][c][0]) : dequant8(wd[s], sc[rb][c][s >> 1]);
+                                        const v8bf16 aw = MX ? dequant8_mx(wd[s], sc[rb][c])
+                                                             : dequant8_h(wd[s], __half2float(__ushort_as_half(
+                                                                   (unsigned short)(scp[rb][c] >> (16u * (s >> 1))))));
 #pragma unroll
                                         for (uint32_t b = 0; b < NB; ++b)
                                             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

@@ -202,12 +202,13 @@ def check_non_finite(inp, got, what):
     return y
 
 
-@pytest.mark.parametrize("K", [160, 2048])
+@pytest.mark.parametrize("K", [160, 2048, 4096])
 def test_non_finite_values_stay_in_their_outputs(orc, dev, K):
     """A NaN scale byte (E4M3 S.1111.111) makes exactly its row's outputs NaN
     for the expert's tokens; an infinite or NaN activation reaches only its own
     token's outputs (K = 160 leaves part of a chunk past K: no lane may read
-    the next token's row there)."""
+    the next token's row there; K = 4096 runs the K-tile path, which keeps its
+    scales as float16 patterns)."""
     es = _routing([5, 6], 11)
     inp = workloads.w4a16_inputs(2, 40, K, es, seed=94 + K, exc_rate=0.05)
     inp.scales[1, 33, 3] = 0x7F                          # expert 1 (tokens 5..10), row 33
@@ -250,18 +251,21 @@ def test_mxfp4_routed_full_shape(orc, dev):
     assert np.array_equal(got_csf, got_dense)
 
 
-def test_mxfp4_scale_extremes_and_nan(orc, dev):
+@pytest.mark.parametrize("K", [160, 5120])
+def test_mxfp4_scale_extremes_and_nan(orc, dev, K):
     """UE8M0 bytes far from 127 scale by their exponent alone (rows whose
     blocks carry 20 and 230, products still inside float32's normal range,
     stay within the bound), and byte 255 (NaN) makes
-    exactly its row's outputs NaN for the expert's tokens."""
+    exactly its row's outputs NaN for the expert's tokens (K = 5120: the
+    K-tile path)."""
     es = _routing([6, 5], 11)
-    inp = workloads.w4a16_inputs(2, 40, 160, es, seed=95, exc_rate=0.05, fmt=workloads.MXFP4)
+    inp = workloads.w4a16_inputs(2, 40, K, es, seed=95, exc_rate=0.05, fmt=workloads.MXFP4)
     inp.scales[0, 3, :] = 20
     inp.scales[0, 4, 1] = 230
-    inp.scales[1, 9, :] = np.array([20, 230, 127, 100, 200], dtype=np.uint8)
+    inp.scales[1, 9, :5] = np.array([20, 230, 127, 100, 200], dtype=np.uint8)
     inp.scales[1, 21, 4] = 0xFF
+    inp.scales[1, 22, K // 32 - 1] = 0xFF                # the last scale column (last K-tile)
     for dense in (False, True):
         got = run(orc, dev, inp, dense=dense)
         y = check_non_finite(inp, got, f"MXFP4 extremes, {'dense' if dense else 'CSF'} scales")
-    assert np.isnan(y[6:11, 21]).all() and np.isfinite(y[:6]).all()
+    assert np.isnan(y[6:11, 21:23]).all() and np.isfinite(y[:6]).all()
