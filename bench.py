@@ -97,7 +97,8 @@ class HipEvents:
 def stack_bytes(stack, active=None):
     """Algorithmic bytes of one decode: (fixed-stream bytes read, exception
     bytes read, dense bytes written).  Exception bytes include the prefix and,
-    for an indexed stack, the tile index.  active: boolean mask of routed
+    for an indexed stack, the tile index (a routed decode reads only the
+    index segments of its routed experts).  active: boolean mask of routed
     experts, or None for all."""
     import numpy as np
     E = stack.E
@@ -110,7 +111,7 @@ def stack_bytes(stack, active=None):
     fixed = n_act * (stack.R + stack.stride)          # bases + offsets
     exc = 4 * entries + 4 * (E + 1)                   # entries + prefix
     if stack.tile_index is not None:
-        exc += 4 * (E * stack.index_tiles + 1)
+        exc += 4 * (E * stack.index_tiles + 1) if active is None else 4 * n_act * (stack.index_tiles + 1)
     dense = n_act * stack.P
     return fixed, exc, dense
 
@@ -121,15 +122,16 @@ _KERNEL_SOURCES = {
 }
 
 
-def source_hash(kernel: str = "csf_fused_kernel") -> str:
+def source_hash(kernel: str = "csf_fused_kernel", csrc: str | None = None) -> str:
     """Fingerprint of the code a kernel is built and launched from (its own
     source plus the shared device helpers, launch structs and host planner):
     comments and whitespace are dropped, so only a change to the code itself
     invalidates that kernel's counter records."""
     import re
     h = hashlib.sha256()
+    csrc = csrc or os.path.join(ROOT, "moe_weight_decode_amd", "csrc")
     for name in _KERNEL_SOURCES[kernel] + ("csf_launch.h", "csf_api.cpp", "csf_device.h"):
-        text = open(os.path.join(ROOT, "moe_weight_decode_amd", "csrc", name)).read()
+        text = open(os.path.join(csrc, name)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
