@@ -227,12 +227,14 @@ __device__ __forceinline__ uint32_t entry_of(uint32_t first, uint32_t i) {
     return first + 4u * ((i / 4u) * kBlock + threadIdx.x) + (i % 4u);
 }
 
-// Issue the loads of unit w (tile positions from q0); l0/h0 are its tile
-// index bounds.  Every load is issued, whatever the tile holds: loads past the
+// Issue the loads of unit w (tile positions from q0); its tile index bounds
+// are lane j of the batch registers blo/bhi, read only after the offset and
+// base loads are issued, so only the entry loads wait for a batch still in
+// flight.  Every load is issued, whatever the tile holds: loads past the
 // expert's offset segment or bases, or past the tile's entries, read 0.
 template <uint32_t RUNS, uint32_t EXC, int POLICY>
 __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, uint32_t q0,
-                                            int32_t l0, int32_t h0, TileLoads<RUNS, EXC> &L) {
+                                            int32_t blo, int32_t bhi, uint32_t j, TileLoads<RUNS, EXC> &L) {
     // Offset groups: run q (positions 16q .. 16q+15) is field q % F of
     // group q / F, F = 8 / w fields per group.
     const rsrc_t seg = make_rsrc(st.offsets + (uint64_t)w.e * st.stride, (uint32_t)st.stride);
@@ -245,11 +247,16 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
     }
     // Row bases of the tile's first 2 * kBlock rows; the resource covers the
     // tile's rows only, so lanes past them read nothing from memory.
-    const uint32_t r_lo = div_exact(q0, st.rcp_cols);
-    const uint32_t r_hi = div_exact(min(q0 + tile_positions(RUNS), st.pend) - 1u, st.rcp_cols) + 1u;
+    const uint32_t r_lo = __builtin_amdgcn_readfirstlane(div_exact(q0, st.rcp_cols));
+    const uint32_t r_hi =
+        __builtin_amdgcn_readfirstlane(div_exact(min(q0 + tile_positions(RUNS), st.pend) - 1u, st.rcp_cols) + 1u);
     const rsrc_t rb = make_rsrc(st.bases + (uint64_t)w.e * st.R + r_lo, r_hi - r_lo);
     L.b0 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)threadIdx.x, 0, 0);
     L.b1 = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(kBlock + threadIdx.x), 0, 0);
+    // the unit's tile-index bounds (lane j of the batch): only the entry loads
+    // below wait for them
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t l0 = __builtin_amdgcn_readlane(blo, j), h0 = __builtin_amdgcn_readlane(bhi, j);
     // Entries from `first` (lo rounded down to a multiple of 4) in 16-byte
     // loads; the resource ends at hi.
     L.hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
@@ -322,8 +329,7 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
     TileLoads<RUNS, EXC> L;
     {
         const StackArgs st = pick(a, cur.s);
-        issue_loads<RUNS, EXC, POLICY>(st, cur, cur.t * TILE, __builtin_amdgcn_readlane(blo, 0),
-                                       __builtin_amdgcn_readlane(bhi, 0), L);
+        issue_loads<RUNS, EXC, POLICY>(st, cur, cur.t * TILE, blo, bhi, 0u, L);
         // As many stores as a tile's store phase, into an empty range (the
         // hardware drops them): the loop is then entered with the same memory
         // operations in flight from here as from its own end, and its waits
@@ -372,19 +378,13 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
         if (more) {
             // Each branch reads its bounds itself, so no later wait covers the
             // batch load.
-            int32_t nl, nh;
             if (++j == kWave) {
                 load_batch(un);
                 j = 0;
-                nl = __builtin_amdgcn_readlane(blo, 0);
-                nh = __builtin_amdgcn_readlane(bhi, 0);
-            } else {
-                nl = __builtin_amdgcn_readlane(blo, j);
-                nh = __builtin_amdgcn_readlane(bhi, j);
             }
             cur = locate<true>(a, un, u0, act, routed);
             // The next unit's loads go out before this tile's stores.
-            issue_loads<RUNS, EXC, POLICY>(pick(a, cur.s), cur, cur.t * TILE, nl, nh, L);
+            issue_loads<RUNS, EXC, POLICY>(pick(a, cur.s), cur, cur.t * TILE, blo, bhi, j, L);
         }
 
         // Tile bytes s0 .. n-1 are stored (s0 > 0 only where a row window
