@@ -42,10 +42,12 @@
 // group), and a 4 x 4 transpose inside the quad across the four step registers
 // (two rounds of DPP quad permutes) moves every piece to its operand lane.  The waves' partial
 // sums meet in LDS and are added in wave order, so the result does not depend
-// on timing.  K above 2048 runs in K-tiles of 2048 (every wave one 256-wide
-// slice of each): the unit's whole scale span is expanded into LDS once, each
-// K-tile loads its codes and activations, and the reduction threads add the
-// K-tiles' wave sums in K order into running sums before the one store.
+// on timing.  K above 2048 runs in K-tiles of 1024 (every wave one 128-wide
+// chunk of each) and passes of 32 tokens: the unit's whole scale span is
+// expanded into LDS once, two register buffers take turns so that K-tile
+// kt + 1's codes and activations load while K-tile kt computes, and every
+// wave accumulates its chunks of all K-tiles, in K order, before the waves'
+// sums meet once per pass.
 #include "csf_device.h"
 
 #include <hip/hip_fp16.h>
@@ -64,8 +66,11 @@ constexpr uint32_t kMoeWaves = 8;       // waves per workgroup
 constexpr uint32_t kMoeThreads = kMoeWaves * kWave;
 constexpr uint32_t kMoeBlocks = 4;      // 16-token MFMA column blocks per pass
 constexpr uint32_t kMoePass = 16 * kMoeBlocks;
+constexpr uint32_t kMoeBlocksM = 2;     // K-tile path: 16-token blocks per pass (two buffers of each)
+constexpr uint32_t kMoePassM = 16 * kMoeBlocksM;
 constexpr uint32_t kMoeSteps = 4;       // MFMA 16x16x32 steps per 128-wide chunk
-constexpr uint32_t kMoeKTile = kMoeWaves * kMoeWaveK;  // K per K-tile: one 256-wide slice per wave
+constexpr uint32_t kMoeKTile = kMoeWaves * kMoeWaveK;  // K of the single-K-tile path: one 256-wide slice per wave
+constexpr uint32_t kMoeKTileM = kMoeWaves * kMoeChunk; // K per K-tile above that: one 128-wide chunk per wave
 constexpr uint32_t kMoeMaxCols = 512;   // scale columns per row: K <= 8192
 constexpr uint32_t kMoeStage = 4096;    // dense-scale bytes read with the unit's first loads (K <= 2048 NVFP4)
 constexpr uint32_t kXcds = 8;           // MI355X: workgroups go round-robin to 8 XCDs
@@ -100,24 +105,6 @@ __device__ __forceinline__ v8bf16 dequant8(uint32_t codes, float scale) {
                      pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), scale),
                      pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), scale),
                      pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), scale)};
-    return __builtin_bit_cast(v8bf16, w);
-}
-
-// An E4M3 scale byte as the float16 bit pattern of its value / 256 (the
-// exponent fields differ in width by one bit and in bias by 8), NaN (S.1111.111)
-// as a float16 NaN: every E4M3 value is exact in float16.
-__device__ __forceinline__ uint32_t e4m3_half(uint32_t b) {
-    const uint32_t sign = (b & 0x80u) << 8;
-    return (b & 0x7fu) == 0x7fu ? (0x7e00u | sign) : (((b & 0x7fu) << 7) | sign);
-}
-
-// dequant8 with the scale given as value / 256: the codes are converted x 256
-// (a power of two, exact), so the products are the same exact values.
-__device__ __forceinline__ v8bf16 dequant8_h(uint32_t codes, float scale256) {
-    const u32x4 w = {pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 0), scale256),
-                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 1), scale256),
-                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 2), scale256),
-                     pack_hi(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 256.0f, 3), scale256)};
     return __builtin_bit_cast(v8bf16, w);
 }
 
@@ -233,7 +220,11 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
         // l % 16 at k0[c] + 8s, the operand layout
         xraw[c] = ((4u * ((lane >> 2) & 3u)) * K + k0[c] + 8u * (lane & 3u)) * 2u;
     }
-    const uint32_t nkt = (K + kMoeKTile - 1u) / kMoeKTile;  // K-tiles
+    // K-tile path: the lane's 32 k of a K-tile, and its lane-constant weight
+    // and activation offsets (as above, one chunk per wave)
+    const uint32_t kwm = wave * kMoeChunk + 32u * kq;
+    const uint32_t woffm = row * half_k + kwm / 2u;
+    const uint32_t xrawm = ((4u * ((lane >> 2) & 3u)) * K + kwm + 8u * (lane & 3u)) * 2u;
     const uint32_t nwaves1 = min(kMoeWaves, (K + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K (one K-tile)
     const uint64_t plane = (uint64_t)a.N * C;
 
@@ -300,16 +291,9 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
             // every load is then a lane-constant offset plus an immediate.
             // 32 codes of row rb*16 + row at k0[c] (rows past the unit's and
             // k past K read 0)
+            // single K-tile: chunk c of the wave's slice in wa[.][c], xa[.][c];
+            // K-tile path: K-tiles in the two buffers c = 0, 1 (double buffering)
             u32x4 wa[kMoeRowBlocks][kMoeChunks];
-#pragma unroll
-            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
-                const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
-                const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
-#pragma unroll
-                for (uint32_t c = 0; c < kMoeChunks; ++c) wa[rb][c] = load_b128(rw, woff[c]);
-            }
-            // 32 activations of token tb + b*16 + row at k0[c] (tokens past
-            // the expert's read 0)
             u32x4 xa[NB][kMoeChunks][kMoeSteps];
             auto load_pass = [&](uint32_t tb) {
 #pragma unroll
@@ -323,7 +307,41 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                         for (uint32_t s = 0; s < kMoeSteps; ++s) xa[b][c][s] = load_b128(rx, (lvalid[c] ? xraw[c] : kOutOfRange) + 2u * s * K);
                 }
             };
-            load_pass(0);
+            // K-tile path: codes and activations of K-tile kt, pass tb, into buffer CB
+            auto load_kt = [&](uint32_t tb, uint32_t kt, auto cbuf) {
+                constexpr uint32_t CB = decltype(cbuf)::value;
+                const uint32_t kb = kt * kMoeKTileM;
+                const bool v = kb + kwm < K;  // alike for the four lanes of a quad
+#pragma unroll
+                for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                    const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
+                    const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
+                    wa[rb][CB] = load_b128(rw, v ? woffm + kb / 2u : kOutOfRange);
+                }
+#pragma unroll
+                for (uint32_t b = 0; b < NB; ++b) {
+                    const uint32_t t = tb + b * 16u;
+                    const uint32_t toks = m > t ? min(16u, m - t) : 0u;
+                    const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + t) * K, toks * K * 2u);
+#pragma unroll
+                    for (uint32_t s = 0; s < kMoeSteps; ++s)
+                        xa[b][CB][s] = load_b128(rx, v ? xrawm + 2u * kb + 2u * s * K : kOutOfRange);
+                }
+            };
+            if constexpr (MULTI) {
+                load_kt(0u, 0u, std::integral_constant<uint32_t, 0>{});
+            } else {
+                // 32 codes of row rb*16 + row at k0[c] (rows past the unit's
+                // and k past K read 0), then the first pass's activations
+#pragma unroll
+                for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                    const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
+                    const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
+#pragma unroll
+                    for (uint32_t c = 0; c < kMoeChunks; ++c) wa[rb][c] = load_b128(rw, woff[c]);
+                }
+                load_pass(0);
+            }
             // every load above is issued before the first wait below
             __builtin_amdgcn_sched_barrier(0);
 
@@ -467,108 +485,79 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
                     }
                 }
             } else {
-                for (uint32_t tb = 0; tb < m; tb += kMoePass) {
-                    // Running sums of the outputs a reduction thread owns (one
-                    // 4-row vector of one 16 x 16 block), over the K-tiles in order.
-                    v4f32 total = {0.f, 0.f, 0.f, 0.f};
-                    for (uint32_t kt = 0; kt < nkt; ++kt) {
-                        const uint32_t kb = kt * kMoeKTile;
-                        bool lv[kMoeChunks];
-#pragma unroll
-                        for (uint32_t c = 0; c < kMoeChunks; ++c) lv[c] = kb + k0[c] < K;
-                        if (tb > 0 || kt > 0) {
-                            __syncthreads();  // the previous partial sums are read
-                            // this K-tile's codes and activations (the first K-tile's
-                            // first pass came with the unit's first loads)
-#pragma unroll
-                            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
-                                const uint32_t rows = nrows > rb * 16u ? min(16u, nrows - rb * 16u) : 0u;
-                                const rsrc_t rw = make_rsrc(a.w + ((uint64_t)e * a.N + n0 + rb * 16u) * half_k, rows * half_k);
-#pragma unroll
-                                for (uint32_t c = 0; c < kMoeChunks; ++c)
-                                    wa[rb][c] = load_b128(rw, lv[c] ? row * half_k + (kb + k0[c]) / 2u : kOutOfRange);
-                            }
-#pragma unroll
-                            for (uint32_t b = 0; b < NB; ++b) {
-                                const uint32_t t = tb + b * 16u;
-                                const uint32_t toks = m > t ? min(16u, m - t) : 0u;
-                                const rsrc_t rx = make_rsrc(a.x + (uint64_t)(t0 + t) * K, toks * K * 2u);
-#pragma unroll
-                                for (uint32_t c = 0; c < kMoeChunks; ++c)
-#pragma unroll
-                                    for (uint32_t s = 0; s < kMoeSteps; ++s)
-                                        xa[b][c][s] = load_b128(rx, lv[c] ? xraw[c] + 2u * kb + 2u * s * K : kOutOfRange);
-                            }
-                        }
-                        const uint32_t nwaves = min(kMoeWaves, (K - kb + kMoeWaveK - 1u) / kMoeWaveK);  // waves with some K
-                        // the scales of the lane's codes: blocks (kb + k0[c])/16 and
-                        // the next (0 past the rows or past K, where the codes read 0)
-                        // NVFP4: both scales as float16 patterns of value / 256 in one word
-                        float sc[kMoeRowBlocks][kMoeChunks];
-                        uint32_t scp[kMoeRowBlocks][kMoeChunks];
-#pragma unroll
-                        for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
-#pragma unroll
-                            for (uint32_t c = 0; c < kMoeChunks; ++c) {
-                                const uint32_t r = rb * 16u + row;
-                                const bool valid = lv[c] && r < nrows;
-                                const uint32_t i = valid ? r * C + (kb + k0[c]) / BLOCK : 0u;
-                                if constexpr (MX) {
-                                    sc[rb][c] = valid ? ue8m0_as_scale(s_scales[i]) : 0.f;
-                                    scp[rb][c] = 0u;
-                                } else {
-                                    sc[rb][c] = 0.f;
-                                    scp[rb][c] = valid ? e4m3_half(s_scales[i]) | (e4m3_half(s_scales[i + 1u]) << 16) : 0u;
-                                }
-                            }
-                        if (wave < nwaves) {
-#pragma unroll
-                            for (uint32_t b = 0; b < NB; ++b)
-#pragma unroll
-                                for (uint32_t c = 0; c < kMoeChunks; ++c) quad_transpose(xa[b][c], qhi1, qhi0);
-#pragma unroll
-                            for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
-                                v4f32 acc[NB];
-#pragma unroll
-                                for (uint32_t b = 0; b < NB; ++b) acc[b] = (v4f32){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                                for (uint32_t c = 0; c < kMoeChunks; ++c) {
-                                    const uint32_t wd[4] = {wa[rb][c].x, wa[rb][c].y, wa[rb][c].z, wa[rb][c].w};
-#pragma unroll
-                                    for (uint32_t s = 0; s < kMoeSteps; ++s) {
-                                        // one step at a time: converted ahead, the weights of every
-                                        // step would hold their float intermediates at once
-                                        const v8bf16 aw = MX ? dequant8_mx(wd[s], sc[rb][c])
-                                                             : dequant8_h(wd[s], __half2float(__ushort_as_half(
-                                                                   (unsigned short)(scp[rb][c] >> (16u * (s >> 1))))));
-#pragma unroll
-                                        for (uint32_t b = 0; b < NB; ++b)
-                                            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                                aw, __builtin_bit_cast(v8bf16, xa[b][c][s]), acc[b], 0, 0, 0);
-                                        __builtin_amdgcn_sched_barrier(0);
-                                    }
-                                }
-#pragma unroll
-                                for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[b];
-                            }
-                        }
-                        __syncthreads();
-                        // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
-                        // of its 16 x 16 block: one thread per such 4-row vector adds
-                        // the waves' vectors in wave order to its running sums.
-                        if (tid < kMoeRowBlocks * NB * kWave) {
-                            const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
-                            v4f32 r = s_part[0][rb][b][l];
-                            for (uint32_t w = 1; w < nwaves; ++w) r += s_part[w][rb][b][l];
-                            total += r;
-                        }
+                // K-tiles of kMoeKTileM, double-buffered: K-tile kt + 1 is
+                // loaded while K-tile kt computes, and every wave accumulates
+                // its chunks of all K-tiles in registers, in K order, so the
+                // waves' sums meet once per pass.
+                const uint32_t nktm = (K + kMoeKTileM - 1u) / kMoeKTileM;
+                for (uint32_t tb = 0; tb < m; tb += kMoePassM) {
+                    if (tb > 0) {
+                        __syncthreads();  // the previous pass's partial sums are read
+                        load_kt(tb, 0u, std::integral_constant<uint32_t, 0>{});
                     }
+                    v4f32 acc[kMoeRowBlocks][NB];
+#pragma unroll
+                    for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
+#pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b) acc[rb][b] = (v4f32){0.f, 0.f, 0.f, 0.f};
+                    auto compute = [&](uint32_t kt, auto cbuf) {
+                        constexpr uint32_t CB = decltype(cbuf)::value;
+                        const uint32_t kb = kt * kMoeKTileM;
+                        if (kb + wave * kMoeChunk >= K) return;  // the wave has no K in this K-tile
+#pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b) quad_transpose(xa[b][CB], qhi1, qhi0);
+#pragma unroll
+                        for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb) {
+                            // the scales of the lane's 32 codes (0 past the rows or
+                            // past K, where the codes read 0)
+                            const uint32_t r = rb * 16u + row;
+                            const bool valid = kb + kwm < K && r < nrows;
+                            const uint32_t i = valid ? r * C + (kb + kwm) / BLOCK : 0u;
+                            float s0, s1;
+                            if constexpr (MX) {
+                                s0 = valid ? ue8m0_as_scale(s_scales[i]) : 0.f;
+                                s1 = s0;
+                            } else {
+                                s0 = valid ? e4m3_value(s_scales[i]) : 0.f;
+                                s1 = valid ? e4m3_value(s_scales[i + 1u]) : 0.f;
+                            }
+                            const uint32_t wd[4] = {wa[rb][CB].x, wa[rb][CB].y, wa[rb][CB].z, wa[rb][CB].w};
+#pragma unroll
+                            for (uint32_t s = 0; s < kMoeSteps; ++s) {
+                                const v8bf16 aw = MX ? dequant8_mx(wd[s], s0) : dequant8(wd[s], s < 2u ? s0 : s1);
+#pragma unroll
+                                for (uint32_t b = 0; b < NB; ++b)
+                                    acc[rb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        aw, __builtin_bit_cast(v8bf16, xa[b][CB][s]), acc[rb][b], 0, 0, 0);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                    };
+                    for (uint32_t kt = 0; kt < nktm; kt += 2u) {
+                        if (kt + 1u < nktm) load_kt(tb, kt + 1u, std::integral_constant<uint32_t, 1>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                        compute(kt, std::integral_constant<uint32_t, 0>{});
+                        if (kt + 1u >= nktm) break;
+                        if (kt + 2u < nktm) load_kt(tb, kt + 2u, std::integral_constant<uint32_t, 0>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                        compute(kt + 1u, std::integral_constant<uint32_t, 1>{});
+                    }
+#pragma unroll
+                    for (uint32_t rb = 0; rb < kMoeRowBlocks; ++rb)
+#pragma unroll
+                        for (uint32_t b = 0; b < NB; ++b) s_part[wave][rb][b][lane] = acc[rb][b];
+                    __syncthreads();
+                    // Lane l of a wave holds rows 4*(l/16) .. +3 of token l % 16
+                    // of its 16 x 16 block: one thread per such 4-row vector adds
+                    // the waves' vectors in wave order and writes 4 outputs.
                     if (tid < kMoeRowBlocks * NB * kWave) {
                         const uint32_t l = tid % kWave, b = (tid / kWave) % NB, rb = tid / (kWave * NB);
+                        v4f32 r = s_part[0][rb][b][l];
+                        for (uint32_t w = 1; w < kMoeWaves; ++w) r += s_part[w][rb][b][l];
                         const uint32_t t = tb + b * 16u + l % 16u, nn = rb * 16u + 4u * (l / 16u);
                         if (t < m) {
                             float *dst = a.y + (uint64_t)(t0 + t) * a.N + n0 + nn;
-                            const float rr[4] = {total.x, total.y, total.z, total.w};
+                            const float rr[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
                             for (uint32_t c = 0; c < 4; ++c)
                                 if (nn + c < nrows) dst[c] = rr[c] * alpha;
@@ -580,12 +569,20 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
         // The next unit's first LDS writes (row bases, scale bytes) touch
         // nothing the reduction reads, and its partial sums are written only
         // after a barrier every wave passes once its reduction is done.
-        switch ((m + 15u) / 16u) {
-            case 0: break;
-            case 1: unit(std::integral_constant<uint32_t, 1>{}); break;
-            case 2: unit(std::integral_constant<uint32_t, 2>{}); break;
-            case 3: unit(std::integral_constant<uint32_t, 3>{}); break;
-            default: unit(std::integral_constant<uint32_t, 4>{}); break;
+        if constexpr (MULTI) {
+            switch ((m + 15u) / 16u) {
+                case 0: break;
+                case 1: unit(std::integral_constant<uint32_t, 1>{}); break;
+                default: unit(std::integral_constant<uint32_t, kMoeBlocksM>{}); break;
+            }
+        } else {
+            switch ((m + 15u) / 16u) {
+                case 0: break;
+                case 1: unit(std::integral_constant<uint32_t, 1>{}); break;
+                case 2: unit(std::integral_constant<uint32_t, 2>{}); break;
+                case 3: unit(std::integral_constant<uint32_t, 3>{}); break;
+                default: unit(std::integral_constant<uint32_t, 4>{}); break;
+            }
         }
     }
 }
