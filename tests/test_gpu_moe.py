@@ -269,3 +269,21 @@ def test_mxfp4_scale_extremes_and_nan(orc, dev, K):
         got = run(orc, dev, inp, dense=dense)
         y = check_non_finite(inp, got, f"MXFP4 extremes, {'dense' if dense else 'CSF'} scales")
     assert np.isnan(y[6:11, 21:23]).all() and np.isfinite(y[:6]).all()
+
+
+@pytest.mark.parametrize("fmt,K", [(workloads.NVFP4, 256), (workloads.MXFP4, 5120)])
+def test_no_routed_tokens_writes_nothing(orc, dev, fmt, K):
+    """expert_start with no expert holding a token (all equal), and one whose
+    ranges all lie past num_tokens: the call writes no output."""
+    E, N, T = 5, 48, 12
+    inp = workloads.w4a16_inputs(E, N, K, _routing([3, 0, 9, 0, 0], T), seed=96, fmt=fmt)
+    stack = mwd.from_numpy(orc.encode(fmt, inp.scales), dev)
+    w = torch.from_numpy(inp.w_packed).to(dev)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev)
+    alpha = torch.from_numpy(inp.alpha).to(dev)
+    for es in (np.full(E + 1, 7, dtype=np.int32),                      # no expert has tokens
+               np.array([T, T, T + 5, T + 9, T + 9, T + 9], dtype=np.int32)):  # all past num_tokens
+        y = torch.full((T, N), float("nan"), dtype=torch.float32, device=dev)
+        mwd.moe_w4a16(stack, w, x, alpha, torch.from_numpy(es).to(dev), out=y)
+        torch.cuda.synchronize()
+        assert torch.isnan(y).all()
