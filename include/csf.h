@@ -64,7 +64,8 @@ typedef enum csf_status {
     CSF_E_NULL = 1,     /* a required pointer is NULL */
     CSF_E_SHAPE = 2,    /* E, R or C <= 0, R*C >= 2^24, or E > CSF_MAX_EXPERTS */
     CSF_E_FORMAT = 3,   /* unknown format */
-    CSF_E_SIZE = 4,     /* stride or exception count inconsistent with the shape */
+    CSF_E_SIZE = 4,     /* stride or exception count inconsistent with the shape (stride below
+                           16 * ceil(R * C / G), not a multiple of 16, or not below 2^31) */
     CSF_E_ALIGN = 5,    /* offsets not 16-byte aligned, or exceptions/prefix not 4-byte aligned */
     CSF_E_CORRUPT = 6,  /* csf_validate: the stream breaks the layout */
     CSF_E_MISMATCH = 7, /* paired stacks have different expert counts */

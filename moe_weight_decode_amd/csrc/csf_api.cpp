@@ -90,7 +90,10 @@ csf_status check_stack(const csf_stack *s, const uint8_t *ws) {
     if (s->bases == nullptr || s->offsets == nullptr || s->exc_prefix == nullptr) return CSF_E_NULL;
     if (s->num_exceptions < 0 || s->num_exceptions >= (int64_t(1) << 31)) return CSF_E_SIZE;
     if (s->num_exceptions > 0 && s->exceptions == nullptr) return CSF_E_NULL;
-    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0)
+    // at least the plane's offset groups, 16-byte steps, and below 2^31 (an
+    // expert segment is addressed by 32-bit buffer offsets)
+    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0 ||
+        s->offsets_stride >= (int64_t(1) << 31))
         return CSF_E_SIZE;
     if (!aligned(s->offsets, 16) || !aligned(s->exc_prefix, 4)) return CSF_E_ALIGN;
     if (s->num_exceptions > 0 && !aligned(s->exceptions, 4)) return CSF_E_ALIGN;
@@ -531,8 +534,9 @@ csf_status validate_impl(const csf_stack *s) {
     if (s->bases == nullptr || s->offsets == nullptr || s->exc_prefix == nullptr) return CSF_E_NULL;
     if (s->num_exceptions < 0) return CSF_E_SIZE;
     if (s->num_exceptions > 0 && s->exceptions == nullptr) return CSF_E_NULL;
-    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0)
-        return CSF_E_SIZE;
+    if (s->offsets_stride < min_stride(s->format, s->rows, s->cols) || s->offsets_stride % 16 != 0 ||
+        s->offsets_stride >= (int64_t(1) << 31))
+        return CSF_E_SIZE;  // as the decoder's check
     const int w = offset_bits(s->format);
     const unsigned W = 1u << w;
     const int64_t G = 128 / w;

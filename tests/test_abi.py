@@ -171,6 +171,7 @@ DECODE_ERRORS = [
     ("too_many_experts", _fake(E=4096), 0x5000, "CSF_E_SHAPE"),
     ("short_stride", _fake(stride=240), 0x5000, "CSF_E_SIZE"),
     ("odd_stride", _fake(stride=264), 0x5000, "CSF_E_SIZE"),
+    ("huge_stride", _fake(stride=1 << 31), 0x5000, "CSF_E_SIZE"),
     ("negative_entries", _fake(n=-1), 0x5000, "CSF_E_SIZE"),
     ("misaligned_offsets", _fake(offsets=0x2008), 0x5000, "CSF_E_ALIGN"),
     ("misaligned_prefix", _fake(prefix=0x4002), 0x5000, "CSF_E_ALIGN"),
