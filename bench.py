@@ -316,9 +316,11 @@ def routed_sets(workloads, E, n_active, max_tokens, seed, count):
     return out
 
 
-def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, copies=2, routings=64):
-    """Paired gate + down decode of 8 routed experts.  Checks the configured
-    routing first.  Then times graph replays (no per-launch CPU cost) of
+def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, copies=2, routings=64,
+                 gate_only=False):
+    """Paired gate + down decode of 8 routed experts (with gate_only, the gate
+    stack alone: the pages' routed figure).  Checks the configured routing
+    first.  Then times graph replays (no per-launch CPU cost) of
     `copies` device copies of both stacks x `routings` disjoint routings, so
     consecutive steps touch different planes, and of the configured routing
     alone (warm)."""
@@ -351,10 +353,14 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
             wdc = torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)
             for r in rs:
                 rt = torch.from_numpy(r).to(dev)
-                calls.append(mwd.Launch(gc, wgc, dc, wdc, rt))
                 act = np.diff(r) > 0
-                nbytes.append(sum(sum(stack_bytes(s, act)) for s in (gc, dc)) + 4 * len(r))
-        warm = [mwd.Launch(g, wg, d, wd, es_t)] * len(calls)
+                if gate_only:
+                    calls.append(mwd.Launch(gc, wgc, expert_start=rt))
+                    nbytes.append(sum(stack_bytes(gc, act)) + 4 * len(r))
+                else:
+                    calls.append(mwd.Launch(gc, wgc, dc, wdc, rt))
+                    nbytes.append(sum(sum(stack_bytes(s, act)) for s in (gc, dc)) + 4 * len(r))
+        warm = [mwd.Launch(g, wg, expert_start=es_t) if gate_only else mwd.Launch(g, wg, d, wd, es_t)] * len(calls)
         for L in calls + warm:  # warm the launch path outside capture
             L()
     torch.cuda.current_stream(dev).wait_stream(side)
@@ -380,9 +386,10 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
     reps = max(1, steps // len(calls))
     wall, evt = timed_loop(torch, ev, [Replay(graphs[0])], reps, max(1, warmup // len(calls)))
     wwall, wevt = timed_loop(torch, ev, [Replay(graphs[1])], reps, max(1, warmup // len(calls)))
-    flushed = flushed_call_ms(torch, ev, mwd.Launch(g, wg, d, wd, es_t), dev)
+    single = mwd.Launch(g, wg, expert_start=es_t) if gate_only else mwd.Launch(g, wg, d, wd, es_t)
+    flushed = flushed_call_ms(torch, ev, single, dev)
     n = len(calls)
-    b = [stack_bytes(s, active) for s in (g, d)]
+    b = [stack_bytes(s, active) for s in ((g,) if gate_only else (g, d))]
     return dict(step_ms=max(wall, evt) / n, event_ms=evt / n, wall_ms=wall / n,
                 bytes=sum(nbytes) / len(nbytes), warm_ms=max(wwall, wevt) / n,
                 warm_bytes=sum(sum(x) for x in b) + 4 * len(es), active=int(active.sum()), flushed_ms=flushed,
@@ -719,10 +726,11 @@ def main():
             log(f"[bench] {name}: {extra[name]}")
             del rr, xd
             torch.cuda.empty_cache()
-        for indexed in (True, False):
-            key = "routed_paired" + ("" if indexed else "_two_pass")
+        for indexed, gate_only in ((True, False), (False, False), (True, True)):
+            key = ("routed_gate" if gate_only else "routed_paired") + ("" if indexed else "_two_pass")
             log(f"[bench] {key}")
-            rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed)
+            rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed,
+                              gate_only=gate_only)
             extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2),
                               gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
                               warm_us=round(rr["warm_ms"] * 1e3, 2), flushed_us=round(rr["flushed_ms"] * 1e3, 2),
