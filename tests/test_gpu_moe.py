@@ -74,7 +74,9 @@ def check(inp, got, what):
     (2, 40, 2080, [17, 5]),
     (2, 33, 4096, [1, 50]),
     (2, 48, 7168, [70, 3]),
-], ids=["mixed_counts", "ragged_rows", "k2048", "tiny", "k160_rows70", "k2080", "k4096", "k7168_two_passes"])
+    (2, 40, 8192, [33, 20]),
+], ids=["mixed_counts", "ragged_rows", "k2048", "tiny", "k160_rows70", "k2080", "k4096", "k7168_two_passes",
+        "k8192_max"])
 def test_small_shapes(orc, dev, E, N, K, counts):
     es = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     inp = workloads.w4a16_inputs(E, N, K, es, seed=E * 100 + N, exc_rate=0.08)
