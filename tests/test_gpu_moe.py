@@ -289,3 +289,30 @@ def test_no_routed_tokens_writes_nothing(orc, dev, fmt, K):
         mwd.moe_w4a16(stack, w, x, alpha, torch.from_numpy(es).to(dev), out=y)
         torch.cuda.synchronize()
         assert torch.isnan(y).all()
+
+
+def test_ahead_of_call_expansion_on_a_side_stream(orc, dev):
+    """The pages' ahead-of-call flow: the routed experts' scales are expanded
+    into a dense workspace on a side stream, and the projection on the main
+    stream waits for that stream's event before reading them.  Equal, bit for
+    bit, to the projection that expands its scales in LDS."""
+    es = _routing([0, 21, 0, 40, 3, 0], 64)
+    inp = workloads.w4a16_inputs(6, 72, 1024, es, seed=97, exc_rate=0.06)
+    stack = mwd.from_numpy(orc.encode(workloads.NVFP4, inp.scales), dev)
+    w = torch.from_numpy(inp.w_packed).to(dev)
+    x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev)
+    alpha = torch.from_numpy(inp.alpha).to(dev)
+    es_t = torch.from_numpy(es).to(dev)
+    stage = mwd.moe_w4a16(stack, w, x, alpha, es_t)
+    ws = torch.full((stack.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        mwd.decode(stack, ws, es_t)
+        expanded = torch.cuda.Event()
+        expanded.record(side)
+    torch.cuda.current_stream(dev).wait_event(expanded)
+    y = mwd.moe_w4a16(stack, w, x, alpha, es_t, dense_scales=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, stage)
+    check(inp, y.cpu().numpy(), "ahead-of-call expansion")
