@@ -66,7 +66,9 @@ typedef enum csf_status {
     CSF_E_FORMAT = 3,   /* unknown format */
     CSF_E_SIZE = 4,     /* stride or exception count inconsistent with the shape (stride below
                            16 * ceil(R * C / G), not a multiple of 16, or not below 2^31) */
-    CSF_E_ALIGN = 5,    /* offsets not 16-byte aligned, or exceptions/prefix not 4-byte aligned */
+    CSF_E_ALIGN = 5,    /* a buffer below its alignment: offsets and W4A16 weights 16 bytes;
+                           exceptions, prefix, tile index, x, alpha, y 4; expert_start its element
+                           size; dense NVFP4 scales of the W4A16 projection 2 */
     CSF_E_CORRUPT = 6,  /* csf_validate: the stream breaks the layout */
     CSF_E_MISMATCH = 7, /* paired stacks have different expert counts */
     CSF_E_HIP = 8       /* the HIP runtime refused a launch */
@@ -269,11 +271,13 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
  *   device buffers.  With dense_scales NULL each workgroup expands the scales
  *   of its 32 rows straight into LDS from the CSF streams (needs the tile
  *   index); otherwise the scales are read from dense_scales, u8[E][N][K/B]
- *   (for example a csf_decode workspace) and the CSF streams are not read.
+ *   (for example a csf_decode workspace; 2-byte aligned for NVFP4) and the
+ *   CSF streams are not read.
  * weights: u8[E][N][K/2], two E2M1 codes per byte, code k of row n in the low
  *   nibble of byte k/2 for even k, the high nibble for odd k; 16-byte aligned.
  * x: bfloat16 [num_tokens][K], tokens sorted by expert (the grouped routing).
- * alpha: float32 [E].  expert_start: int32 [E + 1] on the device; token
+ * alpha: float32 [E].  x, alpha, expert_start and y are 4-byte aligned.
+ * expert_start: int32 [E + 1] on the device; token
  *   indices are clamped to [0, num_tokens].  y: float32 [num_tokens][N]; rows
  *   of tokens outside every expert's range are not written.
  * MXFP4 weights are widened to bfloat16 with their scale applied: exact for
@@ -299,8 +303,10 @@ csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, c
  * strictly within each expert and stay inside the plane; no entry byte lies in
  * its row's offset window; offset fields past the plane and at exception
  * positions are zero, and no field makes base + field exceed 255; the tile
- * index, when present, equals the one the entries define.  Returns CSF_E_CORRUPT on a violation.  Not called by the
- * decoder, which never reads device memory from the host.
+ * index, when present, equals the one the entries define.  The prefix is
+ * checked whole before any entry is read, so a corrupt prefix never sends a
+ * read past entry num_exceptions - 1.  Returns CSF_E_CORRUPT on a violation.
+ * Not called by the decoder, which never reads device memory from the host.
  */
 csf_status csf_validate(const csf_stack *host_copy);
 

@@ -281,8 +281,9 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
     if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;
     if (dense == nullptr && scales->tile_index == nullptr) return CSF_E_NULL;
+    // dense NVFP4 scales are read two bytes at a time (C = K/16 is even)
     if (!aligned(weights, 16) || (x && !aligned(x, 4)) || !aligned(alpha, 4) || !aligned(expert_start, 4) ||
-        !aligned(y, 4))
+        !aligned(y, 4) || (dense && !mx && !aligned(dense, 2)))
         return CSF_E_ALIGN;
     if (num_tokens == 0) return CSF_OK;
 
@@ -541,11 +542,14 @@ csf_status validate_impl(const csf_stack *s) {
     const unsigned W = 1u << w;
     const int64_t G = 128 / w;
     const int64_t R = s->rows, C = s->cols, P = R * C, S = s->offsets_stride;
+    // The whole prefix before any entry: 0, non-decreasing, num_exceptions at
+    // the end, so every expert's entry range lies inside the entry array.
     const int32_t *pf = s->exc_prefix;
     if (pf[0] != 0 || pf[s->num_experts] != s->num_exceptions) return CSF_E_CORRUPT;
+    for (int32_t e = 0; e < s->num_experts; ++e)
+        if (pf[e + 1] < pf[e]) return CSF_E_CORRUPT;
     std::vector<uint8_t> is_exc(static_cast<size_t>(P));
     for (int32_t e = 0; e < s->num_experts; ++e) {
-        if (pf[e + 1] < pf[e]) return CSF_E_CORRUPT;
         const uint8_t *base = s->bases + int64_t(e) * R;
         const uint8_t *seg = s->offsets + int64_t(e) * S;
         std::fill(is_exc.begin(), is_exc.end(), 0);
@@ -595,7 +599,9 @@ const char *csf_status_str(csf_status s) {
         case CSF_E_SHAPE: return "bad shape (E, R, C must be positive, R*C < 2^24, E <= CSF_MAX_EXPERTS)";
         case CSF_E_FORMAT: return "unknown format";
         case CSF_E_SIZE: return "stride, exception count or pass selection inconsistent";
-        case CSF_E_ALIGN: return "misaligned buffer (offsets need 16 bytes, exceptions/prefix/index 4, expert_start its element size)";
+        case CSF_E_ALIGN:
+            return "misaligned buffer (offsets and weights need 16 bytes; exceptions, prefix, index, x, alpha, y 4; "
+                   "expert_start its element size; dense NVFP4 scales 2)";
         case CSF_E_CORRUPT: return "compressed stream breaks the layout";
         case CSF_E_MISMATCH: return "paired stacks have different expert counts";
         case CSF_E_HIP: return "HIP runtime refused the launch";

@@ -131,6 +131,35 @@ def test_validate_rejects_corruption(what):
     assert ei.value.name == "CSF_E_CORRUPT"
 
 
+def test_validate_checks_prefix_before_entries():
+    """A prefix that overshoots the entry count is rejected before any entry is
+    read.  The entries sit at the end of a readable page followed by an
+    inaccessible one, so a read past the last entry would fault the process."""
+    import mmap
+    x = np.full((2, 4, 8), 0x40, dtype=np.uint8)   # expert 0: no entries
+    x[1, 0, 1] = x[1, 1, 3] = x[1, 2, 0] = x[1, 3, 5] = x[1, 3, 7] = 0x00   # expert 1: five
+    st = mwd.prepare(x, workloads.NVFP4)
+    mwd.validate(st)
+    n = st.num_exceptions
+    exc = np.ascontiguousarray(st.exceptions.numpy().view(np.uint32)[:n])
+    assert n == 5 and list(st.prefix.numpy()) == [0, 0, 5]
+    page = mmap.PAGESIZE
+    buf = mmap.mmap(-1, 2 * page)
+    base = ctypes.addressof(ctypes.c_char.from_buffer(buf))
+    libc = ctypes.CDLL(None, use_errno=True)
+    libc.mprotect.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    at = base + page - 4 * n
+    ctypes.memmove(at, exc.ctypes.data, 4 * n)
+    assert libc.mprotect(base + page, page, 0) == 0   # PROT_NONE
+    try:
+        st.prefix[1] = n + 1000
+        d = st.descriptor()
+        d.exceptions = at
+        assert mwd.STATUS[mwd.library().csf_validate(ctypes.byref(d))] == "CSF_E_CORRUPT"
+    finally:
+        assert libc.mprotect(base + page, page, 3) == 0   # PROT_READ | PROT_WRITE
+
+
 def test_validate_rejects_fields_past_plane():
     x = workloads.uniform_bytes(1, 5, 7, 3)  # P = 35: second group holds positions 32..63
     st = mwd.prepare(x, workloads.NVFP4)
@@ -248,6 +277,9 @@ def test_moe_w4a16_errors(lib):
     assert call(ok, T=-1) == "CSF_E_SIZE"
     assert call(ok, w=0x10008) == "CSF_E_ALIGN"
     assert call(ok, y=0x50002) == "CSF_E_ALIGN"
+    assert call(ok, T=0, x=None, dense=0x60001) == "CSF_E_ALIGN"          # NVFP4 dense scales: 2 bytes
+    mx = _fake(fmt=1, R=32, C=5, stride=16 * 2, tile_index=0x8000)      # MXFP4, K = 160, C odd
+    assert call(mx, T=0, x=None, dense=0x60001) == "CSF_OK"               # MXFP4 dense scales: bytes
     assert call(None) == "CSF_E_NULL"
     assert call(ok, T=0, x=None) == "CSF_OK"                              # nothing to do, nothing launched
 
