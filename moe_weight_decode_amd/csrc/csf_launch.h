@@ -84,7 +84,7 @@ struct MoeArgs {
     const float *alpha;            // per-expert tensor scale [E]
     const int32_t *expert_start;   // [E + 1]
     float *y;                      // [T][N]
-    uint32_t E, N, K, C, T;        // C = K / 16
+    uint32_t E, N, K, C, T;        // C = K / 16 (NVFP4) or K / 32 (MXFP4)
     uint32_t ntiles;               // ceil(N / 32) work units per routed expert
     uint32_t bases_stage;          // dynamic LDS bytes for one unit's row bases
     uint32_t pad_;
