@@ -302,17 +302,26 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _check_stack_tensors(stack: CompressedStack, name: str):
+    """Every buffer of the stack holds at least what the layout addresses: the
+    library sees only pointers, so a short tensor would be read past its end."""
+    need = [("bases", stack.bases, torch.uint8, stack.E * stack.R),
+            ("offsets", stack.offsets, torch.uint8, stack.E * stack.stride),
+            ("exceptions", stack.exceptions, torch.int32, max(stack.num_exceptions, 1)),
+            ("prefix", stack.prefix, torch.int32, stack.E + 1)]
+    if stack.tile_index is not None:
+        need.append(("tile_index", stack.tile_index, torch.int32, stack.E * stack.index_tiles + 1))
+    for what, t, dt, n in need:
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or t.numel() < n:
+            raise ValueError(f"{name}: {what} must be a {dt} tensor of at least {n} elements")
+        if t.device != stack.device or not t.is_contiguous():
+            raise ValueError(f"{name}: stack tensors must be contiguous on one device")
+
+
 def _check_device(stack: CompressedStack, ws: torch.Tensor, name: str):
     if stack.device.type != "cuda":
         raise ValueError(f"{name}: compressed stack must be on a GPU")
-    tensors = [stack.bases, stack.offsets, stack.exceptions, stack.prefix]
-    if stack.tile_index is not None:
-        tensors.append(stack.tile_index)
-        if stack.tile_index.numel() != stack.E * stack.index_tiles + 1 or stack.tile_index.dtype != torch.int32:
-            raise ValueError(f"{name}: tile_index must be int32[{stack.E * stack.index_tiles + 1}]")
-    for t in tensors:
-        if t.device != stack.device or not t.is_contiguous():
-            raise ValueError(f"{name}: stack tensors must be contiguous on one device")
+    _check_stack_tensors(stack, name)
     if not isinstance(ws, torch.Tensor) or ws.device != stack.device or ws.dtype != torch.uint8:
         raise ValueError(f"{name}: workspace must be a uint8 tensor on {stack.device}")
     if not ws.is_contiguous() or ws.numel() < stack.dense_bytes:
@@ -411,6 +420,7 @@ def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, a
     dev = scales.device
     if dev.type != "cuda":
         raise ValueError("moe_w4a16: compressed stack must be on a GPU")
+    _check_stack_tensors(scales, "moe_w4a16")
     T = x.shape[0]
     for name, t, dt in (("weights", weights, (torch.uint8,)), ("x", x, (torch.bfloat16, torch.int16, torch.uint16)),
                         ("alpha", alpha, (torch.float32,)), ("expert_start", expert_start, (torch.int32,))):
@@ -480,6 +490,7 @@ def build_index(stack: CompressedStack, stream=None) -> torch.Tensor:
     int32 tensor (also attached to ``stack``)."""
     if stack.device.type != "cuda":
         raise ValueError("build_index: stack must be on a GPU")
+    _check_stack_tensors(stack, "build_index")
     out = torch.empty(stack.E * stack.index_tiles + 1, dtype=torch.int32, device=stack.device)
     d = stack.descriptor()
     _check(_lib().csf_build_index(ctypes.byref(d), out.data_ptr(), _stream_handle(stream, stack.device)),
@@ -491,5 +502,6 @@ def build_index(stack: CompressedStack, stream=None) -> torch.Tensor:
 def validate(stack: CompressedStack):
     """Check the layout invariants on a host copy; raises ``CsfError`` (CSF_E_CORRUPT)."""
     h = stack.to("cpu") if stack.device.type != "cpu" else stack
+    _check_stack_tensors(h, "validate")
     d = h.descriptor()
     _check(_lib().csf_validate(ctypes.byref(d)), "csf_validate")

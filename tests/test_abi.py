@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import workloads
 
@@ -158,6 +159,23 @@ def test_validate_checks_prefix_before_entries():
         assert mwd.STATUS[mwd.library().csf_validate(ctypes.byref(d))] == "CSF_E_CORRUPT"
     finally:
         assert libc.mprotect(base + page, page, 3) == 0   # PROT_READ | PROT_WRITE
+
+
+@pytest.mark.parametrize("what", ["bases", "offsets", "exceptions", "prefix", "tile_index"])
+def test_binding_rejects_short_stack_tensors(what):
+    """The library sees only pointers; the binding refuses a stack whose buffer
+    is shorter than the layout addresses (or of another dtype) before any call."""
+    st = mwd.prepare(workloads.TINY.generate(), workloads.NVFP4)
+    mwd.validate(st)
+    short = st.clone()
+    t = getattr(short, what)
+    setattr(short, what, t[: (t.numel() - 1) if what != "exceptions" else st.num_exceptions - 1])
+    with pytest.raises(ValueError, match=what):
+        mwd.validate(short)
+    wrong = st.clone()
+    setattr(wrong, what, getattr(wrong, what).to(torch.int64))
+    with pytest.raises(ValueError, match=what):
+        mwd.validate(wrong)
 
 
 def test_validate_rejects_fields_past_plane():

@@ -611,3 +611,28 @@ def test_row_window_paired_gate_half(orc, dev, mode):
     wg, wd = run_decode_rows(g, dev, (5, 5), es=es, second=d, rows_second=(100, 900))
     assert np.all(wg == POISON)
     assert_bytes_equal(wd, oracle_rows(orc, sd, (100, 900), es), "down rows 100..899")
+
+
+def test_short_stack_tensors_refused_before_launch(dev):
+    """A stack tensor shorter than the layout addresses is refused by the
+    binding before any kernel is enqueued: the workspace keeps its poison."""
+    st = mwd.prepare(workloads.TINY.generate(), workloads.NVFP4).to(dev)
+    bad = st.clone()
+    bad.offsets = bad.offsets[: st.E * st.stride - 16]
+    ws = torch.full((st.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="offsets"):
+        mwd.decode(bad, ws)
+    with pytest.raises(ValueError, match="offsets"):
+        mwd.Launch(bad, ws)
+    with pytest.raises(ValueError, match="offsets"):
+        mwd.build_index(bad)
+    K = st.C * 16
+    es = torch.tensor([0, 1, 1, 2, 2], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError, match="offsets"):
+        mwd.moe_w4a16(bad, torch.zeros(st.E * st.R * K // 2, dtype=torch.uint8, device=dev),
+                      torch.zeros(2, K, dtype=torch.bfloat16, device=dev),
+                      torch.ones(st.E, dtype=torch.float32, device=dev), es)
+    torch.cuda.synchronize(dev)
+    assert bool((ws == POISON).all())
+    mwd.decode(st, ws)
+    assert torch.equal(ws.cpu(), torch.from_numpy(workloads.TINY.generate().reshape(-1)))
