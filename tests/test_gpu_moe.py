@@ -34,7 +34,7 @@ def dev():
 FMT_NAME = {workloads.NVFP4: "nvfp4", workloads.MXFP4: "mxfp4"}
 
 
-def run(orc, dev, inp: workloads.W4A16Inputs, dense: bool):
+def run(orc, dev, inp: workloads.W4A16Inputs, dense: bool, dense_offset: int = 0):
     st = orc.encode(inp.fmt, inp.scales)
     stack = mwd.from_numpy(st, dev)
     w = torch.from_numpy(inp.w_packed).to(dev)
@@ -44,7 +44,8 @@ def run(orc, dev, inp: workloads.W4A16Inputs, dense: bool):
     out = torch.full((x.shape[0], inp.w_packed.shape[1]), float("nan"), dtype=torch.float32, device=dev)
     dense_t = None
     if dense:
-        dense_t = torch.full((stack.dense_bytes,), 0xA5, dtype=torch.uint8, device=dev)
+        buf = torch.full((stack.dense_bytes + dense_offset,), 0xA5, dtype=torch.uint8, device=dev)
+        dense_t = buf[dense_offset:]
         mwd.decode(stack, dense_t, es)
     mwd.moe_w4a16(stack, w, x, alpha, es, out=out, dense_scales=dense_t)
     torch.cuda.synchronize()
@@ -240,6 +241,22 @@ def test_mxfp4_small_shapes(orc, dev, E, N, K, counts):
     got_csf = run(orc, dev, inp, dense=False)
     got_dense = run(orc, dev, inp, dense=True)
     check(inp, got_csf, "MXFP4 scales from CSF")
+    assert np.array_equal(got_csf, got_dense)
+
+
+@pytest.mark.parametrize("fmt,K,offset", [
+    (workloads.MXFP4, 160, 1), (workloads.MXFP4, 5120, 3),
+    (workloads.NVFP4, 256, 2), (workloads.NVFP4, 4096, 6),
+], ids=["mx_k160_odd", "mx_k5120_odd", "nv_k256_2", "nv_k4096_6"])
+def test_dense_scales_at_unaligned_addresses(orc, dev, fmt, K, offset):
+    """Dense scales need no alignment for MXFP4 (byte loads) and two bytes for
+    NVFP4 (16-bit loads): a workspace starting at such an address gives the
+    same outputs as the scales expanded from the CSF streams."""
+    es = np.array([0, 19, 19, 60], dtype=np.int32)
+    inp = workloads.w4a16_inputs(3, 45, K, es, seed=K + offset, exc_rate=0.15 if fmt else 0.03, fmt=fmt)
+    got_csf = run(orc, dev, inp, dense=False)
+    got_dense = run(orc, dev, inp, dense=True, dense_offset=offset)
+    check(inp, got_csf, "scales from CSF")
     assert np.array_equal(got_csf, got_dense)
 
 
