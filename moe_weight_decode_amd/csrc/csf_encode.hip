@@ -7,8 +7,10 @@
 // prefix and tile index follow the layout in include/csf.h.
 //
 // Four kernels, all byte streams bound by HBM bandwidth:
-//   csf_enc_bases_kernel    one wave per row: 256-bin histogram in LDS,
-//                           window counts, arg-max by a wave reduction.
+//   csf_enc_bases_kernel    one wave per row: 256-bin histogram in LDS (4
+//                           bins per lane), window counts as differences of
+//                           a wave prefix over the bins, arg-max by a wave
+//                           reduction.
 //   csf_enc_pack_kernel     one lane per 16-byte offset group: fields packed
 //                           in the contiguous-decoding order; each index
 //                           tile's out-of-window count reduced across lanes.
@@ -17,6 +19,8 @@
 //   csf_enc_entries_kernel  one wave per index tile: out-of-window positions
 //                           ranked by a wave prefix and written in ascending
 //                           order at the tile's index.
+// The pack and entries kernels read the dense bytes 16 at a time when the
+// stack is 16-byte aligned and R*C is a multiple of 16, else byte by byte.
 #include "csf_launch.h"
 
 namespace csf {
@@ -27,6 +31,29 @@ constexpr uint32_t kScanThreads = 1024;
 
 __device__ __forceinline__ uint32_t div_exact(uint32_t n, double rcp) {
     return (uint32_t)(((double)n + 0.5) * rcp);
+}
+
+// Dense bytes plane[p0 .. p0+16), zero at and past P, as four little-endian
+// words.  vec: the plane is 16-byte aligned and P a multiple of 16, so a run
+// starting below P lies inside the plane.
+__device__ __forceinline__ void load_run16(const uint8_t *plane, uint32_t p0, uint32_t P, bool vec,
+                                           uint32_t x[4]) {
+    if (vec) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(plane + p0);
+        x[0] = v.x;
+        x[1] = v.y;
+        x[2] = v.z;
+        x[3] = v.w;
+        return;
+    }
+    x[0] = x[1] = x[2] = x[3] = 0u;
+#pragma unroll
+    for (uint32_t j = 0; j < 16; ++j)
+        if (p0 + j < P) x[j >> 2] |= (uint32_t)plane[p0 + j] << (8u * (j & 3u));
+}
+
+__device__ __forceinline__ bool runs_aligned(const EncodeArgs &a) {
+    return ((uintptr_t)a.dense & 15u) == 0 && (a.P & 15u) == 0;
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -44,29 +71,46 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __global__ __launch_bounds__(kBlock) void csf_enc_bases_kernel(EncodeArgs a) {
     constexpr uint32_t kWaves = kBlock / kWave;
-    __shared__ uint32_t hist[kWaves][256 + 16];  // 16 zero bins past 255 for window sums
+    __shared__ __align__(16) uint32_t hist[kWaves][256];
     const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     uint32_t *h = hist[wave];
     const uint32_t W = 1u << a.wbits;
     const uint64_t rows = (uint64_t)a.E * a.R;
     for (uint64_t row = (uint64_t)blockIdx.x * kWaves + wave; row < rows;
          row += (uint64_t)gridDim.x * kWaves) {
-        for (uint32_t i = lane; i < 256 + 16; i += kWave) h[i] = 0;
+        reinterpret_cast<uint4 *>(h)[lane] = make_uint4(0u, 0u, 0u, 0u);
         wave_lds_sync();
         const uint8_t *xr = a.dense + row * a.C;
         for (uint32_t c = lane; c < a.C; c += kWave) atomicAdd(&h[xr[c]], 1u);
         wave_lds_sync();
+        // Lane l holds bins 4l .. 4l+3.  below[i] = values < 4l + i, from the
+        // lane's exclusive prefix over the wave plus its own bins.
+        const uint4 c4 = reinterpret_cast<const uint4 *>(h)[lane];
+        const uint32_t cnt[4] = {c4.x, c4.y, c4.z, c4.w};
+        const uint32_t own = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+        uint32_t incl = own;
+#pragma unroll
+        for (uint32_t d = 1; d < kWave; d <<= 1) {
+            const uint32_t y = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += y;
+        }
+        const uint32_t ex = incl - own;
+        const uint32_t below[4] = {ex, ex + cnt[0], ex + cnt[0] + cnt[1], ex + cnt[0] + cnt[1] + cnt[2]};
+        // Values in [v, v + W - 1] (bins past 255 empty) = below(v + W) - below(v);
+        // v + W = 4(l + q) + r with q, r the same for every lane, and
+        // below(256 and up) = C.
         // key = (count in window << 8) | (255 - v) over present values v: the
         // largest key has the largest count, then the smallest v.
         uint32_t best = 0;
 #pragma unroll
         for (uint32_t i = 0; i < 4; ++i) {
-            const uint32_t v = lane + kWave * i;
-            if (h[v] != 0) {
-                uint32_t win = 0;
-                for (uint32_t u = 0; u < W; ++u) win += h[v + u];
-                best = max(best, (win << 8) | (255u - v));
-            }
+            const uint32_t q = (i + W) >> 2, r = (i + W) & 3u;
+            const uint32_t src = lane + q;
+            const uint32_t sel = r == 0 ? below[0] : r == 1 ? below[1] : r == 2 ? below[2] : below[3];
+            const uint32_t far = __shfl(sel, (int)(src & (kWave - 1u)), kWave);
+            const uint32_t top = src < kWave ? far : a.C;
+            const uint32_t v = 4u * lane + i;
+            if (cnt[i] != 0) best = max(best, ((top - below[i]) << 8) | (255u - v));
         }
         best = wave_max(best);
         if (lane == 0) a.bases[row] = (uint8_t)(255u - (best & 0xffu));
@@ -82,6 +126,7 @@ __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
     const uint32_t G = 128u / a.wbits;
     const uint32_t F = 8u / a.wbits;
     const uint32_t seg = kIndexTile / G;  // lanes (groups) per index tile: 64 or 16
+    const bool vec = runs_aligned(a);
     for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
          wv += (uint64_t)gridDim.x * kBlock / kWave) {
         const uint32_t e = (uint32_t)(wv / waves_per_expert);
@@ -94,23 +139,27 @@ __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
             for (uint32_t f = 0; f < F; ++f) {
                 const uint32_t p0 = g * G + 16u * f;
                 if (p0 >= a.P) break;
+                uint32_t x[4];
+                load_run16(plane, p0, a.P, vec, x);
                 uint32_t r = div_exact(p0, a.rcp_cols);
                 uint32_t next = (r + 1u) * a.C;
                 uint32_t b = brow[r];
+#pragma unroll
                 for (uint32_t j = 0; j < 16; ++j) {
                     const uint32_t p = p0 + j;
-                    if (p >= a.P) break;
-                    if (p == next) {
-                        ++r;
-                        next += a.C;
-                        b = brow[r];
+                    if (p < a.P) {
+                        if (p == next) {
+                            ++r;
+                            next += a.C;
+                            b = brow[r];
+                        }
+                        // unsigned 32-bit difference: the window [b, b + W - 1] does
+                        // not wrap past 255, so a value below b is never inside it
+                        const uint32_t d = ((x[j >> 2] >> (8u * (j & 3u))) & 0xffu) - b;
+                        const bool in = d < W;
+                        outside += in ? 0u : 1u;
+                        word[j >> 2] |= (in ? d : 0u) << (8u * (j & 3u) + a.wbits * f);
                     }
-                    // unsigned 32-bit difference: the window [b, b + W - 1] does
-                    // not wrap past 255, so a value below b is never inside it
-                    const uint32_t d = (uint32_t)plane[p] - b;
-                    const bool in = d < W;
-                    outside += in ? 0u : 1u;
-                    word[j >> 2] |= (in ? d : 0u) << (8u * (j & 3u) + a.wbits * f);
                 }
             }
             uint32_t *dst = reinterpret_cast<uint32_t *>(a.offsets + (uint64_t)e * a.stride + 16u * g);
@@ -137,6 +186,7 @@ __global__ __launch_bounds__(kScanThreads) void csf_enc_scan_kernel(EncodeArgs a
     const uint32_t t = threadIdx.x;
     const uint32_t lo = min(t * chunk, N), hi = min(lo + chunk, N);
     uint32_t sum = 0;
+#pragma unroll 8
     for (uint32_t i = lo; i < hi; ++i) sum += (uint32_t)a.tile_index[i];
     part[t] = sum;
     __syncthreads();
@@ -148,6 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void csf_enc_scan_kernel(EncodeArgs a
         __syncthreads();
     }
     uint32_t run = part[t] - sum;  // exclusive
+#pragma unroll 8
     for (uint32_t i = lo; i < hi; ++i) {
         const uint32_t c = (uint32_t)a.tile_index[i];
         a.tile_index[i] = (int32_t)run;
@@ -170,6 +221,7 @@ __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
     const uint32_t lane = threadIdx.x % kWave;
     const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
     const uint32_t W = 1u << a.wbits;
+    const bool vec = runs_aligned(a);
     for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
          wv += (uint64_t)gridDim.x * kBlock / kWave) {
         const uint32_t e = (uint32_t)(wv / a.index_tiles);
@@ -179,18 +231,24 @@ __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
         const uint32_t p0 = it * kIndexTile + lane * kPerLane;
         uint32_t flags = 0;
         if (p0 < a.P) {
+            uint32_t x[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            load_run16(plane, p0, a.P, vec, x);
+            if (p0 + 16u < a.P) load_run16(plane, p0 + 16u, a.P, vec, x + 4);
             uint32_t r = div_exact(p0, a.rcp_cols);
             uint32_t next = (r + 1u) * a.C;
             uint32_t b = brow[r];
+#pragma unroll
             for (uint32_t k = 0; k < kPerLane; ++k) {
                 const uint32_t p = p0 + k;
-                if (p >= a.P) break;
-                if (p == next) {
-                    ++r;
-                    next += a.C;
-                    b = brow[r];
+                if (p < a.P) {
+                    if (p == next) {
+                        ++r;
+                        next += a.C;
+                        b = brow[r];
+                    }
+                    const uint32_t byte = (x[k >> 2] >> (8u * (k & 3u))) & 0xffu;
+                    if (byte - b >= W) flags |= 1u << k;  // no wrap past 255
                 }
-                if ((uint32_t)plane[p] - b >= W) flags |= 1u << k;  // no wrap past 255
             }
         }
         const uint32_t cnt = __popc(flags);
