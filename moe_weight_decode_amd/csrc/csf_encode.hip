@@ -7,10 +7,10 @@
 // prefix and tile index follow the layout in include/csf.h.
 //
 // Four kernels, all byte streams bound by HBM bandwidth:
-//   csf_enc_bases_kernel    one wave per row: 256-bin histogram in LDS (4
-//                           bins per lane), window counts as differences of
-//                           a wave prefix over the bins, arg-max by a wave
-//                           reduction.
+//   csf_enc_bases_kernel    one wave per 4 rows at a time: a 256-bin
+//                           histogram per row in LDS (4 bins per lane),
+//                           window counts as differences of a wave prefix
+//                           over the bins, arg-max by a wave reduction.
 //   csf_enc_pack_kernel     one lane per 16-byte offset group: fields packed
 //                           in the contiguous-decoding order; each index
 //                           tile's out-of-window count reduced across lanes.
@@ -56,12 +56,6 @@ __device__ __forceinline__ bool runs_aligned(const EncodeArgs &a) {
     return ((uintptr_t)a.dense & 15u) == 0 && (a.P & 15u) == 0;
 }
 
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (uint32_t d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, kWave));
-    return v;
-}
-
 // Orders this wave's LDS traffic (a wave works on its own histogram).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -71,49 +65,81 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __global__ __launch_bounds__(kBlock) void csf_enc_bases_kernel(EncodeArgs a) {
     constexpr uint32_t kWaves = kBlock / kWave;
-    __shared__ __align__(16) uint32_t hist[kWaves][256];
+    constexpr uint32_t kRows = 4;  // rows per wave at a time: their dependent chains interleave
+    __shared__ __align__(16) uint32_t hist[kWaves][kRows][256];
     const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    uint32_t *h = hist[wave];
     const uint32_t W = 1u << a.wbits;
     const uint64_t rows = (uint64_t)a.E * a.R;
-    for (uint64_t row = (uint64_t)blockIdx.x * kWaves + wave; row < rows;
-         row += (uint64_t)gridDim.x * kWaves) {
-        reinterpret_cast<uint4 *>(h)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    for (uint64_t r0 = ((uint64_t)blockIdx.x * kWaves + wave) * kRows; r0 < rows;
+         r0 += (uint64_t)gridDim.x * kWaves * kRows) {
+#pragma unroll
+        for (uint32_t r = 0; r < kRows; ++r)
+            reinterpret_cast<uint4 *>(hist[wave][r])[lane] = make_uint4(0u, 0u, 0u, 0u);
         wave_lds_sync();
-        const uint8_t *xr = a.dense + row * a.C;
-        for (uint32_t c = lane; c < a.C; c += kWave) atomicAdd(&h[xr[c]], 1u);
+        for (uint32_t c = lane; c < a.C; c += kWave) {
+            uint32_t v[kRows];
+#pragma unroll
+            for (uint32_t r = 0; r < kRows; ++r)
+                v[r] = r0 + r < rows ? (uint32_t)a.dense[(r0 + r) * a.C + c] : 0x100u;
+#pragma unroll
+            for (uint32_t r = 0; r < kRows; ++r)
+                if (v[r] < 256u) atomicAdd(&hist[wave][r][v[r]], 1u);
+        }
         wave_lds_sync();
-        // Lane l holds bins 4l .. 4l+3.  below[i] = values < 4l + i, from the
-        // lane's exclusive prefix over the wave plus its own bins.
-        const uint4 c4 = reinterpret_cast<const uint4 *>(h)[lane];
-        const uint32_t cnt[4] = {c4.x, c4.y, c4.z, c4.w};
-        const uint32_t own = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-        uint32_t incl = own;
+        // Lane l holds bins 4l .. 4l+3 of each row.  below[i] = values < 4l + i,
+        // from the lane's exclusive prefix over the wave plus its own bins.
+        uint32_t cnt[kRows][4], incl[kRows], own[kRows];
+#pragma unroll
+        for (uint32_t r = 0; r < kRows; ++r) {
+            const uint4 c4 = reinterpret_cast<const uint4 *>(hist[wave][r])[lane];
+            cnt[r][0] = c4.x;
+            cnt[r][1] = c4.y;
+            cnt[r][2] = c4.z;
+            cnt[r][3] = c4.w;
+            own[r] = c4.x + c4.y + c4.z + c4.w;
+            incl[r] = own[r];
+        }
 #pragma unroll
         for (uint32_t d = 1; d < kWave; d <<= 1) {
-            const uint32_t y = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += y;
+#pragma unroll
+            for (uint32_t r = 0; r < kRows; ++r) {
+                const uint32_t y = __shfl_up(incl[r], d, kWave);
+                if (lane >= d) incl[r] += y;
+            }
         }
-        const uint32_t ex = incl - own;
-        const uint32_t below[4] = {ex, ex + cnt[0], ex + cnt[0] + cnt[1], ex + cnt[0] + cnt[1] + cnt[2]};
         // Values in [v, v + W - 1] (bins past 255 empty) = below(v + W) - below(v);
         // v + W = 4(l + q) + r with q, r the same for every lane, and
         // below(256 and up) = C.
         // key = (count in window << 8) | (255 - v) over present values v: the
         // largest key has the largest count, then the smallest v.
-        uint32_t best = 0;
+        uint32_t best[kRows];
 #pragma unroll
-        for (uint32_t i = 0; i < 4; ++i) {
-            const uint32_t q = (i + W) >> 2, r = (i + W) & 3u;
-            const uint32_t src = lane + q;
-            const uint32_t sel = r == 0 ? below[0] : r == 1 ? below[1] : r == 2 ? below[2] : below[3];
-            const uint32_t far = __shfl(sel, (int)(src & (kWave - 1u)), kWave);
-            const uint32_t top = src < kWave ? far : a.C;
-            const uint32_t v = 4u * lane + i;
-            if (cnt[i] != 0) best = max(best, ((top - below[i]) << 8) | (255u - v));
+        for (uint32_t r = 0; r < kRows; ++r) {
+            const uint32_t ex = incl[r] - own[r];
+            const uint32_t below[4] = {ex, ex + cnt[r][0], ex + cnt[r][0] + cnt[r][1],
+                                       ex + cnt[r][0] + cnt[r][1] + cnt[r][2]};
+            best[r] = 0;
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                const uint32_t q = (i + W) >> 2, m = (i + W) & 3u;
+                const uint32_t src = lane + q;
+                const uint32_t sel = m == 0 ? below[0] : m == 1 ? below[1] : m == 2 ? below[2] : below[3];
+                const uint32_t far = __shfl(sel, (int)(src & (kWave - 1u)), kWave);
+                const uint32_t top = src < kWave ? far : a.C;
+                const uint32_t v = 4u * lane + i;
+                if (cnt[r][i] != 0) best[r] = max(best[r], ((top - below[i]) << 8) | (255u - v));
+            }
         }
-        best = wave_max(best);
-        if (lane == 0) a.bases[row] = (uint8_t)(255u - (best & 0xffu));
+#pragma unroll
+        for (uint32_t d = 32; d >= 1; d >>= 1) {
+#pragma unroll
+            for (uint32_t r = 0; r < kRows; ++r) best[r] = max(best[r], (uint32_t)__shfl_xor(best[r], d, kWave));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (uint32_t r = 0; r < kRows; ++r)
+                if (r0 + r < rows) a.bases[r0 + r] = (uint8_t)(255u - (best[r] & 0xffu));
+        }
         wave_lds_sync();
     }
 }
