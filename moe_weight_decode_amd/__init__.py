@@ -263,6 +263,11 @@ def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> Comp
     if n > 0:
         _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), None, exc.data_ptr(),
                                      None, tidx.data_ptr(), ENCODE_ENTRIES, h), "csf_encode_device(entries)")
+    if stream is not None and stream != torch.cuda.current_stream(dev):
+        # allocated on the current stream, written on `stream`: keep the memory
+        # from being reused before `stream` is done with it
+        for t in (bases, offsets, prefix, tidx, exc, x):
+            t.record_stream(stream)
     return CompressedStack(fmt, E, R, C, S, n, bases, offsets, exc, prefix, tidx if index else None)
 
 
@@ -270,7 +275,10 @@ def prepare(dense, fmt: int, index: bool = True, stream=None) -> CompressedStack
     """Encode ``dense`` (uint8 [E, R, C], tensor or array), with the tile index
     unless ``index`` is False; the result lives on ``dense``'s device.  A GPU
     tensor is encoded on the GPU (the count of exception entries is read back
-    once, to size their buffer); host data by the host encoder."""
+    once, to size their buffer); host data by the host encoder.  The GPU
+    encode runs on ``stream`` (default: the current stream): ``dense`` must be
+    ready there, and work on another stream that uses the result must wait
+    for ``stream`` (for example ``current_stream().wait_stream(stream)``)."""
     if isinstance(dense, torch.Tensor) and dense.device.type == "cuda":
         return _prepare_device(dense, fmt, index, stream)
     lib = _lib()

@@ -476,6 +476,19 @@ def test_gpu_encoder_no_exceptions_and_side_stream(orc, dev):
     _same_streams(got.numpy(), orc.encode(workloads.NVFP4, x), "no exceptions")
 
 
+def test_gpu_encoder_on_a_stream_that_is_not_current(orc, dev):
+    """Outputs allocated on the current stream, written on another: after the
+    caller's wait the streams equal the oracle's encoding."""
+    x = workloads.nvfp4_stack(3, 64, 128, 7, 0.05)
+    side = torch.cuda.Stream(device=dev)
+    xt = torch.from_numpy(x).to(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    got = mwd.prepare(xt, workloads.NVFP4, stream=side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    assert got.num_exceptions > 0
+    _same_streams(got.numpy(), orc.encode(workloads.NVFP4, x), "encode on a side stream")
+
+
 def test_gpu_encoder_high_bases(orc, dev):
     """Rows whose base is above 240 next to small values: the window does not
     wrap past 255, so the small values are exceptions."""
