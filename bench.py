@@ -8,14 +8,18 @@ stack and workspace (together larger than the 256 MB Infinity Cache), so
 every step reads and writes HBM.
 
 Prints ONE JSON line on stdout:
-  value       whole-run throughput, GB/s = (compressed bytes read + dense
-              bytes written) per step x steps / elapsed time
-  roofline    the fused kernel (the only kernel of a step): its algorithmic
-              bytes per launch / its mean launch time, from two HIP events on
-              its stream bracketing the back-to-back launches of the timed
-              region (no event sits between two launches), against the MI355X
-              HBM3E peak (8 TB/s)
-  cpu_baseline the CPU oracle decoding the same stack on one host core
+  value        whole-run throughput, GB/s = algorithmic bytes per step (the
+               compressed streams read: bases, offsets, exception entries,
+               entry prefix; the dense bytes written) x steps / elapsed time
+  roofline     the fused kernel (the only kernel of a step): the same bytes
+               per launch / its mean launch time, from two HIP events on its
+               stream bracketing the back-to-back launches of the timed
+               region, against the MI355X HBM3E peak (8 TB/s); next to it the
+               kernel average of the committed rocprofv3 trace of the same
+               sources, and the plain stream-mix kernel's rate on the same
+               buffers (the ceiling of this access pattern on this chip)
+  cpu_baseline the CPU oracle decoding the same stack on the host's cores (one
+               thread, and threads over disjoint expert ranges)
 
   python bench.py [--steps K] [--warmup W] [--sets N] [--workload NAME] [--all] [--no-cpu]
 
@@ -29,8 +33,11 @@ dense scales; routed_moe_mx does the same on the MXFP4 stack's projection
 
 --all also measures the other workloads (down-like, MXFP4, routed paired,
 tiny), the two-pass decode of each (fixed-stream kernel, then exception
-kernel), warm and cache-flushed single calls, the floor of two dependent tiny
-launches, and a plain copy; one line each on stderr.
+kernel), warm and cache-flushed single calls, the stream-mix ceiling of each
+stack, the launch floors (an empty kernel and kernels with 0-3 dependent
+round trips to memory at the routed decode's grid), the host cost of a
+decode call (C and Python), the per-step timestamps of the routed decode and
+the GPU encode; one line each on stderr.
 """
 from __future__ import annotations
 
@@ -40,6 +47,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -94,12 +102,27 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def stack_bytes(stack, active=None):
-    """Algorithmic bytes of one decode: (fixed-stream bytes read, exception
-    bytes read, dense bytes written).  Exception bytes include the prefix and,
-    for an indexed stack, the tile index (a routed decode reads only the
-    index segments of its routed experts).  active: boolean mask of routed
-    experts, or None for all."""
+class StackBytes(tuple):
+    """Algorithmic bytes of one decode of a stack: ``fixed`` (bases and
+    offset segments read), ``exc`` (exception entries and the entry prefix
+    read), ``dense`` (bytes written) and, apart, ``index`` (the tile index
+    this build adds to the format; a routed decode reads only its routed
+    experts' segments).  ``metric`` = fixed + exc + dense, the compressed
+    bytes read plus the dense bytes written."""
+
+    def __new__(cls, fixed, exc, dense, index):
+        return super().__new__(cls, (fixed, exc, dense, index))
+
+    fixed = property(lambda self: self[0])
+    exc = property(lambda self: self[1])
+    dense = property(lambda self: self[2])
+    index = property(lambda self: self[3])
+    metric = property(lambda self: self[0] + self[1] + self[2])
+
+
+def stack_bytes(stack, active=None) -> StackBytes:
+    """Bytes one decode of ``stack`` reads and writes; ``active`` is a boolean
+    mask of routed experts, or None for all."""
     import numpy as np
     E = stack.E
     n_act = E if active is None else int(np.count_nonzero(active))
@@ -110,10 +133,10 @@ def stack_bytes(stack, active=None):
         entries = int(np.diff(prefix)[np.asarray(active, dtype=bool)].sum())
     fixed = n_act * (stack.R + stack.stride)          # bases + offsets
     exc = 4 * entries + 4 * (E + 1)                   # entries + prefix
+    index = 0
     if stack.tile_index is not None:
-        exc += 4 * (E * stack.index_tiles + 1) if active is None else 4 * n_act * (stack.index_tiles + 1)
-    dense = n_act * stack.P
-    return fixed, exc, dense
+        index = 4 * (E * stack.index_tiles + 1) if active is None else 4 * n_act * (stack.index_tiles + 1)
+    return StackBytes(fixed, exc, n_act * stack.P, index)
 
 
 _KERNEL_SOURCES = {
@@ -149,6 +172,19 @@ def pmc_traffic(kernel: str, workload: str):
     if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def profile_time(kernel: str, workload: str):
+    """Average kernel duration (ns) from the committed rocprofv3 kernel trace
+    of this workload, if it was taken on the current kernel sources; else
+    None."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}/{workload}")
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec
 
 
 def make_sets(mwd, torch, stack, nsets, dev):
@@ -220,11 +256,12 @@ def check_equal(torch, ws, x, what):
         raise SystemExit(f"{what}: GPU decode differs from the input in {(got != x).sum()} bytes")
 
 
-def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
-    """Time the full decode of `spec` (fused, indexed stack); with `split`
-    also the two-pass decode of the same stack and its fixed pass alone, one
-    stack decoded over and over (warm: its 85-109 MB stay in the MALL), and
-    single calls on flushed caches."""
+def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False, ceiling=True):
+    """Time the full decode of `spec` (fused, indexed stack) and, with
+    `ceiling`, the stream-mix kernel on the same buffers; with `split` also
+    the two-pass decode of the same stack and its fixed pass alone, one stack
+    decoded over and over (warm: its 85-109 MB stay in the MALL), and single
+    calls on flushed caches."""
     x = spec.generate()
     stack = mwd.prepare(x, spec.fmt).to(dev)
     sets = make_sets(mwd, torch, stack, nsets, dev)
@@ -233,9 +270,9 @@ def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
     torch.cuda.synchronize()
     check_equal(torch, sets[0][1], x, spec.name)
     wall, evt = timed_loop(torch, ev, launches, steps, warmup)
-    fb, eb, db = stack_bytes(stack)
-    out = dict(x=x, stack=stack, fixed_bytes=fb, exc_bytes=eb, dense_bytes=db,
-               step_ms=max(wall, evt), wall_ms=wall, event_ms=evt)
+    out = dict(x=x, stack=stack, bytes=stack_bytes(stack), step_ms=max(wall, evt), wall_ms=wall, event_ms=evt)
+    if ceiling and spec.E > 4:
+        out["ceiling"] = bench_ceiling(mwd, torch, ev, sets, min(steps, 2000), warmup, dev)
     if split:
         two = [mwd.Launch(s.without_index(), ws) for s, ws in sets]
         two[0]()
@@ -249,6 +286,28 @@ def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False):
     return out
 
 
+def bench_ceiling(mwd, torch, ev, sets, steps, warmup, dev):
+    """The stream-mix kernel (csf_probe_mix) on each rotating set's own
+    buffers: it reads the offset segments, the exception entries and the row
+    bases and writes the workspace, the bytes and access shape of the decode
+    without its work.  Best of 4, 6 and 8 workgroups per CU, with cached and
+    with non-temporal entry loads; also the same without the entry stream.
+    Event time per step (ms) and the configuration of the best."""
+    from moe_weight_decode_amd import probe
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best, best_cfg = None, None
+    for wg in (4, 6, 8):
+        for flags in (probe.NT_STORES, probe.NT_STORES | (probe.NT_LOADS0 << 1)):
+            mixes = [probe.Mix([s.offsets, s.exceptions[:s.num_exceptions], s.bases], ws, cus * wg, flags)
+                     for s, ws in sets]
+            _, evt = timed_loop(torch, ev, mixes, steps, warmup)
+            if best is None or evt < best:
+                best, best_cfg = evt, dict(wg_per_cu=wg, entry_loads="nt" if flags & (probe.NT_LOADS0 << 1) else "cached")
+    two = [probe.Mix([s.offsets, s.bases], ws, cus * best_cfg["wg_per_cu"], probe.NT_STORES) for s, ws in sets]
+    _, evt2 = timed_loop(torch, ev, two, steps, warmup)
+    return dict(event_ms=best, config=best_cfg, without_entries_ms=evt2)
+
+
 def _repeat(fn, budget_s):
     times = []
     t_end = time.perf_counter() + budget_s
@@ -259,46 +318,110 @@ def _repeat(fn, budget_s):
     return statistics.median(times), len(times)
 
 
+def cpu_info():
+    """The host CPU: model, sockets and the threads this process may run on."""
+    model, sockets = None, None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() == "Model name" and model is None:
+                model = v.strip()
+            elif k.strip() == "Socket(s)":
+                sockets = int(v.strip()) if v.strip().isdigit() else v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None and os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    return dict(model=model, sockets=sockets, affinity=len(os.sched_getaffinity(0)))
+
+
+def cpu_threads() -> int:
+    """Threads of the threaded oracle runs: the process's CPUs, at most the
+    OMP_NUM_THREADS share when it is set."""
+    n = len(os.sched_getaffinity(0))
+    v = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(v))) if v.isdigit() else n
+
+
+def _slices(E, n):
+    step = (E + n - 1) // n
+    return [(e, min(E, e + step)) for e in range(0, E, step)]
+
+
+def oracle_runs(orc, jobs, budget_s):
+    """Median seconds of one round of `jobs` (callables decoding disjoint
+    expert ranges, each from one thread per job), about budget_s / 2 seconds
+    on one thread and as much on len(jobs) threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    one, n1 = _repeat(lambda: [j() for j in jobs], budget_s / 2)
+    with ThreadPoolExecutor(len(jobs)) as pool:
+        many, nn = _repeat(lambda: list(pool.map(lambda j: j(), jobs)), budget_s / 2)
+    return one, n1, many, nn
+
+
 def cpu_baseline(spec, x, budget_s=10.0):
-    """The oracle (plain C, one thread) decoding the whole stack, repeated for
-    about `budget_s` seconds; GB/s on the same byte formula as the GPU."""
+    """The oracle (plain C) decoding the whole stack on one host thread, and
+    on N threads over disjoint expert ranges (the same C function per range),
+    each repeated for about budget_s / 2 seconds; GB/s on the GPU's byte
+    formula.  The oracle's encode of the stack (one thread) is timed once, as
+    context."""
+    import numpy as np
     import oracle
     orc = oracle.load()
+    t = time.perf_counter()
     st = orc.encode(spec.fmt, x)
-    ws = orc.decode(st)
-    if not (ws == x).all():
+    encode_s = time.perf_counter() - t
+    ws = np.empty_like(x)
+    n = cpu_threads()
+    jobs = [lambda a=a, b=b: orc.decode_experts(st, a, b, ws) for a, b in _slices(spec.E, n)]
+    for j in jobs:
+        j()
+    if not np.array_equal(ws, x):
         raise SystemExit("oracle round trip failed")
-    sec, n = _repeat(lambda: orc.decode(st, None, ws), budget_s)
+    one, n1, many, nn = oracle_runs(orc, jobs, budget_s)
+    if not np.array_equal(ws, x):
+        raise SystemExit("threaded oracle decode failed")
     E = spec.E
-    comp = E * spec.R + E * st["stride"] + 4 * st["exceptions"].size + 4 * (E + 1)
-    return dict(value=round((comp + x.size) / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                us_per_stack=round(sec * 1e6, 1),
-                sample=f"whole {spec.name} stack ({spec.E}x{spec.R}x{spec.C}), decoded {n} "
-                       f"times on one host core, median")
+    nbytes = E * spec.R + E * st["stride"] + 4 * st["exceptions"].size + 4 * (E + 1) + x.size
+    return dict(value=round(nbytes / many / 1e9, 4), unit="GB/s", cores=len(jobs), kind="oracle",
+                us_per_stack=round(many * 1e6, 1),
+                single_thread=dict(value=round(nbytes / one / 1e9, 4), us_per_stack=round(one * 1e6, 1), runs=n1),
+                cpu=cpu_info(), oracle_encode_s=round(encode_s, 3),
+                sample=f"whole {spec.name} stack ({spec.E}x{spec.R}x{spec.C}) decoded {nn} times on {len(jobs)} "
+                       f"threads (disjoint expert ranges) and {n1} times on one thread, median of each")
 
 
 def cpu_baseline_routed(workloads, budget_s=10.0):
     """The oracle's routed decode of the gate and down stacks (8 of 512
-    experts), one host core; GB/s on the GPU's byte formula."""
+    experts), on one host thread and on N threads over disjoint expert
+    ranges; GB/s on the GPU's byte formula."""
     import numpy as np
     import oracle
     orc = oracle.load()
     gspec, dspec = workloads.ROUTED.stacks
     es = workloads.ROUTED.expert_start()
     act = np.diff(es) > 0
-    sts, wss, nbytes = [], [], 4 * len(es)
+    jobs, nbytes = [], 4 * len(es)
+    n = cpu_threads()
     for spec in (gspec, dspec):
         x = spec.generate()
         st = orc.encode(spec.fmt, x)
-        sts.append(st)
-        wss.append(np.zeros(x.shape, dtype=np.uint8))
+        ws = np.zeros(x.shape, dtype=np.uint8)
+        jobs += [lambda a=a, b=b, st=st, ws=ws: orc.decode_experts(st, a, b, ws, es)
+                 for a, b in _slices(spec.E, max(1, n // 2))]
         ent = int(np.diff(st["prefix"])[act].sum())
         nbytes += int(act.sum()) * (spec.R + st["stride"] + spec.R * spec.C) + 4 * ent + 4 * (spec.E + 1)
-    sec, n = _repeat(lambda: [orc.decode(st, es, ws) for st, ws in zip(sts, wss)], budget_s)
-    return dict(value=round(nbytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                us_per_stack=round(sec * 1e6, 1),
-                sample=f"routed paired decode (8 of 512 experts) of the gate and down stacks, "
-                       f"{n} times on one host core, median")
+    one, n1, many, nn = oracle_runs(orc, jobs, budget_s)
+    return dict(value=round(nbytes / many / 1e9, 4), unit="GB/s", cores=len(jobs), kind="oracle",
+                us_per_call=round(many * 1e6, 1),
+                single_thread=dict(value=round(nbytes / one / 1e9, 4), us_per_call=round(one * 1e6, 1), runs=n1),
+                cpu=cpu_info(),
+                sample=f"routed paired decode (8 of 512 experts) of the gate and down stacks, {nn} times on "
+                       f"{len(jobs)} threads (disjoint expert ranges) and {n1} times on one thread, median of each")
 
 
 def routed_sets(workloads, E, n_active, max_tokens, seed, count):
@@ -345,7 +468,7 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
     rs = routed_sets(workloads, gspec.E, spec.n_active, spec.max_tokens, spec.seed + 100, routings)
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
-    calls, nbytes, keep = [], [], []
+    calls, nbytes, index_bytes = [], [], []
     with torch.cuda.stream(side):
         for c in range(copies):
             gc, dc = (g, d) if c == 0 else (g.clone(), d.clone())
@@ -354,12 +477,14 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
             for r in rs:
                 rt = torch.from_numpy(r).to(dev)
                 act = np.diff(r) > 0
+                stacks = (gc,) if gate_only else (gc, dc)
                 if gate_only:
                     calls.append(mwd.Launch(gc, wgc, expert_start=rt))
-                    nbytes.append(sum(stack_bytes(gc, act)) + 4 * len(r))
                 else:
                     calls.append(mwd.Launch(gc, wgc, dc, wdc, rt))
-                    nbytes.append(sum(sum(stack_bytes(s, act)) for s in (gc, dc)) + 4 * len(r))
+                b = [stack_bytes(s, act) for s in stacks]
+                nbytes.append(sum(x.metric for x in b) + 4 * len(r))  # + expert_start
+                index_bytes.append(sum(x.index for x in b))
         warm = [mwd.Launch(g, wg, expert_start=es_t) if gate_only else mwd.Launch(g, wg, d, wd, es_t)] * len(calls)
         for L in calls + warm:  # warm the launch path outside capture
             L()
@@ -391,8 +516,9 @@ def bench_routed(mwd, torch, ev, workloads, steps, warmup, dev, indexed=True, co
     n = len(calls)
     b = [stack_bytes(s, active) for s in ((g,) if gate_only else (g, d))]
     return dict(step_ms=max(wall, evt) / n, event_ms=evt / n, wall_ms=wall / n,
-                bytes=sum(nbytes) / len(nbytes), warm_ms=max(wwall, wevt) / n,
-                warm_bytes=sum(sum(x) for x in b) + 4 * len(es), active=int(active.sum()), flushed_ms=flushed,
+                bytes=sum(nbytes) / len(nbytes), index_bytes=sum(index_bytes) / len(index_bytes),
+                warm_ms=max(wwall, wevt) / n,
+                warm_bytes=sum(x.metric for x in b) + 4 * len(es), active=int(active.sum()), flushed_ms=flushed,
                 sets=n, steps=reps * n)
 
 
@@ -521,30 +647,21 @@ def _blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def launch_floor(torch, ev, dev, steps=2000):
-    """The floor under a decode call of two dependent launches: two tiny
-    kernels (one-element adds) per step, launched directly and replayed from
-    a HIP graph of 64 steps; µs per step."""
-    t = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    class Pair:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-
-        def __call__(self):
-            t.add_(1)
-            t.add_(1)
-
-    wall, evt = timed_loop(torch, ev, [Pair()], steps, 100)
+def graph_of(torch, dev, calls):
+    """A HIP graph of `calls` in order (warmed outside capture), replayed on
+    the current stream: returns a callable with the replay stream's handle."""
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(side):
-        Pair()()
+        for c in calls:
+            c()
     torch.cuda.current_stream(dev).wait_stream(side)
     torch.cuda.synchronize()
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr, stream=side):
-        for _ in range(64):
-            Pair()()
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
 
     class Replay:
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -552,22 +669,150 @@ def launch_floor(torch, ev, dev, steps=2000):
         def __call__(self):
             gr.replay()
 
-    gw, ge = timed_loop(torch, ev, [Replay()], max(1, steps // 64), 2)
-    return dict(direct_us=round(max(wall, evt) * 1e3, 2), graph_us=round(max(gw, ge) / 64 * 1e3, 2))
+    r = Replay()
+    r.graph = gr
+    return r
 
 
-def bench_copy(torch, ev, mwd, dev, nbytes, nsets, steps):
-    srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
-    dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
-    for i in range(10):
-        dsts[i % nsets].copy_(srcs[i % nsets])
+def launch_floors(torch, ev, dev, grid, reps=40, per_graph=64):
+    """Floors under a routed decode call, from graph replays of per_graph
+    launches (µs per launch): an empty one-wave kernel; an empty kernel at
+    the routed decode's grid (grid x 256 lanes); the same storing 16 bytes
+    per lane; and with 1, 2, 3 dependent round trips to memory before the
+    stores (csf_probe_chain: each workgroup follows a chain of 4-byte loads
+    through 1 GiB, from a start set by the workgroup and the launch, so the
+    loads miss the caches); and the latency of one dependent load, from a
+    chain of 64 links through 1 GiB with cold caches (HBM) and again warm
+    (L2)."""
+    from moe_weight_decode_amd import probe
+    words = 1 << 28
+    i = torch.arange(words, dtype=torch.int64, device=dev)
+    buf = ((i * 0x9E3779B1 + 12345) & (words - 1)).to(torch.int32)  # a permutation of 0 .. words-1
+    del i
+    outs = [torch.empty(grid * 256 * 16, dtype=torch.uint8, device=dev) for _ in range(8)]
+    cases = {"empty_1wave": (0, False, 1, 64), "empty_grid": (0, False, grid, 256),
+             "store_grid": (0, True, grid, 256), "chain1_store": (1, True, grid, 256),
+             "chain2_store": (2, True, grid, 256), "chain3_store": (3, True, grid, 256)}
+    out = {}
+    for name, (hops, store, g, block) in cases.items():
+        calls = [probe.Chain(buf if hops else None, hops, outs[k % len(outs)] if store else None, g, block,
+                             seed=k + 1) for k in range(per_graph)]
+        rep = graph_of(torch, dev, calls)
+        wall, evt = timed_loop(torch, ev, [rep], reps, 3)
+        out[name + "_us"] = round(max(wall, evt) / per_graph * 1e3, 3)
+    # latency of one dependent load: one wave following 0 and 64 links of the
+    # 1 GiB chain after a 512 MiB write has evicted it from the caches (HBM),
+    # and the same chain again right after (L2); event pairs around the
+    # launch alone, median of 15
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = ev.create(2)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lat = {"hbm": {}, "l2": {}}
+    for hops in (0, 64):
+        for name in ("hbm", "l2"):
+            lat[name][hops] = []
+        for r in range(15):
+            call = probe.Chain(buf, hops, None, 1, 64, seed=1000 + r)
+            flush.fill_(r & 0xFF)
+            for name in ("hbm", "l2"):
+                ev.record(evs[0], stream)
+                call()
+                ev.record(evs[1], stream)
+                torch.cuda.synchronize()
+                lat[name][hops].append(ev.ms(evs[0], evs[1]) * 1e6)
+    ev.destroy(evs)
+    for name in ("hbm", "l2"):
+        out[f"load_latency_{name}_ns"] = round(
+            (statistics.median(lat[name][64]) - statistics.median(lat[name][0])) / 64, 1)
+    del buf, outs, flush
+    torch.cuda.empty_cache()
+    out["grid"] = grid
+    return out
+
+
+def host_cost(mwd, torch, dev, g, d, es_t, calls=300):
+    """Host time per decode call, enqueue only: the C ABI called from C
+    (csf_probe_host_ns) and from Python through the binding's Launch; full
+    gate-stack decode and routed paired decode (µs)."""
+    from moe_weight_decode_amd import probe
+    wg = torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev)
+    wd = torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)
+    out = {}
+    for name, args in (("full_gate", (g, wg, None, None, None)), ("routed_paired", (g, wg, d, wd, es_t))):
+        probe.host_ns(*args, calls=20)
+        torch.cuda.synchronize()
+        c_ns = probe.host_ns(*args, calls=calls)
+        torch.cuda.synchronize()
+        L = mwd.Launch(*args)
+        for _ in range(20):
+            L()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(calls):
+            L()
+        py_ns = (time.perf_counter() - t) / calls * 1e9
+        torch.cuda.synchronize()
+        out[name] = dict(c_call_us=round(c_ns / 1e3, 3), python_launch_us=round(py_ns / 1e3, 3))
+    return out
+
+
+def clock_hz(mwd, torch, g, dev, wait_s=0.25):
+    """Rate of the clock the traced decode reads: the earliest start stamp of
+    two traced calls wait_s seconds apart, against the host's clock."""
+    import numpy as np
+    es = torch.zeros(g.E + 1, dtype=torch.int32, device=dev)
+    es[1:] = 1  # expert 0 routed
+    ws = torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev)
+    a = mwd.decode_traced(g, ws, expert_start=es)
     torch.cuda.synchronize()
-    t = time.perf_counter()
-    for i in range(steps):
-        dsts[i % nsets].copy_(srcs[i % nsets])
+    t0 = time.perf_counter()
+    time.sleep(wait_s)
+    b = mwd.decode_traced(g, ws, expert_start=es)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t) * 1e3 / steps
-    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+    t1 = time.perf_counter()
+    ticks = int(b[:, 0].cpu().numpy().view(np.uint64).min()) - int(a[:, 0].cpu().numpy().view(np.uint64).min())
+    return ticks / (t1 - t0)
+
+
+def trace_routed(mwd, torch, dev, g, d, routings, copies=2):
+    """Per-step timestamps of routed paired decodes (csf_decode_traced), one
+    call per routing and stack copy, launched one by one; medians over the
+    workgroups that decoded a tile, in ns from the call's first workgroup
+    start (the clock is the device's constant-rate wall clock)."""
+    import numpy as np
+    ns_per_tick = 1e9 / clock_hz(mwd, torch, g, dev)
+    stacks = [(g, d)] + [(g.clone(), d.clone()) for _ in range(copies - 1)]
+    wss = [(torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev),
+            torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev)) for _ in stacks]
+    rts = [torch.from_numpy(r).to(dev) for r in routings]
+    names = ["routing", "loads", "expand", "patch", "store_issue", "store_done"]
+    rows, spans, long_tiles, units = [], [], 0, 0
+    for k in range(2 + len(rts) * len(stacks)):
+        (gc, dc), (wg, wd) = stacks[k % len(stacks)], wss[k % len(stacks)]
+        st = mwd.decode_traced(gc, wg, dc, wd, rts[k % len(rts)])
+        torch.cuda.synchronize()
+        if k < 2:
+            continue  # warm the launch path
+        t = st.cpu().numpy().view(np.uint64).astype(np.float64)
+        tags = st[:, 7].cpu().numpy().view(np.uint64)
+        busy = (tags != 0) & (tags != np.uint64(0xFFFFFFFFFFFFFFFF))
+        t0 = t[:, 0].min()
+        rel = (t[busy, :7] - t0) * ns_per_tick
+        rows.append(rel)
+        spans.append((t[busy, 6].max() - t0) * ns_per_tick)
+        long_tiles += int(np.count_nonzero((tags[busy] >> np.uint64(32)) & np.uint64(1)))
+        units += int(busy.sum())
+    rel = np.concatenate(rows)
+    steps = np.diff(rel, axis=1)
+    out = dict(start_ns_median=round(float(np.median(rel[:, 0])), 1),
+               start_ns_p90=round(float(np.percentile(rel[:, 0], 90)), 1),
+               done_ns_median=round(float(np.median(rel[:, 6])), 1),
+               span_ns_median=round(float(np.median(spans)), 1),
+               calls=len(spans), tiles=units, tiles_beyond_prefetch=long_tiles, ns_per_tick=ns_per_tick)
+    for i, n in enumerate(names):
+        out[n + "_ns_median"] = round(float(np.median(steps[:, i])), 1)
+        out[n + "_ns_p90"] = round(float(np.percentile(steps[:, i], 90)), 1)
+    return out
 
 
 def main():
@@ -638,6 +883,7 @@ def main():
             "decode": "single pass (fused kernel, tile index), routed; steps replayed from a "
                       "HIP graph of all rotating sets",
             "bytes_per_step": round(step_bytes),
+            "index_bytes_per_step": round(rr["index_bytes"]),
             "rotating_sets": rr["sets"],
             "timed_steps": rr["steps"],
             "warm_us_same_routing": round(rr["warm_ms"] * 1e3, 3),
@@ -648,8 +894,8 @@ def main():
         log(f"[bench] {spec.name}: generating and encoding {spec.E}x{spec.R}x{spec.C}")
         r = bench_stack(mwd, torch, ev, spec, args.steps, args.warmup,
                         args.sets if spec.E > 4 else 2, dev)
-        stack = r["stack"]
-        step_bytes = r["fixed_bytes"] + r["exc_bytes"] + r["dense_bytes"]
+        stack, b = r["stack"], r["bytes"]
+        step_bytes = b.metric
         fmt = "NVFP4 (E4M3 scales)" if spec.fmt == workloads.NVFP4 else "MXFP4 (UE8M0 scales)"
         config = {
             "workload": f"{spec.name}: full-stack CSF decode of {spec.E} experts x {spec.R} rows x "
@@ -658,9 +904,10 @@ def main():
             "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": fmt,
             "decode": "single pass (fused kernel, tile index)",
             "exception_entries": stack.num_exceptions,
-            "compressed_bytes": r["fixed_bytes"] + r["exc_bytes"],
-            "dense_bytes": r["dense_bytes"],
+            "compressed_bytes": b.fixed + b.exc,
+            "dense_bytes": b.dense,
             "bytes_per_step": step_bytes,
+            "index_bytes_per_step": b.index,
             "rotating_sets": args.sets if spec.E > 4 else 2,
         }
         x_head = r["x"]
@@ -671,6 +918,29 @@ def main():
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
     kernel = "csf_moe_w4a16_kernel" if moe else "csf_fused_kernel"
     traffic = pmc_traffic(kernel, args.workload)
+    roof = {
+        "kernel": kernel,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": round(step_bytes),
+        "mean_launch_us": round(launch_us, 3),
+        "timing": "mean launch time from HIP events on the launch stream around the timed launches",
+    }
+    prof = profile_time(kernel, args.workload)
+    if prof is not None:
+        roof["profile"] = {"avg_us": round(prof["avg_ns"] / 1e3, 3), "calls": prof["calls"],
+                           "frac": round(step_bytes / (prof["avg_ns"] * 1e-9) / 1e9 / HBM_PEAK_GBPS, 4),
+                           "source": "profiles/kernel_times.json (rocprofv3 --kernel-trace --stats, same sources)"}
+    if not moe and "ceiling" in r:
+        c = r["ceiling"]
+        cg = step_bytes / (c["event_ms"] * 1e-3) / 1e9
+        roof["ceiling"] = {"gbps": round(cg, 1), "frac": round(achieved / cg, 4), **c["config"],
+                           "kind": "csf_probe_mix on the same buffers: the decode's streams and access shape "
+                                   "without its work"}
     out = {
         "metric": MOE_METRIC if moe else METRIC,
         "value": round(gbps, 2),
@@ -686,65 +956,13 @@ def main():
         "dtype": "bf16" if moe else "u8",
         "data": "synthetic",
         "config": config,
-        "roofline": {
-            "kernel": kernel,
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": round(step_bytes),
-            "mean_launch_us": round(launch_us, 3),
-        },
+        "roofline": roof,
     }
     if args.all:
-        extra = {}
-        del r
-        for name in ("gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4"):
-            s = workloads.STACKS[name]
-            log(f"[bench] {name}")
-            rr = bench_stack(mwd, torch, ev, s, min(args.steps, 2000), args.warmup,
-                             args.sets if s.E > 4 else 2, dev, split=True)
-            b = rr["fixed_bytes"] + rr["exc_bytes"] + rr["dense_bytes"]
-            extra[name] = dict(us=round(rr["step_ms"] * 1e3, 2),
-                               gbps=round(b / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                               two_pass_us=round(rr["two_pass_ms"] * 1e3, 2),
-                               fixed_only_us=round(rr["fixed_only_ms"] * 1e3, 2),
-                               warm_us=round(rr["warm_ms"] * 1e3, 2),
-                               flushed_us=round(rr["flushed_ms"] * 1e3, 2),
-                               bytes=b, entries=rr["stack"].num_exceptions)
-            xd = torch.from_numpy(rr["x"]).to(dev)
-            enc = []
-            for i in range(12):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                mwd.prepare(xd, s.fmt)  # device encode; reads back the entry count once
-                torch.cuda.synchronize()
-                enc.append(time.perf_counter() - t0)
-            extra[name]["gpu_encode_us"] = round(statistics.median(enc[2:]) * 1e6, 1)
-            log(f"[bench] {name}: {extra[name]}")
-            del rr, xd
-            torch.cuda.empty_cache()
-        for indexed, gate_only in ((True, False), (False, False), (True, True)):
-            key = ("routed_gate" if gate_only else "routed_paired") + ("" if indexed else "_two_pass")
-            log(f"[bench] {key}")
-            rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed,
-                              gate_only=gate_only)
-            extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2),
-                              gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
-                              warm_us=round(rr["warm_ms"] * 1e3, 2), flushed_us=round(rr["flushed_ms"] * 1e3, 2),
-                              bytes=round(rr["bytes"]),
-                              active=rr["active"], sets=rr["sets"])
-            log(f"[bench] {key}: {extra[key]}")
-        extra["launch_floor"] = launch_floor(torch, ev, dev)
-        log(f"[bench] launch floor: {extra['launch_floor']}")
-        cg, cms = bench_copy(torch, ev, mwd, dev, 64 << 20, 8, 500)
-        extra["copy_64MiB"] = dict(gbps=round(cg, 1), us=round(cms * 1e3, 2))
-        log(f"[bench] plain copy 64 MiB: {extra['copy_64MiB']}")
+        out_all = run_all(mwd, torch, ev, workloads, args, dev)
         if args.all_json:
             os.makedirs(os.path.dirname(os.path.abspath(args.all_json)), exist_ok=True)
-            json.dump(extra, open(args.all_json, "w"), indent=1)
+            json.dump(out_all, open(args.all_json, "w"), indent=1)
     if args.calibrate_copy:
         # an elementwise kernel (a large device-to-device copy_ may go to a DMA
         # engine, which the counters do not see): 256 MiB read, 256 MiB written
@@ -766,6 +984,75 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def run_all(mwd, torch, ev, workloads, args, dev):
+    """The --all measurements; one line each on stderr; returns them."""
+    import numpy as np
+    extra = {}
+    for name in ("gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4"):
+        s = workloads.STACKS[name]
+        log(f"[bench] {name}")
+        rr = bench_stack(mwd, torch, ev, s, min(args.steps, 2000), args.warmup,
+                         args.sets if s.E > 4 else 2, dev, split=True)
+        b = rr["bytes"]
+        e = dict(us=round(rr["step_ms"] * 1e3, 2), event_us=round(rr["event_ms"] * 1e3, 2),
+                 gbps=round(b.metric / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                 event_gbps=round(b.metric / (rr["event_ms"] * 1e-3) / 1e9, 1),
+                 two_pass_us=round(rr["two_pass_ms"] * 1e3, 2),
+                 fixed_only_us=round(rr["fixed_only_ms"] * 1e3, 2),
+                 warm_us=round(rr["warm_ms"] * 1e3, 2),
+                 flushed_us=round(rr["flushed_ms"] * 1e3, 2),
+                 bytes=b.metric, index_bytes=b.index, entries=rr["stack"].num_exceptions)
+        if "ceiling" in rr:
+            c = rr["ceiling"]
+            cg = b.metric / (c["event_ms"] * 1e-3) / 1e9
+            e.update(ceiling_us=round(c["event_ms"] * 1e3, 2), ceiling_gbps=round(cg, 1),
+                     frac_of_ceiling=round(c["event_ms"] / rr["event_ms"], 4), ceiling_config=c["config"],
+                     ceiling_without_entries_gbps=round((b.metric - b.exc) / (c["without_entries_ms"] * 1e-3) / 1e9,
+                                                        1))
+        xd = torch.from_numpy(rr["x"]).to(dev)
+        enc = []
+        for i in range(12):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            mwd.prepare(xd, s.fmt)  # device encode; reads back the entry count once
+            torch.cuda.synchronize()
+            enc.append(time.perf_counter() - t0)
+        e["gpu_encode_us"] = round(statistics.median(enc[2:]) * 1e6, 1)
+        extra[name] = e
+        log(f"[bench] {name}: {e}")
+        del rr, xd
+        torch.cuda.empty_cache()
+    for indexed, gate_only in ((True, False), (False, False), (True, True)):
+        key = ("routed_gate" if gate_only else "routed_paired") + ("" if indexed else "_two_pass")
+        log(f"[bench] {key}")
+        rr = bench_routed(mwd, torch, ev, workloads, min(args.steps, 2000), args.warmup, dev, indexed,
+                          gate_only=gate_only)
+        extra[key] = dict(us=round(rr["step_ms"] * 1e3, 2), event_us=round(rr["event_ms"] * 1e3, 3),
+                          gbps=round(rr["bytes"] / (rr["step_ms"] * 1e-3) / 1e9, 1),
+                          warm_us=round(rr["warm_ms"] * 1e3, 2), flushed_us=round(rr["flushed_ms"] * 1e3, 2),
+                          bytes=round(rr["bytes"]), index_bytes=round(rr["index_bytes"]),
+                          active=rr["active"], sets=rr["sets"])
+        log(f"[bench] {key}: {extra[key]}")
+    gspec, dspec = workloads.ROUTED.stacks
+    g = mwd.prepare(gspec.generate(), gspec.fmt).to(dev)
+    d = mwd.prepare(dspec.generate(), dspec.fmt).to(dev)
+    es_t = torch.from_numpy(workloads.ROUTED.expert_start()).to(dev)
+    groups = mwd.decode_traced(g, torch.empty(g.dense_bytes, dtype=torch.uint8, device=dev), d,
+                               torch.empty(d.dense_bytes, dtype=torch.uint8, device=dev), es_t).shape[0]
+    torch.cuda.synchronize()
+    extra["launch_floors"] = launch_floors(torch, ev, dev, groups)
+    log(f"[bench] launch floors: {extra['launch_floors']}")
+    extra["host_cost"] = host_cost(mwd, torch, dev, g, d, es_t)
+    log(f"[bench] host cost per call: {extra['host_cost']}")
+    spec = workloads.ROUTED
+    rs = routed_sets(workloads, gspec.E, spec.n_active, spec.max_tokens, spec.seed + 100, 64)
+    extra["routed_trace"] = trace_routed(mwd, torch, dev, g, d, rs)
+    log(f"[bench] routed paired decode, per-step timestamps: {extra['routed_trace']}")
+    del g, d
+    torch.cuda.empty_cache()
+    return extra
 
 
 if __name__ == "__main__":

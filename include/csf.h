@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSF_ABI_VERSION 4
+#define CSF_ABI_VERSION 5
 
 /* Positions per exception-index tile. */
 #define CSF_INDEX_TILE 2048
@@ -296,6 +296,33 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
 csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, const uint8_t *weights,
                          const uint16_t *x, int32_t num_tokens, const float *alpha,
                          const int32_t *expert_start, float *y, void *hip_stream);
+
+/*
+ * Routed csf_decode_paired with timestamps, to show where the time of a
+ * routed call goes (PR 1236, measurements paragraph, times the decode of the
+ * routed experts' scales alone).  Decodes exactly as csf_decode_paired with
+ * a non-NULL int32 expert_start (second may be NULL for one stack); both
+ * stacks need a tile index.  Each workgroup also writes, from the GPU's
+ * constant-rate clock (s_memrealtime, 100 MHz on MI355X), eight words to
+ * stamps[8 g .. 8 g + 7] (g = workgroup):
+ *   0 start;  1 routing read (expert_start loaded, active experts counted);
+ *   2 the tile's loads complete (offsets, row bases and tile-index bounds,
+ *   then the tile's first 1024 exception entries);  3 tile expanded in LDS;
+ *   4 exceptions patched;  5 stores issued;  6 stores complete;  7 a tag:
+ *   0 = no tile for this workgroup, 1 + u = tile u (plus 2^32 when the tile
+ *   has more entries than those first ones), all ones = more tiles than
+ *   workgroups (the pipelined loop ran).  Steps a workgroup does not reach
+ *   read 0.
+ * The waits before steps 2 and 6 make the traced call a little slower than
+ * the untraced one.  Two-call pattern: with stamps NULL, *groups receives the
+ * number of workgroups the call launches and nothing is enqueued; otherwise
+ * capacity (words) must be at least 8 * that number.
+ * Errors: CSF_E_NULL (expert_start, groups, or a tile index missing),
+ *   CSF_E_SIZE (capacity), otherwise as csf_decode_paired.
+ */
+csf_status csf_decode_traced(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
+                             uint8_t *ws_second, const int32_t *expert_start, uint64_t *stamps,
+                             uint64_t capacity, uint32_t *groups, void *hip_stream);
 
 /*
  * Full host-side check of a stack whose buffers are in HOST memory: prefix

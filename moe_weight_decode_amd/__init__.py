@@ -24,6 +24,8 @@ The functions mirror the C ABI in ``include/csf.h``:
   from the CSF streams, or reads them from a dense workspace;
 * ``Launch(...)``: a decode with its arguments marshalled once, for loops
   and graph capture;
+* ``decode_traced(...)``: a routed decode that also records per-workgroup
+  timestamps of its steps;
 * ``build_index(stack)`` (the per-tile exception index, built on the GPU);
 * ``validate(stack)`` (host-side layout check).
 
@@ -57,7 +59,8 @@ STATUS = {0: "CSF_OK", 1: "CSF_E_NULL", 2: "CSF_E_SHAPE", 3: "CSF_E_FORMAT", 4: 
 
 EXPORTS = ("csf_abi_version", "csf_status_str", "csf_prepare", "csf_encode_device", "csf_build_index",
            "csf_decode", "csf_decode_paired", "csf_decode_i64", "csf_decode_passes", "csf_decode_rows",
-           "csf_moe_w4a16", "csf_validate")
+           "csf_moe_w4a16", "csf_decode_traced", "csf_validate")
+STAMPS_PER_GROUP = 8
 
 
 class CsfError(RuntimeError):
@@ -125,6 +128,9 @@ def _lib():
                                         ctypes.c_uint32, vp]
         lib.csf_moe_w4a16.restype = ctypes.c_int
         lib.csf_moe_w4a16.argtypes = [ctypes.POINTER(csf_stack), vp, vp, vp, i32, vp, vp, vp, vp]
+        lib.csf_decode_traced.restype = ctypes.c_int
+        lib.csf_decode_traced.argtypes = [ctypes.POINTER(csf_stack), vp, ctypes.POINTER(csf_stack), vp, vp, vp,
+                                          ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint32), vp]
         lib.csf_validate.restype = ctypes.c_int
         lib.csf_validate.argtypes = [ctypes.POINTER(csf_stack)]
         _LIB = lib
@@ -158,6 +164,10 @@ class CompressedStack:
     @property
     def P(self) -> int:
         return self.R * self.C
+
+    def tiles_per_plane(self, tile: int) -> int:
+        """Tiles of ``tile`` positions covering one plane."""
+        return (self.P + tile - 1) // tile
 
     @property
     def dense_bytes(self) -> int:
@@ -252,6 +262,13 @@ def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> Comp
     offsets = torch.empty(E * S, dtype=torch.uint8, device=dev)
     prefix = torch.empty(E + 1, dtype=torch.int32, device=dev)
     tidx = torch.empty(E * NT + 1, dtype=torch.int32, device=dev)
+    cur = torch.cuda.current_stream(dev)
+    side = stream is not None and _stream_handle(stream, dev) != cur.cuda_stream
+    if side:
+        # the outputs were allocated on the current stream, whose queued work
+        # may still use their memory (freed there just before): `stream`
+        # writes them only after that work
+        stream.wait_stream(cur)
     h = _stream_handle(stream, dev)
     _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), offsets.data_ptr(), None,
                                  prefix.data_ptr(), tidx.data_ptr(), ENCODE_STREAMS, h),
@@ -263,7 +280,7 @@ def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> Comp
     if n > 0:
         _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), None, exc.data_ptr(),
                                      None, tidx.data_ptr(), ENCODE_ENTRIES, h), "csf_encode_device(entries)")
-    if stream is not None and stream != torch.cuda.current_stream(dev):
+    if side:
         # allocated on the current stream, written on `stream`: keep the memory
         # from being reused before `stream` is done with it
         for t in (bases, offsets, prefix, tidx, exc, x):
@@ -278,7 +295,9 @@ def prepare(dense, fmt: int, index: bool = True, stream=None) -> CompressedStack
     once, to size their buffer); host data by the host encoder.  The GPU
     encode runs on ``stream`` (default: the current stream): ``dense`` must be
     ready there, and work on another stream that uses the result must wait
-    for ``stream`` (for example ``current_stream().wait_stream(stream)``)."""
+    for ``stream`` (for example ``current_stream().wait_stream(stream)``).
+    A ``stream`` other than the current one first waits for the current
+    stream's queued work, since the result's memory is allocated there."""
     if isinstance(dense, torch.Tensor) and dense.device.type == "cuda":
         return _prepare_device(dense, fmt, index, stream)
     lib = _lib()
@@ -491,6 +510,32 @@ class Launch:
                           self._stream)
         if st != 0:
             raise CsfError(st, "csf_decode_passes")
+
+
+def decode_traced(first: CompressedStack, ws_first: torch.Tensor, second=None, ws_second=None,
+                  expert_start=None, stream=None) -> torch.Tensor:
+    """Enqueue a routed decode (int32 ``expert_start``, stacks with a tile
+    index) that also records per-workgroup timestamps (see
+    ``csf_decode_traced``); returns the uint64 stamps as an int64 tensor
+    [groups, 8] on the device."""
+    _check_device(first, ws_first, "decode_traced")
+    b_ref, ws_b = None, None
+    if second is not None:
+        _check_device(second, ws_second, "decode_traced")
+        b = second.descriptor()
+        b_ref, ws_b = ctypes.byref(b), ws_second.data_ptr()
+    if expert_start is None or _is_wide(expert_start):
+        raise ValueError("decode_traced takes an int32 expert_start")
+    a = first.descriptor()
+    es, h = _es_ptr(expert_start, first), _stream_handle(stream, first.device)
+    groups = ctypes.c_uint32(0)
+    lib = _lib()
+    _check(lib.csf_decode_traced(ctypes.byref(a), ws_first.data_ptr(), b_ref, ws_b, es, None, 0,
+                                 ctypes.byref(groups), h), "csf_decode_traced(groups)")
+    stamps = torch.zeros(groups.value, STAMPS_PER_GROUP, dtype=torch.int64, device=first.device)
+    _check(lib.csf_decode_traced(ctypes.byref(a), ws_first.data_ptr(), b_ref, ws_b, es, stamps.data_ptr(),
+                                 stamps.numel(), ctypes.byref(groups), h), "csf_decode_traced")
+    return stamps
 
 
 def build_index(stack: CompressedStack, stream=None) -> torch.Tensor:

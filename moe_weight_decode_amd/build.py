@@ -16,6 +16,10 @@ SOURCES = [os.path.join(CSRC, "csf_api.cpp"), os.path.join(CSRC, "csf_kernels.hi
 HEADERS = [os.path.join(ROOT, "include", "csf.h"), os.path.join(CSRC, "csf_launch.h"),
            os.path.join(CSRC, "csf_device.h")]
 LIBRARY = os.path.join(PKG, "libcsf.so")
+# measurement kernels (ceilings, launch floors, host cost), linked to libcsf.so
+PROBE_SOURCES = [os.path.join(CSRC, "csf_probe.hip")]
+PROBE_HEADERS = [os.path.join(ROOT, "include", "csf_probe.h")]
+PROBE_LIBRARY = os.path.join(PKG, "libcsf_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -32,11 +36,20 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(output: str = LIBRARY, defines=(), extra_flags=()) -> str:
-    """Compile the library; returns its path.  ``defines`` are NAME=VALUE strings."""
+def build(output: str = LIBRARY, defines=(), extra_flags=(), probe: bool = True) -> str:
+    """Compile the library (and, with ``probe``, libcsf_probe.so next to it);
+    returns the library's path.  ``defines`` are NAME=VALUE strings."""
+    _compile(SOURCES, output, defines, extra_flags)
+    if probe and output == LIBRARY:
+        _compile(PROBE_SOURCES, PROBE_LIBRARY, defines, extra_flags,
+                 link=["-L", PKG, "-lcsf", "-Wl,-rpath,$ORIGIN"])
+    return output
+
+
+def _compile(sources, output, defines=(), extra_flags=(), link=()):
     tmp = output + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *[f"-D{d}" for d in defines],
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *SOURCES, "-o", tmp]
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, *sources, "-o", tmp, *link]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass names the device-only target feature it ignores; only
     # that warning is tolerated
@@ -47,14 +60,13 @@ def build(output: str = LIBRARY, defines=(), extra_flags=()) -> str:
     if err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, output)
-    return output
 
 
 def stale(path: str = LIBRARY) -> bool:
-    if not os.path.exists(path):
+    if not os.path.exists(path) or not os.path.exists(PROBE_LIBRARY):
         return True
-    t = os.path.getmtime(path)
-    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+    t = min(os.path.getmtime(path), os.path.getmtime(PROBE_LIBRARY))
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS + PROBE_SOURCES + PROBE_HEADERS)
 
 
 if __name__ == "__main__":

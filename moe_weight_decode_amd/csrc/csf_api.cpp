@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <new>
 #include <thread>
@@ -158,7 +159,7 @@ Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
     }
     Plan p;
     if (routed)
-        p = {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU, csf::kSchedStreamAll, 4};
+        p = {CSF_ROUTED_RUNS, CSF_ROUTED_WG_PER_CU, csf::kSchedRouted, 4};
     else if (nvfp4 && entries * 1000000 <= dense * int64_t(CSF_SPARSE_PPM))
         p = {CSF_SPARSE_RUNS, CSF_SPARSE_WG_PER_CU, csf::kSchedPipelined, 4};
     else
@@ -170,19 +171,51 @@ Plan plan_tiles(const csf_stack *s0, const csf_stack *s1, bool routed) {
     return p;
 }
 
-uint32_t cu_count(hipStream_t stream) {
-    int dev = 0;
-    if (stream != nullptr) {
-        if (hipStreamGetDevice(stream, &dev) != hipSuccess) dev = -1;
-    } else {
+// Compute units of each device, read once per device (the grid of every
+// launch is a multiple of it).  A stream's device is remembered per thread
+// for the last stream seen: a stale entry (a stream destroyed and its handle
+// reused on another device) could only change a grid size, never a result,
+// since every kernel is correct for any grid.
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_cus[kMaxDevices];
+
+int stream_device(hipStream_t stream) {
+    thread_local hipStream_t last_stream = nullptr;
+    thread_local int last_dev = -1;
+    int dev = -1;
+    if (stream == nullptr) {
+        if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    } else if (stream == last_stream && last_dev >= 0) {
+        dev = last_dev;
+    } else if (hipStreamGetDevice(stream, &dev) == hipSuccess) {
+        last_stream = stream;
+        last_dev = dev;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
         dev = -1;
     }
-    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 256;
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        return 256;
-    return uint32_t(n);
+    (void)hipGetLastError();  // a failed query leaves no error for the launch that follows
+    return dev;
 }
+
+uint32_t cu_count(hipStream_t stream) {
+    const int dev = stream_device(stream);
+    if (dev < 0 || dev >= kMaxDevices) return 256;
+    uint32_t n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+            (void)hipGetLastError();
+            return 256;
+        }
+        n = uint32_t(v);
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// HIP reports the last error of any runtime call on the thread: one left by
+// an earlier call must not be taken for a failure of this call's launches.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 // Row window of a stack: rows, or every row when rows is NULL.
 bool window(const csf_stack *s, const csf_rows *rows, int32_t &rb, int32_t &re) {
@@ -191,9 +224,16 @@ bool window(const csf_stack *s, const csf_rows *rows, int32_t &rb, int32_t &re) 
     return 0 <= rb && rb <= re && re <= s->rows;
 }
 
+// A traced decode (csf_decode_traced): where the timestamps go.
+struct Trace {
+    uint64_t *stamps;
+    uint64_t capacity;
+    uint32_t *groups;
+};
+
 csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, const csf_stack *s1,
                    uint8_t *ws1, const csf_rows *rows1, const void *expert_start, bool es_wide,
-                   uint32_t passes, void *hip_stream) {
+                   uint32_t passes, void *hip_stream, const Trace *trace = nullptr) {
     if (passes == 0 || (passes & ~CSF_PASS_ALL) != 0) return CSF_E_SIZE;
     csf_status st = check_stack(s0, ws0);
     if (st != CSF_OK) return st;
@@ -243,6 +283,20 @@ csf_status enqueue(const csf_stack *s0, uint8_t *ws0, const csf_rows *rows0, con
     const uint32_t tile_grid = uint32_t(std::max<uint64_t>(1, std::min(tile_units, tile_cap)));
 
     const bool indexed = s0->tile_index != nullptr && (s1 == nullptr || s1->tile_index != nullptr);
+    if (trace != nullptr) {
+        if (!indexed || !routed) return CSF_E_NULL;
+        if (trace->stamps == nullptr) {
+            *trace->groups = tile_grid;
+            return CSF_OK;
+        }
+        if (trace->capacity < uint64_t(csf::kStampsPerGroup) * tile_grid) return CSF_E_SIZE;
+        a.stamps = trace->stamps;
+        clear_stale_error();
+        if (csf::launch_fused_traced(a, tile_grid, stream) != hipSuccess) return CSF_E_HIP;
+        *trace->groups = tile_grid;
+        return CSF_OK;
+    }
+    clear_stale_error();
     if (passes == CSF_PASS_ALL && indexed) {
         if (csf::launch_fused(a, tile_grid, stream) != hipSuccess) return CSF_E_HIP;
         return CSF_OK;
@@ -307,6 +361,7 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     const uint64_t units = uint64_t(a.E) * a.ntiles;
     const uint64_t cap = uint64_t(cu_count(stream)) * CSF_MOE_WG_PER_CU;
     const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(units, cap)));
+    clear_stale_error();
     if (csf::launch_moe_w4a16(a, grid, stream) != hipSuccess) return CSF_E_HIP;
     return CSF_OK;
 }
@@ -320,6 +375,7 @@ csf_status build_index_impl(const csf_stack *s, int32_t *tile_index, void *hip_s
     fill_stack(a, *s, nullptr, csf::kIndexTile, 0, s->rows);
     if (a.n_exc == 0) a.exc = nullptr;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    clear_stale_error();
     if (csf::launch_build_index(a, uint32_t(s->num_experts), tile_index, stream) != hipSuccess)
         return CSF_E_HIP;
     return CSF_OK;
@@ -359,6 +415,7 @@ csf_status encode_device_impl(int32_t format, int32_t E, int32_t R, int32_t C, c
     a.wbits = uint32_t(offset_bits(format));
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const uint32_t cus = cu_count(stream);
+    clear_stale_error();
     const hipError_t err = phase == CSF_ENCODE_STREAMS ? csf::launch_encode_streams(a, cus, stream)
                                                        : csf::launch_encode_entries(a, cus, stream);
     return err == hipSuccess ? CSF_OK : CSF_E_HIP;
@@ -701,6 +758,19 @@ csf_status csf_moe_w4a16(const csf_stack *scales, const uint8_t *dense_scales, c
                          const int32_t *expert_start, float *y, void *hip_stream) {
     try {
         return moe_impl(scales, dense_scales, weights, x, num_tokens, alpha, expert_start, y, hip_stream);
+    } catch (...) {
+        return CSF_E_HIP;
+    }
+}
+
+csf_status csf_decode_traced(const csf_stack *first, uint8_t *ws_first, const csf_stack *second,
+                             uint8_t *ws_second, const int32_t *expert_start, uint64_t *stamps,
+                             uint64_t capacity, uint32_t *groups, void *hip_stream) {
+    if (expert_start == nullptr || groups == nullptr) return CSF_E_NULL;
+    const Trace trace{stamps, capacity, groups};
+    try {
+        return enqueue(first, ws_first, nullptr, second, second ? ws_second : nullptr, nullptr, expert_start,
+                       false, CSF_PASS_ALL, hip_stream, &trace);
     } catch (...) {
         return CSF_E_HIP;
     }

@@ -199,15 +199,18 @@ __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *d
 //   kPipelined      pipelined loop, cached loads (stacks with few exceptions)
 //   kStreamEntries  serial loop, non-temporal entry loads (dense exception
 //                   streams)
-//   kStreamAll      pipelined loop, non-temporal offset and entry loads
-//                   (routed decodes: their planes are read once and are
-//                   rarely cache-resident)
+//   kRouted         routed decodes: at most one tile per workgroup, its
+//                   loads issued in one round trip after the routing's
+//                   (routed_decode); more tiles than workgroups take the
+//                   pipelined loop.  Offset and entry loads are
+//                   non-temporal: routed planes are read once and are
+//                   rarely cache-resident.
 // Which loop suits which stream was measured on MI355X: on dense exception
 // streams the serial loop with non-temporal entries is the fastest.
 enum Sched : uint32_t {
     kPipelined = kSchedPipelined,
     kStreamEntries = kSchedStreamEntries,
-    kStreamAll = kSchedStreamAll
+    kRouted = kSchedRouted
 };
 
 // Everything a tile needs from memory, loaded ahead of its decode: the
@@ -275,6 +278,46 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
     }
 }
 
+// Store tile bytes s0 .. n-1 of the LDS tile to plane positions q0 .. q1-1
+// (s0 > 0 only where a row window starts inside the tile).  Whole 16-byte
+// runs of an aligned tile from the first run boundary at or after s0,
+// h .. wend-1, take one non-temporal 128-bit store each, issued for every
+// run: the resource starts at h, so runs before it have offsets that wrap
+// past the resource and runs past wend lie beyond it; the hardware drops
+// both.  A ragged window edge or a misaligned workspace leaves bytes for the
+// byte loop.
+template <uint32_t RUNS, bool WINDOW>
+__device__ __forceinline__ void store_tile(const StackArgs &st, uint8_t *plane, uint32_t q0, uint32_t q1,
+                                           const uint8_t *tile) {
+    uint8_t *dst = plane + q0;
+    const uint32_t n = q1 - q0;
+    const uint32_t s0 = WINDOW && st.pbeg > q0 ? st.pbeg - q0 : 0u;
+    const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+    const uint32_t h = aligned ? (WINDOW ? min((s0 + 15u) & ~15u, n) : 0u) : n;
+    const uint32_t wend = max(h, n & ~15u);
+    const rsrc_t rw = make_rsrc(dst + h, wend - h);
+#pragma unroll
+    for (uint32_t i = 0; i < RUNS; ++i) {
+        const uint32_t off = kRunBytes * (i * kBlock + threadIdx.x);
+        const u32x4 out = *reinterpret_cast<const u32x4 *>(tile + off);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)(off - h), 0,
+                                               kNonTemporal);
+    }
+    if (WINDOW || !aligned)
+        for (uint32_t b = s0 + threadIdx.x; b < h; b += kBlock) dst[b] = tile[b];
+    for (uint32_t b = wend + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
+}
+
+// Row bases of a tile's rows into LDS: the first 2 * kBlock from the loaded
+// bytes b0 / b1, any further rows from memory.
+__device__ __forceinline__ void stage_bases(const StackArgs &st, uint32_t e, uint32_t r_lo, uint32_t nrows,
+                                            uint8_t b0, uint8_t b1, uint8_t *lds_bases) {
+    if (threadIdx.x < nrows) lds_bases[threadIdx.x] = b0;
+    if (threadIdx.x + kBlock < nrows) lds_bases[threadIdx.x + kBlock] = b1;
+    const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
+    for (uint32_t r = threadIdx.x + 2u * kBlock; r < nrows; r += kBlock) lds_bases[r] = brow[r];
+}
+
 // ---------------------------------------------------------------------------
 // Pipelined tile loop of the fused kernel.
 //
@@ -290,19 +333,16 @@ __device__ __forceinline__ void issue_loads(const StackArgs &st, const Unit &w, 
 // patches the tile's entries into it and stores the finished tile with
 // non-temporal stores.  The next tile's loads go out before this tile's
 // stores, so no wait on a tile's data also waits for the stores before it.
-// POLICY is the cache policy of the offset and entry loads.
+// POLICY is the cache policy of the offset and entry loads.  Routed launches
+// pass their nact active experts in act[] (routed), others every expert.
 // ---------------------------------------------------------------------------
 template <uint32_t RUNS, uint32_t EXC, int POLICY, bool WINDOW>
-__device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+__device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t *lds_bases, uint8_t *tile,
+                                                    uint32_t nact, const uint16_t *act, bool routed) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
     static_assert(EXC % 4 == 0, "entries are prefetched in 16-byte loads");
-    uint8_t *lds_bases = dyn;
-    uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
-    uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
 
-    const bool routed = a.expert_start != nullptr;
-    const uint32_t nact = routed ? active_experts(a, act, flags) : a.E;
     const uint32_t u0 = nact * a.st[0].tiles;
     const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
     if (blockIdx.x >= total) return;
@@ -350,10 +390,7 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
         const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
 
         // Row bases into LDS (the barrier also ends the previous tile's LDS reads).
-        if (threadIdx.x < nrows) lds_bases[threadIdx.x] = L.b0;
-        if (threadIdx.x + kBlock < nrows) lds_bases[threadIdx.x + kBlock] = L.b1;
-        const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
-        for (uint32_t r = threadIdx.x + 2u * kBlock; r < nrows; r += kBlock) lds_bases[r] = brow[r];
+        stage_bases(st, e, r_lo, nrows, L.b0, L.b1, lds_bases);
         __syncthreads();
 
         uint8_t *plane = st.ws + (uint64_t)e * st.P;
@@ -386,32 +423,7 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
             // The next unit's loads go out before this tile's stores.
             issue_loads<RUNS, EXC, POLICY>(pick(a, cur.s), cur, cur.t * TILE, blo, bhi, j, L);
         }
-
-        // Tile bytes s0 .. n-1 are stored (s0 > 0 only where a row window
-        // starts inside the tile).  Whole 16-byte runs of an aligned tile
-        // from the first run boundary at or after s0, h .. wend-1, take one
-        // non-temporal 128-bit store each, issued for every run: the resource
-        // starts at h, so runs before it have offsets that wrap past the
-        // resource and runs past wend lie beyond it; the hardware drops both.
-        // A ragged window edge or a misaligned workspace leaves bytes for the
-        // byte loop.
-        uint8_t *dst = plane + q0;
-        const uint32_t n = q1 - q0;
-        const uint32_t s0 = WINDOW && st.pbeg > q0 ? st.pbeg - q0 : 0u;
-        const bool aligned = (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
-        const uint32_t h = aligned ? (WINDOW ? min((s0 + 15u) & ~15u, n) : 0u) : n;
-        const uint32_t wend = max(h, n & ~15u);
-        const rsrc_t rw = make_rsrc(dst + h, wend - h);
-#pragma unroll
-        for (uint32_t i = 0; i < RUNS; ++i) {
-            const uint32_t off = kRunBytes * (i * kBlock + threadIdx.x);
-            const u32x4 out = *reinterpret_cast<const u32x4 *>(tile + off);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)(off - h),
-                                                   0, kNonTemporal);
-        }
-        if (WINDOW || !aligned)
-            for (uint32_t b = s0 + threadIdx.x; b < h; b += kBlock) dst[b] = tile[b];
-        for (uint32_t b = wend + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
+        store_tile<RUNS, WINDOW>(st, plane, q0, q1, tile);
         // The next tile's first barrier orders these LDS reads before the
         // next expansion overwrites the tile.
         if (!more) break;
@@ -419,15 +431,331 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
     }
 }
 
+// ---------------------------------------------------------------------------
+// Routed decode (kRouted).
+//
+// Every wave reads expert_start on its own with 16-byte loads: lane l of
+// chunk i holds the V = 16 / sizeof(T) values from 64 V i + V l (and, by one
+// more load, the value after them), so the active flags of 64 V experts take
+// one load per lane plus one, and V ballots hold them in scalar registers
+// (no LDS, no barrier).  When the launch has a workgroup for every unit
+// (stack, active expert, tile), workgroup b takes unit b: the workgroup's
+// expert is the k-th active one, found from the ballots with per-lane bit
+// counts.  Its tile then costs two more round trips: the offset groups, the
+// row bases each lane's 16-byte run touches (read into registers) and the
+// tile-index bounds, then the tile's exception entries.  More units than
+// workgroups, or more experts, take the pipelined loop.
+// STAMP records s_memrealtime values per workgroup in a.stamps (phases in
+// csf_decode_traced's documentation).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kFastExperts = 512;
+
+// Position of the k-th set bit (k < popcount) of w.
+__device__ __forceinline__ uint32_t nth_set_bit(uint64_t w, uint32_t k) {
+    uint32_t pos = 0;
+#pragma unroll
+    for (uint32_t s = 32; s >= 1; s >>= 1) {
+        const uint32_t c = (uint32_t)__popcll(w & ((1ull << s) - 1ull));
+        if (k >= c) {
+            k -= c;
+            w >>= s;
+            pos += s;
+        }
+    }
+    return pos;
+}
+
+// Set bits of m below this lane.
+__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The routed unit of this workgroup.
+struct RoutedUnit {
+    uint32_t total;    // units of the launch
+    uint32_t s, e, t;  // this workgroup's unit (when blockIdx.x < total <= gridDim.x)
+};
+
+template <typename T>
+__device__ __forceinline__ RoutedUnit route_unit(const DecodeArgs &a, const T *es) {
+    constexpr uint32_t V = 16 / sizeof(T);                 // experts per lane per chunk
+    constexpr uint32_t CH = kFastExperts / (kWave * V);    // chunks at most
+    typedef T tv __attribute__((ext_vector_type(V)));
+    const uint32_t E = a.E, lane = threadIdx.x % kWave;
+    // Loads are issued unconditionally, at addresses clamped into the tensor,
+    // so none waits for another; lanes and chunks past E are masked below.
+    // Whole 16-byte loads when they cannot run past the tensor.
+    const bool vec = (reinterpret_cast<uintptr_t>(es) & 15u) == 0 && E % V == 0;
+    T x[CH][V], nxt[CH];
+    if (vec) {
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) {
+            const uint32_t b = kWave * V * i + V * lane;  // first expert of this lane
+            const tv q = *reinterpret_cast<const tv *>(es + min(b, E - V));
+#pragma unroll
+            for (uint32_t c = 0; c < V; ++c) x[i][c] = q[c];
+            nxt[i] = es[min(b + V, E)];
+        }
+    } else {
+#pragma unroll
+        for (uint32_t i = 0; i < CH; ++i) {
+            const uint32_t b = kWave * V * i + V * lane;
+#pragma unroll
+            for (uint32_t c = 0; c < V; ++c) x[i][c] = es[min(b + c, E)];
+            nxt[i] = es[min(b + V, E)];
+        }
+    }
+    // f[i]: bit c = expert 64 V i + V lane + c has tokens; ballots per c.
+    uint32_t f[CH];
+    uint64_t m[CH][V];
+    uint32_t nact = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < CH; ++i) {
+        const uint32_t b = kWave * V * i + V * lane;
+        f[i] = 0;
+#pragma unroll
+        for (uint32_t c = 0; c < V; ++c) {
+            const T after = c + 1 < V ? x[i][c + 1 < V ? c + 1 : 0] : nxt[i];
+            const bool on = b + c < E && after > x[i][c];
+            f[i] |= on ? 1u << c : 0u;
+            m[i][c] = __ballot(on);
+            nact += (uint32_t)__popcll(m[i][c]);
+        }
+    }
+    RoutedUnit r;
+    const uint32_t u0 = nact * a.st[0].tiles;
+    r.total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
+    r.s = r.e = r.t = 0;
+    const uint32_t u = blockIdx.x;
+    if (u >= r.total || r.total > gridDim.x) return r;
+    r.s = u >= u0 ? 1u : 0u;
+    const uint32_t tiles = r.s ? a.st[1].tiles : a.st[0].tiles;
+    const uint32_t uu = u - (r.s ? u0 : 0u);
+    uint32_t k = uu / tiles;
+    r.t = (r.s ? a.st[1].tile0 : a.st[0].tile0) + uu - k * tiles;
+    // The k-th active expert: its chunk, then its lane (the lane whose bits
+    // below it in the chunk count at most k), then its bit.
+    uint32_t e = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < CH; ++i) {
+        uint32_t cnt = 0, below = 0;
+#pragma unroll
+        for (uint32_t c = 0; c < V; ++c) {
+            cnt += (uint32_t)__popcll(m[i][c]);
+            below += bits_below(m[i][c]);
+        }
+        if (k < cnt) {
+            const uint32_t own = (uint32_t)__popc(f[i]);
+            const uint64_t hit = __ballot(below <= k && k < below + own);
+            const uint32_t L = (uint32_t)__builtin_ctzll(hit);
+            const uint32_t fl = __builtin_amdgcn_readlane(f[i], (int)L);
+            const uint32_t bl = __builtin_amdgcn_readlane(below, (int)L);
+            e = kWave * V * i + V * L + nth_set_bit(fl, k - bl);
+            k = ~0u >> 1;  // found: no later chunk matches
+        } else {
+            k -= cnt;
+        }
+    }
+    r.e = __builtin_amdgcn_readfirstlane(e);
+    return r;
+}
+
+template <bool STAMP>
+struct Clock {
+    uint64_t t[kStampsPerGroup];
+    __device__ __forceinline__ Clock() {
+        if constexpr (STAMP)
+            for (uint32_t i = 0; i < kStampsPerGroup; ++i) t[i] = 0;
+    }
+    __device__ __forceinline__ void mark(uint32_t i) {
+        if constexpr (STAMP) t[i] = __builtin_amdgcn_s_memrealtime();
+    }
+    // Wait for every memory operation of the thread, then mark.
+    __device__ __forceinline__ void mark_drained(uint32_t i) {
+        if constexpr (STAMP) {
+            __builtin_amdgcn_s_waitcnt(0);
+            t[i] = __builtin_amdgcn_s_memrealtime();
+        }
+    }
+    __device__ __forceinline__ void write(const DecodeArgs &a, uint64_t tag) {
+        if constexpr (STAMP) {
+            if (threadIdx.x == 0) {
+                t[kStampsPerGroup - 1] = tag;
+                uint64_t *dst = a.stamps + (uint64_t)blockIdx.x * kStampsPerGroup;
+#pragma unroll
+                for (uint32_t i = 0; i < kStampsPerGroup; ++i) dst[i] = t[i];
+            }
+        }
+    }
+};
+
+// One lane's run of a routed tile, widened and based from the row bases s0
+// (row r0 = pos / C) and s1 (row r0 + 1), both splat over four bytes.
+template <int WB, int MODE>
+__device__ __forceinline__ u32x4 expand_run(u32x4 v, uint32_t pos, uint32_t r0, uint32_t C, uint32_t s0,
+                                            uint32_t s1) {
+    constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
+    constexpr uint32_t FMASK = 8 / WB - 1;
+    const uint32_t f = (pos >> 4) & FMASK;
+    const u32x4 field = (v >> (uint32_t)(WB * f)) & MASK;
+    u32x4 b = {s0, s0, s0, s0};
+    if constexpr (MODE == kRowTwo) {
+        const int left = (int)((r0 + 1) * C - pos);
+        if (left < 16) {
+            uint32_t m;
+            m = low_bytes_mask(left);      b.x = (s0 & m) | (s1 & ~m);
+            m = low_bytes_mask(left - 4);  b.y = (s0 & m) | (s1 & ~m);
+            m = low_bytes_mask(left - 8);  b.z = (s0 & m) | (s1 & ~m);
+            m = low_bytes_mask(left - 12); b.w = (s0 & m) | (s1 & ~m);
+        }
+    }
+    return add_bytes4(field, b);
+}
+
+template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP>
+__device__ __forceinline__ void routed_decode(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+    constexpr uint32_t TILE = tile_positions(RUNS);
+    constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
+    static_assert(EXC % 4 == 0, "entries are read in 16-byte loads");
+    Clock<STAMP> clk;
+    clk.mark(0);
+    uint8_t *lds_bases = dyn;
+
+    // (route_unit reads only inside the tensor, so it runs before the expert
+    // count is checked and its loads go out with the argument loads.)
+    const RoutedUnit ru = a.es_wide ? route_unit(a, static_cast<const int64_t *>(a.expert_start))
+                                    : route_unit(a, static_cast<const int32_t *>(a.expert_start));
+    const bool fast = a.E <= kFastExperts;
+    clk.mark(1);
+    if (!fast || ru.total > gridDim.x) {
+        uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
+        uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
+        const uint32_t nact = active_experts(a, act, flags);
+        tile_loop_pipelined<RUNS, EXC, kNonTemporal, WINDOW>(a, lds_bases, tile, nact, act, true);
+        clk.write(a, ~0ull);
+        return;
+    }
+    if (blockIdx.x >= ru.total) {
+        clk.write(a, 0ull);
+        return;
+    }
+
+    const uint32_t u = blockIdx.x;
+    const uint32_t s = ru.s, e = ru.e, t = ru.t;
+    const StackArgs st = pick(a, s);
+    const uint32_t q0 = t * TILE;
+    const uint32_t q1 = min(q0 + TILE, st.pend);
+
+    // Offset groups of the tile (run q: field q % F of group q / F).
+    u32x4 v[RUNS];
+    const rsrc_t seg = make_rsrc(st.offsets + (uint64_t)e * st.stride, (uint32_t)st.stride);
+    const uint32_t gshift = st.wbits == 4 ? 1u : 3u;
+#pragma unroll
+    for (uint32_t i = 0; i < RUNS; ++i) {
+        const uint32_t run = (q0 >> 4) + i * kBlock + threadIdx.x;
+        v[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg, (int)((run >> gshift) << 4), 0, kNonTemporal));
+    }
+    // Row bases: for C >= 16 the two rows each run may touch, into registers;
+    // for C < 16 the tile's rows, to be staged in LDS.
+    const rsrc_t rb = make_rsrc(st.bases + (uint64_t)e * st.R, st.R);
+    const bool direct = st.row_mode != kRowBytes;
+    const uint32_t r_lo = div_exact(q0, st.rcp_cols);
+    uint32_t rrow[RUNS], bb0[RUNS], bb1[RUNS];
+#pragma unroll
+    for (uint32_t i = 0; i < RUNS; ++i) {
+        const uint32_t pos = q0 + kRunBytes * (i * kBlock + threadIdx.x);
+        rrow[i] = direct ? div_exact(min(pos, q1 - 1u), st.rcp_cols) : r_lo + i * kBlock + threadIdx.x;
+        bb0[i] = __builtin_amdgcn_raw_buffer_load_b8(rb, (int)rrow[i], 0, 0);
+        bb1[i] = direct ? __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(rrow[i] + 1u), 0, 0)
+                        : __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(rrow[i] + RUNS * kBlock), 0, 0);
+    }
+    // The tile's index bounds, then its first EXC * kBlock entries in 16-byte
+    // loads from `first` (lo rounded down to a multiple of 4).
+    const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles + t * INDEX_PER_TILE;
+    const int32_t l0 = ti[0], h0 = ti[min(INDEX_PER_TILE, st.index_tiles - t * INDEX_PER_TILE)];
+    const uint32_t hi = h0 < 0 ? 0u : min((uint32_t)h0, st.n_exc);
+    const uint32_t lo = l0 < 0 ? 0u : min((uint32_t)l0, hi);
+    const uint32_t first = lo & ~3u;
+    const rsrc_t rx = make_rsrc(st.exc + first, 4u * (hi - first));
+    uint32_t w[EXC];
+#pragma unroll
+    for (uint32_t i = 0; i < EXC / 4; ++i) {
+        const u32x4 q = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(16u * (i * kBlock + threadIdx.x)), 0,
+                                                         kNonTemporal));
+        w[4 * i] = q.x;
+        w[4 * i + 1] = q.y;
+        w[4 * i + 2] = q.z;
+        w[4 * i + 3] = q.w;
+    }
+    clk.mark_drained(2);
+
+    uint8_t *plane = st.ws + (uint64_t)e * st.P;
+    if (direct) {
+#pragma unroll
+        for (uint32_t i = 0; i < RUNS; ++i) {
+            const uint32_t j = i * kBlock + threadIdx.x;
+            const uint32_t pos = q0 + kRunBytes * j;
+            if (pos >= q1) break;
+            const uint32_t s0 = bb0[i] * 0x01010101u, s1 = bb1[i] * 0x01010101u;
+            u32x4 out;
+            switch ((st.wbits == 4 ? 0u : 2u) + (st.row_mode == kRowSplat ? 0u : 1u)) {
+                case 0: out = expand_run<4, kRowSplat>(v[i], pos, rrow[i], st.C, s0, s1); break;
+                case 1: out = expand_run<4, kRowTwo>(v[i], pos, rrow[i], st.C, s0, s1); break;
+                case 2: out = expand_run<1, kRowSplat>(v[i], pos, rrow[i], st.C, s0, s1); break;
+                default: out = expand_run<1, kRowTwo>(v[i], pos, rrow[i], st.C, s0, s1); break;
+            }
+            *reinterpret_cast<u32x4 *>(tile + kRunBytes * j) = out;
+        }
+    } else {
+        const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
+#pragma unroll
+        for (uint32_t i = 0; i < RUNS; ++i) {
+            const uint32_t r = i * kBlock + threadIdx.x;
+            if (r < nrows) lds_bases[r] = (uint8_t)bb0[i];
+            if (r + RUNS * kBlock < nrows) lds_bases[r + RUNS * kBlock] = (uint8_t)bb1[i];
+        }
+        const uint8_t *brow = st.bases + (uint64_t)e * st.R + r_lo;
+        for (uint32_t r = threadIdx.x + 2u * RUNS * kBlock; r < nrows; r += kBlock) lds_bases[r] = brow[r];
+        __syncthreads();
+        expand_dispatch<true, RUNS, false>(st, v, q0, q1, q0, lds_bases, r_lo, tile, plane);
+    }
+    __syncthreads();  // tile expanded
+    clk.mark(3);
+
+    // The prefetched entries, then any beyond them.
+#pragma unroll
+    for (uint32_t i = 0; i < EXC; ++i) {
+        const uint32_t kk = entry_of(first, i);
+        const uint32_t pos = w[i] >> 8;
+        if (kk >= lo && kk < hi && pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(w[i] & 0xffu);
+    }
+    for (uint32_t kk = first + EXC * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
+        const uint32_t x = st.exc[kk];
+        const uint32_t pos = x >> 8;
+        if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
+    }
+    __syncthreads();  // tile patched
+    clk.mark(4);
+    store_tile<RUNS, WINDOW>(st, plane, q0, q1, tile);
+    clk.mark(5);
+    clk.mark_drained(6);
+    clk.write(a, 1ull + u + ((uint64_t)(hi - first > EXC * kBlock) << 32));
+}
+
 // WINDOW: some stack's row window does not cover its whole plane (csf_decode_rows).
-template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED, bool WINDOW>
-__global__ __launch_bounds__(kBlock) void csf_fused_kernel(DecodeArgs a) {
+// STAMP: a traced routed decode (timestamps per workgroup).
+template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED, bool WINDOW, bool STAMP = false>
+__global__ __launch_bounds__(kBlock, SCHED == kPipelined ? 6 : 1) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
     if constexpr (SCHED == kStreamEntries)
         tile_loop_serial<true, RUNS, EXC, false, true, WINDOW>(a, dyn_lds, tile);
+    else if constexpr (SCHED == kRouted)
+        routed_decode<RUNS, EXC, WINDOW, STAMP>(a, dyn_lds, tile);
     else
-        tile_loop_pipelined<RUNS, EXC, SCHED == kStreamAll ? kNonTemporal : 0, WINDOW>(a, dyn_lds, tile);
+        tile_loop_pipelined<RUNS, EXC, 0, WINDOW>(a, dyn_lds, tile, a.E, reinterpret_cast<const uint16_t *>(dyn_lds), a.expert_start != nullptr);
 }
 
 template <uint32_t RUNS, bool WINDOW>
@@ -573,7 +901,7 @@ __global__ __launch_bounds__(kBlock) void csf_index_kernel(StackArgs s, uint32_t
 
 size_t tile_lds_bytes(const DecodeArgs &a) {
     size_t n = a.bases_stage;
-    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + a.E;
+    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + a.E;  // act + flags
     return n;
 }
 
@@ -603,8 +931,8 @@ hipError_t launch_fused_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream
     const size_t lds = tile_lds_bytes(a);
     const dim3 g(grid), b(kBlock);
     // (runs, entries per lane, load schedule) combinations the host plans
-    if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedStreamAll)
-        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kStreamAll, WINDOW>), g, b, lds, stream, a);
+    if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedRouted)
+        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kRouted, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 4 && a.sched == kSchedStreamEntries)
         hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 8 && a.sched == kSchedStreamEntries)
@@ -618,6 +946,15 @@ hipError_t launch_fused_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream
 
 hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     return a.windowed ? launch_fused_t<true>(a, grid, stream) : launch_fused_t<false>(a, grid, stream);
+}
+
+hipError_t launch_fused_traced(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
+    const size_t lds = tile_lds_bytes(a);
+    const dim3 g(grid), b(kBlock);
+    if (a.windowed || a.stamps == nullptr || a.sched != kSchedRouted || a.runs != 1) return hipErrorInvalidValue;
+    if (a.exc_regs != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((csf_fused_kernel<1, 4, kRouted, false, true>), g, b, lds, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {

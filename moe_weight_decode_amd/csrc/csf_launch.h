@@ -15,11 +15,13 @@ constexpr uint32_t kIndexTile = 2048;               // positions per exception-i
 constexpr uint32_t tile_positions(uint32_t runs) { return kBlock * kRunBytes * runs; }
 constexpr uint32_t kExcPerLane = 8;                 // entries per lane per scatter chunk
 constexpr uint32_t kBasesSlack = 32;                // rows read past a tile's last row by edge runs
+constexpr uint32_t kMaxExperts = 2048;              // experts per stack (the ABI's limit)
+constexpr uint32_t kStampsPerGroup = 8;             // timestamps a traced decode records per workgroup
 
 // Load schedules of the fused kernel (csf_kernels.hip describes them).
 constexpr uint32_t kSchedPipelined = 0;
 constexpr uint32_t kSchedStreamEntries = 1;
-constexpr uint32_t kSchedStreamAll = 2;
+constexpr uint32_t kSchedRouted = 2;
 
 // How a 16-byte output run finds its row bases.
 enum RowMode : uint32_t {
@@ -61,6 +63,7 @@ struct DecodeArgs {
     uint32_t exc_regs;            // entries per lane loaded with the offsets (fused: 4 or 8)
     uint32_t es_wide;             // expert_start holds int64 (else int32)
     uint32_t windowed;            // some stack decodes a row window short of its whole plane
+    uint64_t *stamps;             // traced decodes: kStampsPerGroup clock values per workgroup, else nullptr
 };
 
 // Dynamic LDS bytes a tile kernel needs for these arguments.
@@ -72,6 +75,8 @@ hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 hipError_t launch_exceptions(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 // Both in one pass, exceptions patched on chip before the stores (needs tile_index).
 hipError_t launch_fused(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
+// The same with per-workgroup timestamps written to a.stamps (routed decodes only).
+hipError_t launch_fused_traced(const DecodeArgs &a, uint32_t grid, hipStream_t stream);
 // Per-tile exception index of one stack from its entries and prefix.
 hipError_t launch_build_index(const StackArgs &s, uint32_t E, int32_t *tile_index, hipStream_t stream);
 

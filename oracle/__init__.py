@@ -145,6 +145,37 @@ class Oracle:
         return ws
 
 
+    def decode_experts(self, stack: dict, e0: int, e1: int, ws: np.ndarray,
+                       expert_start: np.ndarray | None = None) -> None:
+        """``decode`` of experts e0 .. e1-1 only, into their planes of ``ws``
+        (uint8[E, R, C], C-contiguous): the same C function called on the
+        sub-stack those experts form (their bases, offset segments, prefix
+        entries and planes; entry indices stay those of the whole stream).
+        Several threads may decode disjoint expert ranges at once; the call
+        releases the GIL."""
+        fmt, E, R, C = stack["fmt"], stack["E"], stack["R"], stack["C"]
+        assert 0 <= e0 <= e1 <= E and ws.shape == (E, R, C) and ws.dtype == np.uint8 and ws.flags["C_CONTIGUOUS"]
+        if e0 == e1:
+            return
+        S = self.segment_bytes(fmt, R, C)
+        bases = np.ascontiguousarray(stack["bases"], dtype=np.uint8)
+        offsets = np.ascontiguousarray(stack["offsets"], dtype=np.uint8)
+        prefix = np.ascontiguousarray(stack["prefix"], dtype=np.int32)
+        exc = np.ascontiguousarray(stack["exceptions"], dtype=np.uint32)
+        if exc.size == 0:
+            exc = np.zeros(1, dtype=np.uint32)
+        es = None
+        if expert_start is not None:
+            es = np.ascontiguousarray(expert_start, dtype=np.int32)
+            assert es.shape == (E + 1,)
+        at = lambda a, off, t: ctypes.cast(a.ctypes.data + off, t)
+        rc = self.lib.oracle_decode(fmt, e1 - e0, R, C, at(bases, e0 * R, _u8p), at(offsets, e0 * S, _u8p),
+                                    _ptr(exc, _u32p), at(prefix, 4 * e0, _i32p),
+                                    at(es, 4 * e0, _i32p) if es is not None else ctypes.cast(None, _i32p),
+                                    at(ws, e0 * R * C, _u8p))
+        if rc != 0:
+            raise ValueError("oracle_decode rejected its arguments")
+
     def decode_rows(self, stack: dict, row_begin: int, row_end: int,
                     expert_start: np.ndarray | None = None, ws: np.ndarray | None = None) -> np.ndarray:
         """Expand rows ``row_begin .. row_end-1`` of every (routed) plane into

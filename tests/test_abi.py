@@ -35,8 +35,34 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_every_declared_symbol():
+    from moe_weight_decode_amd import probe
+    text = open(os.path.join(os.path.dirname(HERE), "include", "csf_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(csf_[a-z0-9_]+)\s*\(", text)))
+    assert set(names) == set(probe.EXPORTS)
+    plib = probe.library()
+    for n in names:
+        assert hasattr(plib, n), n
+
+
+def test_probe_argument_errors():
+    from moe_weight_decode_amd import probe
+    plib = probe.library()
+    u64 = ctypes.c_uint64
+    srcs = (ctypes.c_void_p * 1)(0x1000)
+    big = (u64 * 1)(1 << 30)
+    # a read stream whose per-tile piece exceeds what a lane loads
+    assert mwd.STATUS[plib.csf_probe_mix(srcs, big, 1, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
+    assert mwd.STATUS[plib.csf_probe_mix(srcs, big, 4, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
+    assert mwd.STATUS[plib.csf_probe_mix(None, None, 1, 0x2000, 16384, 1, 0, None)] == "CSF_E_NULL"
+    assert mwd.STATUS[plib.csf_probe_chain(None, 0, 0, 3, None, 1, 64, None)] == "CSF_E_NULL"
+    assert mwd.STATUS[plib.csf_probe_chain(0x1000, 16, 0, 3, None, 1, 100, None)] == "CSF_E_SIZE"
+    assert mwd.STATUS[plib.csf_probe_chain(0x1000, 1 << 30, 0, 3, None, 1, 64, None)] == "CSF_E_SIZE"
+
+
 def test_abi_version_and_status_strings(lib):
-    assert lib.csf_abi_version() == 4
+    assert lib.csf_abi_version() == 5
     for s in range(9):
         assert lib.csf_status_str(s)
     assert lib.csf_status_str(99) == b"unknown status"
@@ -338,4 +364,22 @@ def test_prepare_errors(lib):
     assert mwd.STATUS[st] == "CSF_E_NULL"
     st = lib.csf_prepare(0, 2, 3, 4, x.ctypes.data, ctypes.byref(sz), None, None, None, None,
                          buf.ctypes.data)
+    assert mwd.STATUS[st] == "CSF_E_NULL"
+
+
+def test_traced_decode_host_checks(lib):
+    """The traced decode's two-call pattern and errors, decided on the host
+    before anything is launched (descriptors with fake device pointers)."""
+    a = _fake(E=512, R=800, C=128, stride=51200, tile_index=0x9000)
+    b = _fake(E=512, R=2048, C=50, stride=51200, tile_index=0xA000)
+    groups = ctypes.c_uint32(0)
+    args = (ctypes.byref(a), 0x5000, ctypes.byref(b), 0x6000)
+    st = lib.csf_decode_traced(*args, 0x7000, None, 0, ctypes.byref(groups), None)
+    assert mwd.STATUS[st] == "CSF_OK" and groups.value > 0
+    st = lib.csf_decode_traced(*args, 0x7000, 0x8000, 8 * groups.value - 1, ctypes.byref(groups), None)
+    assert mwd.STATUS[st] == "CSF_E_SIZE"
+    assert mwd.STATUS[lib.csf_decode_traced(*args, None, None, 0, ctypes.byref(groups), None)] == "CSF_E_NULL"
+    assert mwd.STATUS[lib.csf_decode_traced(*args, 0x7000, None, 0, None, None)] == "CSF_E_NULL"
+    c = _fake(E=512, R=800, C=128, stride=51200)
+    st = lib.csf_decode_traced(ctypes.byref(c), 0x5000, None, None, 0x7000, None, 0, ctypes.byref(groups), None)
     assert mwd.STATUS[st] == "CSF_E_NULL"

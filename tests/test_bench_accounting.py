@@ -25,19 +25,22 @@ def closed_form(spec, n, active=None):
     NT = math.ceil(R * C / 2048)
     k = E if active is None else int(np.count_nonzero(active))
     index = 4 * (E * NT + 1) if active is None else 4 * k * (NT + 1)
-    return k * (R + S), 4 * n + 4 * (E + 1) + index, k * R * C
+    return k * (R + S), 4 * n + 4 * (E + 1), k * R * C, index
 
 
 @pytest.mark.parametrize("name", ["tiny_nvfp4", "gate_nvfp4", "mxfp4"])
 def test_full_decode_bytes(name):
     spec = workloads.STACKS[name]
     stack = mwd.prepare(spec.generate(), spec.fmt)
-    assert bench.stack_bytes(stack) == closed_form(spec, stack.num_exceptions)
+    b = bench.stack_bytes(stack)
+    assert tuple(b) == closed_form(spec, stack.num_exceptions)
+    assert b.metric == b.fixed + b.exc + b.dense
     if name == "gate_nvfp4":
         # the default benchmark line's bytes per step: 512 x 800 x 128 dense
         # bytes (52,428,800, as on the pages) plus the compressed streams
-        assert sum(bench.stack_bytes(stack)) == 85_450_904
-        assert bench.stack_bytes(stack)[2] == 52_428_800
+        # (bases, offsets, entries, prefix); the tile index is listed apart
+        assert b.metric == 85_348_500
+        assert b.dense == 52_428_800 and b.index == 102_404
 
 
 def test_routed_decode_bytes_count_routed_experts_only():
@@ -46,9 +49,16 @@ def test_routed_decode_bytes_count_routed_experts_only():
     active = np.array([True, False, False, True])
     pfx = stack.prefix.numpy()
     n = int(pfx[1] - pfx[0] + pfx[4] - pfx[3])
-    assert bench.stack_bytes(stack, active) == closed_form(spec, n, active)
-    fixed, exc, dense = bench.stack_bytes(stack.without_index(), active)
-    assert exc == 4 * n + 4 * (spec.E + 1)       # no index without one
+    assert tuple(bench.stack_bytes(stack, active)) == closed_form(spec, n, active)
+    b = bench.stack_bytes(stack.without_index(), active)
+    assert b.exc == 4 * n + 4 * (spec.E + 1) and b.index == 0   # no index without one
+
+
+def test_cpu_baseline_slices_cover_every_expert():
+    for E, n in ((512, 16), (384, 7), (4, 16), (1, 1)):
+        sl = bench._slices(E, n)
+        assert sl[0][0] == 0 and sl[-1][1] == E and len(sl) <= n
+        assert all(a < b for a, b in sl) and all(sl[i][1] == sl[i + 1][0] for i in range(len(sl) - 1))
 
 
 def test_routed_sets_are_disjoint_groups_of_one_permutation():

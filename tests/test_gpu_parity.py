@@ -303,6 +303,76 @@ def test_paired_all_active_equals_full(orc, dev, mode):
     assert_bytes_equal(gd, xd, "all active down")
 
 
+def _skewed_stack(E, R, C, seed, where):
+    """NVFP4 planes with few outliers except a band of rows of uniform bytes
+    (nearly all outliers) near the plane's start, middle or end."""
+    x = workloads.nvfp4_stack(E, R, C, seed, 0.01)
+    u = workloads.uniform_bytes(E, R, C, seed + 1)
+    band = {"start": slice(0, R // 8), "middle": slice(R // 2 - R // 16, R // 2 + R // 16),
+            "end": slice(R - R // 8, R)}[where]
+    x[:, band, :] = u[:, band, :]
+    return x
+
+
+@pytest.mark.parametrize("where", ["start", "middle", "end"])
+def test_routed_tiles_with_many_entries(orc, dev, where):
+    """Routed tiles with more entries than a workgroup prefetches read the rest
+    from the stream directly; the traced decode shows such tiles occurred and
+    its output is the plain decode's."""
+    E, R, C = 12, 2048, 50
+    x = _skewed_stack(E, R, C, 91 + len(where), where)
+    st = orc.encode(workloads.NVFP4, x)
+    stack = upload(st, dev)
+    es = workloads.expert_start_from_mask(np.array([1, 0, 1, 1, 0, 0, 1, 0, 0, 1, 1, 0]), tokens=3)
+    print(f"[parity] routed tiles with many entries, band at {where}", flush=True)
+    assert_bytes_equal(run_decode(stack, dev, es=es), oracle_expect(orc, st, es), f"routed, band at {where}")
+    ws = torch.full((stack.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    stamps = mwd.decode_traced(stack, ws, expert_start=torch.from_numpy(es).to(dev))
+    torch.cuda.synchronize()
+    assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), oracle_expect(orc, st, es), "traced")
+    tags = stamps[:, 7].cpu().numpy().astype(np.uint64)
+    assert np.any(tags >> np.uint64(32) == 1), "no tile had more entries than prefetched: the case is not exercised"
+
+
+def test_traced_decode_stamps(orc, dev):
+    """The traced routed pair writes what csf_decode_paired writes, one tag
+    per routed tile, and clock values in step order."""
+    es = workloads.ROUTED.expert_start()
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev), upload(sd, dev)
+    wg = torch.full((g.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    wd = torch.full((d.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    stamps = mwd.decode_traced(g, wg, d, wd, torch.from_numpy(es).to(dev))
+    torch.cuda.synchronize()
+    assert_bytes_equal(wg.cpu().numpy().reshape(xg.shape), oracle_expect(orc, sg, es), "traced gate")
+    assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), oracle_expect(orc, sd, es), "traced down")
+    t = stamps.cpu().numpy().astype(np.uint64)
+    tags = t[:, 7]
+    units = int(np.count_nonzero(np.diff(es) > 0)) * (g.tiles_per_plane(4096) + d.tiles_per_plane(4096))
+    busy = (tags != 0) & (tags != np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert int(busy.sum()) == units
+    assert sorted(int(v & np.uint64(0xFFFFFFFF)) - 1 for v in tags[busy]) == list(range(units))
+    for row in t[busy]:
+        assert all(row[i] <= row[i + 1] for i in range(6)), row
+    assert np.all(t[:, 0] <= t[:, 1])
+
+
+def test_routed_without_exceptions_and_empty_experts(orc, dev):
+    """Routed stacks with no entry at all (no entry buffer), and experts
+    without entries between experts with many."""
+    x = workloads.nvfp4_stack(6, 300, 64, 95, 0.0)
+    st = orc.encode(workloads.NVFP4, x)
+    assert st["exceptions"].size == 0
+    es = workloads.expert_start_from_mask(np.array([0, 1, 1, 0, 1, 1]), tokens=2)
+    assert_bytes_equal(run_decode(upload(st, dev), dev, es=es), oracle_expect(orc, st, es), "no entries")
+    x[1] = workloads.uniform_bytes(1, 300, 64, 96)[0]
+    x[4] = workloads.uniform_bytes(1, 300, 64, 97)[0]
+    st = orc.encode(workloads.NVFP4, x)
+    es = workloads.expert_start_from_mask(np.array([1, 1, 1, 0, 1, 1]), tokens=2)
+    assert_bytes_equal(run_decode(upload(st, dev), dev, es=es), oracle_expect(orc, st, es), "mixed")
+
+
 @pytest.mark.parametrize("mode", MODES + ["one_indexed"])
 def test_paired_mixed_formats(orc, dev, mode):
     xa = workloads.nvfp4_stack(16, 100, 50, 51, 0.1)
@@ -487,6 +557,25 @@ def test_gpu_encoder_on_a_stream_that_is_not_current(orc, dev):
     torch.cuda.current_stream(dev).wait_stream(side)
     assert got.num_exceptions > 0
     _same_streams(got.numpy(), orc.encode(workloads.NVFP4, x), "encode on a side stream")
+
+
+def test_gpu_encoder_side_stream_waits_for_freed_memory(orc, dev):
+    """The current stream still writes memory freed just before the call, and
+    the caller makes no wait: the encode on the side stream allocates its
+    outputs from that memory and must still see none of those writes."""
+    x = workloads.nvfp4_stack(64, 800, 128, 9, 0.03)
+    xt = torch.from_numpy(x).to(dev)
+    uploaded = torch.cuda.Event()
+    uploaded.record(torch.cuda.current_stream(dev))
+    side = torch.cuda.Stream(device=dev)
+    side.wait_event(uploaded)  # the input is ready on the side stream; nothing else is ordered
+    scratch = torch.empty(32 << 20, dtype=torch.uint8, device=dev)
+    for i in range(200):  # queued work on the current stream, writing memory about to be freed
+        scratch.fill_(i & 0xFF)
+    del scratch
+    got = mwd.prepare(xt, workloads.NVFP4, stream=side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    _same_streams(got.numpy(), orc.encode(workloads.NVFP4, x), "encode after freed memory")
 
 
 def test_gpu_encoder_high_bases(orc, dev):

@@ -64,3 +64,20 @@ def test_rejects_bad_shapes(orc):
         orc.choose_bases(workloads.NVFP4, np.zeros((1, 1 << 12, 1 << 12), dtype=np.uint8))
     with pytest.raises(ValueError):
         orc.choose_bases(7, np.zeros((1, 2, 2), dtype=np.uint8))
+
+
+def test_decode_experts_slices_equal_whole_decode(orc):
+    """The CPU baseline's threaded decode: disjoint expert ranges decoded from
+    several threads give the whole-stack decode, full and routed."""
+    from concurrent.futures import ThreadPoolExecutor
+    x = workloads.nvfp4_stack(16, 40, 50, 3, 0.1)
+    st = orc.encode(workloads.NVFP4, x)
+    ws = np.zeros_like(x)
+    with ThreadPoolExecutor(4) as pool:
+        list(pool.map(lambda r: orc.decode_experts(st, r[0], r[1], ws), [(0, 3), (3, 9), (9, 16)]))
+    assert np.array_equal(ws, x)
+    es = workloads.routing(16, 5, 4, seed=1)
+    ws = np.full_like(x, 0xA5)
+    orc.decode_experts(st, 0, 7, ws, es)
+    orc.decode_experts(st, 7, 16, ws, es)
+    assert np.array_equal(ws, orc.decode(st, es, np.full_like(x, 0xA5)))
