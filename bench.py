@@ -297,13 +297,13 @@ def bench_ceiling(mwd, torch, ev, sets, steps, warmup, dev):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     best, best_cfg = None, None
     for wg in (4, 6, 8):
-        for flags in (probe.NT_STORES, probe.NT_STORES | (probe.NT_LOADS0 << 1)):
+        for flags in (0, probe.NT_ENTRIES):
             mixes = [probe.Mix([s.offsets, s.exceptions[:s.num_exceptions], s.bases], ws, cus * wg, flags)
                      for s, ws in sets]
             _, evt = timed_loop(torch, ev, mixes, steps, warmup)
             if best is None or evt < best:
-                best, best_cfg = evt, dict(wg_per_cu=wg, entry_loads="nt" if flags & (probe.NT_LOADS0 << 1) else "cached")
-    two = [probe.Mix([s.offsets, s.bases], ws, cus * best_cfg["wg_per_cu"], probe.NT_STORES) for s, ws in sets]
+                best, best_cfg = evt, dict(wg_per_cu=wg, entry_loads="nt" if flags else "cached")
+    two = [probe.Mix([s.offsets, s.bases], ws, cus * best_cfg["wg_per_cu"]) for s, ws in sets]
     _, evt2 = timed_loop(torch, ev, two, steps, warmup)
     return dict(event_ms=best, config=best_cfg, without_entries_ms=evt2)
 

@@ -20,19 +20,20 @@ extern "C" {
 #endif
 
 /* Flags of csf_probe_mix. */
-#define CSF_PROBE_NT_STORES 1u  /* non-temporal stores (the decoder's) */
-#define CSF_PROBE_NT_LOADS0 2u  /* non-temporal loads of read stream 0; stream s: CSF_PROBE_NT_LOADS0 << s */
+#define CSF_PROBE_NT_ENTRIES 1u /* non-temporal loads of read stream 1 (the decoder's entry stream) */
 
 /*
  * Stream mix at the decoder's access shape: dst (device, dst_bytes) is cut
  * into tiles of 16 KiB; read stream s (device src[s], src_bytes[s] bytes,
- * nsrc <= 3) is cut into as many pieces, on 16-byte boundaries.  Workgroups
- * of 256 lanes take tiles grid-stride (grid workgroups); per tile every lane
- * issues 16-byte loads of each stream's piece (up to four per stream) and,
- * once they are in, four 16-byte stores whose bytes depend on every loaded
- * byte; each wave store instruction covers 1 KiB.  Bytes read = sum of
- * src_bytes, written = dst_bytes.  A stream's piece may hold at most 16 KiB
- * (src_bytes[s] / tiles + 16, else CSF_E_SIZE).
+ * 1 <= nsrc <= 3) is cut into as many pieces, on 16-byte boundaries.
+ * Workgroups of 256 lanes take tiles grid-stride (grid workgroups); per tile
+ * every lane issues, for each stream, the 16-byte loads of its share of the
+ * piece (as many as the largest piece needs: at most two for stream 0, three
+ * for stream 1, one for stream 2), and stores four 16-byte runs whose bytes
+ * depend on every loaded byte, non-temporal; each wave store instruction
+ * covers 1 KiB, and the next tile's loads are issued before this tile's
+ * stores.  Bytes read = sum of src_bytes, written = dst_bytes.  A larger
+ * piece (above 8, 12 or 4 KiB) returns CSF_E_SIZE.
  * Errors: CSF_E_NULL, CSF_E_SIZE, CSF_E_HIP.
  */
 csf_status csf_probe_mix(const uint8_t *const *src, const uint64_t *src_bytes, uint32_t nsrc, uint8_t *dst,

@@ -12,8 +12,7 @@ from . import _check, _lib, _stream_handle, csf_stack
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsf_probe.so")
 EXPORTS = ("csf_probe_mix", "csf_probe_chain", "csf_probe_host_ns")
-NT_STORES = 1
-NT_LOADS0 = 2
+NT_ENTRIES = 1
 
 _PLIB = None
 
@@ -40,7 +39,7 @@ class Mix:
     """One stream-mix launch (``csf_probe_mix``) with its arguments marshalled
     once: reads every tensor of ``srcs``, writes ``dst``."""
 
-    def __init__(self, srcs, dst: torch.Tensor, grid: int, flags: int = NT_STORES, stream=None):
+    def __init__(self, srcs, dst: torch.Tensor, grid: int, flags: int = 0, stream=None):
         self.keep = (tuple(srcs), dst)
         n = len(srcs)
         self.src = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in srcs])

@@ -55,6 +55,10 @@ def test_probe_argument_errors():
     # a read stream whose per-tile piece exceeds what a lane loads
     assert mwd.STATUS[plib.csf_probe_mix(srcs, big, 1, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
     assert mwd.STATUS[plib.csf_probe_mix(srcs, big, 4, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
+    three = (ctypes.c_void_p * 3)(0x1000, 0x1000, 0x1000)
+    sizes = (u64 * 3)(1 << 13, 1 << 13, 1 << 13)  # stream 2's piece above 4 KiB
+    assert mwd.STATUS[plib.csf_probe_mix(three, sizes, 0, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
+    assert mwd.STATUS[plib.csf_probe_mix(three, sizes, 3, 0x2000, 16384, 1, 0, None)] == "CSF_E_SIZE"
     assert mwd.STATUS[plib.csf_probe_mix(None, None, 1, 0x2000, 16384, 1, 0, None)] == "CSF_E_NULL"
     assert mwd.STATUS[plib.csf_probe_chain(None, 0, 0, 3, None, 1, 64, None)] == "CSF_E_NULL"
     assert mwd.STATUS[plib.csf_probe_chain(0x1000, 16, 0, 3, None, 1, 100, None)] == "CSF_E_SIZE"
