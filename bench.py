@@ -647,6 +647,32 @@ def _blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def bench_encode(mwd, torch, workloads, name, steps, warmup, dev):
+    """GPU encodes (csf_encode_device through prepare) of a workload stack
+    already in device memory, checked once against the host encoder; wall
+    time per encode (with its one read-back of the entry count)."""
+    import numpy as np
+    spec = workloads.STACKS[name]
+    x = spec.generate()
+    xd = torch.from_numpy(x).to(dev)
+    want = mwd.prepare(x, spec.fmt).numpy()
+    got = mwd.prepare(xd, spec.fmt).numpy()
+    for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
+        if not np.array_equal(np.asarray(got[k]).ravel(), np.asarray(want[k]).ravel()):
+            raise SystemExit(f"GPU encode of {name} differs from the host encoder in {k}")
+    for _ in range(warmup):
+        mwd.prepare(xd, spec.fmt)
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        mwd.prepare(xd, spec.fmt)
+        torch.cuda.synchronize()
+        t.append(time.perf_counter() - t0)
+    return dict(encode=name, shape=[spec.E, spec.R, spec.C], dense_bytes=int(x.size), steps=steps,
+                us_per_encode=round(statistics.median(t) * 1e6, 1))
+
+
 def graph_of(torch, dev, calls):
     """A HIP graph of `calls` in order (warmed outside capture), replayed on
     the current stream: returns a callable with the replay stream's handle."""
@@ -828,6 +854,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="N",
                     help="after the timed run, N plain 256 MiB device copies (reference for "
                          "hardware byte counters)")
+    ap.add_argument("--encode", default=None, metavar="STACK",
+                    help="instead: time the GPU encoder (csf_encode_device) on a workload stack, --steps times, "
+                         "and print one JSON line (for profiling the encoder kernels)")
     ap.add_argument("--workload", default="gate_nvfp4",
                     choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe",
                              "routed_moe_mx"],
@@ -846,6 +875,9 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     ev = HipEvents()
+    if args.encode:
+        print(json.dumps(bench_encode(mwd, torch, workloads, args.encode, args.steps, args.warmup, dev)), flush=True)
+        return
     moe = args.workload.startswith("routed_moe")
     if moe:
         mx = args.workload == "routed_moe_mx"

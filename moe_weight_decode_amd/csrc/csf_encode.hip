@@ -7,7 +7,10 @@
 // prefix and tile index follow the layout in include/csf.h.
 //
 // Four kernels, all byte streams bound by HBM bandwidth:
-//   csf_enc_bases_kernel    one wave per 4 rows at a time: a 256-bin
+//   csf_enc_bases_short_kernel  rows of at most 255 columns (every workload
+//                           stack): 16 lanes per row, byte-wide bins, window
+//                           counts by SWAR arithmetic and DPP (below).
+//   csf_enc_bases_kernel    any row: one wave per 4 rows at a time, a 256-bin
 //                           histogram per row in LDS (4 bins per lane),
 //                           window counts as differences of a wave prefix
 //                           over the bins, arg-max by a wave reduction.
@@ -54,6 +57,22 @@ __device__ __forceinline__ void load_run16(const uint8_t *plane, uint32_t p0, ui
 
 __device__ __forceinline__ bool runs_aligned(const EncodeArgs &a) {
     return ((uintptr_t)a.dense & 15u) == 0 && (a.P & 15u) == 0;
+}
+
+// Buffer resource of the byte range [base, base + bytes): loads past it read 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Orders this wave's LDS traffic without waiting for its global memory
+// operations: a wave's LDS operations are performed in issue order, so
+// waiting for its outstanding ones (lgkmcnt(0) alone; gfx9 s_waitcnt
+// encoding, vmcnt and expcnt left at their maxima) is all the ordering
+// between this wave's histogram writes and reads needs.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
 }
 
 // Orders this wave's LDS traffic (a wave works on its own histogram).
@@ -142,6 +161,212 @@ __global__ __launch_bounds__(kBlock) void csf_enc_bases_kernel(EncodeArgs a) {
         }
         wave_lds_sync();
     }
+}
+
+constexpr uint32_t kShortRows = 4;     // rows per wave at a time
+constexpr uint32_t kShortWords = 4;    // 32-bit loads per lane per group: 4 * 4 * 64 bytes >= 4 * 255
+
+// ---------------------------------------------------------------------------
+// Row bases of rows of at most 255 columns (every count then fits a byte).
+//
+// A wave takes 4 rows at a time, 16 lanes per row (lane j of the row's
+// group owns values 16 j .. 16 j + 15).  The rows' bytes (4 C, contiguous)
+// are read as 32-bit words, the next 4 rows' while this group is counted.
+// Counting: byte-wide bins in LDS, 4 per 32-bit word, by LDS atomic adds of
+// 1 << 8 (v % 4) at word v / 4 of one of four copies (below).  Lane j then
+// holds its 16 bins in four words h[0..3]; with SWAR byte arithmetic (no
+// carry crosses a byte, as every sum of bins is at most C <= 255):
+//   W = 16:  count(16 j + i) = T_j - pre_j(i) + pre_{j+1}(i), T_j the lane's
+//            total and pre_j(i) its bins below i, pre_{j+1} taken from the
+//            next lane by DPP (0 past the row's last lane: no values above
+//            255);
+//   W = 2:   count(v) = bin v + bin v + 1, bin 16 j + 16 being the next
+//            lane's first.
+// Counts of values absent from the row are zeroed; the row maximum M comes
+// from packed 16-bit maxima and a 16-lane DPP rotation; the base is the
+// smallest value whose count is M (a present value, since M >= 1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x101, 0xf, 0xf, true);  // row_shl:1
+}
+
+__device__ __forceinline__ uint32_t row_max16(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));  // row_ror:2
+    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));  // row_ror:1
+}
+
+__device__ __forceinline__ uint32_t row_min16(uint32_t x) {
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
+    return min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
+}
+
+// 0xff in each byte of x that is not zero, else 0.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    const uint32_t t = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
+    return (t >> 7) * 0xffu;
+}
+
+// 0x80 in each byte of x that is zero, else 0.
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
+    return ~((((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) | 0x7f7f7f7fu);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                   __builtin_bit_cast(u16x2, b)));
+}
+
+// The base of row g of a group whose 4 rows' bytes are the words w (nbytes
+// of them, whole words), counted in the wave's LDS bins hw; written by lane
+// 0 of the row's 16 for rows below `rows`.
+// LDS bins of one wave: 4 rows x 256 byte-wide bins (64 words per row), in
+// K copies.  K = 1: row r's bin word d at 64 r + d.  K = 4: lane l counts
+// into copy l % 4, so lanes adding to the same bin mostly hit different
+// words, at word 16 d + 4 r + c: the 16 words of one d lie in 16 different
+// banks, and one 16-byte read returns the four copies of a row's word.
+// Four copies pay where most of a row's values fall in a few bins (the
+// two-value window of one-bit offsets); elsewhere the extra clearing and
+// reading cost more than the conflicts they remove.
+template <uint32_t K>
+__device__ __forceinline__ uint32_t bin_word(uint32_t d, uint32_t r, uint32_t lane) {
+    return K == 1 ? 64u * r + d : 16u * d + 4u * r + lane % K;
+}
+
+template <uint32_t WB, uint32_t K, typename AfterCount>
+__device__ __forceinline__ void group_bases(const EncodeArgs &a, uint32_t *hw, const uint32_t (&w)[kShortWords],
+                                            uint32_t r0, uint32_t nbytes, uint32_t rows, AfterCount after_count) {
+    const uint32_t lane = threadIdx.x % kWave, g = lane / 16, j = lane % 16;
+    const uint32_t C = a.C;
+#pragma unroll
+    for (uint32_t t = 0; t < K; ++t)
+        reinterpret_cast<uint4 *>(hw)[t * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_order();
+    // One branch per word (the group holds whole words).  A word's bytes may
+    // straddle a row boundary: one when C >= 4, up to three when C < 4.
+    if (C >= 4) {
+#pragma unroll
+        for (uint32_t i = 0; i < kShortWords; ++i) {
+            const uint32_t o = 4u * (i * kWave + lane);  // first byte of the word in the group
+            if (o < nbytes) {
+                const uint32_t row = (o >= C) + (o >= 2 * C) + (o >= 3 * C);
+                const uint32_t next = (row + 1) * C;  // first byte of the next row
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) {
+                    const uint32_t v = __builtin_amdgcn_ubfe(w[i], 8 * k, 8);
+                    const uint32_t rk = row + (o + k >= next ? 1u : 0u);
+                    atomicAdd(&hw[bin_word<K>(v >> 2, rk, lane)], 1u << ((v & 3u) << 3));
+                }
+            }
+        }
+    } else {
+        // 4 C <= 12 bytes: lanes 0 .. C - 1 hold the group's words
+        const uint32_t o = 4u * lane;
+        if (o < nbytes) {
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                const uint32_t ob = o + k;
+                const uint32_t v = __builtin_amdgcn_ubfe(w[0], 8 * k, 8);
+                const uint32_t rk = (ob >= C) + (ob >= 2 * C) + (ob >= 3 * C);
+                atomicAdd(&hw[bin_word<K>(v >> 2, rk, lane)], 1u << ((v & 3u) << 3));
+            }
+        }
+    }
+    after_count();  // (the words are no longer needed)
+    wave_lds_order();
+    // row g, bins 16 j .. 16 j + 15: words 4 j .. 4 j + 3, the copies summed
+    // (byte-wise: every sum of bins is at most C <= 255)
+    uint32_t h[4];
+    if constexpr (K == 1) {
+        const uint4 hv = reinterpret_cast<const uint4 *>(hw)[lane];
+        h[0] = hv.x;
+        h[1] = hv.y;
+        h[2] = hv.z;
+        h[3] = hv.w;
+    } else {
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) {
+            const uint4 cp = reinterpret_cast<const uint4 *>(hw)[4 * (4 * j + t) + g];
+            h[t] = cp.x + cp.y + cp.z + cp.w;
+        }
+    }
+    uint32_t cnt[4];
+    if constexpr (WB == 4) {
+        uint32_t pre[4], run = 0;
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) {
+            pre[t] = h[t] * 0x01010100u + run * 0x01010101u;  // bins of the lane below each byte
+            run += (h[t] * 0x01010101u) >> 24;
+        }
+        const uint32_t total = run * 0x01010101u;
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) cnt[t] = total - pre[t] + next_lane(pre[t]);
+    } else {
+        const uint32_t nh0 = next_lane(h[0]);
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) cnt[t] = h[t] + (h[t] >> 8) + ((t < 3 ? h[t < 3 ? t + 1 : 0] : nh0) << 24);
+    }
+#pragma unroll
+    for (uint32_t t = 0; t < 4; ++t) cnt[t] &= nonzero_bytes(h[t]);
+    // the row's largest count
+    uint32_t m = max_u16x2(max_u16x2(cnt[0] & 0x00ff00ffu, cnt[1] & 0x00ff00ffu),
+                           max_u16x2(cnt[2] & 0x00ff00ffu, cnt[3] & 0x00ff00ffu));
+    m = max_u16x2(m, max_u16x2(max_u16x2((cnt[0] >> 8) & 0x00ff00ffu, (cnt[1] >> 8) & 0x00ff00ffu),
+                               max_u16x2((cnt[2] >> 8) & 0x00ff00ffu, (cnt[3] >> 8) & 0x00ff00ffu)));
+    const uint32_t M = row_max16(max(m & 0xffffu, m >> 16));
+    // the smallest value with that count
+    const uint32_t sm = M * 0x01010101u;
+    const uint64_t z01 = (uint64_t)zero_bytes(cnt[0] ^ sm) | ((uint64_t)zero_bytes(cnt[1] ^ sm) << 32);
+    const uint64_t z23 = (uint64_t)zero_bytes(cnt[2] ^ sm) | ((uint64_t)zero_bytes(cnt[3] ^ sm) << 32);
+    const uint32_t local = z01 ? (uint32_t)__builtin_ctzll(z01) >> 3
+                               : (z23 ? 8u + ((uint32_t)__builtin_ctzll(z23) >> 3) : 256u);
+    const uint32_t base = row_min16(local < 256u ? 16u * j + local : 256u);
+    if (j == 0 && r0 + g < rows) a.bases[r0 + g] = (uint8_t)base;
+    wave_lds_order();  // this group's bins read before the next group clears them
+}
+
+// The host sends stacks of fewer than 2^31 bytes, a multiple of 4, with
+// rows of at most 255 columns; so the 32-bit group offsets below are exact
+// and every group is whole words.
+template <uint32_t WB, uint32_t K>
+__global__ __launch_bounds__(kBlock) void csf_enc_bases_short_kernel(EncodeArgs a) {
+    constexpr uint32_t kWaves = kBlock / kWave;
+    __shared__ __align__(16) uint32_t hist[kWaves][256 * K];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane = threadIdx.x % kWave;
+    const uint32_t C = a.C;
+    const uint32_t rows = a.E * a.R;
+    const uint32_t groups = (rows + kShortRows - 1) / kShortRows;
+    const uint32_t stride = gridDim.x * kWaves;
+    uint32_t *hw = hist[wave];
+
+    // The words of group q: bytes [4 q C, min(4 q C + 4 C, rows C)), word d
+    // at byte 4 d, loaded through a resource over exactly those bytes.
+    auto load_group = [&](uint32_t q, uint32_t (&w)[kShortWords]) {
+        // (uniform; said so, so the resource stays in scalar registers)
+        const uint32_t first = __builtin_amdgcn_readfirstlane(q * kShortRows * C);
+        const uint32_t end = __builtin_amdgcn_readfirstlane(min(first + kShortRows * C, rows * C));
+        const rsrc_t r = make_rsrc(a.dense + first, end - first);
+#pragma unroll
+        for (uint32_t i = 0; i < kShortWords; ++i)
+            w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(4u * (i * kWave + lane)), 0, 0);
+    };
+    auto nbytes_of = [&](uint32_t q) { return (min(q * kShortRows + kShortRows, rows) - q * kShortRows) * C; };
+
+    // The next group's words are loaded once this group's are counted, while
+    // its bases are found.
+    uint32_t q = blockIdx.x * kWaves + wave;
+    uint32_t w[kShortWords];
+    if (q < groups) load_group(q, w);
+    for (; q < groups; q += stride)
+        group_bases<WB, K>(a, hw, w, q * kShortRows, nbytes_of(q), rows, [&] {
+            if (q + stride < groups) load_group(q + stride, w);
+        });
 }
 
 __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
@@ -302,8 +527,19 @@ static uint32_t grid_for(uint64_t waves_needed, uint32_t cus) {
 }
 
 hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t stream) {
-    uint32_t grid = grid_for((uint64_t)a.E * a.R, cus);
-    hipLaunchKernelGGL(csf_enc_bases_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    uint32_t grid;
+    const uint64_t n = (uint64_t)a.E * a.R * a.C;
+    if (a.C <= 255 && ((uintptr_t)a.dense & 3u) == 0 && n % 4 == 0 && n < (1ull << 31)) {
+        const uint64_t groups = ((uint64_t)a.E * a.R + kShortRows - 1) / kShortRows;
+        grid = grid_for(groups, cus);
+        if (a.wbits == 4)
+            hipLaunchKernelGGL((csf_enc_bases_short_kernel<4, 1>), dim3(grid), dim3(kBlock), 0, stream, a);
+        else
+            hipLaunchKernelGGL((csf_enc_bases_short_kernel<1, 4>), dim3(grid), dim3(kBlock), 0, stream, a);
+    } else {
+        grid = grid_for((uint64_t)a.E * a.R, cus);
+        hipLaunchKernelGGL(csf_enc_bases_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     grid = grid_for((uint64_t)a.E * ((a.groups + kWave - 1) / kWave), cus);
     hipLaunchKernelGGL(csf_enc_pack_kernel, dim3(grid), dim3(kBlock), 0, stream, a);

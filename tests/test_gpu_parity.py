@@ -511,7 +511,13 @@ def test_gpu_encoder_matches_oracle(orc, dev, name):
 
 
 ENCODE_SHAPES = RAGGED + [(workloads.NVFP4, 2, 3000, 50), (workloads.MXFP4, 2, 1500, 160),
-                          (workloads.NVFP4, 1, 1048575, 16)]
+                          (workloads.NVFP4, 1, 1048575, 16),
+                          # stacks of a multiple of 4 bytes with rows of at most 255 columns (the
+                          # 16-lanes-per-row base search), last group of 4 rows partial
+                          (workloads.NVFP4, 3, 33, 12), (workloads.MXFP4, 1, 5, 4), (workloads.NVFP4, 2, 7, 254),
+                          (workloads.MXFP4, 4, 7, 255), (workloads.NVFP4, 1, 255, 4), (workloads.MXFP4, 3, 100, 52),
+                          # one column more than the byte-wide bins allow
+                          (workloads.NVFP4, 4, 5, 256)]
 
 
 @pytest.mark.parametrize("fmt,E,R,C", ENCODE_SHAPES, ids=[f"f{c[0]}_{c[1]}x{c[2]}x{c[3]}" for c in ENCODE_SHAPES])
