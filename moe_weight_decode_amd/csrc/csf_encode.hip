@@ -14,9 +14,11 @@
 //                           histogram per row in LDS (4 bins per lane),
 //                           window counts as differences of a wave prefix
 //                           over the bins, arg-max by a wave reduction.
-//   csf_enc_pack_kernel     one lane per 16-byte offset group: fields packed
-//                           in the contiguous-decoding order; each index
-//                           tile's out-of-window count reduced across lanes.
+//   csf_enc_pack_kernel     one wave per index tile, one 16-byte run of
+//                           dense bytes per lane and load: fields packed in
+//                           the contiguous-decoding order, a group's runs
+//                           combined across lanes; the tile's out-of-window
+//                           count reduced across the wave.
 //   csf_enc_scan_kernel     one workgroup: exclusive scan of the per-tile
 //                           counts, in place, into tile_index and prefix.
 //   csf_enc_entries_kernel  one wave per index tile: out-of-window positions
@@ -369,29 +371,52 @@ __global__ __launch_bounds__(kBlock) void csf_enc_bases_short_kernel(EncodeArgs 
         });
 }
 
+// OR of x over this lane and the s - 1 lanes below it in its 16-lane row
+// (s = 1, 2, 4 or 8): the last lane of each aligned group of s holds the
+// group's OR.
+__device__ __forceinline__ uint32_t or_down(uint32_t x, uint32_t s) {
+    if (s > 1) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    if (s > 2) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    if (s > 4) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    return x;
+}
+
+// One wave per index tile (kIndexTile positions = 128 runs of 16); lane l
+// takes runs l and l + 64 of the tile, so each load instruction of a wave
+// reads 1 KiB of contiguous dense bytes.  Run q holds field q % F of group
+// q / F (F = 8 / w runs per group): its 16 values' offsets (0 out of the
+// window) at bits w (q % F) of the group's 16 bytes.  The F runs of a group
+// are F consecutive lanes; an OR down those lanes gives the group to its
+// last lane, which stores it.  The tile's out-of-window count is a sum over
+// the wave.
 __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
+    constexpr uint32_t kRuns = kIndexTile / 16;  // 128
     const uint32_t lane = threadIdx.x % kWave;
-    const uint32_t waves_per_expert = (a.groups + kWave - 1) / kWave;
-    const uint64_t total_waves = (uint64_t)a.E * waves_per_expert;
+    const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
     const uint32_t W = 1u << a.wbits;
-    const uint32_t G = 128u / a.wbits;
     const uint32_t F = 8u / a.wbits;
-    const uint32_t seg = kIndexTile / G;  // lanes (groups) per index tile: 64 or 16
     const bool vec = runs_aligned(a);
     for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
          wv += (uint64_t)gridDim.x * kBlock / kWave) {
-        const uint32_t e = (uint32_t)(wv / waves_per_expert);
-        const uint32_t g = (uint32_t)(wv - (uint64_t)e * waves_per_expert) * kWave + lane;
+        const uint32_t e = (uint32_t)(wv / a.index_tiles);
+        const uint32_t it = (uint32_t)(wv - (uint64_t)e * a.index_tiles);
         const uint8_t *plane = a.dense + (uint64_t)e * a.P;
         const uint8_t *brow = a.bases + (uint64_t)e * a.R;
-        uint32_t word[4] = {0u, 0u, 0u, 0u};
+        uint32_t x[2][4];
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t p0 = 16u * (it * kRuns + h * kWave + lane);
+            x[h][0] = x[h][1] = x[h][2] = x[h][3] = 0u;
+            if (p0 < a.P) load_run16(plane, p0, a.P, vec, x[h]);
+        }
         uint32_t outside = 0;
-        if (g < a.groups) {
-            for (uint32_t f = 0; f < F; ++f) {
-                const uint32_t p0 = g * G + 16u * f;
-                if (p0 >= a.P) break;
-                uint32_t x[4];
-                load_run16(plane, p0, a.P, vec, x);
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t q = it * kRuns + h * kWave + lane;  // run in the plane
+            const uint32_t p0 = 16u * q;
+            const uint32_t f = q % F;
+            uint32_t word[4] = {0u, 0u, 0u, 0u};
+            if (p0 < a.P) {
                 uint32_t r = div_exact(p0, a.rcp_cols);
                 uint32_t next = (r + 1u) * a.C;
                 uint32_t b = brow[r];
@@ -406,24 +431,23 @@ __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
                         }
                         // unsigned 32-bit difference: the window [b, b + W - 1] does
                         // not wrap past 255, so a value below b is never inside it
-                        const uint32_t d = ((x[j >> 2] >> (8u * (j & 3u))) & 0xffu) - b;
+                        const uint32_t d = ((x[h][j >> 2] >> (8u * (j & 3u))) & 0xffu) - b;
                         const bool in = d < W;
                         outside += in ? 0u : 1u;
                         word[j >> 2] |= (in ? d : 0u) << (8u * (j & 3u) + a.wbits * f);
                     }
                 }
             }
-            uint32_t *dst = reinterpret_cast<uint32_t *>(a.offsets + (uint64_t)e * a.stride + 16u * g);
-            dst[0] = word[0];
-            dst[1] = word[1];
-            dst[2] = word[2];
-            dst[3] = word[3];
+#pragma unroll
+            for (uint32_t t = 0; t < 4; ++t) word[t] = or_down(word[t], F);
+            const uint32_t g = q / F;
+            if (f == F - 1u && g < a.groups) {
+                uint4 *dst = reinterpret_cast<uint4 *>(a.offsets + (uint64_t)e * a.stride + 16u * g);
+                *dst = make_uint4(word[0], word[1], word[2], word[3]);
+            }
         }
-        // Sum the counts of each index tile's lanes (seg consecutive lanes).
-        for (uint32_t d = 1; d < seg; d <<= 1) outside += __shfl_xor(outside, d, kWave);
-        const uint32_t tile = g / seg;
-        if (lane % seg == 0 && tile < a.index_tiles && g < a.groups)
-            a.tile_index[(uint64_t)e * a.index_tiles + tile] = (int32_t)outside;
+        for (uint32_t d = 1; d < kWave; d <<= 1) outside += __shfl_xor(outside, d, kWave);
+        if (lane == 0) a.tile_index[wv] = (int32_t)outside;
     }
 }
 
@@ -541,7 +565,7 @@ hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t 
         hipLaunchKernelGGL(csf_enc_bases_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
     }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    grid = grid_for((uint64_t)a.E * ((a.groups + kWave - 1) / kWave), cus);
+    grid = grid_for((uint64_t)a.E * a.index_tiles, cus);
     hipLaunchKernelGGL(csf_enc_pack_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(csf_enc_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
