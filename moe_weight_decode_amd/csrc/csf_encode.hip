@@ -20,10 +20,12 @@
 //                           combined across lanes; the tile's out-of-window
 //                           count reduced across the wave.
 //   csf_enc_scan_kernel     one workgroup: exclusive scan of the per-tile
-//                           counts, in place, into tile_index and prefix.
-//   csf_enc_entries_kernel  one wave per index tile: out-of-window positions
-//                           ranked by a wave prefix and written in ascending
-//                           order at the tile's index.
+//                           counts, in place, into tile_index and prefix;
+//                           each wave reads and writes coalesced lines.
+//   csf_enc_entries_kernel  one wave per index tile, one 16-byte run per lane
+//                           and load: out-of-window positions ranked by wave
+//                           prefixes and written in ascending order at the
+//                           tile's index.
 // The pack and entries kernels read the dense bytes 16 at a time when the
 // stack is 16-byte aligned and R*C is a multiple of 16, else byte by byte.
 #include "csf_launch.h"
@@ -59,6 +61,102 @@ __device__ __forceinline__ void load_run16(const uint8_t *plane, uint32_t p0, ui
 
 __device__ __forceinline__ bool runs_aligned(const EncodeArgs &a) {
     return ((uintptr_t)a.dense & 15u) == 0 && (a.P & 15u) == 0;
+}
+
+// Row bases along ascending positions of a plane from p0 on: the base of
+// p0's row, then each further row's base read when a position reaches it.
+struct RunBases {
+    uint32_t r, next, b;
+    __device__ __forceinline__ RunBases(const EncodeArgs &a, const uint8_t *brow, uint32_t p0) {
+        r = div_exact(p0, a.rcp_cols);
+        next = (r + 1u) * a.C;
+        b = brow[r];
+    }
+    // base of position p; calls in ascending p
+    __device__ __forceinline__ uint32_t at(const EncodeArgs &a, const uint8_t *brow, uint32_t p) {
+        if (p == next) {
+            ++r;
+            next += a.C;
+            b = brow[r];
+        }
+        return b;
+    }
+};
+
+// 0xff in the bytes k >= s of a word, 0 below.
+__device__ __forceinline__ uint32_t bytes_from(int32_t s) {
+    return s <= 0 ? 0xffffffffu : (s >= 4 ? 0u : 0xffffffffu << (8 * s));
+}
+
+// Byte-wise x - y modulo 256 (no borrow between bytes).
+__device__ __forceinline__ uint32_t byte_sub(uint32_t x, uint32_t y) {
+    return ((x | 0x80808080u) - (y & 0x7f7f7f7fu)) ^ ((x ^ ~y) & 0x80808080u);
+}
+
+// 0x80 in each byte of x that is zero, else 0.
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
+    return ~((((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) | 0x7f7f7f7fu);
+}
+
+// The two runs of 16 dense bytes a lane takes in an index tile (runs l and
+// l + 64 of the tile for lane l) and, for rows of at least 16 columns, the
+// bases of the row each run starts in and of the row after it: a run of 16
+// meets at most two rows then.
+struct TileRuns {
+    uint32_t x[2][4];
+    uint32_t b0[2], b1[2];
+};
+
+// (Tile numbers fit 32 bits: the host keeps E * P below 2^31.)
+__device__ __forceinline__ uint32_t run_start(const EncodeArgs &a, uint64_t wv, uint32_t h, uint32_t lane) {
+    const uint32_t it = (uint32_t)wv % a.index_tiles;
+    return 16u * (it * (kIndexTile / 16) + h * kWave + lane);
+}
+
+__device__ __forceinline__ void fetch_runs(const EncodeArgs &a, uint64_t wv, uint32_t lane, bool vec,
+                                           bool long_rows, TileRuns &t) {
+    const uint32_t e = (uint32_t)wv / a.index_tiles;
+    const uint8_t *plane = a.dense + (uint64_t)e * a.P;
+    const uint8_t *brow = a.bases + (uint64_t)e * a.R;
+#pragma unroll
+    for (uint32_t h = 0; h < 2; ++h) {
+        const uint32_t p0 = run_start(a, wv, h, lane);
+        t.x[h][0] = t.x[h][1] = t.x[h][2] = t.x[h][3] = 0u;
+        t.b0[h] = t.b1[h] = 0u;
+        if (p0 < a.P) {
+            load_run16(plane, p0, a.P, vec, t.x[h]);
+            if (long_rows) {
+                const uint32_t r = div_exact(p0, a.rcp_cols);
+                t.b0[h] = brow[r];
+                t.b1[h] = r + 1u < a.R ? brow[r + 1u] : 0u;
+            }
+        }
+    }
+}
+
+// Window test of run h of t (positions p0 .. p0 + 15, rows of at least 16
+// columns), four bytes at a time: d[j] holds the byte differences (modulo
+// 256) to the bases of their rows, valid[j] 0x80 in each byte inside the
+// plane, keep[j] 0x80 in each valid byte inside its row's window: a
+// difference below W without a borrow (a base may exceed 256 - W, so a byte
+// below it can still differ by less than W modulo 256).
+__device__ __forceinline__ void window_test16(const EncodeArgs &a, const TileRuns &t, uint32_t h, uint32_t p0,
+                                              uint32_t (&d)[4], uint32_t (&keep)[4], uint32_t (&valid)[4]) {
+    const uint32_t next = (div_exact(p0, a.rcp_cols) + 1u) * a.C;  // first position of the next row
+    const uint32_t B0 = t.b0[h] * 0x01010101u, B1 = t.b1[h] * 0x01010101u;
+    const uint32_t hi = (0x100u - (1u << a.wbits)) * 0x01010101u;  // bits that must be 0 in a kept difference
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t pt = p0 + 4u * j;
+        const uint32_t x = t.x[h][j];
+        const uint32_t in_next = bytes_from((int32_t)(next - pt));
+        valid[j] = ~bytes_from((int32_t)(a.P - pt)) & 0x80808080u;
+        const uint32_t bv = (B0 & ~in_next) | (B1 & in_next);
+        d[j] = byte_sub(x, bv);
+        // borrow out of each byte's top bit: the byte is below its base
+        const uint32_t below = ((~x & bv) | (~(x ^ bv) & d[j])) & 0x80808080u;
+        keep[j] = zero_bytes(d[j] & hi) & ~below & valid[j];
+    }
 }
 
 // Buffer resource of the byte range [base, base + bytes): loads past it read 0.
@@ -210,11 +308,6 @@ __device__ __forceinline__ uint32_t row_min16(uint32_t x) {
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
     const uint32_t t = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
     return (t >> 7) * 0xffu;
-}
-
-// 0x80 in each byte of x that is zero, else 0.
-__device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
-    return ~((((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) | 0x7f7f7f7fu);
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -390,48 +483,43 @@ __device__ __forceinline__ uint32_t or_down(uint32_t x, uint32_t s) {
 // last lane, which stores it.  The tile's out-of-window count is a sum over
 // the wave.
 __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
-    constexpr uint32_t kRuns = kIndexTile / 16;  // 128
     const uint32_t lane = threadIdx.x % kWave;
     const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock / kWave;
     const uint32_t W = 1u << a.wbits;
     const uint32_t F = 8u / a.wbits;
     const bool vec = runs_aligned(a);
-    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
-         wv += (uint64_t)gridDim.x * kBlock / kWave) {
-        const uint32_t e = (uint32_t)(wv / a.index_tiles);
-        const uint32_t it = (uint32_t)(wv - (uint64_t)e * a.index_tiles);
-        const uint8_t *plane = a.dense + (uint64_t)e * a.P;
+    const bool long_rows = a.C >= 16u;
+    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves; wv += stride) {
+        TileRuns cur;
+        fetch_runs(a, wv, lane, vec, long_rows, cur);
+        const uint32_t e = (uint32_t)wv / a.index_tiles;
         const uint8_t *brow = a.bases + (uint64_t)e * a.R;
-        uint32_t x[2][4];
-#pragma unroll
-        for (uint32_t h = 0; h < 2; ++h) {
-            const uint32_t p0 = 16u * (it * kRuns + h * kWave + lane);
-            x[h][0] = x[h][1] = x[h][2] = x[h][3] = 0u;
-            if (p0 < a.P) load_run16(plane, p0, a.P, vec, x[h]);
-        }
         uint32_t outside = 0;
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {
-            const uint32_t q = it * kRuns + h * kWave + lane;  // run in the plane
-            const uint32_t p0 = 16u * q;
+            const uint32_t p0 = run_start(a, wv, h, lane);
+            const uint32_t q = p0 / 16u;  // run in the plane
             const uint32_t f = q % F;
             uint32_t word[4] = {0u, 0u, 0u, 0u};
-            if (p0 < a.P) {
-                uint32_t r = div_exact(p0, a.rcp_cols);
-                uint32_t next = (r + 1u) * a.C;
-                uint32_t b = brow[r];
+            if (p0 < a.P && long_rows) {
+                uint32_t d[4], keep[4], valid[4];
+                window_test16(a, cur, h, p0, d, keep, valid);
+#pragma unroll
+                for (uint32_t t = 0; t < 4; ++t) {
+                    // a kept difference is below W: its field is its low w bits
+                    word[t] = (d[t] & ((keep[t] >> 7) * 0xffu)) << (a.wbits * f);
+                    outside += __popc(valid[t] & ~keep[t]);
+                }
+            } else if (p0 < a.P) {
+                RunBases rb(a, brow, p0);
 #pragma unroll
                 for (uint32_t j = 0; j < 16; ++j) {
                     const uint32_t p = p0 + j;
                     if (p < a.P) {
-                        if (p == next) {
-                            ++r;
-                            next += a.C;
-                            b = brow[r];
-                        }
-                        // unsigned 32-bit difference: the window [b, b + W - 1] does
-                        // not wrap past 255, so a value below b is never inside it
-                        const uint32_t d = ((x[h][j >> 2] >> (8u * (j & 3u))) & 0xffu) - b;
+                        const uint32_t b = rb.at(a, brow, p);
+                        // unsigned 32-bit difference: a value below b differs by far more than W
+                        const uint32_t d = ((cur.x[h][j >> 2] >> (8u * (j & 3u))) & 0xffu) - b;
                         const bool in = d < W;
                         outside += in ? 0u : 1u;
                         word[j >> 2] |= (in ? d : 0u) << (8u * (j & 3u) + a.wbits * f);
@@ -451,93 +539,143 @@ __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
     }
 }
 
+// Inclusive sum of x over lanes 0 .. lane of the wave: a scan inside each
+// 16-lane row by DPP row shifts (lanes shifted in from outside the row add
+// 0), then the totals of the rows below added from their last lanes.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    const uint32_t row = (threadIdx.x % kWave) / 16;
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    return x + (row > 0 ? t0 : 0u) + (row > 1 ? t1 : 0u) + (row > 2 ? t2 : 0u);
+}
+
 // One workgroup: tile_index[0 .. N) holds per-tile counts; replace them by
 // their exclusive prefix, set tile_index[N] = total, prefix[e] =
 // tile_index[e * NT] and prefix[E] = total.  The host keeps E * P < 2^31.
+// Wave w owns the contiguous segment [w * seg, (w + 1) * seg) of whole
+// 64-count lines and reads it kScanBatch lines at a time, each load one
+// coalesced line, every load of a batch in flight together; when the
+// segment fits one batch its counts stay in registers for the second pass.
 __global__ __launch_bounds__(kScanThreads) void csf_enc_scan_kernel(EncodeArgs a) {
-    __shared__ uint32_t part[kScanThreads];
+    constexpr uint32_t kScanBatch = 32;
+    constexpr uint32_t kWaves = kScanThreads / kWave;
+    __shared__ uint32_t wave_sums[kWaves];
     const uint32_t N = a.E * a.index_tiles;
-    const uint32_t chunk = (N + kScanThreads - 1) / kScanThreads;
-    const uint32_t t = threadIdx.x;
-    const uint32_t lo = min(t * chunk, N), hi = min(lo + chunk, N);
+    const uint32_t seg = (N + kScanThreads - 1) / kScanThreads * kWave;  // counts per wave
+    const uint32_t wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const uint32_t lo = min(wid * seg, N), hi = min(lo + seg, N);
+    int32_t *ti = a.tile_index;
+    uint32_t v[kScanBatch];
     uint32_t sum = 0;
-#pragma unroll 8
-    for (uint32_t i = lo; i < hi; ++i) sum += (uint32_t)a.tile_index[i];
-    part[t] = sum;
+    for (uint32_t b = lo; b < hi; b += kScanBatch * kWave) {
+#pragma unroll
+        for (uint32_t i = 0; i < kScanBatch; ++i) {
+            const uint32_t k = b + i * kWave + lane;
+            v[i] = k < hi ? (uint32_t)ti[k] : 0u;
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < kScanBatch; ++i) sum += v[i];
+    }
+    const uint32_t wave_total = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(sum), kWave - 1);
+    if (lane == 0) wave_sums[wid] = wave_total;
     __syncthreads();
-    // Hillis-Steele inclusive scan of the partial sums.
-    for (uint32_t d = 1; d < kScanThreads; d <<= 1) {
-        const uint32_t v = t >= d ? part[t - d] : 0u;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
+    uint32_t run = 0, total = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kWaves; ++w) {
+        const uint32_t s = wave_sums[w];
+        run += w < wid ? s : 0u;
+        total += s;
     }
-    uint32_t run = part[t] - sum;  // exclusive
-#pragma unroll 8
-    for (uint32_t i = lo; i < hi; ++i) {
-        const uint32_t c = (uint32_t)a.tile_index[i];
-        a.tile_index[i] = (int32_t)run;
-        run += c;
+    const bool kept = seg <= kScanBatch * kWave;  // v holds this wave's whole segment
+    for (uint32_t b = lo; b < hi; b += kScanBatch * kWave) {
+        if (!kept) {
+#pragma unroll
+            for (uint32_t i = 0; i < kScanBatch; ++i) {
+                const uint32_t k = b + i * kWave + lane;
+                v[i] = k < hi ? (uint32_t)ti[k] : 0u;
+            }
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < kScanBatch; ++i) {
+            const uint32_t k = b + i * kWave + lane;
+            const uint32_t inc = wave_inclusive_sum(v[i]);
+            if (k < hi) ti[k] = (int32_t)(run + inc - v[i]);
+            run += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+        }
     }
-    const uint32_t total = part[kScanThreads - 1];
-    if (t == 0) {
-        a.tile_index[N] = (int32_t)total;
+    if (threadIdx.x == 0) {
+        ti[N] = (int32_t)total;
         a.prefix[a.E] = (int32_t)total;
     }
     __syncthreads();  // every thread's tile_index writes are visible in the workgroup
-    for (uint32_t e = t; e < a.E; e += kScanThreads)
-        a.prefix[e] = a.tile_index[(uint64_t)e * a.index_tiles];
+    for (uint32_t e = threadIdx.x; e < a.E; e += kScanThreads) a.prefix[e] = ti[(uint64_t)e * a.index_tiles];
 }
 
-// One wave per index tile of kIndexTile positions; lane l takes positions
-// 32l .. 32l+31 of the tile, so lane order is position order.
+// One wave per index tile (128 runs of 16 positions); lane l takes runs l
+// and l + 64 of the tile, so each load instruction reads 1 KiB of contiguous
+// dense bytes.  Position order is (half, lane, position in run): a wave
+// prefix of the out-of-window counts of each half ranks the entries, and
+// each lane writes its own in ascending order, bytes taken from the loaded
+// registers.
 __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
-    constexpr uint32_t kPerLane = kIndexTile / kWave;  // 32
     const uint32_t lane = threadIdx.x % kWave;
     const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock / kWave;
     const uint32_t W = 1u << a.wbits;
     const bool vec = runs_aligned(a);
-    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves;
-         wv += (uint64_t)gridDim.x * kBlock / kWave) {
-        const uint32_t e = (uint32_t)(wv / a.index_tiles);
-        const uint32_t it = (uint32_t)(wv - (uint64_t)e * a.index_tiles);
-        const uint8_t *plane = a.dense + (uint64_t)e * a.P;
+    const bool long_rows = a.C >= 16u;
+    for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves; wv += stride) {
+        TileRuns cur;
+        fetch_runs(a, wv, lane, vec, long_rows, cur);
+        const uint32_t e = (uint32_t)wv / a.index_tiles;
         const uint8_t *brow = a.bases + (uint64_t)e * a.R;
-        const uint32_t p0 = it * kIndexTile + lane * kPerLane;
-        uint32_t flags = 0;
-        if (p0 < a.P) {
-            uint32_t x[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-            load_run16(plane, p0, a.P, vec, x);
-            if (p0 + 16u < a.P) load_run16(plane, p0 + 16u, a.P, vec, x + 4);
-            uint32_t r = div_exact(p0, a.rcp_cols);
-            uint32_t next = (r + 1u) * a.C;
-            uint32_t b = brow[r];
+        uint32_t flags[2] = {0u, 0u};
 #pragma unroll
-            for (uint32_t k = 0; k < kPerLane; ++k) {
-                const uint32_t p = p0 + k;
-                if (p < a.P) {
-                    if (p == next) {
-                        ++r;
-                        next += a.C;
-                        b = brow[r];
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t p0 = run_start(a, wv, h, lane);
+            if (p0 < a.P && long_rows) {
+                uint32_t d[4], keep[4], valid[4];
+                window_test16(a, cur, h, p0, d, keep, valid);
+#pragma unroll
+                for (uint32_t t = 0; t < 4; ++t) {
+                    // gather the 0x80 bits of the word's outside bytes into 4 bits
+                    const uint32_t out = valid[t] & ~keep[t];
+                    flags[h] |= ((out * 0x00204081u) >> 28) << (4u * t);
+                }
+            } else if (p0 < a.P) {
+                RunBases rb(a, brow, p0);
+#pragma unroll
+                for (uint32_t j = 0; j < 16; ++j) {
+                    const uint32_t p = p0 + j;
+                    if (p < a.P) {
+                        const uint32_t b = rb.at(a, brow, p);
+                        const uint32_t byte = (cur.x[h][j >> 2] >> (8u * (j & 3u))) & 0xffu;
+                        if (byte - b >= W) flags[h] |= 1u << j;  // 32-bit difference: below b is outside
                     }
-                    const uint32_t byte = (x[k >> 2] >> (8u * (k & 3u))) & 0xffu;
-                    if (byte - b >= W) flags |= 1u << k;  // no wrap past 255
                 }
             }
         }
-        const uint32_t cnt = __popc(flags);
-        uint32_t incl = cnt;
+        const uint32_t c0 = __popc(flags[0]), c1 = __popc(flags[1]);
+        const uint32_t i0 = wave_inclusive_sum(c0), i1 = wave_inclusive_sum(c1);
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)i0, kWave - 1);
+        const uint32_t first = (uint32_t)a.tile_index[wv];
+        const uint32_t out0[2] = {first + i0 - c0, first + t0 + i1 - c1};
 #pragma unroll
-        for (uint32_t d = 1; d < kWave; d <<= 1) {
-            const uint32_t y = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += y;
-        }
-        uint32_t k_out = (uint32_t)a.tile_index[wv] + (incl - cnt);
-        while (flags != 0) {
-            const uint32_t k = __ffs(flags) - 1;
-            flags &= flags - 1;
-            a.exc[k_out++] = ((p0 + k) << 8) | plane[p0 + k];
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t p0 = run_start(a, wv, h, lane);
+            uint32_t fl = flags[h], o = out0[h];
+            while (fl != 0u) {
+                const uint32_t j = __ffs(fl) - 1u;
+                fl &= fl - 1u;
+                const uint32_t w = j < 8u ? (j < 4u ? cur.x[h][0] : cur.x[h][1])
+                                          : (j < 12u ? cur.x[h][2] : cur.x[h][3]);
+                a.exc[o++] = ((p0 + j) << 8) | __builtin_amdgcn_ubfe(w, 8u * (j & 3u), 8u);
+            }
         }
     }
 }

@@ -517,7 +517,10 @@ ENCODE_SHAPES = RAGGED + [(workloads.NVFP4, 2, 3000, 50), (workloads.MXFP4, 2, 1
                           (workloads.NVFP4, 3, 33, 12), (workloads.MXFP4, 1, 5, 4), (workloads.NVFP4, 2, 7, 254),
                           (workloads.MXFP4, 4, 7, 255), (workloads.NVFP4, 1, 255, 4), (workloads.MXFP4, 3, 100, 52),
                           # one column more than the byte-wide bins allow
-                          (workloads.NVFP4, 4, 5, 256)]
+                          (workloads.NVFP4, 4, 5, 256),
+                          # more index tiles (E x tiles per plane) than the scan keeps in
+                          # registers: its counts are read twice
+                          (workloads.NVFP4, 40000, 3, 11), (workloads.MXFP4, 70001, 1, 3)]
 
 
 @pytest.mark.parametrize("fmt,E,R,C", ENCODE_SHAPES, ids=[f"f{c[0]}_{c[1]}x{c[2]}x{c[3]}" for c in ENCODE_SHAPES])
@@ -529,6 +532,25 @@ def test_gpu_encoder_ragged(orc, dev, fmt, E, R, C):
     got = mwd.prepare(torch.from_numpy(x).to(dev), fmt)
     torch.cuda.synchronize()
     _same_streams(got.numpy(), orc.encode(fmt, x), f"{fmt} {E}x{R}x{C}")
+
+
+def test_gpu_encoder_bases_above_256_minus_w(orc, dev):
+    """A row's base is one of its values and may exceed 256 - W; bytes just
+    above 0 then differ from it by less than W modulo 256 but lie below the
+    window, so they are exceptions."""
+    rng = np.random.default_rng(11)
+    for fmt, top, low, C in ((workloads.NVFP4, 250, 6, 32), (workloads.NVFP4, 245, 10, 40),
+                             (workloads.MXFP4, 255, 2, 32), (workloads.MXFP4, 255, 3, 17)):
+        rows = []
+        for _ in range(2 * 8):
+            row = np.concatenate([np.full(C - low, top), np.arange(low)]).astype(np.uint8)
+            rows.append(rng.permutation(row))
+        x = np.stack(rows).reshape(2, 8, C)
+        want = orc.encode(fmt, x)
+        assert (want["bases"] == top).all() and len(want["exceptions"]) == 2 * 8 * low
+        got = mwd.prepare(torch.from_numpy(x).to(dev), fmt)
+        torch.cuda.synchronize()
+        _same_streams(got.numpy(), want, f"high bases {fmt} C={C}")
 
 
 def test_gpu_encoder_two_column_exhaustive(orc, dev):
