@@ -6,11 +6,12 @@
 // [v, v + 2^w - 1], ties to the smallest v; offsets, exception entries,
 // prefix and tile index follow the layout in include/csf.h.
 //
-// Four kernels, all byte streams bound by HBM bandwidth:
-//   csf_enc_bases_short_kernel  rows of at most 255 columns (every workload
-//                           stack): 16 lanes per row, byte-wide bins, window
-//                           counts by SWAR arithmetic and DPP (below).
-//   csf_enc_bases_kernel    any row: one wave per 4 rows at a time, a 256-bin
+// The kernels, in launch order:
+//   csf_enc_bases_pair_kernel  rows of at most 255 columns in a 16-byte
+//                           aligned stack (every workload stack): two lanes
+//                           per row, the row's byte-wide bins in LDS, window
+//                           counts by SWAR arithmetic (below).
+//   csf_enc_bases_kernel    any other stack: one wave per 4 rows, a 256-bin
 //                           histogram per row in LDS (4 bins per lane),
 //                           window counts as differences of a wave prefix
 //                           over the bins, arg-max by a wave reduction.
@@ -165,16 +166,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Orders this wave's LDS traffic without waiting for its global memory
-// operations: a wave's LDS operations are performed in issue order, so
-// waiting for its outstanding ones (lgkmcnt(0) alone; gfx9 s_waitcnt
-// encoding, vmcnt and expcnt left at their maxima) is all the ordering
-// between this wave's histogram writes and reads needs.
-__device__ __forceinline__ void wave_lds_order() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-}
-
 // Orders this wave's LDS traffic (a wave works on its own histogram).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -263,205 +254,12 @@ __global__ __launch_bounds__(kBlock) void csf_enc_bases_kernel(EncodeArgs a) {
     }
 }
 
-constexpr uint32_t kShortRows = 4;     // rows per wave at a time
-constexpr uint32_t kShortWords = 4;    // 32-bit loads per lane per group: 4 * 4 * 64 bytes >= 4 * 255
-
-// ---------------------------------------------------------------------------
-// Row bases of rows of at most 255 columns (every count then fits a byte).
-//
-// A wave takes 4 rows at a time, 16 lanes per row (lane j of the row's
-// group owns values 16 j .. 16 j + 15).  The rows' bytes (4 C, contiguous)
-// are read as 32-bit words, the next 4 rows' while this group is counted.
-// Counting: byte-wide bins in LDS, 4 per 32-bit word, by LDS atomic adds of
-// 1 << 8 (v % 4) at word v / 4 of one of four copies (below).  Lane j then
-// holds its 16 bins in four words h[0..3]; with SWAR byte arithmetic (no
-// carry crosses a byte, as every sum of bins is at most C <= 255):
-//   W = 16:  count(16 j + i) = T_j - pre_j(i) + pre_{j+1}(i), T_j the lane's
-//            total and pre_j(i) its bins below i, pre_{j+1} taken from the
-//            next lane by DPP (0 past the row's last lane: no values above
-//            255);
-//   W = 2:   count(v) = bin v + bin v + 1, bin 16 j + 16 being the next
-//            lane's first.
-// Counts of values absent from the row are zeroed; the row maximum M comes
-// from packed 16-bit maxima and a 16-lane DPP rotation; the base is the
-// smallest value whose count is M (a present value, since M >= 1).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x101, 0xf, 0xf, true);  // row_shl:1
-}
-
-__device__ __forceinline__ uint32_t row_max16(uint32_t x) {
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
-    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));  // row_ror:2
-    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));  // row_ror:1
-}
-
-__device__ __forceinline__ uint32_t row_min16(uint32_t x) {
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false));
-    return min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false));
-}
-
-// 0xff in each byte of x that is not zero, else 0.
-__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
-    const uint32_t t = (((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x) & 0x80808080u;
-    return (t >> 7) * 0xffu;
-}
-
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                    __builtin_bit_cast(u16x2, b)));
-}
-
-// The base of row g of a group whose 4 rows' bytes are the words w (nbytes
-// of them, whole words), counted in the wave's LDS bins hw; written by lane
-// 0 of the row's 16 for rows below `rows`.
-// LDS bins of one wave: 4 rows x 256 byte-wide bins (64 words per row), in
-// K copies.  K = 1: row r's bin word d at 64 r + d.  K = 4: lane l counts
-// into copy l % 4, so lanes adding to the same bin mostly hit different
-// words, at word 16 d + 4 r + c: the 16 words of one d lie in 16 different
-// banks, and one 16-byte read returns the four copies of a row's word.
-// Four copies pay where most of a row's values fall in a few bins (the
-// two-value window of one-bit offsets); elsewhere the extra clearing and
-// reading cost more than the conflicts they remove.
-template <uint32_t K>
-__device__ __forceinline__ uint32_t bin_word(uint32_t d, uint32_t r, uint32_t lane) {
-    return K == 1 ? 64u * r + d : 16u * d + 4u * r + lane % K;
-}
-
-template <uint32_t WB, uint32_t K, typename AfterCount>
-__device__ __forceinline__ void group_bases(const EncodeArgs &a, uint32_t *hw, const uint32_t (&w)[kShortWords],
-                                            uint32_t r0, uint32_t nbytes, uint32_t rows, AfterCount after_count) {
-    const uint32_t lane = threadIdx.x % kWave, g = lane / 16, j = lane % 16;
-    const uint32_t C = a.C;
-#pragma unroll
-    for (uint32_t t = 0; t < K; ++t)
-        reinterpret_cast<uint4 *>(hw)[t * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
-    wave_lds_order();
-    // One branch per word (the group holds whole words).  A word's bytes may
-    // straddle a row boundary: one when C >= 4, up to three when C < 4.
-    if (C >= 4) {
-#pragma unroll
-        for (uint32_t i = 0; i < kShortWords; ++i) {
-            const uint32_t o = 4u * (i * kWave + lane);  // first byte of the word in the group
-            if (o < nbytes) {
-                const uint32_t row = (o >= C) + (o >= 2 * C) + (o >= 3 * C);
-                const uint32_t next = (row + 1) * C;  // first byte of the next row
-#pragma unroll
-                for (uint32_t k = 0; k < 4; ++k) {
-                    const uint32_t v = __builtin_amdgcn_ubfe(w[i], 8 * k, 8);
-                    const uint32_t rk = row + (o + k >= next ? 1u : 0u);
-                    atomicAdd(&hw[bin_word<K>(v >> 2, rk, lane)], 1u << ((v & 3u) << 3));
-                }
-            }
-        }
-    } else {
-        // 4 C <= 12 bytes: lanes 0 .. C - 1 hold the group's words
-        const uint32_t o = 4u * lane;
-        if (o < nbytes) {
-#pragma unroll
-            for (uint32_t k = 0; k < 4; ++k) {
-                const uint32_t ob = o + k;
-                const uint32_t v = __builtin_amdgcn_ubfe(w[0], 8 * k, 8);
-                const uint32_t rk = (ob >= C) + (ob >= 2 * C) + (ob >= 3 * C);
-                atomicAdd(&hw[bin_word<K>(v >> 2, rk, lane)], 1u << ((v & 3u) << 3));
-            }
-        }
-    }
-    after_count();  // (the words are no longer needed)
-    wave_lds_order();
-    // row g, bins 16 j .. 16 j + 15: words 4 j .. 4 j + 3, the copies summed
-    // (byte-wise: every sum of bins is at most C <= 255)
-    uint32_t h[4];
-    if constexpr (K == 1) {
-        const uint4 hv = reinterpret_cast<const uint4 *>(hw)[lane];
-        h[0] = hv.x;
-        h[1] = hv.y;
-        h[2] = hv.z;
-        h[3] = hv.w;
-    } else {
-#pragma unroll
-        for (uint32_t t = 0; t < 4; ++t) {
-            const uint4 cp = reinterpret_cast<const uint4 *>(hw)[4 * (4 * j + t) + g];
-            h[t] = cp.x + cp.y + cp.z + cp.w;
-        }
-    }
-    uint32_t cnt[4];
-    if constexpr (WB == 4) {
-        uint32_t pre[4], run = 0;
-#pragma unroll
-        for (uint32_t t = 0; t < 4; ++t) {
-            pre[t] = h[t] * 0x01010100u + run * 0x01010101u;  // bins of the lane below each byte
-            run += (h[t] * 0x01010101u) >> 24;
-        }
-        const uint32_t total = run * 0x01010101u;
-#pragma unroll
-        for (uint32_t t = 0; t < 4; ++t) cnt[t] = total - pre[t] + next_lane(pre[t]);
-    } else {
-        const uint32_t nh0 = next_lane(h[0]);
-#pragma unroll
-        for (uint32_t t = 0; t < 4; ++t) cnt[t] = h[t] + (h[t] >> 8) + ((t < 3 ? h[t < 3 ? t + 1 : 0] : nh0) << 24);
-    }
-#pragma unroll
-    for (uint32_t t = 0; t < 4; ++t) cnt[t] &= nonzero_bytes(h[t]);
-    // the row's largest count
-    uint32_t m = max_u16x2(max_u16x2(cnt[0] & 0x00ff00ffu, cnt[1] & 0x00ff00ffu),
-                           max_u16x2(cnt[2] & 0x00ff00ffu, cnt[3] & 0x00ff00ffu));
-    m = max_u16x2(m, max_u16x2(max_u16x2((cnt[0] >> 8) & 0x00ff00ffu, (cnt[1] >> 8) & 0x00ff00ffu),
-                               max_u16x2((cnt[2] >> 8) & 0x00ff00ffu, (cnt[3] >> 8) & 0x00ff00ffu)));
-    const uint32_t M = row_max16(max(m & 0xffffu, m >> 16));
-    // the smallest value with that count
-    const uint32_t sm = M * 0x01010101u;
-    const uint64_t z01 = (uint64_t)zero_bytes(cnt[0] ^ sm) | ((uint64_t)zero_bytes(cnt[1] ^ sm) << 32);
-    const uint64_t z23 = (uint64_t)zero_bytes(cnt[2] ^ sm) | ((uint64_t)zero_bytes(cnt[3] ^ sm) << 32);
-    const uint32_t local = z01 ? (uint32_t)__builtin_ctzll(z01) >> 3
-                               : (z23 ? 8u + ((uint32_t)__builtin_ctzll(z23) >> 3) : 256u);
-    const uint32_t base = row_min16(local < 256u ? 16u * j + local : 256u);
-    if (j == 0 && r0 + g < rows) a.bases[r0 + g] = (uint8_t)base;
-    wave_lds_order();  // this group's bins read before the next group clears them
-}
-
-// The host sends stacks of fewer than 2^31 bytes, a multiple of 4, with
-// rows of at most 255 columns; so the 32-bit group offsets below are exact
-// and every group is whole words.
-template <uint32_t WB, uint32_t K>
-__global__ __launch_bounds__(kBlock) void csf_enc_bases_short_kernel(EncodeArgs a) {
-    constexpr uint32_t kWaves = kBlock / kWave;
-    __shared__ __align__(16) uint32_t hist[kWaves][256 * K];
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint32_t lane = threadIdx.x % kWave;
-    const uint32_t C = a.C;
-    const uint32_t rows = a.E * a.R;
-    const uint32_t groups = (rows + kShortRows - 1) / kShortRows;
-    const uint32_t stride = gridDim.x * kWaves;
-    uint32_t *hw = hist[wave];
-
-    // The words of group q: bytes [4 q C, min(4 q C + 4 C, rows C)), word d
-    // at byte 4 d, loaded through a resource over exactly those bytes.
-    auto load_group = [&](uint32_t q, uint32_t (&w)[kShortWords]) {
-        // (uniform; said so, so the resource stays in scalar registers)
-        const uint32_t first = __builtin_amdgcn_readfirstlane(q * kShortRows * C);
-        const uint32_t end = __builtin_amdgcn_readfirstlane(min(first + kShortRows * C, rows * C));
-        const rsrc_t r = make_rsrc(a.dense + first, end - first);
-#pragma unroll
-        for (uint32_t i = 0; i < kShortWords; ++i)
-            w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(4u * (i * kWave + lane)), 0, 0);
-    };
-    auto nbytes_of = [&](uint32_t q) { return (min(q * kShortRows + kShortRows, rows) - q * kShortRows) * C; };
-
-    // The next group's words are loaded once this group's are counted, while
-    // its bases are found.
-    uint32_t q = blockIdx.x * kWaves + wave;
-    uint32_t w[kShortWords];
-    if (q < groups) load_group(q, w);
-    for (; q < groups; q += stride)
-        group_bases<WB, K>(a, hw, w, q * kShortRows, nbytes_of(q), rows, [&] {
-            if (q + stride < groups) load_group(q + stride, w);
-        });
 }
 
 // OR of x over this lane and the s - 1 lanes below it in its 16-lane row
@@ -472,6 +270,175 @@ __device__ __forceinline__ uint32_t or_down(uint32_t x, uint32_t s) {
     if (s > 2) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
     if (s > 4) x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
     return x;
+}
+
+// ---------------------------------------------------------------------------
+// Row bases, two lanes per row (rows of at most 255 columns, a 16-byte
+// aligned stack).  A wave takes 32 rows at a time: lanes r and r + 32 share
+// row r.  The row's histogram of the 256 byte values lives in LDS, one byte
+// per bin (a row's count fits a byte), 64 words plus one of padding, so
+// word w of row r sits in bank (r + w) mod 32 and the 32 lanes of a half
+// wave never meet in a bank.  Lane half h reads the 16-byte chunks h, h + 2,
+// ... that cover the row (buffer loads, the next group of rows in flight
+// while this one is counted) and adds each of the row's bytes to its bin.
+// Then half h walks bin words 32h .. 32h + 31: byte-wise prefix sums give
+// every window count four candidates at a time (the four windows that cross
+// into the upper half take the upper lane's first prefixes by one lane
+// exchange); the largest key (count << 8 | 255 - v) over the two lanes
+// gives the best count and its first v, and the first value present from
+// that v on is the base (most values in the window, then the smallest
+// present v).  The lanes then clear their bins.  Nothing else crosses
+// lanes, so there is no barrier.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kRowWords = 65;       // 64 bin words + 1 of padding
+constexpr uint32_t kPairRows = 32;       // rows per wave at a time
+constexpr uint32_t kPairWavesPerCu = 18;  // one-wave workgroups per CU: 18 x 8,320 B of LDS
+
+// Byte b (< 256) in all four bytes.
+__device__ __forceinline__ uint32_t splat_byte(uint32_t b) { return __builtin_amdgcn_perm(0u, b, 0u); }
+
+// Fold the window counts cnt of candidates 4s .. 4s + 3 (s relative to the
+// lane's half) into best: two u16 keys per word, count << 8 | 255 - v.
+__device__ __forceinline__ uint32_t fold_keys(uint32_t best, uint32_t cnt, uint32_t s) {
+    const uint32_t v = 4u * s;
+    const uint32_t lo = ((cnt << 8) & 0xff00ff00u) | ((255u - v - 2u) << 16) | (255u - v);  // v, v + 2
+    const uint32_t hi = (cnt & 0xff00ff00u) | ((255u - v - 3u) << 16) | (255u - v - 1u);    // v + 1, v + 3
+    return max_u16x2(best, max_u16x2(lo, hi));
+}
+
+template <uint32_t WB, uint32_t CPL, bool ALIGNED>  // CPL: chunks per lane at most
+__global__ __launch_bounds__(kWave) void csf_enc_bases_pair_kernel(EncodeArgs a) {
+    __shared__ uint32_t hist[kPairRows * kRowWords];
+    const uint32_t lane = threadIdx.x, r = lane % kPairRows, half = lane / kPairRows;
+    uint32_t *h = hist + r * kRowWords;
+    uint32_t *hh = h + 32u * half;  // this lane's half of the bins
+    const uint32_t C = a.C, rows = a.E * a.R;  // rows * C < 2^31
+    const uint32_t n = rows * C;
+    const uint32_t groups = (rows + kPairRows - 1) / kPairRows;
+    // chunks a row can meet: it starts at a multiple of gcd(C, 16) within its chunk
+    const uint32_t nch = ALIGNED ? C / 16u : (C + 31u - min(C & (0u - C), 16u)) / 16u;
+    const rsrc_t src = make_rsrc(a.dense, n);
+#pragma unroll
+    for (uint32_t w = 0; w < 32; ++w) hh[w] = 0u;
+    // (The buffer's range check zeroes a whole dword that runs past the stack,
+    // so the chunk holding the stack's last bytes, when they are not whole
+    // dwords, is read byte by byte.)
+    auto load = [&](uint32_t g, uint32_t (&x)[CPL][4]) {
+        const uint32_t first = ((g * kPairRows + r) * C) & ~15u;
+#pragma unroll
+        for (uint32_t c = 0; c < CPL; ++c) {
+            x[c][0] = x[c][1] = x[c][2] = x[c][3] = 0u;
+            const uint32_t i = 2u * c + half;
+            const uint32_t off = first + 16u * i;
+            if (i < nch) {
+                if (off + 16u <= n || off >= n) {
+                    const v4u q = __builtin_amdgcn_raw_buffer_load_b128(src, (int)off, 0, 0);
+                    x[c][0] = q[0];
+                    x[c][1] = q[1];
+                    x[c][2] = q[2];
+                    x[c][3] = q[3];
+                } else {
+#pragma unroll
+                    for (uint32_t b = 0; b < 16; ++b)
+                        if (off + b < n) x[c][b >> 2] |= (uint32_t)a.dense[off + b] << (8u * (b & 3u));
+                }
+            }
+        }
+    };
+    uint32_t x[CPL][4];
+    uint32_t g = blockIdx.x;
+    if (g < groups) load(g, x);
+    for (; g < groups; g += gridDim.x) {
+        uint32_t y[CPL][4];
+        if (g + gridDim.x < groups) load(g + gridDim.x, y);
+        const uint32_t row = g * kPairRows + r;
+        const bool live = row < rows;  // the same for both lanes of a row
+        if (live) {
+            const uint32_t o = ALIGNED ? 0u : (row * C) & 15u;  // the row's first byte in chunk 0
+#pragma unroll
+            for (uint32_t c = 0; c < CPL; ++c) {
+                const uint32_t i = 2u * c + half;
+                if (i < nch) {
+#pragma unroll
+                    for (uint32_t j = 0; j < 16; ++j) {
+                        const uint32_t v = __builtin_amdgcn_ubfe(x[c][j >> 2], 8u * (j & 3u), 8u);
+                        uint32_t add = 1u << (8u * (v & 3u));
+                        if (!ALIGNED) add = (16u * i + j - o) < C ? add : 0u;  // a byte of this row
+                        atomicAdd(&h[v >> 2], add);
+                    }
+                }
+            }
+        }
+        // Both lanes of a row have added their bytes before either reads the
+        // bins: the wave's LDS operations are performed in order (and the
+        // compiler keeps them in program order).
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint32_t run = 0, best = 0;
+        if constexpr (WB == 4) {
+            // px[t]: byte k = values of this half below bin 4t + k (t local);
+            // the window of v = 4s + k holds px[s + 4] - px[s]; the upper
+            // half's first four prefixes, plus the lower half's total, close
+            // the lower half's last four windows; the upper half's close on
+            // its own total (bins up to 255).
+            uint32_t pxq[4], up[4];
+#pragma unroll
+            for (uint32_t t = 0; t < 32; ++t) {
+                const uint32_t hw = live ? hh[t] : 0u;
+                const uint32_t px = (hw << 8) + (hw << 16) + (hw << 24) + splat_byte(run);
+                run = __builtin_amdgcn_udot4(hw, 0x01010101u, run, false);
+                if (t < 4) up[t] = __shfl_xor(px, kPairRows, kWave);
+                if (t >= 4) best = fold_keys(best, px - pxq[t % 4], t - 4);
+                pxq[t % 4] = px;
+            }
+            const uint32_t tail = splat_byte(run);
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) best = fold_keys(best, (half ? 0u : up[k]) + tail - pxq[k], 28u + k);
+        } else {
+            // W = 2: the window of v holds bins v and v + 1; the lower half's
+            // last window takes the upper half's first bin.
+            uint32_t prev = 0, first = 0;
+#pragma unroll
+            for (uint32_t t = 0; t < 32; ++t) {
+                const uint32_t hw = live ? hh[t] : 0u;
+                if (t == 0) first = __shfl_xor(hw, kPairRows, kWave);
+                if (t >= 1) best = fold_keys(best, prev + (prev >> 8) + (hw << 24), t - 1);
+                prev = hw;
+            }
+            const uint32_t nxt = half ? 0u : first;
+            best = fold_keys(best, prev + (prev >> 8) + (nxt << 24), 31u);
+        }
+        // keys of the upper half used 255 - (v - 128)
+        uint32_t key = max(best & 0xffffu, best >> 16) - (half ? 128u : 0u);
+        key = max(key, (uint32_t)__shfl_xor((int)key, kPairRows, kWave));
+        if (live && half == 0) {
+            // The keys counted every v, present in the row or not.  The first
+            // best v, u, has a value in its window; the smallest such value
+            // has a window at least as full (it loses only bins below it,
+            // which are empty) and no smaller present value has the best
+            // count, so it is the base.  It lies in bins u .. u + W - 1.
+            const uint32_t u = 255u - (key & 0xffu);
+            constexpr uint32_t NW = WB == 4 ? 5u : 2u;  // bin words that can hold it
+            uint32_t base = 256u;
+#pragma unroll
+            for (uint32_t i = NW; i-- > 0;) {
+                const uint32_t w = (u >> 2) + i;
+                uint32_t z = w < 64u ? h[w] : 0u;
+                if (i == 0) z &= 0xffffffffu << (8u * (u & 3u));  // bins below u
+                const uint32_t nz = (((z & 0x7f7f7f7fu) + 0x7f7f7f7fu) | z) & 0x80808080u;
+                base = nz ? 4u * w + ((uint32_t)__builtin_ctz(nz) >> 3) : base;
+            }
+            a.bases[row] = (uint8_t)base;
+        }
+        if (live) {
+#pragma unroll
+            for (uint32_t t = 0; t < 32; ++t) hh[t] = 0u;
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // bins cleared before the next group's adds
+#pragma unroll
+        for (uint32_t c = 0; c < CPL; ++c)
+#pragma unroll
+            for (uint32_t j = 0; j < 4; ++j) x[c][j] = y[c][j];
+    }
 }
 
 // One wave per index tile (kIndexTile positions = 128 runs of 16); lane l
@@ -691,13 +658,26 @@ static uint32_t grid_for(uint64_t waves_needed, uint32_t cus) {
 hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t stream) {
     uint32_t grid;
     const uint64_t n = (uint64_t)a.E * a.R * a.C;
-    if (a.C <= 255 && ((uintptr_t)a.dense & 3u) == 0 && n % 4 == 0 && n < (1ull << 31)) {
-        const uint64_t groups = ((uint64_t)a.E * a.R + kShortRows - 1) / kShortRows;
-        grid = grid_for(groups, cus);
-        if (a.wbits == 4)
-            hipLaunchKernelGGL((csf_enc_bases_short_kernel<4, 1>), dim3(grid), dim3(kBlock), 0, stream, a);
-        else
-            hipLaunchKernelGGL((csf_enc_bases_short_kernel<1, 4>), dim3(grid), dim3(kBlock), 0, stream, a);
+    if (a.C <= 255 && ((uintptr_t)a.dense & 15u) == 0 && n < (1ull << 31)) {
+        const bool aligned = a.C % 16 == 0;
+        const uint32_t low = std::min<uint32_t>(a.C & (0u - a.C), 16u);
+        const uint32_t nch = aligned ? a.C / 16 : (a.C + 31 - low) / 16;
+        const uint64_t groups = ((uint64_t)a.E * a.R + kPairRows - 1) / kPairRows;
+        grid = (uint32_t)std::min<uint64_t>(groups, (uint64_t)cus * kPairWavesPerCu);
+#define CSF_PAIR(WB, CPL, AL) \
+    hipLaunchKernelGGL((csf_enc_bases_pair_kernel<WB, CPL, AL>), dim3(grid), dim3(kWave), 0, stream, a)
+#define CSF_PAIR_CPL(WB, AL)            \
+    if (nch <= 4) CSF_PAIR(WB, 2, AL);       \
+    else if (nch <= 8) CSF_PAIR(WB, 4, AL);  \
+    else if (nch <= 12) CSF_PAIR(WB, 6, AL); \
+    else CSF_PAIR(WB, 9, AL);
+        if (a.wbits == 4) {
+            if (aligned) { CSF_PAIR_CPL(4, true) } else { CSF_PAIR_CPL(4, false) }
+        } else {
+            if (aligned) { CSF_PAIR_CPL(1, true) } else { CSF_PAIR_CPL(1, false) }
+        }
+#undef CSF_PAIR_CPL
+#undef CSF_PAIR
     } else {
         grid = grid_for((uint64_t)a.E * a.R, cus);
         hipLaunchKernelGGL(csf_enc_bases_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
