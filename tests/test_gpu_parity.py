@@ -553,6 +553,22 @@ def test_gpu_encoder_bases_above_256_minus_w(orc, dev):
         _same_streams(got.numpy(), want, f"high bases {fmt} C={C}")
 
 
+@pytest.mark.parametrize("shift", [1, 4, 8])
+def test_gpu_encoder_unaligned_dense(orc, dev, shift):
+    """A stack that starts 1, 4 or 8 bytes past a 16-byte boundary: the row
+    bases come from the kernel for any alignment, the offset and entry passes
+    read the bytes one by one."""
+    for fmt, E, R, C in ((workloads.NVFP4, 3, 33, 50), (workloads.MXFP4, 2, 17, 160), (workloads.NVFP4, 2, 9, 128)):
+        x = workloads.nvfp4_stack(E, R, C, 13, 0.08) if fmt == workloads.NVFP4 else workloads.mxfp4_stack(E, R, C, 13, 0.15)
+        buf = torch.empty(x.size + 32, dtype=torch.uint8, device=dev)
+        xd = buf[shift:shift + x.size].view(E, R, C)
+        xd.copy_(torch.from_numpy(x))
+        assert xd.data_ptr() % 16 == shift % 16
+        got = mwd.prepare(xd, fmt)
+        torch.cuda.synchronize()
+        _same_streams(got.numpy(), orc.encode(fmt, x), f"shift {shift} {fmt} {E}x{R}x{C}")
+
+
 def test_gpu_encoder_two_column_exhaustive(orc, dev):
     a, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
     x = np.stack([a.ravel(), b.ravel()], axis=1).astype(np.uint8).reshape(4, 16384, 2)
