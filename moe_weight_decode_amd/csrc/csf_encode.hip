@@ -60,7 +60,7 @@ __device__ __forceinline__ void load_run16(const uint8_t *plane, uint32_t p0, ui
         if (p0 + j < P) x[j >> 2] |= (uint32_t)plane[p0 + j] << (8u * (j & 3u));
 }
 
-__device__ __forceinline__ bool runs_aligned(const EncodeArgs &a) {
+__host__ __device__ inline bool runs_aligned(const EncodeArgs &a) {
     return ((uintptr_t)a.dense & 15u) == 0 && (a.P & 15u) == 0;
 }
 
@@ -86,8 +86,16 @@ struct RunBases {
 
 // 0xff in the bytes k >= s of a word, 0 below.
 __device__ __forceinline__ uint32_t bytes_from(int32_t s) {
-    return s <= 0 ? 0xffffffffu : (s >= 4 ? 0u : 0xffffffffu << (8 * s));
+    const uint32_t c = (uint32_t)min(max(s, 0), 4);
+    return (uint32_t)(0xffffffffffffffffull << (8u * c));
 }
+
+// 0xff in each byte of x whose bit 7 is set, else 0 (v_perm's sign
+// selectors 8-11 read bit 7 of bytes 1, 3, 5, 7 of {x, x << 8}).
+__device__ __forceinline__ uint32_t widen80(uint32_t x) { return __builtin_amdgcn_perm(x, x << 8, 0x0b090a08u); }
+
+// Byte b (< 256) in all four bytes.
+__device__ __forceinline__ uint32_t splat_byte(uint32_t b) { return __builtin_amdgcn_perm(0u, b, 0u); }
 
 // Byte-wise x - y modulo 256 (no borrow between bytes).
 __device__ __forceinline__ uint32_t byte_sub(uint32_t x, uint32_t y) {
@@ -138,25 +146,26 @@ __device__ __forceinline__ void fetch_runs(const EncodeArgs &a, uint64_t wv, uin
 // Window test of run h of t (positions p0 .. p0 + 15, rows of at least 16
 // columns), four bytes at a time: d[j] holds the byte differences (modulo
 // 256) to the bases of their rows, valid[j] 0x80 in each byte inside the
-// plane, keep[j] 0x80 in each valid byte inside its row's window: a
-// difference below W without a borrow (a base may exceed 256 - W, so a byte
-// below it can still differ by less than W modulo 256).
+// plane (every byte when VEC: the plane is whole runs), keep[j] 0x80 in each
+// valid byte inside its row's window: a difference below W, without a
+// borrow when HIGH (some base in the wave exceeds 256 - W, so a byte below
+// it can still differ from it by less than W modulo 256).
+template <bool VEC, bool HIGH>
 __device__ __forceinline__ void window_test16(const EncodeArgs &a, const TileRuns &t, uint32_t h, uint32_t p0,
                                               uint32_t (&d)[4], uint32_t (&keep)[4], uint32_t (&valid)[4]) {
-    const uint32_t next = (div_exact(p0, a.rcp_cols) + 1u) * a.C;  // first position of the next row
-    const uint32_t B0 = t.b0[h] * 0x01010101u, B1 = t.b1[h] * 0x01010101u;
+    const int32_t to_next = (int32_t)((div_exact(p0, a.rcp_cols) + 1u) * a.C - p0);  // bytes left in p0's row
+    const uint32_t B0 = splat_byte(t.b0[h]), B1 = splat_byte(t.b1[h]);
     const uint32_t hi = (0x100u - (1u << a.wbits)) * 0x01010101u;  // bits that must be 0 in a kept difference
 #pragma unroll
     for (uint32_t j = 0; j < 4; ++j) {
-        const uint32_t pt = p0 + 4u * j;
         const uint32_t x = t.x[h][j];
-        const uint32_t in_next = bytes_from((int32_t)(next - pt));
-        valid[j] = ~bytes_from((int32_t)(a.P - pt)) & 0x80808080u;
+        const uint32_t in_next = bytes_from(to_next - (int32_t)(4u * j));
+        valid[j] = VEC ? 0x80808080u : ~bytes_from((int32_t)(a.P - p0 - 4u * j)) & 0x80808080u;
         const uint32_t bv = (B0 & ~in_next) | (B1 & in_next);
         d[j] = byte_sub(x, bv);
-        // borrow out of each byte's top bit: the byte is below its base
-        const uint32_t below = ((~x & bv) | (~(x ^ bv) & d[j])) & 0x80808080u;
-        keep[j] = zero_bytes(d[j] & hi) & ~below & valid[j];
+        uint32_t k = zero_bytes(d[j] & hi) & valid[j];
+        if (HIGH) k &= ~((~x & bv) | (~(x ^ bv) & d[j]));  // borrow out of a byte: below its base
+        keep[j] = k;
     }
 }
 
@@ -294,8 +303,6 @@ constexpr uint32_t kRowWords = 65;       // 64 bin words + 1 of padding
 constexpr uint32_t kPairRows = 32;       // rows per wave at a time
 constexpr uint32_t kPairWavesPerCu = 18;  // one-wave workgroups per CU: 18 x 8,320 B of LDS
 
-// Byte b (< 256) in all four bytes.
-__device__ __forceinline__ uint32_t splat_byte(uint32_t b) { return __builtin_amdgcn_perm(0u, b, 0u); }
 
 // Fold the window counts cnt of candidates 4s .. 4s + 3 (s relative to the
 // lane's half) into best: two u16 keys per word, count << 8 | 255 - v.
@@ -449,35 +456,46 @@ __global__ __launch_bounds__(kWave) void csf_enc_bases_pair_kernel(EncodeArgs a)
 // are F consecutive lanes; an OR down those lanes gives the group to its
 // last lane, which stores it.  The tile's out-of-window count is a sum over
 // the wave.
+// Offset fields of run h of t (rows of at least 16 columns) at bits w f of
+// word[0..3]; returns the run's out-of-window count.
+template <bool VEC, bool HIGH>
+__device__ __forceinline__ uint32_t pack_run(const EncodeArgs &a, const TileRuns &t, uint32_t h, uint32_t p0,
+                                             uint32_t f, uint32_t (&word)[4]) {
+    uint32_t d[4], keep[4], valid[4], outside = 0;
+    window_test16<VEC, HIGH>(a, t, h, p0, d, keep, valid);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+        // a kept difference is below W: its field is its low w bits
+        word[j] = (d[j] & widen80(keep[j])) << (a.wbits * f);
+        outside += __popc(valid[j] & ~keep[j]);
+    }
+    return outside;
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
     const uint32_t lane = threadIdx.x % kWave;
     const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
     const uint64_t stride = (uint64_t)gridDim.x * kBlock / kWave;
     const uint32_t W = 1u << a.wbits;
-    const uint32_t F = 8u / a.wbits;
-    const bool vec = runs_aligned(a);
+    const uint32_t F = 8u / a.wbits, fshift = a.wbits == 4 ? 1u : 3u;  // runs per group: 2 or 8
     const bool long_rows = a.C >= 16u;
     for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves; wv += stride) {
         TileRuns cur;
-        fetch_runs(a, wv, lane, vec, long_rows, cur);
+        fetch_runs(a, wv, lane, VEC, long_rows, cur);
         const uint32_t e = (uint32_t)wv / a.index_tiles;
         const uint8_t *brow = a.bases + (uint64_t)e * a.R;
+        // a base above 256 - W anywhere in the wave needs the borrow check
+        const bool high = __ballot(max(max(cur.b0[0], cur.b1[0]), max(cur.b0[1], cur.b1[1])) > 256u - W) != 0;
         uint32_t outside = 0;
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {
             const uint32_t p0 = run_start(a, wv, h, lane);
             const uint32_t q = p0 / 16u;  // run in the plane
-            const uint32_t f = q % F;
+            const uint32_t f = q & (F - 1u);
             uint32_t word[4] = {0u, 0u, 0u, 0u};
             if (p0 < a.P && long_rows) {
-                uint32_t d[4], keep[4], valid[4];
-                window_test16(a, cur, h, p0, d, keep, valid);
-#pragma unroll
-                for (uint32_t t = 0; t < 4; ++t) {
-                    // a kept difference is below W: its field is its low w bits
-                    word[t] = (d[t] & ((keep[t] >> 7) * 0xffu)) << (a.wbits * f);
-                    outside += __popc(valid[t] & ~keep[t]);
-                }
+                outside += high ? pack_run<VEC, true>(a, cur, h, p0, f, word) : pack_run<VEC, false>(a, cur, h, p0, f, word);
             } else if (p0 < a.P) {
                 RunBases rb(a, brow, p0);
 #pragma unroll
@@ -495,7 +513,7 @@ __global__ __launch_bounds__(kBlock) void csf_enc_pack_kernel(EncodeArgs a) {
             }
 #pragma unroll
             for (uint32_t t = 0; t < 4; ++t) word[t] = or_down(word[t], F);
-            const uint32_t g = q / F;
+            const uint32_t g = q >> fshift;
             if (f == F - 1u && g < a.groups) {
                 uint4 *dst = reinterpret_cast<uint4 *>(a.offsets + (uint64_t)e * a.stride + 16u * g);
                 *dst = make_uint4(word[0], word[1], word[2], word[3]);
@@ -589,31 +607,41 @@ __global__ __launch_bounds__(kScanThreads) void csf_enc_scan_kernel(EncodeArgs a
 // prefix of the out-of-window counts of each half ranks the entries, and
 // each lane writes its own in ascending order, bytes taken from the loaded
 // registers.
+// 0x80 in each byte of run h of t (rows of at least 16 columns) that lies
+// outside its row's window, four bytes per word of out.
+template <bool VEC, bool HIGH>
+__device__ __forceinline__ void outside_run(const EncodeArgs &a, const TileRuns &t, uint32_t h, uint32_t p0,
+                                            uint32_t (&out)[4]) {
+    uint32_t d[4], keep[4], valid[4];
+    window_test16<VEC, HIGH>(a, t, h, p0, d, keep, valid);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) out[j] = valid[j] & ~keep[j];
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
     const uint32_t lane = threadIdx.x % kWave;
     const uint64_t total_waves = (uint64_t)a.E * a.index_tiles;
     const uint64_t stride = (uint64_t)gridDim.x * kBlock / kWave;
     const uint32_t W = 1u << a.wbits;
-    const bool vec = runs_aligned(a);
     const bool long_rows = a.C >= 16u;
     for (uint64_t wv = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) / kWave; wv < total_waves; wv += stride) {
         TileRuns cur;
-        fetch_runs(a, wv, lane, vec, long_rows, cur);
+        fetch_runs(a, wv, lane, VEC, long_rows, cur);
         const uint32_t e = (uint32_t)wv / a.index_tiles;
         const uint8_t *brow = a.bases + (uint64_t)e * a.R;
-        uint32_t flags[2] = {0u, 0u};
+        const bool high = __ballot(max(max(cur.b0[0], cur.b1[0]), max(cur.b0[1], cur.b1[1])) > 256u - W) != 0;
+        // outside bytes of each run: bit 8 j + 7 of m[h][j / 8] for byte j
+        uint64_t m[2][2] = {{0u, 0u}, {0u, 0u}};
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {
             const uint32_t p0 = run_start(a, wv, h, lane);
+            uint32_t out[4] = {0u, 0u, 0u, 0u};
             if (p0 < a.P && long_rows) {
-                uint32_t d[4], keep[4], valid[4];
-                window_test16(a, cur, h, p0, d, keep, valid);
-#pragma unroll
-                for (uint32_t t = 0; t < 4; ++t) {
-                    // gather the 0x80 bits of the word's outside bytes into 4 bits
-                    const uint32_t out = valid[t] & ~keep[t];
-                    flags[h] |= ((out * 0x00204081u) >> 28) << (4u * t);
-                }
+                if (high)
+                    outside_run<VEC, true>(a, cur, h, p0, out);
+                else
+                    outside_run<VEC, false>(a, cur, h, p0, out);
             } else if (p0 < a.P) {
                 RunBases rb(a, brow, p0);
 #pragma unroll
@@ -622,12 +650,15 @@ __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
                     if (p < a.P) {
                         const uint32_t b = rb.at(a, brow, p);
                         const uint32_t byte = (cur.x[h][j >> 2] >> (8u * (j & 3u))) & 0xffu;
-                        if (byte - b >= W) flags[h] |= 1u << j;  // 32-bit difference: below b is outside
+                        if (byte - b >= W) out[j >> 2] |= 0x80u << (8u * (j & 3u));  // below b is outside too
                     }
                 }
             }
+            m[h][0] = (uint64_t)out[0] | ((uint64_t)out[1] << 32);
+            m[h][1] = (uint64_t)out[2] | ((uint64_t)out[3] << 32);
         }
-        const uint32_t c0 = __popc(flags[0]), c1 = __popc(flags[1]);
+        const uint32_t c0 = (uint32_t)(__popcll(m[0][0]) + __popcll(m[0][1]));
+        const uint32_t c1 = (uint32_t)(__popcll(m[1][0]) + __popcll(m[1][1]));
         const uint32_t i0 = wave_inclusive_sum(c0), i1 = wave_inclusive_sum(c1);
         const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)i0, kWave - 1);
         const uint32_t first = (uint32_t)a.tile_index[wv];
@@ -635,13 +666,17 @@ __global__ __launch_bounds__(kBlock) void csf_enc_entries_kernel(EncodeArgs a) {
 #pragma unroll
         for (uint32_t h = 0; h < 2; ++h) {
             const uint32_t p0 = run_start(a, wv, h, lane);
-            uint32_t fl = flags[h], o = out0[h];
-            while (fl != 0u) {
-                const uint32_t j = __ffs(fl) - 1u;
-                fl &= fl - 1u;
-                const uint32_t w = j < 8u ? (j < 4u ? cur.x[h][0] : cur.x[h][1])
-                                          : (j < 12u ? cur.x[h][2] : cur.x[h][3]);
-                a.exc[o++] = ((p0 + j) << 8) | __builtin_amdgcn_ubfe(w, 8u * (j & 3u), 8u);
+            uint32_t o = out0[h];
+#pragma unroll
+            for (uint32_t k = 0; k < 2; ++k) {
+                uint64_t mk = m[h][k];
+                while (mk != 0u) {
+                    const uint32_t j = 8u * k + ((uint32_t)__builtin_ctzll(mk) >> 3);
+                    mk &= mk - 1u;
+                    const uint32_t w = j < 8u ? (j < 4u ? cur.x[h][0] : cur.x[h][1])
+                                              : (j < 12u ? cur.x[h][2] : cur.x[h][3]);
+                    a.exc[o++] = ((p0 + j) << 8) | __builtin_amdgcn_ubfe(w, 8u * (j & 3u), 8u);
+                }
             }
         }
     }
@@ -684,7 +719,10 @@ hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t 
     }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     grid = grid_for((uint64_t)a.E * a.index_tiles, cus);
-    hipLaunchKernelGGL(csf_enc_pack_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    if (runs_aligned(a))
+        hipLaunchKernelGGL(csf_enc_pack_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL(csf_enc_pack_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(csf_enc_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
     return hipGetLastError();
@@ -692,7 +730,10 @@ hipError_t launch_encode_streams(const EncodeArgs &a, uint32_t cus, hipStream_t 
 
 hipError_t launch_encode_entries(const EncodeArgs &a, uint32_t cus, hipStream_t stream) {
     const uint32_t grid = grid_for((uint64_t)a.E * a.index_tiles, cus);
-    hipLaunchKernelGGL(csf_enc_entries_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    if (runs_aligned(a))
+        hipLaunchKernelGGL(csf_enc_entries_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL(csf_enc_entries_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
