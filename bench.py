@@ -13,8 +13,9 @@ Prints ONE JSON line on stdout:
                entry prefix; the dense bytes written) x steps / elapsed time
   roofline     the fused kernel (the only kernel of a step): the same bytes
                per launch / its mean launch time, from two HIP events on its
-               stream bracketing the back-to-back launches of the timed
-               region, against the MI355X HBM3E peak (8 TB/s); next to it the
+               stream bracketing a second run of the same back-to-back steps
+               (the wall-clock run has no events in it), against the MI355X
+               HBM3E peak (8 TB/s); next to it the
                kernel average of the committed rocprofv3 trace of the same
                sources, and the plain stream-mix kernel's rate on the same
                buffers (the ceiling of this access pattern on this chip)
@@ -197,23 +198,29 @@ def make_sets(mwd, torch, stack, nsets, dev):
 
 
 def timed_loop(torch, ev, calls, steps, warmup):
-    """Run `steps` calls (after `warmup`), rotating over `calls`, with one HIP
-    event before and one after the whole run on the launch stream.  Returns
-    (wall-clock ms per step, event ms per step)."""
+    """Run `steps` calls (after `warmup`), rotating over `calls`, twice: once
+    bracketed by torch.cuda.synchronize() alone (the wall clock of exactly
+    those steps), once with one HIP event before and one after the run on
+    the launch stream (an event record costs the stream a few µs and the host
+    more, so it stays out of the wall-clock run).  Returns (wall-clock ms per
+    step, event ms per step)."""
     stream = calls[0].stream
+    n = len(calls)
     for i in range(warmup):
-        calls[i % len(calls)]()
-    torch.cuda.synchronize()
-    evs = ev.create(2)
+        calls[i % n]()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    evs = ev.create(2)
+    torch.cuda.synchronize()
     ev.record(evs[0], stream)
-    n = len(calls)
     for i in range(steps):
         calls[i % n]()
     ev.record(evs[1], stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
     total_ms = ev.ms(evs[0], evs[1])
     ev.destroy(evs)
     return wall_ms / steps, total_ms / steps
