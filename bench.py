@@ -657,27 +657,31 @@ def _blas_threads() -> int:
 def bench_encode(mwd, torch, workloads, name, steps, warmup, dev):
     """GPU encodes (csf_encode_device through prepare) of a workload stack
     already in device memory, checked once against the host encoder; wall
-    time per encode (with its one read-back of the entry count)."""
+    time per encode (with its one read-back of the entry count).  name
+    "layer" encodes the gate-like and down-like stacks together (one layer's
+    two projections, prepare_many: one read-back for both)."""
     import numpy as np
-    spec = workloads.STACKS[name]
-    x = spec.generate()
-    xd = torch.from_numpy(x).to(dev)
-    want = mwd.prepare(x, spec.fmt).numpy()
-    got = mwd.prepare(xd, spec.fmt).numpy()
-    for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
-        if not np.array_equal(np.asarray(got[k]).ravel(), np.asarray(want[k]).ravel()):
-            raise SystemExit(f"GPU encode of {name} differs from the host encoder in {k}")
+    specs = [workloads.GATE, workloads.DOWN] if name == "layer" else [workloads.STACKS[name]]
+    xs = [s.generate() for s in specs]
+    xds = [torch.from_numpy(x).to(dev) for x in xs]
+    fmts = [s.fmt for s in specs]
+    wants = [mwd.prepare(x, f).numpy() for x, f in zip(xs, fmts)]
+    gots = [g.numpy() for g in mwd.prepare_many(xds, fmts)]
+    for spec, got, want in zip(specs, gots, wants):
+        for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
+            if not np.array_equal(np.asarray(got[k]).ravel(), np.asarray(want[k]).ravel()):
+                raise SystemExit(f"GPU encode of {spec.name} differs from the host encoder in {k}")
     for _ in range(warmup):
-        mwd.prepare(xd, spec.fmt)
+        mwd.prepare_many(xds, fmts)
     torch.cuda.synchronize()
     t = []
     for _ in range(steps):
         t0 = time.perf_counter()
-        mwd.prepare(xd, spec.fmt)
+        mwd.prepare_many(xds, fmts)
         torch.cuda.synchronize()
         t.append(time.perf_counter() - t0)
-    return dict(encode=name, shape=[spec.E, spec.R, spec.C], dense_bytes=int(x.size), steps=steps,
-                us_per_encode=round(statistics.median(t) * 1e6, 1))
+    return dict(encode=name, shapes=[[s.E, s.R, s.C] for s in specs], dense_bytes=int(sum(x.size for x in xs)),
+                steps=steps, us_per_encode=round(statistics.median(t) * 1e6, 1))
 
 
 def graph_of(torch, dev, calls):
@@ -862,8 +866,8 @@ def main():
                     help="after the timed run, N plain 256 MiB device copies (reference for "
                          "hardware byte counters)")
     ap.add_argument("--encode", default=None, metavar="STACK",
-                    help="instead: time the GPU encoder (csf_encode_device) on a workload stack, --steps times, "
-                         "and print one JSON line (for profiling the encoder kernels)")
+                    help="instead: time the GPU encoder (csf_encode_device) on a workload stack (or 'layer': "
+                         "the gate-like and down-like stacks together), --steps times, and print one JSON line")
     ap.add_argument("--workload", default="gate_nvfp4",
                     choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe",
                              "routed_moe_mx"],
@@ -1063,6 +1067,9 @@ def run_all(mwd, torch, ev, workloads, args, dev):
         log(f"[bench] {name}: {e}")
         del rr, xd
         torch.cuda.empty_cache()
+    le = bench_encode(mwd, torch, workloads, "layer", 20, 3, dev)
+    extra["layer_encode"] = dict(us=le["us_per_encode"], dense_bytes=le["dense_bytes"], shapes=le["shapes"])
+    log(f"[bench] layer_encode (gate-like + down-like stacks, one prepare_many): {extra['layer_encode']}")
     for indexed, gate_only in ((True, False), (False, False), (True, True)):
         key = ("routed_gate" if gate_only else "routed_paired") + ("" if indexed else "_two_pass")
         log(f"[bench] {key}")

@@ -250,42 +250,82 @@ def offsets_stride(fmt: int, R: int, C: int) -> int:
     return 16 * ((R * C + G - 1) // G)
 
 
-def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> CompressedStack:
-    lib = _lib()
-    if x.dtype != torch.uint8 or x.dim() != 3 or not x.is_contiguous():
-        raise ValueError("dense must be a contiguous uint8 [E, R, C] tensor")
-    E, R, C = (int(v) for v in x.shape)
-    dev = x.device
-    S = offsets_stride(fmt, R, C)
-    NT = (R * C + INDEX_TILE - 1) // INDEX_TILE
-    bases = torch.empty(E * R, dtype=torch.uint8, device=dev)
-    offsets = torch.empty(E * S, dtype=torch.uint8, device=dev)
-    prefix = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    tidx = torch.empty(E * NT + 1, dtype=torch.int32, device=dev)
-    cur = torch.cuda.current_stream(dev)
-    side = stream is not None and _stream_handle(stream, dev) != cur.cuda_stream
-    if side:
-        # the outputs were allocated on the current stream, whose queued work
-        # may still use their memory (freed there just before): `stream`
-        # writes them only after that work
-        stream.wait_stream(cur)
-    h = _stream_handle(stream, dev)
-    _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), offsets.data_ptr(), None,
-                                 prefix.data_ptr(), tidx.data_ptr(), ENCODE_STREAMS, h),
-           "csf_encode_device(streams)")
+class _DeviceEncode:
+    """One stack's GPU encode between its two phases."""
+
+    def __init__(self, x: torch.Tensor, fmt: int, index: bool, stream):
+        lib = _lib()
+        if x.dtype != torch.uint8 or x.dim() != 3 or not x.is_contiguous():
+            raise ValueError("dense must be a contiguous uint8 [E, R, C] tensor")
+        E, R, C = (int(v) for v in x.shape)
+        dev = x.device
+        S = offsets_stride(fmt, R, C)
+        NT = (R * C + INDEX_TILE - 1) // INDEX_TILE
+        self.x, self.fmt, self.index, self.stream = x, fmt, index, stream
+        self.E, self.R, self.C, self.S = E, R, C, S
+        self.bases = torch.empty(E * R, dtype=torch.uint8, device=dev)
+        self.offsets = torch.empty(E * S, dtype=torch.uint8, device=dev)
+        self.prefix = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.tidx = torch.empty(E * NT + 1, dtype=torch.int32, device=dev)
+        cur = torch.cuda.current_stream(dev)
+        self.side = stream is not None and _stream_handle(stream, dev) != cur.cuda_stream
+        if self.side:
+            # the outputs were allocated on the current stream, whose queued work
+            # may still use their memory (freed there just before): `stream`
+            # writes them only after that work
+            stream.wait_stream(cur)
+        self.h = _stream_handle(stream, dev)
+        _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), self.bases.data_ptr(), self.offsets.data_ptr(),
+                                     None, self.prefix.data_ptr(), self.tidx.data_ptr(), ENCODE_STREAMS, self.h),
+               "csf_encode_device(streams)")
+
+    def finish(self, n: int) -> CompressedStack:
+        """The entries phase, once the entry count n (exc_prefix[E]) is known."""
+        lib = _lib()
+        exc = torch.empty(max(n, 1), dtype=torch.int32, device=self.x.device)
+        if n > 0:
+            _check(lib.csf_encode_device(self.fmt, self.E, self.R, self.C, self.x.data_ptr(), self.bases.data_ptr(),
+                                         None, exc.data_ptr(), None, self.tidx.data_ptr(), ENCODE_ENTRIES, self.h),
+                   "csf_encode_device(entries)")
+        if self.side:
+            # allocated on the current stream, written on `stream`: keep the memory
+            # from being reused before `stream` is done with it
+            for t in (self.bases, self.offsets, self.prefix, self.tidx, exc, self.x):
+                t.record_stream(self.stream)
+        return CompressedStack(self.fmt, self.E, self.R, self.C, self.S, n, self.bases, self.offsets, exc,
+                               self.prefix, self.tidx if self.index else None)
+
+
+def _prepare_devices(xs, fmts, index: bool, stream=None) -> list:
+    """The streams phase of every stack, one read-back of all their entry
+    counts, then every entries phase."""
+    encs = [_DeviceEncode(x, f, index, stream) for x, f in zip(xs, fmts)]
     if stream is not None:
         stream.synchronize()
-    n = int(prefix[E].item())  # the one read-back: sizes the entry buffer
-    exc = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
-    if n > 0:
-        _check(lib.csf_encode_device(fmt, E, R, C, x.data_ptr(), bases.data_ptr(), None, exc.data_ptr(),
-                                     None, tidx.data_ptr(), ENCODE_ENTRIES, h), "csf_encode_device(entries)")
-    if side:
-        # allocated on the current stream, written on `stream`: keep the memory
-        # from being reused before `stream` is done with it
-        for t in (bases, offsets, prefix, tidx, exc, x):
-            t.record_stream(stream)
-    return CompressedStack(fmt, E, R, C, S, n, bases, offsets, exc, prefix, tidx if index else None)
+    if len(encs) == 1:
+        counts = [encs[0].prefix[encs[0].E].item()]
+    else:
+        counts = torch.stack([e.prefix[e.E] for e in encs]).tolist()
+    return [e.finish(int(n)) for e, n in zip(encs, counts)]
+
+
+def _prepare_device(x: torch.Tensor, fmt: int, index: bool, stream=None) -> CompressedStack:
+    return _prepare_devices([x], [fmt], index, stream)[0]
+
+
+def prepare_many(denses, fmts, index: bool = True, stream=None) -> list:
+    """``prepare`` of several stacks (for example a layer's gate/up and down
+    projections).  Stacks on one GPU are encoded with a single read-back of
+    their entry counts: every stack's first phase is enqueued, the counts are
+    read together, then every stack's entries phase (same streams, result and
+    stream rules as ``prepare``).  ``fmts`` is one format per stack."""
+    denses, fmts = list(denses), list(fmts)
+    if len(denses) != len(fmts):
+        raise ValueError("one format per stack")
+    on_gpu = [isinstance(d, torch.Tensor) and d.device.type == "cuda" for d in denses]
+    if denses and all(on_gpu) and len({d.device for d in denses}) == 1:
+        return _prepare_devices(denses, fmts, index, stream)
+    return [prepare(d, f, index, stream) for d, f in zip(denses, fmts)]
 
 
 def prepare(dense, fmt: int, index: bool = True, stream=None) -> CompressedStack:

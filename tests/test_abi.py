@@ -387,3 +387,17 @@ def test_traced_decode_host_checks(lib):
     c = _fake(E=512, R=800, C=128, stride=51200)
     st = lib.csf_decode_traced(ctypes.byref(c), 0x5000, None, None, 0x7000, None, 0, ctypes.byref(groups), None)
     assert mwd.STATUS[st] == "CSF_E_NULL"
+
+
+def test_prepare_many_on_host_arrays_equals_prepare():
+    """Host arrays take the host encoder, stack by stack."""
+    xs = [workloads.nvfp4_stack(2, 8, 20, 5, 0.1), workloads.mxfp4_stack(1, 4, 64, 6, 0.2)]
+    fmts = [workloads.NVFP4, workloads.MXFP4]
+    got = mwd.prepare_many(xs, fmts)
+    for x, f, g in zip(xs, fmts, got):
+        want = mwd.prepare(x, f).numpy()
+        have = g.numpy()
+        for k in ("bases", "offsets", "exceptions", "prefix", "tile_index"):
+            assert np.array_equal(np.asarray(have[k]).ravel(), np.asarray(want[k]).ravel()), k
+    with pytest.raises(ValueError):
+        mwd.prepare_many(xs, fmts[:1])

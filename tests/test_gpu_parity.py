@@ -569,6 +569,25 @@ def test_gpu_encoder_unaligned_dense(orc, dev, shift):
         _same_streams(got.numpy(), orc.encode(fmt, x), f"shift {shift} {fmt} {E}x{R}x{C}")
 
 
+def test_gpu_prepare_many_equals_one_by_one(orc, dev):
+    """Several stacks (both formats, one without exceptions, one with rows
+    wider than 255) encoded with one read-back of their entry counts, on the
+    current and on a side stream."""
+    xs = [(workloads.nvfp4_stack(3, 40, 50, 21, 0.1), workloads.NVFP4),
+          (workloads.mxfp4_stack(2, 33, 160, 22, 0.15), workloads.MXFP4),
+          (workloads.nvfp4_stack(2, 16, 128, 23, 0.0), workloads.NVFP4),
+          (workloads.uniform_bytes(2, 3, 300, 24), workloads.NVFP4)]
+    side = torch.cuda.Stream(device=dev)
+    for stream in (None, side):
+        got = mwd.prepare_many([torch.from_numpy(x).to(dev) for x, _ in xs], [f for _, f in xs], stream=stream)
+        if stream is not None:
+            torch.cuda.current_stream(dev).wait_stream(stream)
+        torch.cuda.synchronize()
+        assert got[2].num_exceptions == 0
+        for (x, f), g in zip(xs, got):
+            _same_streams(g.numpy(), orc.encode(f, x), f"prepare_many {f} {x.shape}")
+
+
 def test_gpu_encoder_two_column_exhaustive(orc, dev):
     a, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
     x = np.stack([a.ravel(), b.ravel()], axis=1).astype(np.uint8).reshape(4, 16384, 2)
