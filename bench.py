@@ -142,6 +142,7 @@ def stack_bytes(stack, active=None) -> StackBytes:
 
 _KERNEL_SOURCES = {
     "csf_fused_kernel": ("csf_kernels.hip",),
+    "csf_routed_kernel": ("csf_kernels.hip",),
     "csf_moe_w4a16_kernel": ("csf_moe.hip",),
 }
 
@@ -959,7 +960,8 @@ def main():
     achieved = step_bytes / (r["event_ms"] * 1e-3) / 1e9
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
-    kernel = "csf_moe_w4a16_kernel" if moe else "csf_fused_kernel"
+    kernel = ("csf_moe_w4a16_kernel" if moe else
+              "csf_routed_kernel" if args.workload == "routed_paired" else "csf_fused_kernel")
     traffic = pmc_traffic(kernel, args.workload)
     roof = {
         "kernel": kernel,

@@ -476,12 +476,24 @@ struct RoutedUnit {
     uint32_t s, e, t;  // this workgroup's unit (when blockIdx.x < total <= gridDim.x)
 };
 
+// The routing's inputs, passed to the routed kernel as leading scalar
+// arguments: the hardware loads those into scalar registers when it launches
+// a wave (kernel-argument preloading), so the routing read is issued without
+// first waiting for a load of the argument block.
+struct RouteHead {
+    const void *expert_start;
+    uint32_t E;
+    uint32_t flags;            // kHeadWide: int64 expert_start; kHeadPair: two stacks
+    uint32_t tiles[2], first[2];  // per stack: tiles decoded per plane, first tile
+};
+constexpr uint32_t kHeadWide = 1, kHeadPair = 2;
+
 template <typename T>
-__device__ __forceinline__ RoutedUnit route_unit(const DecodeArgs &a, const T *es) {
+__device__ __forceinline__ RoutedUnit route_unit(const RouteHead &h, const T *es) {
     constexpr uint32_t V = 16 / sizeof(T);                 // experts per lane per chunk
     constexpr uint32_t CH = kFastExperts / (kWave * V);    // chunks at most
     typedef T tv __attribute__((ext_vector_type(V)));
-    const uint32_t E = a.E, lane = threadIdx.x % kWave;
+    const uint32_t E = h.E, lane = threadIdx.x % kWave;
     // Loads are issued unconditionally, at addresses clamped into the tensor,
     // so none waits for another; lanes and chunks past E are masked below.
     // Whole 16-byte loads when they cannot run past the tensor.
@@ -523,16 +535,16 @@ __device__ __forceinline__ RoutedUnit route_unit(const DecodeArgs &a, const T *e
         }
     }
     RoutedUnit r;
-    const uint32_t u0 = nact * a.st[0].tiles;
-    r.total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
+    const uint32_t u0 = nact * h.tiles[0];
+    r.total = u0 + ((h.flags & kHeadPair) ? nact * h.tiles[1] : 0u);
     r.s = r.e = r.t = 0;
     const uint32_t u = blockIdx.x;
     if (u >= r.total || r.total > gridDim.x) return r;
     r.s = u >= u0 ? 1u : 0u;
-    const uint32_t tiles = r.s ? a.st[1].tiles : a.st[0].tiles;
+    const uint32_t tiles = h.tiles[r.s];
     const uint32_t uu = u - (r.s ? u0 : 0u);
     uint32_t k = uu / tiles;
-    r.t = (r.s ? a.st[1].tile0 : a.st[0].tile0) + uu - k * tiles;
+    r.t = h.first[r.s] + uu - k * tiles;
     // The k-th active expert: its chunk, then its lane (the lane whose bits
     // below it in the chunk count at most k), then its bit.
     uint32_t e = 0;
@@ -613,7 +625,8 @@ __device__ __forceinline__ u32x4 expand_run(u32x4 v, uint32_t pos, uint32_t r0, 
 }
 
 template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP>
-__device__ __forceinline__ void routed_decode(const DecodeArgs &a, uint8_t *dyn, uint8_t *tile) {
+__device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeArgs &a, uint8_t *dyn,
+                                              uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
     static_assert(EXC % 4 == 0, "entries are read in 16-byte loads");
@@ -622,10 +635,10 @@ __device__ __forceinline__ void routed_decode(const DecodeArgs &a, uint8_t *dyn,
     uint8_t *lds_bases = dyn;
 
     // (route_unit reads only inside the tensor, so it runs before the expert
-    // count is checked and its loads go out with the argument loads.)
-    const RoutedUnit ru = a.es_wide ? route_unit(a, static_cast<const int64_t *>(a.expert_start))
-                                    : route_unit(a, static_cast<const int32_t *>(a.expert_start));
-    const bool fast = a.E <= kFastExperts;
+    // count is checked; its loads need only the preloaded leading arguments.)
+    const RoutedUnit ru = (h.flags & kHeadWide) ? route_unit(h, static_cast<const int64_t *>(h.expert_start))
+                                                : route_unit(h, static_cast<const int32_t *>(h.expert_start));
+    const bool fast = h.E <= kFastExperts;
     clk.mark(1);
     if (!fast || ru.total > gridDim.x) {
         uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
@@ -745,17 +758,26 @@ __device__ __forceinline__ void routed_decode(const DecodeArgs &a, uint8_t *dyn,
 }
 
 // WINDOW: some stack's row window does not cover its whole plane (csf_decode_rows).
-// STAMP: a traced routed decode (timestamps per workgroup).
-template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED, bool WINDOW, bool STAMP = false>
+template <uint32_t RUNS, uint32_t EXC, uint32_t SCHED, bool WINDOW>
 __global__ __launch_bounds__(kBlock, SCHED == kPipelined ? 6 : 1) void csf_fused_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
     if constexpr (SCHED == kStreamEntries)
         tile_loop_serial<true, RUNS, EXC, false, true, WINDOW>(a, dyn_lds, tile);
-    else if constexpr (SCHED == kRouted)
-        routed_decode<RUNS, EXC, WINDOW, STAMP>(a, dyn_lds, tile);
     else
         tile_loop_pipelined<RUNS, EXC, 0, WINDOW>(a, dyn_lds, tile, a.E, reinterpret_cast<const uint16_t *>(dyn_lds), a.expert_start != nullptr);
+}
+
+// The routed schedule (kRouted), its routing inputs ahead of the argument
+// block (RouteHead).  STAMP: a traced routed decode (timestamps per workgroup).
+template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP = false>
+__global__ __launch_bounds__(kBlock, 1) void csf_routed_kernel(const void *expert_start, uint32_t E, uint32_t flags,
+                                                               uint32_t tiles0, uint32_t tiles1, uint32_t first0,
+                                                               uint32_t first1, DecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t dyn_lds[];
+    __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
+    const RouteHead h = {expert_start, E, flags, {tiles0, tiles1}, {first0, first1}};
+    routed_decode<RUNS, EXC, WINDOW, STAMP>(h, a, dyn_lds, tile);
 }
 
 template <uint32_t RUNS, bool WINDOW>
@@ -926,13 +948,18 @@ hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) 
     return a.windowed ? launch_fixed_t<true>(a, grid, stream) : launch_fixed_t<false>(a, grid, stream);
 }
 
+static uint32_t head_flags(const DecodeArgs &a) {
+    return (a.es_wide ? kHeadWide : 0u) | (a.nstacks > 1 ? kHeadPair : 0u);
+}
+
 template <bool WINDOW>
 hipError_t launch_fused_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream) {
     const size_t lds = tile_lds_bytes(a);
     const dim3 g(grid), b(kBlock);
     // (runs, entries per lane, load schedule) combinations the host plans
     if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedRouted)
-        hipLaunchKernelGGL((csf_fused_kernel<1, 4, kRouted, WINDOW>), g, b, lds, stream, a);
+        hipLaunchKernelGGL((csf_routed_kernel<1, 4, WINDOW>), g, b, lds, stream, a.expert_start, a.E, head_flags(a),
+                           a.st[0].tiles, a.st[1].tiles, a.st[0].tile0, a.st[1].tile0, a);
     else if (a.runs == 2 && a.exc_regs == 4 && a.sched == kSchedStreamEntries)
         hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 8 && a.sched == kSchedStreamEntries)
@@ -953,7 +980,8 @@ hipError_t launch_fused_traced(const DecodeArgs &a, uint32_t grid, hipStream_t s
     const dim3 g(grid), b(kBlock);
     if (a.windowed || a.stamps == nullptr || a.sched != kSchedRouted || a.runs != 1) return hipErrorInvalidValue;
     if (a.exc_regs != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((csf_fused_kernel<1, 4, kRouted, false, true>), g, b, lds, stream, a);
+    hipLaunchKernelGGL((csf_routed_kernel<1, 4, false, true>), g, b, lds, stream, a.expert_start, a.E, head_flags(a),
+                       a.st[0].tiles, a.st[1].tiles, a.st[0].tile0, a.st[1].tile0, a);
     return hipGetLastError();
 }
 

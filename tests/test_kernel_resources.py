@@ -15,15 +15,16 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "moe_weight_decode_amd", "csrc")
 
-# fused kernel instantiation (runs, entries per lane, load schedule) -> waves per SIMD the plan needs
+# fused kernel instantiation (runs, entries per lane, load schedule; the routed kernel is schedule 2)
+# -> waves per SIMD the plan needs
 PLAN_WAVES = {("2", "4", "1"): 7, ("2", "8", "1"): 7, ("4", "4", "0"): 6, ("1", "4", "2"): 2}
 
 
 def _kernel_resources(source):
     from moe_weight_decode_amd import build as b
     with tempfile.TemporaryDirectory() as d:
-        cmd = [b.hipcc(), f"--offload-arch={b.ARCH}", "-O3", "-std=c++17", "-fPIC",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        flags = [f for f in b.HIPCC_FLAGS if f not in ("-shared", "-Wall", "-Werror")]
+        cmd = [b.hipcc(), *flags,
                "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--save-temps", "-c", source,
                "-o", os.path.join(d, "k.o")]
         subprocess.run(cmd, cwd=d, check=True, capture_output=True)
@@ -45,8 +46,9 @@ def test_no_scratch_and_plan_occupancy(source):
     for name, (vgpr, scratch) in res.items():
         assert scratch == 0, f"{name} uses {scratch} bytes of scratch"
         m = re.search(r"csf_fused_kernelILj(\d+)ELj(\d+)ELj(\d)E", name)
-        if m:
-            waves = PLAN_WAVES[m.groups()]
+        r = re.search(r"csf_routed_kernelILj(\d+)ELj(\d+)E", name)
+        if m or r:
+            waves = PLAN_WAVES[m.groups() if m else r.groups() + ("2",)]
             granted = 512 // (((vgpr + 7) // 8) * 8)
             assert granted >= waves, f"{name}: {vgpr} VGPRs allow {granted} waves per SIMD, plan needs {waves}"
         if "csf_moe_w4a16_kernel" in name:  # one 8-wave workgroup per CU: 2 waves per SIMD
