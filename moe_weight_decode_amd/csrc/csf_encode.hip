@@ -305,11 +305,13 @@ constexpr uint32_t kPairWavesPerCu = 18;  // one-wave workgroups per CU: 18 x 8,
 
 
 // Fold the window counts cnt of candidates 4s .. 4s + 3 (s relative to the
-// lane's half) into best: two u16 keys per word, count << 8 | 255 - v.
+// lane's half) into best: two u16 keys per word, count << 8 | 255 - v.  The
+// keys interleave cnt's bytes with those of k = (255 - v, 254 - v, 253 - v,
+// 252 - v) for v = 4s, one byte permute each.
 __device__ __forceinline__ uint32_t fold_keys(uint32_t best, uint32_t cnt, uint32_t s) {
-    const uint32_t v = 4u * s;
-    const uint32_t lo = ((cnt << 8) & 0xff00ff00u) | ((255u - v - 2u) << 16) | (255u - v);  // v, v + 2
-    const uint32_t hi = (cnt & 0xff00ff00u) | ((255u - v - 3u) << 16) | (255u - v - 1u);    // v + 1, v + 3
+    const uint32_t k = 0xfcfdfeffu - 0x04040404u * s;
+    const uint32_t lo = __builtin_amdgcn_perm(cnt, k, 0x06020400u);  // v, v + 2
+    const uint32_t hi = __builtin_amdgcn_perm(cnt, k, 0x07030501u);  // v + 1, v + 3
     return max_u16x2(best, max_u16x2(lo, hi));
 }
 

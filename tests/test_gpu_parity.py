@@ -685,6 +685,30 @@ def test_routed_int64_expert_start(orc, dev, mode):
     assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), want, "int64 single")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_routed_expert_start_not_16_byte_aligned(orc, dev, mode):
+    """expert_start tensors that start 4 or 12 (int32) or 8 (int64) bytes past
+    a 16-byte boundary are read value by value instead of 16 bytes at a time:
+    the same planes as from the aligned tensor."""
+    es32 = workloads.ROUTED.expert_start()
+    _, xg, sg = stack_case("gate_nvfp4", orc)
+    _, xd, sd = stack_case("down_nvfp4", orc)
+    g, d = upload(sg, dev, mode), upload(sd, dev, mode)
+    want_g, want_d = oracle_expect(orc, sg, es32), oracle_expect(orc, sd, es32)
+    for dtype, shift in ((torch.int32, 1), (torch.int32, 3), (torch.int64, 1)):
+        print(f"[parity] routed pair, {dtype} expert_start {shift} elements past an aligned start", flush=True)
+        buf = torch.zeros(len(es32) + 4, dtype=dtype, device=dev)
+        es_t = buf[shift: shift + len(es32)]
+        es_t.copy_(torch.from_numpy(es32).to(dev))
+        assert es_t.data_ptr() % 16 != 0
+        wg = torch.full((g.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+        wd = torch.full((d.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+        mwd.decode_paired(g, wg, d, wd, es_t)
+        torch.cuda.synchronize()
+        assert_bytes_equal(wg.cpu().numpy().reshape(xg.shape), want_g, f"gate, {dtype} shift {shift}")
+        assert_bytes_equal(wd.cpu().numpy().reshape(xd.shape), want_d, f"down, {dtype} shift {shift}")
+
+
 # -- row windows (decode only the rows a consumer reads) -----------------------
 
 def run_decode_rows(stack, dev, rows, es=None, offset=0, second=None, rows_second=None):
