@@ -10,12 +10,14 @@
 // ahead-of-call scale expansion (canonical twin of #477)", b12x PR 478, commit
 // messages).
 //
-// Three kernels:
+// Four kernels:
 //   csf_fused_kernel  both parts in one pass: a tile is expanded into LDS, the
 //                     tile's exception entries (found through the per-tile
 //                     exception index) are patched into LDS, then the tile is
 //                     written with full-line stores.  Every dense byte is
 //                     written once.
+//   csf_routed_kernel the same pass for routed calls, one tile per workgroup,
+//                     its routing inputs passed ahead of the argument block.
 //   csf_fixed_kernel  the fixed stream alone, stored straight from registers.
 //   csf_exc_kernel    the exception pass alone, indexed by a wave-level prefix
 //                     over per-expert entry counts (needs no tile index).
