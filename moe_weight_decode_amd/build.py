@@ -27,7 +27,7 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # load a kernel's leading scalar arguments (up to 8 dwords) into scalar
+    # load a kernel's leading scalar arguments (up to 8 arguments) into scalar
     # registers at wave launch (the routed decode's routing inputs)
     "-mllvm", "-amdgpu-kernarg-preload-count=8",
 ]

@@ -305,9 +305,10 @@ __device__ __forceinline__ void store_tile(const StackArgs &st, uint8_t *plane, 
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int32x4_t, out), rw, (int)(off - h), 0,
                                                kNonTemporal);
     }
-    if (WINDOW || !aligned)
+    if (WINDOW || !aligned) [[unlikely]]
         for (uint32_t b = s0 + threadIdx.x; b < h; b += kBlock) dst[b] = tile[b];
-    for (uint32_t b = wend + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
+    if (wend < n) [[unlikely]]
+        for (uint32_t b = wend + threadIdx.x; b < n; b += kBlock) dst[b] = tile[b];
 }
 
 // Row bases of a tile's rows into LDS: the first 2 * kBlock from the loaded
@@ -485,10 +486,11 @@ struct RoutedUnit {
 struct RouteHead {
     const void *expert_start;
     uint32_t E;
-    uint32_t flags;            // kHeadWide: int64 expert_start; kHeadPair: two stacks
+    uint32_t flags;            // kHeadPair: two stacks
     uint32_t tiles[2], first[2];  // per stack: tiles decoded per plane, first tile
+    uint32_t grid;             // workgroups of the launch
 };
-constexpr uint32_t kHeadWide = 1, kHeadPair = 2;
+constexpr uint32_t kHeadPair = 2;
 
 template <typename T>
 __device__ __forceinline__ RoutedUnit route_unit(const RouteHead &h, const T *es) {
@@ -501,7 +503,7 @@ __device__ __forceinline__ RoutedUnit route_unit(const RouteHead &h, const T *es
     // Whole 16-byte loads when they cannot run past the tensor.
     const bool vec = (reinterpret_cast<uintptr_t>(es) & 15u) == 0 && E % V == 0;
     T x[CH][V], nxt[CH];
-    if (vec) {
+    if (vec) [[likely]] {
 #pragma unroll
         for (uint32_t i = 0; i < CH; ++i) {
             const uint32_t b = kWave * V * i + V * lane;  // first expert of this lane
@@ -510,7 +512,7 @@ __device__ __forceinline__ RoutedUnit route_unit(const RouteHead &h, const T *es
             for (uint32_t c = 0; c < V; ++c) x[i][c] = q[c];
             nxt[i] = es[min(b + V, E)];
         }
-    } else {
+    } else [[unlikely]] {
 #pragma unroll
         for (uint32_t i = 0; i < CH; ++i) {
             const uint32_t b = kWave * V * i + V * lane;
@@ -541,7 +543,7 @@ __device__ __forceinline__ RoutedUnit route_unit(const RouteHead &h, const T *es
     r.total = u0 + ((h.flags & kHeadPair) ? nact * h.tiles[1] : 0u);
     r.s = r.e = r.t = 0;
     const uint32_t u = blockIdx.x;
-    if (u >= r.total || r.total > gridDim.x) return r;
+    if (u >= r.total || r.total > h.grid) return r;
     r.s = u >= u0 ? 1u : 0u;
     const uint32_t tiles = h.tiles[r.s];
     const uint32_t uu = u - (r.s ? u0 : 0u);
@@ -604,29 +606,29 @@ struct Clock {
 };
 
 // One lane's run of a routed tile, widened and based from the row bases s0
-// (row r0 = pos / C) and s1 (row r0 + 1), both splat over four bytes.
-template <int WB, int MODE>
+// (row r0 = pos / C) and s1 (row r0 + 1), both splat over four bytes; w
+// offset bits per field (4 or 1).  One code path for both formats and row
+// kinds (a run of a stack whose C is a multiple of 16 never crosses a row,
+// so the blend below never applies there): the routed kernel keeps its code
+// short, since most of its workgroups run it once on a cold instruction cache.
 __device__ __forceinline__ u32x4 expand_run(u32x4 v, uint32_t pos, uint32_t r0, uint32_t C, uint32_t s0,
-                                            uint32_t s1) {
-    constexpr uint32_t MASK = WB == 4 ? 0x0f0f0f0fu : 0x01010101u;
-    constexpr uint32_t FMASK = 8 / WB - 1;
-    const uint32_t f = (pos >> 4) & FMASK;
-    const u32x4 field = (v >> (uint32_t)(WB * f)) & MASK;
+                                            uint32_t s1, uint32_t w) {
+    const uint32_t mask = w == 4 ? 0x0f0f0f0fu : 0x01010101u;
+    const uint32_t f = (pos >> 4) & (w == 4 ? 1u : 7u);  // field of the run within its group
+    const u32x4 field = (v >> (w * f)) & mask;
     u32x4 b = {s0, s0, s0, s0};
-    if constexpr (MODE == kRowTwo) {
-        const int left = (int)((r0 + 1) * C - pos);
-        if (left < 16) {
-            uint32_t m;
-            m = low_bytes_mask(left);      b.x = (s0 & m) | (s1 & ~m);
-            m = low_bytes_mask(left - 4);  b.y = (s0 & m) | (s1 & ~m);
-            m = low_bytes_mask(left - 8);  b.z = (s0 & m) | (s1 & ~m);
-            m = low_bytes_mask(left - 12); b.w = (s0 & m) | (s1 & ~m);
-        }
+    const int left = (int)((r0 + 1) * C - pos);
+    if (left < 16) {
+        uint32_t m;
+        m = low_bytes_mask(left);      b.x = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 4);  b.y = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 8);  b.z = (s0 & m) | (s1 & ~m);
+        m = low_bytes_mask(left - 12); b.w = (s0 & m) | (s1 & ~m);
     }
     return add_bytes4(field, b);
 }
 
-template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP>
+template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP, bool WIDE>
 __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeArgs &a, uint8_t *dyn,
                                               uint8_t *tile) {
     constexpr uint32_t TILE = tile_positions(RUNS);
@@ -638,11 +640,10 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
 
     // (route_unit reads only inside the tensor, so it runs before the expert
     // count is checked; its loads need only the preloaded leading arguments.)
-    const RoutedUnit ru = (h.flags & kHeadWide) ? route_unit(h, static_cast<const int64_t *>(h.expert_start))
-                                                : route_unit(h, static_cast<const int32_t *>(h.expert_start));
+    const RoutedUnit ru = route_unit(h, static_cast<const std::conditional_t<WIDE, int64_t, int32_t> *>(h.expert_start));
     const bool fast = h.E <= kFastExperts;
     clk.mark(1);
-    if (!fast || ru.total > gridDim.x) {
+    if (!fast || ru.total > h.grid) [[unlikely]] {
         uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
         uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
         const uint32_t nact = active_experts(a, act, flags);
@@ -674,7 +675,7 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
     // Row bases: for C >= 16 the two rows each run may touch, into registers;
     // for C < 16 the tile's rows, to be staged in LDS.
     const rsrc_t rb = make_rsrc(st.bases + (uint64_t)e * st.R, st.R);
-    const bool direct = st.row_mode != kRowBytes;
+    const bool direct = __builtin_amdgcn_readfirstlane(st.row_mode) != kRowBytes;  // the same in every lane
     const uint32_t r_lo = div_exact(q0, st.rcp_cols);
     uint32_t rrow[RUNS], bb0[RUNS], bb1[RUNS];
 #pragma unroll
@@ -685,6 +686,9 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
         bb1[i] = direct ? __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(rrow[i] + 1u), 0, 0)
                         : __builtin_amdgcn_raw_buffer_load_b8(rb, (int)(rrow[i] + RUNS * kBlock), 0, 0);
     }
+    // (the offset and base loads above are issued before the wait for the
+    // index bounds below)
+    __builtin_amdgcn_sched_barrier(0);
     // The tile's index bounds, then its first EXC * kBlock entries in 16-byte
     // loads from `first` (lo rounded down to a multiple of 4).
     const int32_t *ti = st.tile_index + (uint64_t)e * st.index_tiles + t * INDEX_PER_TILE;
@@ -707,23 +711,30 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
     clk.mark_drained(2);
 
     uint8_t *plane = st.ws + (uint64_t)e * st.P;
-    if (direct) {
+    // The prefetched entries, then any beyond them; the tile's stores.
+    auto patch_and_store = [&]() {
 #pragma unroll
-        for (uint32_t i = 0; i < RUNS; ++i) {
-            const uint32_t j = i * kBlock + threadIdx.x;
-            const uint32_t pos = q0 + kRunBytes * j;
-            if (pos >= q1) break;
-            const uint32_t s0 = bb0[i] * 0x01010101u, s1 = bb1[i] * 0x01010101u;
-            u32x4 out;
-            switch ((st.wbits == 4 ? 0u : 2u) + (st.row_mode == kRowSplat ? 0u : 1u)) {
-                case 0: out = expand_run<4, kRowSplat>(v[i], pos, rrow[i], st.C, s0, s1); break;
-                case 1: out = expand_run<4, kRowTwo>(v[i], pos, rrow[i], st.C, s0, s1); break;
-                case 2: out = expand_run<1, kRowSplat>(v[i], pos, rrow[i], st.C, s0, s1); break;
-                default: out = expand_run<1, kRowTwo>(v[i], pos, rrow[i], st.C, s0, s1); break;
-            }
-            *reinterpret_cast<u32x4 *>(tile + kRunBytes * j) = out;
+        for (uint32_t i = 0; i < EXC; ++i) {
+            const uint32_t kk = entry_of(first, i);
+            const uint32_t pos = w[i] >> 8;
+            if (kk >= lo && kk < hi && pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(w[i] & 0xffu);
         }
-    } else {
+        if (first + EXC * kBlock < hi) [[unlikely]] {
+            for (uint32_t kk = first + EXC * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
+                const uint32_t x = st.exc[kk];
+                const uint32_t pos = x >> 8;
+                if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
+            }
+        }
+        __syncthreads();  // tile patched
+        clk.mark(4);
+        store_tile<RUNS, WINDOW>(st, plane, q0, q1, tile);
+        clk.mark(5);
+        clk.mark_drained(6);
+        clk.write(a, 1ull + u + ((uint64_t)(hi - first > EXC * kBlock) << 32));
+    };
+    if (!direct) [[unlikely]] {
+        // rows of fewer than 16 columns: the tile's row bases staged in LDS
         const uint32_t nrows = div_exact(q1 - 1u, st.rcp_cols) - r_lo + 1u;
 #pragma unroll
         for (uint32_t i = 0; i < RUNS; ++i) {
@@ -735,28 +746,22 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
         for (uint32_t r = threadIdx.x + 2u * RUNS * kBlock; r < nrows; r += kBlock) lds_bases[r] = brow[r];
         __syncthreads();
         expand_dispatch<true, RUNS, false>(st, v, q0, q1, q0, lds_bases, r_lo, tile, plane);
+        __syncthreads();  // tile expanded
+        clk.mark(3);
+        patch_and_store();
+        return;
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < RUNS; ++i) {
+        const uint32_t j = i * kBlock + threadIdx.x;
+        const uint32_t pos = q0 + kRunBytes * j;
+        if (pos >= q1) break;
+        const uint32_t s0 = bb0[i] * 0x01010101u, s1 = bb1[i] * 0x01010101u;
+        *reinterpret_cast<u32x4 *>(tile + kRunBytes * j) = expand_run(v[i], pos, rrow[i], st.C, s0, s1, st.wbits);
     }
     __syncthreads();  // tile expanded
     clk.mark(3);
-
-    // The prefetched entries, then any beyond them.
-#pragma unroll
-    for (uint32_t i = 0; i < EXC; ++i) {
-        const uint32_t kk = entry_of(first, i);
-        const uint32_t pos = w[i] >> 8;
-        if (kk >= lo && kk < hi && pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(w[i] & 0xffu);
-    }
-    for (uint32_t kk = first + EXC * kBlock + threadIdx.x; kk < hi; kk += kBlock) {
-        const uint32_t x = st.exc[kk];
-        const uint32_t pos = x >> 8;
-        if (pos >= q0 && pos < q1) tile[pos - q0] = (uint8_t)(x & 0xffu);
-    }
-    __syncthreads();  // tile patched
-    clk.mark(4);
-    store_tile<RUNS, WINDOW>(st, plane, q0, q1, tile);
-    clk.mark(5);
-    clk.mark_drained(6);
-    clk.write(a, 1ull + u + ((uint64_t)(hi - first > EXC * kBlock) << 32));
+    patch_and_store();
 }
 
 // WINDOW: some stack's row window does not cover its whole plane (csf_decode_rows).
@@ -771,15 +776,16 @@ __global__ __launch_bounds__(kBlock, SCHED == kPipelined ? 6 : 1) void csf_fused
 }
 
 // The routed schedule (kRouted), its routing inputs ahead of the argument
-// block (RouteHead).  STAMP: a traced routed decode (timestamps per workgroup).
-template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP = false>
+// block (RouteHead).  STAMP: a traced routed decode (timestamps per workgroup);
+// WIDE: int64 expert_start.
+template <uint32_t RUNS, uint32_t EXC, bool WINDOW, bool STAMP, bool WIDE>
 __global__ __launch_bounds__(kBlock, 1) void csf_routed_kernel(const void *expert_start, uint32_t E, uint32_t flags,
                                                                uint32_t tiles0, uint32_t tiles1, uint32_t first0,
-                                                               uint32_t first1, DecodeArgs a) {
+                                                               uint32_t first1, uint32_t grid, DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ __align__(16) uint8_t tile[tile_positions(RUNS)];
-    const RouteHead h = {expert_start, E, flags, {tiles0, tiles1}, {first0, first1}};
-    routed_decode<RUNS, EXC, WINDOW, STAMP>(h, a, dyn_lds, tile);
+    const RouteHead h = {expert_start, E, flags, {tiles0, tiles1}, {first0, first1}, grid};
+    routed_decode<RUNS, EXC, WINDOW, STAMP, WIDE>(h, a, dyn_lds, tile);
 }
 
 template <uint32_t RUNS, bool WINDOW>
@@ -951,7 +957,7 @@ hipError_t launch_fixed(const DecodeArgs &a, uint32_t grid, hipStream_t stream) 
 }
 
 static uint32_t head_flags(const DecodeArgs &a) {
-    return (a.es_wide ? kHeadWide : 0u) | (a.nstacks > 1 ? kHeadPair : 0u);
+    return a.nstacks > 1 ? kHeadPair : 0u;
 }
 
 template <bool WINDOW>
@@ -960,8 +966,10 @@ hipError_t launch_fused_t(const DecodeArgs &a, uint32_t grid, hipStream_t stream
     const dim3 g(grid), b(kBlock);
     // (runs, entries per lane, load schedule) combinations the host plans
     if (a.runs == 1 && a.exc_regs == 4 && a.sched == kSchedRouted)
-        hipLaunchKernelGGL((csf_routed_kernel<1, 4, WINDOW>), g, b, lds, stream, a.expert_start, a.E, head_flags(a),
-                           a.st[0].tiles, a.st[1].tiles, a.st[0].tile0, a.st[1].tile0, a);
+        hipLaunchKernelGGL((a.es_wide ? csf_routed_kernel<1, 4, WINDOW, false, true>
+                                      : csf_routed_kernel<1, 4, WINDOW, false, false>),
+                           g, b, lds, stream, a.expert_start, a.E, head_flags(a), a.st[0].tiles, a.st[1].tiles,
+                           a.st[0].tile0, a.st[1].tile0, grid, a);
     else if (a.runs == 2 && a.exc_regs == 4 && a.sched == kSchedStreamEntries)
         hipLaunchKernelGGL((csf_fused_kernel<2, 4, kStreamEntries, WINDOW>), g, b, lds, stream, a);
     else if (a.runs == 2 && a.exc_regs == 8 && a.sched == kSchedStreamEntries)
@@ -982,8 +990,10 @@ hipError_t launch_fused_traced(const DecodeArgs &a, uint32_t grid, hipStream_t s
     const dim3 g(grid), b(kBlock);
     if (a.windowed || a.stamps == nullptr || a.sched != kSchedRouted || a.runs != 1) return hipErrorInvalidValue;
     if (a.exc_regs != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((csf_routed_kernel<1, 4, false, true>), g, b, lds, stream, a.expert_start, a.E, head_flags(a),
-                       a.st[0].tiles, a.st[1].tiles, a.st[0].tile0, a.st[1].tile0, a);
+    hipLaunchKernelGGL((a.es_wide ? csf_routed_kernel<1, 4, false, true, true>
+                                  : csf_routed_kernel<1, 4, false, true, false>),
+                       g, b, lds, stream, a.expert_start, a.E, head_flags(a), a.st[0].tiles, a.st[1].tiles,
+                       a.st[0].tile0, a.st[1].tile0, grid, a);
     return hipGetLastError();
 }
 
