@@ -447,7 +447,13 @@ __device__ __forceinline__ void tile_loop_pipelined(const DecodeArgs &a, uint8_t
 // counts.  Its tile then costs two more round trips: the offset groups, the
 // row bases each lane's 16-byte run touches (read into registers) and the
 // tile-index bounds, then the tile's exception entries.  More units than
-// workgroups, or more experts, take the pipelined loop.
+// workgroups, or more experts, take the pipelined loop.  The routing's inputs
+// and the grid come as leading kernel arguments that the hardware preloads
+// into scalar registers, so the routing read is the first memory access.
+// Most workgroups of a routed call are the first on their CU and fetch the
+// kernel's code cold, so the common path is kept short and straight: int64
+// routing is its own instantiation, and rows of fewer than 16 columns and
+// tiles with more entries than the registers prefetch branch off it.
 // STAMP records s_memrealtime values per workgroup in a.stamps (phases in
 // csf_decode_traced's documentation).
 // ---------------------------------------------------------------------------
