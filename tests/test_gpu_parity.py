@@ -825,3 +825,104 @@ def test_short_stack_tensors_refused_before_launch(dev):
     assert bool((ws == POISON).all())
     mwd.decode(st, ws)
     assert torch.equal(ws.cpu(), torch.from_numpy(workloads.TINY.generate().reshape(-1)))
+
+
+# -- seeded random combinations -------------------------------------------------
+
+def _random_case(rng, seed):
+    E = int(rng.choice([1, 2, 3, 4, 5, 8, 31, 64, 100, 257, 511, 512, 513, 600]))
+    fmt = int(rng.integers(0, 2))
+
+    def shape():
+        C = int(rng.choice([1, 2, 3, 7, 8, 15, 16, 17, 31, 32, 33, 50, 64, 100, 128, 129, 160, 200, 255, 256, 300]))
+        return int(rng.integers(1, max(1, min(3000, 2_000_000 // (E * C))) + 1)), C
+
+    def stack(f, R, C, s):
+        k = rng.integers(0, 3)
+        if k == 0:
+            return workloads.uniform_bytes(E, R, C, s)
+        if f == workloads.NVFP4:
+            return workloads.nvfp4_stack(E, R, C, s, float(rng.uniform(0, 0.3)),
+                                         hot_row_frac=float(rng.choice([0.0, 0.02])))
+        return workloads.mxfp4_stack(E, R, C, s, float(rng.uniform(0, 0.3)))
+
+    R, C = shape()
+    return E, fmt, R, C, stack(fmt, R, C, seed), shape, stack
+
+
+@pytest.mark.parametrize("block", range(4))
+def test_random_feature_combinations(orc, dev, block):
+    """60 seeded cases per block, each drawing a stack (uniform bytes or a
+    generated distribution, either format, 1 to 600 experts, rows of 1 to 300
+    columns) and a combination of: fused or two-pass decode, routing (active
+    subsets, garbage values, int32 or int64, off a 16-byte boundary), a second
+    stack of other shape and format in the same launch, row windows, workspace
+    byte offsets, and a GPU encode of the same bytes off a 16-byte boundary.
+    Every result is compared with the oracle, workspace guard bands included."""
+    for i in range(60):
+        seed = 7000 + 60 * block + i
+        rng = np.random.default_rng(seed)
+        E, fmt, R, C, x, shape, stack = _random_case(rng, 9000 + seed)
+        st = orc.encode(fmt, x)
+        mode = str(rng.choice(MODES))
+        es = None
+        if rng.random() < 0.6:
+            if rng.random() < 0.1:
+                es = rng.integers(-5, 50, E + 1).astype(np.int32)
+            else:
+                act = np.zeros(E, bool)
+                act[rng.choice(E, int(rng.integers(0, min(E, 40) + 1)), replace=False)] = True
+                es = workloads.expert_start_from_mask(act, tokens=int(rng.integers(1, 5)))
+        paired = rng.random() < 0.4
+        window = rng.random() < 0.3
+        off = int(rng.choice([0, 0, 1, 7, 13]))
+        wide = es is not None and not window and rng.random() < 0.3
+        shift = int(rng.choice([0, 0, 1]))
+        print(f"[parity] random case {seed}: fmt {fmt} E {E} R {R} C {C} {mode} routed {es is not None} "
+              f"wide {wide} shift {shift} paired {paired} window {window} offset {off}", flush=True)
+        stacks = [(st, upload(st, dev, mode), (E, R, C))]
+        if paired:
+            f2 = int(rng.integers(0, 2))
+            R2, C2 = shape()
+            st2 = orc.encode(f2, stack(f2, R2, C2, 19000 + seed))
+            stacks.append((st2, upload(st2, dev, mode), (E, R2, C2)))
+        es_t = None
+        if es is not None:
+            dt = torch.int64 if wide else torch.int32
+            es_t = torch.zeros(E + 5, dtype=dt, device=dev)[shift: shift + E + 1]
+            es_t.copy_(torch.from_numpy(es.astype(np.int64)).to(dev))
+        bufs, wss, wants, rows = [], [], [], []
+        for s_np, s_gpu, shp in stacks:
+            n = s_gpu.dense_bytes
+            buf = torch.full((GUARD_BYTES + off + n + GUARD_BYTES,), GUARD, dtype=torch.uint8, device=dev)
+            ws = buf[GUARD_BYTES + off: GUARD_BYTES + off + n]
+            ws.fill_(POISON)
+            fill = np.full(shp, POISON, np.uint8)
+            if window:
+                b = int(rng.integers(0, shp[1] + 1))
+                e = int(rng.integers(b, shp[1] + 1))
+                rows.append((b, e))
+                wants.append(orc.decode_rows(s_np, b, e, es, fill))
+            else:
+                wants.append(orc.decode(s_np, es, fill))
+            bufs.append(buf)
+            wss.append(ws)
+        if window:
+            second = (stacks[1][1], wss[1], rows[1]) if paired else (None, None, None)
+            mwd.decode_rows(stacks[0][1], wss[0], rows[0], *second, es_t)
+        elif paired:
+            mwd.decode_paired(stacks[0][1], wss[0], stacks[1][1], wss[1], es_t)
+        else:
+            mwd.decode(stacks[0][1], wss[0], es_t)
+        torch.cuda.synchronize()
+        for (s_np, s_gpu, shp), buf, want in zip(stacks, bufs, wants):
+            h = buf.cpu().numpy()
+            n = s_gpu.dense_bytes
+            assert np.all(h[:GUARD_BYTES + off] == GUARD), f"case {seed}: write before the workspace"
+            assert np.all(h[GUARD_BYTES + off + n:] == GUARD), f"case {seed}: write past the workspace"
+            assert_bytes_equal(h[GUARD_BYTES + off: GUARD_BYTES + off + n].reshape(shp), want, f"case {seed}")
+        if rng.random() < 0.3:
+            sh = int(rng.choice([0, 1, 4]))
+            xd = torch.empty(x.size + 16, dtype=torch.uint8, device=dev)[sh: sh + x.size].view(E, R, C)
+            xd.copy_(torch.from_numpy(x).to(dev))
+            _same_streams(mwd.prepare(xd, fmt).numpy(), st, f"case {seed} GPU encode")
