@@ -926,3 +926,41 @@ def test_random_feature_combinations(orc, dev, block):
             xd = torch.empty(x.size + 16, dtype=torch.uint8, device=dev)[sh: sh + x.size].view(E, R, C)
             xd.copy_(torch.from_numpy(x).to(dev))
             _same_streams(mwd.prepare(xd, fmt).numpy(), st, f"case {seed} GPU encode")
+
+
+def test_gpu_encoder_random_value_patterns(orc, dev):
+    """150 seeded stacks whose values stress the base search: a few values
+    anywhere, most values in the top 16 bytes with the rest just above 0 (a
+    base above 256 - W, and bytes within W of it modulo 256), two equal
+    clusters (ties), uniform bytes, and constant planes with a few stray
+    bytes; rows of 1 to 400 columns, both formats, dense bytes 0 to 8 bytes
+    past a 16-byte boundary.  The GPU encoder's streams equal the oracle's."""
+    for i in range(150):
+        seed = 500000 + i
+        rng = np.random.default_rng(seed)
+        E = int(rng.choice([1, 2, 3, 7, 64, 300]))
+        C = int(rng.choice([1, 2, 3, 4, 5, 15, 16, 17, 31, 32, 33, 48, 50, 64, 100, 128, 160, 200, 254, 255, 256,
+                            257, 400]))
+        R = int(rng.integers(1, max(1, min(500, 1_000_000 // (E * C))) + 1))
+        kind = int(rng.integers(0, 5))
+        shp = (E, R, C)
+        if kind == 0:
+            x = rng.choice(rng.integers(0, 256, int(rng.integers(1, 6))), shp).astype(np.uint8)
+        elif kind == 1:
+            x = np.where(rng.random(shp) < 0.8, rng.integers(240, 256, shp), rng.integers(0, 20, shp)).astype(np.uint8)
+        elif kind == 2:
+            a, b = rng.integers(0, 256, 2)
+            x = np.clip(np.where(rng.random(shp) < 0.5, a + rng.integers(0, 2, shp), b + rng.integers(0, 2, shp)),
+                        0, 255).astype(np.uint8)
+        elif kind == 3:
+            x = workloads.uniform_bytes(E, R, C, seed)
+        else:
+            x = np.full(shp, int(rng.integers(0, 256)), np.uint8)
+            k = max(1, x.size // 50)
+            x.reshape(-1)[rng.integers(0, x.size, k)] = rng.integers(0, 256, k)
+        fmt = int(rng.integers(0, 2))
+        sh = int(rng.choice([0, 0, 1, 3, 8]))
+        print(f"[parity] encoder pattern {kind} case {seed}: fmt {fmt} {shp} shift {sh}", flush=True)
+        xd = torch.empty(x.size + 16, dtype=torch.uint8, device=dev)[sh: sh + x.size].view(*shp)
+        xd.copy_(torch.from_numpy(x).to(dev))
+        _same_streams(mwd.prepare(xd, fmt).numpy(), orc.encode(fmt, x), f"encoder case {seed}")
