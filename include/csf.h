@@ -279,7 +279,8 @@ csf_status csf_decode_rows(const csf_stack *first, uint8_t *ws_first, const csf_
  * alpha: float32 [E].  x, alpha, expert_start and y are 4-byte aligned.
  * expert_start: int32 [E + 1] on the device; token
  *   indices are clamped to [0, num_tokens].  y: float32 [num_tokens][N]; rows
- *   of tokens outside every expert's range are not written.
+ *   of tokens outside every expert's range are not written.  With num_tokens 0
+ *   x and y may be NULL and nothing is enqueued.
  * MXFP4 weights are widened to bfloat16 with their scale applied: exact for
  *   scale bytes 2..252 and 255; with bytes 0, 1 (weights below bfloat16's
  *   normal range) or 253, 254 (weights up to 6 * 2^127, beyond its largest

@@ -509,7 +509,8 @@ def moe_w4a16(scales: CompressedStack, weights: torch.Tensor, x: torch.Tensor, a
     d = scales.descriptor()
     _check(_lib().csf_moe_w4a16(ctypes.byref(d), None if dense_scales is None else dense_scales.data_ptr(),
                                 weights.data_ptr(), x.data_ptr() if T > 0 else None, T, alpha.data_ptr(),
-                                expert_start.data_ptr(), out.data_ptr(), _stream_handle(stream, dev)),
+                                expert_start.data_ptr(), out.data_ptr() if T > 0 else None,
+                                _stream_handle(stream, dev)),
            "csf_moe_w4a16")
     return out
 

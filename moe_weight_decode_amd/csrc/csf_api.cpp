@@ -332,12 +332,12 @@ csf_status moe_impl(const csf_stack *scales, const uint8_t *dense, const uint8_t
     const int64_t C = scales->cols, K = (mx ? 32 : 16) * C;
     if (K % 32 != 0 || K > 8192) return CSF_E_SHAPE;  // whole 32-wide MFMA lane groups, at most 4 K-tiles
     if (num_tokens < 0) return CSF_E_SIZE;
-    if (alpha == nullptr || expert_start == nullptr || y == nullptr) return CSF_E_NULL;
-    if (num_tokens > 0 && x == nullptr) return CSF_E_NULL;
+    if (alpha == nullptr || expert_start == nullptr) return CSF_E_NULL;
+    if (num_tokens > 0 && (x == nullptr || y == nullptr)) return CSF_E_NULL;  // no tokens: x, y may be NULL
     if (dense == nullptr && scales->tile_index == nullptr) return CSF_E_NULL;
     // dense NVFP4 scales are read two bytes at a time (C = K/16 is even)
     if (!aligned(weights, 16) || (x && !aligned(x, 4)) || !aligned(alpha, 4) || !aligned(expert_start, 4) ||
-        !aligned(y, 4) || (dense && !mx && !aligned(dense, 2)))
+        (y && !aligned(y, 4)) || (dense && !mx && !aligned(dense, 2)))
         return CSF_E_ALIGN;
     if (num_tokens == 0) return CSF_OK;
 

@@ -330,6 +330,8 @@ def test_moe_w4a16_errors(lib):
     assert call(mx, T=0, x=None, dense=0x60001) == "CSF_OK"               # MXFP4 dense scales: bytes
     assert call(None) == "CSF_E_NULL"
     assert call(ok, T=0, x=None) == "CSF_OK"                              # nothing to do, nothing launched
+    assert call(ok, T=0, x=None, y=None) == "CSF_OK"                      # no tokens: no output rows either
+    assert call(ok, y=None) == "CSF_E_NULL"
 
 
 def test_encode_device_errors(lib):

@@ -333,3 +333,13 @@ def test_ahead_of_call_expansion_on_a_side_stream(orc, dev):
     torch.cuda.synchronize()
     assert torch.equal(y, stage)
     check(inp, y.cpu().numpy(), "ahead-of-call expansion")
+
+
+def test_no_routed_tokens(orc, dev):
+    """A routing with no tokens at all: an empty output, nothing launched,
+    for both scale sources and formats."""
+    for fmt in (workloads.NVFP4, workloads.MXFP4):
+        inp = workloads.w4a16_inputs(3, 40, 256, np.zeros(4, dtype=np.int32), seed=5, fmt=fmt)
+        for dense in (False, True):
+            got = run(orc, dev, inp, dense=dense)
+            assert got.shape == (0, 40)
