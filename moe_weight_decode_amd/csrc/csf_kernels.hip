@@ -821,36 +821,139 @@ __device__ __forceinline__ uint32_t find_expert(const uint32_t *M, uint32_t k, u
 // Exception pass alone.
 //
 // The entries of all active experts of both stacks form one index space
-// [0, N0 + N1), laid out by the wave-level prefixes M_s.  Workgroups take
-// chunks of kBlock*kExcPerLane consecutive indices; lane l handles index
-// t = chunk + l + i*kBlock, so each load instruction of a wave reads 64
-// consecutive entries.  Entry t of stack s belongs to the listed expert k with
-// M_s[k] <= t < M_s[k+1]; it is word prefix_s[act[k]] + (t - M_s[k]).
+// [0, N0 + N1), laid out by the prefixes M_s over the listed experts' entry
+// counts.  Workgroups take chunks of kBlock*kExcPerLane consecutive indices;
+// lane l handles index t = chunk + l + i*kBlock, so each load instruction of
+// a wave reads 64 consecutive entries.  Entry t of stack s belongs to the
+// listed expert k with M_s[k] <= t < M_s[k+1]; it is word B_s[k] + (t -
+// M_s[k]), B_s[k] being that expert's prefix value.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kListChunks = 8;  // 64-expert chunks of routing read per round trip
+constexpr uint32_t kCountChunks = 4; // 64-expert chunks of prefix bounds read per round trip
+
+// Wave 0 lists the active experts in act (every expert when es is null) and
+// returns their number.  The routing of kListChunks * 64 experts is read in
+// one round trip: each lane loads two neighbouring values per chunk, at
+// addresses clamped into the tensor.
+template <typename T>
+__device__ __forceinline__ uint32_t list_experts(const T *es, uint32_t E, uint16_t *act) {
+    const uint32_t lane = threadIdx.x;
+    uint32_t n = 0;
+    for (uint32_t base = 0; base < E; base += kWave * kListChunks) {
+        bool on[kListChunks];
+        if (es != nullptr) {
+            T lo[kListChunks], hi[kListChunks];
+#pragma unroll
+            for (uint32_t u = 0; u < kListChunks; ++u) {
+                const uint32_t e = min(base + kWave * u + lane, E - 1u);
+                lo[u] = es[e];
+                hi[u] = es[e + 1];
+            }
+#pragma unroll
+            for (uint32_t u = 0; u < kListChunks; ++u) on[u] = base + kWave * u + lane < E && hi[u] > lo[u];
+        } else {
+#pragma unroll
+            for (uint32_t u = 0; u < kListChunks; ++u) on[u] = base + kWave * u + lane < E;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kListChunks; ++u) {
+            const uint64_t mask = __ballot(on[u]);
+            if (on[u]) act[n + bits_below(mask)] = (uint16_t)(base + kWave * u + lane);
+            n += (uint32_t)__popcll(mask);
+        }
+    }
+    return n;
+}
+
+// Inclusive scan over the wave of counts capped at cap (< 2^31, so a sum of
+// two capped values fits in 32 bits): lane l gets min(cap, c_0 + ... + c_l).
+__device__ __forceinline__ uint32_t capped_scan(uint32_t c, uint32_t cap) {
+    const uint32_t lane = threadIdx.x % kWave;
+#pragma unroll
+    for (uint32_t d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(c, d, kWave);
+        if (lane >= d) c = min(c + y, cap);
+    }
+    return c;
+}
+
+// Wave 0, after list_experts: for the n listed experts of stack s, B_s[k] =
+// prefix_s[act[k]] and M_s[k + 1] = min(n_exc_s, entries of listed experts
+// 0..k), an expert's entry count being prefix_s[e+1] - prefix_s[e] clamped
+// to [0, n_exc_s]; M_s[0] = 0.  The prefix bounds of kCountChunks * 64
+// experts are read in one round trip.
+__device__ __forceinline__ void count_entries(const DecodeArgs &a, uint32_t ns, const uint16_t *act,
+                                              uint32_t n, int32_t *B0, int32_t *B1, uint32_t *M0,
+                                              uint32_t *M1) {
+    const uint32_t lane = threadIdx.x;
+    // With one stack, stack 1's bounds are read from stack 0's prefix (so
+    // every load is unconditional) and capped to nothing.
+    const int32_t *pf0 = a.st[0].prefix, *pf1 = ns > 1 ? a.st[1].prefix : pf0;
+    const uint32_t cap0 = a.st[0].n_exc, cap1 = ns > 1 ? a.st[1].n_exc : 0u;
+    if (lane == 0) {
+        M0[0] = 0;
+        M1[0] = 0;
+    }
+    uint32_t run0 = 0, run1 = 0;
+    for (uint32_t kb = 0; kb < n; kb += kWave * kCountChunks) {
+        int32_t lo0[kCountChunks], hi0[kCountChunks], lo1[kCountChunks], hi1[kCountChunks];
+#pragma unroll
+        for (uint32_t u = 0; u < kCountChunks; ++u) {
+            const uint32_t k = kb + kWave * u + lane;
+            const uint32_t e = act[min(k, n - 1u)];
+            lo0[u] = pf0[e];
+            hi0[u] = pf0[e + 1];
+            lo1[u] = pf1[e];
+            hi1[u] = pf1[e + 1];
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kCountChunks; ++u) {
+            const uint32_t k = kb + kWave * u + lane;
+            const bool live = k < n;
+            const int64_t d0 = (int64_t)hi0[u] - lo0[u], d1 = (int64_t)hi1[u] - lo1[u];
+            const uint32_t c0 = live ? (uint32_t)(d0 < 0 ? 0 : d0 > cap0 ? cap0 : d0) : 0u;
+            const uint32_t c1 = live ? (uint32_t)(d1 < 0 ? 0 : d1 > cap1 ? cap1 : d1) : 0u;
+            const uint32_t s0 = min(run0 + capped_scan(c0, cap0), cap0);
+            const uint32_t s1 = min(run1 + capped_scan(c1, cap1), cap1);
+            if (live) {
+                B0[k] = lo0[u];
+                M0[k + 1] = s0;
+                if (ns > 1) {
+                    B1[k] = lo1[u];
+                    M1[k + 1] = s1;
+                }
+            }
+            run0 = __shfl(s0, kWave - 1, kWave);
+            run1 = __shfl(s1, kWave - 1, kWave);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     extern __shared__ __align__(16) uint8_t dyn_lds[];
     __shared__ uint32_t s_nact;
 
     const uint32_t E = a.E;
     const uint32_t ns = a.nstacks;
-    const uint32_t words = (E + 1u + 3u) & ~3u;  // one int32[E+1] map, padded to 16 B
-    uint8_t *flags = dyn_lds;
-    int32_t *p0 = reinterpret_cast<int32_t *>(dyn_lds + ((E + 15u) & ~15u));
-    int32_t *p1 = p0 + words;
-    uint32_t *M0 = reinterpret_cast<uint32_t *>(p1 + words);
+    const uint32_t words = (E + 1u + 3u) & ~3u;  // one [E+1] map of 4-byte words, padded to 16 B
+    uint16_t *act = reinterpret_cast<uint16_t *>(dyn_lds);
+    int32_t *B0 = reinterpret_cast<int32_t *>(dyn_lds + ((2u * E + 15u) & ~15u));
+    int32_t *B1 = B0 + words;
+    uint32_t *M0 = reinterpret_cast<uint32_t *>(B1 + words);
     uint32_t *M1 = M0 + words;
-    uint16_t *act = reinterpret_cast<uint16_t *>(M1 + words);
 
-    const bool routed = a.expert_start != nullptr;
-    if (routed) routed_flags(a, flags);
-    for (uint32_t i = threadIdx.x; i <= E; i += kBlock) {
-        p0[i] = a.st[0].prefix[i];
-        if (ns > 1) p1[i] = a.st[1].prefix[i];
-    }
-    __syncthreads();
     if (threadIdx.x < kWave) {
-        const uint32_t n = build_maps(routed ? flags : nullptr, E, act, ns, p0, p1, a.st[0].n_exc,
-                                      ns > 1 ? a.st[1].n_exc : 0u, M0, M1);
+        uint32_t n;
+        if (a.expert_start == nullptr)
+            n = list_experts(static_cast<const int32_t *>(nullptr), E, act);
+        else if (a.es_wide)
+            n = list_experts(static_cast<const int64_t *>(a.expert_start), E, act);
+        else
+            n = list_experts(static_cast<const int32_t *>(a.expert_start), E, act);
+        // act was written by other lanes of this wave; LDS accesses of one
+        // wave take effect in order.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        if (n > 0) count_entries(a, ns, act, n, B0, B1, M0, M1);
         if (threadIdx.x == 0) s_nact = n;
     }
     __syncthreads();
@@ -859,17 +962,30 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     const uint32_t N0 = M0[nact];
     const uint32_t N = N0 + (ns > 1 ? M1[nact] : 0u);
     const uint32_t chunk = kBlock * kExcPerLane;
+    // Both stacks' fields as values: the stack is picked per entry, that is
+    // per lane, and a field read through an address picked per lane would be
+    // a vector load from the argument block, waited for before each entry.
+    const uint32_t *const exc0 = a.st[0].exc, *const exc1 = a.st[1].exc;
+    uint8_t *const ws0 = a.st[0].ws, *const ws1 = a.st[1].ws;
+    const uint32_t nexc0 = a.st[0].n_exc, nexc1 = a.st[1].n_exc;
+    const uint32_t P0 = a.st[0].P, P1 = a.st[1].P;
+    const uint32_t beg0 = a.st[0].pbeg, beg1 = a.st[1].pbeg;
+    const uint32_t end0 = a.st[0].pend, end1 = a.st[1].pend;
 
     for (uint32_t c0 = blockIdx.x * chunk; c0 < N; c0 += gridDim.x * chunk) {
-        uint32_t word[kExcPerLane];
+        uint32_t id[kExcPerLane], x[kExcPerLane];
         uint8_t *dst[kExcPerLane];
+        bool hi[kExcPerLane], ok[kExcPerLane];
         uint32_t k = 0, prev_s = 0;
-        // Locate every entry first so the loads below are all in flight together.
+        // Locate every entry first, then load them all unconditionally, so the
+        // loads are in flight together: lanes past N re-read entry N - 1, and
+        // an index past its stack's entries (a prefix that overruns them)
+        // reads the stack's last entry; neither is stored.  A stack that
+        // owns a compacted index has at least one entry.
 #pragma unroll
         for (uint32_t i = 0; i < kExcPerLane; ++i) {
-            const uint32_t t = c0 + threadIdx.x + i * kBlock;
-            dst[i] = nullptr;
-            if (t >= N) continue;
+            const uint32_t tl = c0 + threadIdx.x + i * kBlock;
+            const uint32_t t = tl < N ? tl : N - 1u;
             const uint32_t s = t >= N0 ? 1u : 0u;
             const uint32_t tt = t - (s ? N0 : 0u);
             if (s != prev_s) {
@@ -879,28 +995,20 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
             const uint32_t *M = s ? M1 : M0;
             k = find_expert(M, k, nact, tt);
             const uint32_t e = act[k];
-            const int32_t *pf = s ? p1 : p0;
-            const uint32_t idx = (uint32_t)pf[e] + (tt - M[k]);
-            const StackArgs st = pick(a, s);
-            if (idx < st.n_exc) {
-                word[i] = idx;
-                dst[i] = st.ws + (uint64_t)e * st.P;
-            }
+            const uint32_t j = (uint32_t)(s ? B1 : B0)[k] + (tt - M[k]);
+            const uint32_t n = s ? nexc1 : nexc0;
+            hi[i] = s != 0;
+            ok[i] = tl < N && j < n;
+            id[i] = j < n ? j : n - 1u;
+            dst[i] = (s ? ws1 : ws0) + (uint64_t)e * (s ? P1 : P0);
         }
 #pragma unroll
-        for (uint32_t i = 0; i < kExcPerLane; ++i) {
-            if (dst[i] == nullptr) continue;
-            const uint32_t t = c0 + threadIdx.x + i * kBlock;
-            const uint32_t *exc = t >= N0 ? a.st[1].exc : a.st[0].exc;
-            word[i] = exc[word[i]];
-        }
+        for (uint32_t i = 0; i < kExcPerLane; ++i) x[i] = (hi[i] ? exc1 : exc0)[id[i]];
 #pragma unroll
         for (uint32_t i = 0; i < kExcPerLane; ++i) {
-            if (dst[i] == nullptr) continue;
-            const uint32_t t = c0 + threadIdx.x + i * kBlock;
-            const StackArgs &st = t >= N0 ? a.st[1] : a.st[0];
-            const uint32_t pos = word[i] >> 8;
-            if (pos >= st.pbeg && pos < st.pend) dst[i][pos] = (uint8_t)(word[i] & 0xffu);
+            const uint32_t pos = x[i] >> 8;
+            if (ok[i] && pos >= (hi[i] ? beg1 : beg0) && pos < (hi[i] ? end1 : end0))
+                dst[i][pos] = (uint8_t)(x[i] & 0xffu);
         }
     }
 }
@@ -943,7 +1051,7 @@ size_t tile_lds_bytes(const DecodeArgs &a) {
 
 static size_t exc_lds_bytes(const DecodeArgs &a) {
     const size_t words = (a.E + 1u + 3u) & ~3u;
-    return ((a.E + 15u) & ~15u) + 4u * 4u * words + 2u * a.E;
+    return ((2u * a.E + 15u) & ~15u) + 4u * 4u * words;
 }
 
 template <bool WINDOW>
