@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 kernels of the CSF library (the decoder
 // and the W4A16 consumer): byte arithmetic, buffer resources, row-base
-// lookup, tile expansion into LDS and the routing maps.  Internal; every
+// lookup, tile expansion into LDS and the list of routed experts.  Internal; every
 // definition has internal linkage, so each kernel file gets its own copy.
 #pragma once
 
@@ -109,68 +109,47 @@ __device__ __forceinline__ void store_run(uint8_t *dst, u32x4 v, uint32_t first,
         if (j >= first && j < n) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
 }
 
-// flags[e] = 1 iff expert e has routed tokens, expert_start[e + 1] >
-// expert_start[e], for e in [first, E) with stride step; the routing tensor is
-// int32 or int64 (the grouped routing comes in both widths).
-template <typename T>
-__device__ __forceinline__ void stage_flags(const T *es, uint32_t E, uint32_t first, uint32_t step,
-                                            uint8_t *flags) {
-    for (uint32_t i = first; i < E; i += step) flags[i] = es[i + 1] > es[i] ? 1 : 0;
+// Set bits of m below this lane.
+__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Wave 0 of the workgroup: list the active experts (flags[e] != 0, or all
-// when flags is null) in increasing order into act[];
-// for each stack s < ns also the exclusive prefix M_s over the listed experts
-// of their entry counts (prefix[e+1] - prefix[e], clamped to [0, n_exc]),
-// capped at n_exc.  Returns the number of active experts.  A wave-level
-// prefix: ballot + popcount for the positions, a shuffle scan for the counts.
-__device__ uint32_t build_maps(const uint8_t *flags, uint32_t E, uint16_t *act, uint32_t ns,
-                               const int32_t *pfx0, const int32_t *pfx1, uint32_t n0,
-                               uint32_t n1, uint32_t *M0, uint32_t *M1) {
+constexpr uint32_t kListChunks = 8;  // 64-expert chunks of routing read per round trip
+
+// Wave 0 of the workgroup lists the experts with routed tokens (expert e has
+// them iff es[e + 1] > es[e]; every expert when es is null) in increasing
+// order into act[] and returns their number.  The routing of CH chunks of 64
+// experts is read in one round trip (kListChunks chunks, fewer in a kernel
+// whose registers are tight): each lane loads two neighbouring values per
+// chunk, at addresses clamped into the tensor; a ballot per chunk gives each
+// listed expert its slot.  The routing is int32 or int64 (the grouped routing
+// comes in both widths), in global memory or in LDS.
+template <uint32_t CH = kListChunks, typename T>
+__device__ __forceinline__ uint32_t list_experts(const T *es, uint32_t E, uint16_t *act) {
     const uint32_t lane = threadIdx.x;
     uint32_t n = 0;
-    uint64_t run0 = 0, run1 = 0;
-    if (lane == 0 && ns > 0) {
-        M0[0] = 0;
-        if (ns > 1) M1[0] = 0;
-    }
-    for (uint32_t base = 0; base < E; base += kWave) {
-        const uint32_t e = base + lane;
-        const bool on = e < E && (flags == nullptr || flags[e] != 0);
-        const uint64_t mask = __ballot(on);
-        const uint32_t slot = n + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-        if (on) act[slot] = (uint16_t)e;
-        if (ns > 0) {
-            int64_t c0 = on ? (int64_t)pfx0[e + 1] - (int64_t)pfx0[e] : 0;
-            c0 = c0 < 0 ? 0 : (c0 > (int64_t)n0 ? (int64_t)n0 : c0);
-            uint64_t s0 = (uint64_t)c0;
-            int64_t c1 = 0;
-            if (ns > 1) {
-                c1 = on ? (int64_t)pfx1[e + 1] - (int64_t)pfx1[e] : 0;
-                c1 = c1 < 0 ? 0 : (c1 > (int64_t)n1 ? (int64_t)n1 : c1);
-            }
-            uint64_t s1 = (uint64_t)c1;
+    for (uint32_t base = 0; base < E; base += kWave * CH) {
+        bool on[CH];
+        if (es != nullptr) {
+            T lo[CH], hi[CH];
 #pragma unroll
-            for (uint32_t d = 1; d < kWave; d <<= 1) {
-                const uint64_t y0 = __shfl_up(s0, d, kWave);
-                const uint64_t y1 = __shfl_up(s1, d, kWave);
-                if (lane >= d) {
-                    s0 += y0;
-                    s1 += y1;
-                }
+            for (uint32_t u = 0; u < CH; ++u) {
+                const uint32_t e = min(base + kWave * u + lane, E - 1u);
+                lo[u] = es[e];
+                hi[u] = es[e + 1];
             }
-            if (on) {
-                const uint64_t t0 = run0 + s0;
-                M0[slot + 1] = (uint32_t)(t0 < n0 ? t0 : n0);
-                if (ns > 1) {
-                    const uint64_t t1 = run1 + s1;
-                    M1[slot + 1] = (uint32_t)(t1 < n1 ? t1 : n1);
-                }
-            }
-            run0 += __shfl(s0, kWave - 1, kWave);
-            run1 += __shfl(s1, kWave - 1, kWave);
+#pragma unroll
+            for (uint32_t u = 0; u < CH; ++u) on[u] = base + kWave * u + lane < E && hi[u] > lo[u];
+        } else {
+#pragma unroll
+            for (uint32_t u = 0; u < CH; ++u) on[u] = base + kWave * u + lane < E;
         }
-        n += (uint32_t)__popcll(mask);
+#pragma unroll
+        for (uint32_t u = 0; u < CH; ++u) {
+            const uint64_t mask = __ballot(on[u]);
+            if (on[u]) act[n + bits_below(mask)] = (uint16_t)(base + kWave * u + lane);
+            n += (uint32_t)__popcll(mask);
+        }
     }
     return n;
 }

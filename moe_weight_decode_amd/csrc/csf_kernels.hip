@@ -36,20 +36,14 @@ __device__ __forceinline__ StackArgs pick(const DecodeArgs &a, uint32_t s) {
     return s ? a.st[1] : a.st[0];
 }
 
-__device__ __forceinline__ void routed_flags(const DecodeArgs &a, uint8_t *flags) {
-    if (a.es_wide)
-        stage_flags(static_cast<const int64_t *>(a.expert_start), a.E, threadIdx.x, kBlock, flags);
-    else
-        stage_flags(static_cast<const int32_t *>(a.expert_start), a.E, threadIdx.x, kBlock, flags);
-}
-
-// Routed mode: the active-expert list in LDS (all threads take part).
-__device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act, uint8_t *flags) {
+// Routed mode: the active-expert list in LDS, written by wave 0 straight from
+// the routing and shared by a barrier.  Two chunks of 64 experts per round
+// trip keep the tile loops' register budgets.
+__device__ uint32_t active_experts(const DecodeArgs &a, uint16_t *act) {
     __shared__ uint32_t s_nact;
-    routed_flags(a, flags);
-    __syncthreads();
     if (threadIdx.x < kWave) {
-        const uint32_t n = build_maps(flags, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
+        const uint32_t n = a.es_wide ? list_experts<2>(static_cast<const int64_t *>(a.expert_start), a.E, act)
+                                     : list_experts<2>(static_cast<const int32_t *>(a.expert_start), a.E, act);
         if (threadIdx.x == 0) s_nact = n;
     }
     __syncthreads();
@@ -98,10 +92,9 @@ __device__ __forceinline__ void tile_loop_serial(const DecodeArgs &a, uint8_t *d
     constexpr uint32_t INDEX_PER_TILE = TILE / kIndexTile;
     uint8_t *lds_bases = dyn;
     uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
-    uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
 
     const bool routed = a.expert_start != nullptr;
-    const uint32_t nact = routed ? active_experts(a, act, flags) : a.E;
+    const uint32_t nact = routed ? active_experts(a, act) : a.E;
     const uint32_t u0 = nact * a.st[0].tiles;
     const uint32_t total = u0 + (a.nstacks > 1 ? nact * a.st[1].tiles : 0u);
 
@@ -474,11 +467,6 @@ __device__ __forceinline__ uint32_t nth_set_bit(uint64_t w, uint32_t k) {
     return pos;
 }
 
-// Set bits of m below this lane.
-__device__ __forceinline__ uint32_t bits_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // The routed unit of this workgroup.
 struct RoutedUnit {
     uint32_t total;    // units of the launch
@@ -651,8 +639,7 @@ __device__ __forceinline__ void routed_decode(const RouteHead &h, const DecodeAr
     clk.mark(1);
     if (!fast || ru.total > h.grid) [[unlikely]] {
         uint16_t *act = reinterpret_cast<uint16_t *>(dyn + a.bases_stage);
-        uint8_t *flags = dyn + a.bases_stage + ((2u * a.E + 15u) & ~15u);
-        const uint32_t nact = active_experts(a, act, flags);
+        const uint32_t nact = active_experts(a, act);
         tile_loop_pipelined<RUNS, EXC, kNonTemporal, WINDOW>(a, lds_bases, tile, nact, act, true);
         clk.write(a, ~0ull);
         return;
@@ -822,48 +809,14 @@ __device__ __forceinline__ uint32_t find_expert(const uint32_t *M, uint32_t k, u
 //
 // The entries of all active experts of both stacks form one index space
 // [0, N0 + N1), laid out by the prefixes M_s over the listed experts' entry
-// counts.  Workgroups take chunks of kBlock*kExcPerLane consecutive indices;
-// lane l handles index t = chunk + l + i*kBlock, so each load instruction of
-// a wave reads 64 consecutive entries.  Entry t of stack s belongs to the
+// counts.  Workgroups take chunks of kBlock*EPL consecutive indices, EPL (1,
+// 2, 4 or kExcPerLane entries per lane) the fewest that leave each workgroup
+// at most one chunk; lane l handles index t = chunk + l + i*kBlock, so each
+// load instruction of a wave reads 64 consecutive entries.  Entry t of stack s belongs to the
 // listed expert k with M_s[k] <= t < M_s[k+1]; it is word B_s[k] + (t -
 // M_s[k]), B_s[k] being that expert's prefix value.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kListChunks = 8;  // 64-expert chunks of routing read per round trip
 constexpr uint32_t kCountChunks = 4; // 64-expert chunks of prefix bounds read per round trip
-
-// Wave 0 lists the active experts in act (every expert when es is null) and
-// returns their number.  The routing of kListChunks * 64 experts is read in
-// one round trip: each lane loads two neighbouring values per chunk, at
-// addresses clamped into the tensor.
-template <typename T>
-__device__ __forceinline__ uint32_t list_experts(const T *es, uint32_t E, uint16_t *act) {
-    const uint32_t lane = threadIdx.x;
-    uint32_t n = 0;
-    for (uint32_t base = 0; base < E; base += kWave * kListChunks) {
-        bool on[kListChunks];
-        if (es != nullptr) {
-            T lo[kListChunks], hi[kListChunks];
-#pragma unroll
-            for (uint32_t u = 0; u < kListChunks; ++u) {
-                const uint32_t e = min(base + kWave * u + lane, E - 1u);
-                lo[u] = es[e];
-                hi[u] = es[e + 1];
-            }
-#pragma unroll
-            for (uint32_t u = 0; u < kListChunks; ++u) on[u] = base + kWave * u + lane < E && hi[u] > lo[u];
-        } else {
-#pragma unroll
-            for (uint32_t u = 0; u < kListChunks; ++u) on[u] = base + kWave * u + lane < E;
-        }
-#pragma unroll
-        for (uint32_t u = 0; u < kListChunks; ++u) {
-            const uint64_t mask = __ballot(on[u]);
-            if (on[u]) act[n + bits_below(mask)] = (uint16_t)(base + kWave * u + lane);
-            n += (uint32_t)__popcll(mask);
-        }
-    }
-    return n;
-}
 
 // Inclusive scan over the wave of counts capped at cap (< 2^31, so a sum of
 // two capped values fits in 32 bits): lane l gets min(cap, c_0 + ... + c_l).
@@ -961,7 +914,6 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     if (nact == 0) return;
     const uint32_t N0 = M0[nact];
     const uint32_t N = N0 + (ns > 1 ? M1[nact] : 0u);
-    const uint32_t chunk = kBlock * kExcPerLane;
     // Both stacks' fields as values: the stack is picked per entry, that is
     // per lane, and a field read through an address picked per lane would be
     // a vector load from the argument block, waited for before each entry.
@@ -972,45 +924,63 @@ __global__ __launch_bounds__(kBlock) void csf_exc_kernel(DecodeArgs a) {
     const uint32_t beg0 = a.st[0].pbeg, beg1 = a.st[1].pbeg;
     const uint32_t end0 = a.st[0].pend, end1 = a.st[1].pend;
 
-    for (uint32_t c0 = blockIdx.x * chunk; c0 < N; c0 += gridDim.x * chunk) {
-        uint32_t id[kExcPerLane], x[kExcPerLane];
-        uint8_t *dst[kExcPerLane];
-        bool hi[kExcPerLane], ok[kExcPerLane];
-        uint32_t k = 0, prev_s = 0;
-        // Locate every entry first, then load them all unconditionally, so the
-        // loads are in flight together: lanes past N re-read entry N - 1, and
-        // an index past its stack's entries (a prefix that overruns them)
-        // reads the stack's last entry; neither is stored.  A stack that
-        // owns a compacted index has at least one entry.
+    // EPL entries per lane per chunk.
+    auto scatter = [&](auto eplc) {
+        constexpr uint32_t EPL = decltype(eplc)::value;
+        const uint32_t chunk = kBlock * EPL;
+        for (uint32_t c0 = blockIdx.x * chunk; c0 < N; c0 += gridDim.x * chunk) {
+            uint32_t id[EPL], x[EPL];
+            uint8_t *dst[EPL];
+            bool hi[EPL], ok[EPL];
+            uint32_t k = 0, prev_s = 0;
+            // Locate every entry first, then load them all unconditionally, so
+            // the loads are in flight together: lanes past N re-read entry
+            // N - 1, and an index past its stack's entries (a prefix that
+            // overruns them) reads the stack's last entry; neither is stored.
+            // A stack that owns a compacted index has at least one entry.
 #pragma unroll
-        for (uint32_t i = 0; i < kExcPerLane; ++i) {
-            const uint32_t tl = c0 + threadIdx.x + i * kBlock;
-            const uint32_t t = tl < N ? tl : N - 1u;
-            const uint32_t s = t >= N0 ? 1u : 0u;
-            const uint32_t tt = t - (s ? N0 : 0u);
-            if (s != prev_s) {
-                k = 0;
-                prev_s = s;
+            for (uint32_t i = 0; i < EPL; ++i) {
+                const uint32_t tl = c0 + threadIdx.x + i * kBlock;
+                const uint32_t t = tl < N ? tl : N - 1u;
+                const uint32_t s = t >= N0 ? 1u : 0u;
+                const uint32_t tt = t - (s ? N0 : 0u);
+                if (s != prev_s) {
+                    k = 0;
+                    prev_s = s;
+                }
+                const uint32_t *M = s ? M1 : M0;
+                k = find_expert(M, k, nact, tt);
+                const uint32_t e = act[k];
+                const uint32_t j = (uint32_t)(s ? B1 : B0)[k] + (tt - M[k]);
+                const uint32_t n = s ? nexc1 : nexc0;
+                hi[i] = s != 0;
+                ok[i] = tl < N && j < n;
+                id[i] = j < n ? j : n - 1u;
+                dst[i] = (s ? ws1 : ws0) + (uint64_t)e * (s ? P1 : P0);
             }
-            const uint32_t *M = s ? M1 : M0;
-            k = find_expert(M, k, nact, tt);
-            const uint32_t e = act[k];
-            const uint32_t j = (uint32_t)(s ? B1 : B0)[k] + (tt - M[k]);
-            const uint32_t n = s ? nexc1 : nexc0;
-            hi[i] = s != 0;
-            ok[i] = tl < N && j < n;
-            id[i] = j < n ? j : n - 1u;
-            dst[i] = (s ? ws1 : ws0) + (uint64_t)e * (s ? P1 : P0);
-        }
 #pragma unroll
-        for (uint32_t i = 0; i < kExcPerLane; ++i) x[i] = (hi[i] ? exc1 : exc0)[id[i]];
+            for (uint32_t i = 0; i < EPL; ++i) x[i] = (hi[i] ? exc1 : exc0)[id[i]];
 #pragma unroll
-        for (uint32_t i = 0; i < kExcPerLane; ++i) {
-            const uint32_t pos = x[i] >> 8;
-            if (ok[i] && pos >= (hi[i] ? beg1 : beg0) && pos < (hi[i] ? end1 : end0))
-                dst[i][pos] = (uint8_t)(x[i] & 0xffu);
+            for (uint32_t i = 0; i < EPL; ++i) {
+                const uint32_t pos = x[i] >> 8;
+                if (ok[i] && pos >= (hi[i] ? beg1 : beg0) && pos < (hi[i] ? end1 : end0))
+                    dst[i][pos] = (uint8_t)(x[i] & 0xffu);
+            }
         }
-    }
+    };
+    // The fewest entries per lane that still give every workgroup at most one
+    // chunk: a routed call has few entries for its grid, and smaller chunks
+    // spread them over more workgroups, so each lane locates, loads and stores
+    // fewer one after another.  The grid-stride loop is correct for any grid.
+    const uint32_t per_group = (N + gridDim.x - 1u) / gridDim.x;
+    if (per_group <= kBlock)
+        scatter(std::integral_constant<uint32_t, 1>{});
+    else if (per_group <= 2u * kBlock)
+        scatter(std::integral_constant<uint32_t, 2>{});
+    else if (per_group <= 4u * kBlock)
+        scatter(std::integral_constant<uint32_t, 4>{});
+    else
+        scatter(std::integral_constant<uint32_t, kExcPerLane>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1045,7 +1015,7 @@ __global__ __launch_bounds__(kBlock) void csf_index_kernel(StackArgs s, uint32_t
 
 size_t tile_lds_bytes(const DecodeArgs &a) {
     size_t n = a.bases_stage;
-    if (a.expert_start != nullptr) n += ((2u * a.E + 15u) & ~15u) + a.E;  // act + flags
+    if (a.expert_start != nullptr) n += (2u * a.E + 15u) & ~15u;  // active list
     return n;
 }
 

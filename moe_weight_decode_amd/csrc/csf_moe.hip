@@ -175,21 +175,18 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
     __shared__ __align__(16) uint8_t s_scales[kMoeRows * kMoeMaxCols];
     __shared__ __align__(16) v4f32 s_part[kMoeWaves][kMoeRowBlocks][kMoeBlocks][kWave];
     __shared__ uint32_t s_nact;
-    // dynamic LDS: row bases | expert_start copy | active list | flags
+    // dynamic LDS: row bases | expert_start copy | active list
     uint8_t *lds_bases = dyn_lds;
     int32_t *s_es = reinterpret_cast<int32_t *>(dyn_lds + a.bases_stage);
     uint16_t *act = reinterpret_cast<uint16_t *>(s_es + ((a.E + 1u + 3u) & ~3u));
-    uint8_t *flags = reinterpret_cast<uint8_t *>(act) + ((2u * a.E + 15u) & ~15u);
     const uint32_t tid = threadIdx.x;
 
     // Routing: expert_start into LDS (token ranges later cost no round trip),
-    // routed experts listed by wave 0.
+    // routed experts listed from that copy by wave 0.
     for (uint32_t i = tid; i <= a.E; i += kMoeThreads) s_es[i] = a.expert_start[i];
     __syncthreads();
-    stage_flags(s_es, a.E, tid, kMoeThreads, flags);
-    __syncthreads();
     if (tid < kWave) {
-        const uint32_t n = build_maps(flags, a.E, act, 0, nullptr, nullptr, 0, 0, nullptr, nullptr);
+        const uint32_t n = list_experts(static_cast<const int32_t *>(s_es), a.E, act);
         if (tid == 0) s_nact = n;
     }
     __syncthreads();
@@ -590,7 +587,7 @@ __global__ __launch_bounds__(kMoeThreads) void csf_moe_w4a16_kernel(MoeArgs a) {
 }  // namespace
 
 size_t moe_lds_bytes(const MoeArgs &a) {
-    return a.bases_stage + 4u * ((a.E + 1u + 3u) & ~3u) + ((2u * a.E + 15u) & ~15u) + a.E;
+    return a.bases_stage + 4u * ((a.E + 1u + 3u) & ~3u) + ((2u * a.E + 15u) & ~15u);
 }
 
 template <bool DENSE, bool MULTI, bool MX>
