@@ -283,6 +283,23 @@ def test_routed_paired_gate_down(orc, dev, mode):
     assert np.all(gg[inactive] == POISON) and np.all(gd[inactive] == POISON)
 
 
+@pytest.mark.parametrize("n_active", [1, 60, 120, 250, 511])
+def test_two_pass_routed_entry_spread(orc, dev, n_active):
+    """Routed two-pass decodes of the gate stack with 1 to 511 of 512 experts
+    routed: the exception pass spreads the routed entries over its grid in
+    chunks of 1, 2, 4 or 8 entries per lane, and with most experts routed a
+    workgroup takes several chunks."""
+    _, _, st = stack_case("gate_nvfp4", orc)
+    rng = np.random.default_rng(4100 + n_active)
+    act = np.zeros(512, bool)
+    act[rng.choice(512, n_active, replace=False)] = True
+    es = workloads.expert_start_from_mask(act, tokens=3)
+    print(f"[parity] two-pass routed gate, {n_active} experts routed", flush=True)
+    got = run_decode(upload(st, dev, "two_pass"), dev, es)
+    assert_bytes_equal(got, oracle_expect(orc, st, es), f"{n_active} routed")
+    assert np.all(got[~act] == POISON), "unrouted planes written"
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_paired_full_and_all_inactive(orc, dev, mode):
     gg, gd, wg, wd = _paired(orc, dev, None, mode)
