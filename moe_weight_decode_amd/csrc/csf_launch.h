@@ -13,7 +13,7 @@ constexpr uint32_t kIndexTile = 2048;               // positions per exception-i
 
 // Tile = kBlock * kRunBytes * runs positions, runs (per lane) in {1, 2, 4}.
 constexpr uint32_t tile_positions(uint32_t runs) { return kBlock * kRunBytes * runs; }
-constexpr uint32_t kExcPerLane = 8;                 // entries per lane per scatter chunk
+constexpr uint32_t kExcPerLane = 8;                 // entries per lane of an exception-pass chunk, at most (the grid is sized for it)
 constexpr uint32_t kBasesSlack = 32;                // rows read past a tile's last row by edge runs
 constexpr uint32_t kMaxExperts = 2048;              // experts per stack (the ABI's limit)
 constexpr uint32_t kStampsPerGroup = 8;             // timestamps a traced decode records per workgroup
