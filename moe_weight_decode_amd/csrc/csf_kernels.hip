@@ -812,9 +812,9 @@ __device__ __forceinline__ uint32_t find_expert(const uint32_t *M, uint32_t k, u
 // counts.  Workgroups take chunks of kBlock*EPL consecutive indices, EPL (1,
 // 2, 4 or kExcPerLane entries per lane) the fewest that leave each workgroup
 // at most one chunk; lane l handles index t = chunk + l + i*kBlock, so each
-// load instruction of a wave reads 64 consecutive entries.  Entry t of stack s belongs to the
-// listed expert k with M_s[k] <= t < M_s[k+1]; it is word B_s[k] + (t -
-// M_s[k]), B_s[k] being that expert's prefix value.
+// load instruction of a wave reads 64 consecutive entries.  Entry t of stack
+// s belongs to the listed expert k with M_s[k] <= t < M_s[k+1]; it is word
+// B_s[k] + (t - M_s[k]), B_s[k] being that expert's prefix value.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kCountChunks = 4; // 64-expert chunks of prefix bounds read per round trip
 
