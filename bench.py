@@ -264,21 +264,23 @@ def check_equal(torch, ws, x, what):
         raise SystemExit(f"{what}: GPU decode differs from the input in {(got != x).sum()} bytes")
 
 
-def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False, ceiling=True):
-    """Time the full decode of `spec` (fused, indexed stack) and, with
-    `ceiling`, the stream-mix kernel on the same buffers; with `split` also
-    the two-pass decode of the same stack and its fixed pass alone, one stack
-    decoded over and over (warm: its 85-109 MB stay in the MALL), and single
-    calls on flushed caches."""
+def bench_stack(mwd, torch, ev, spec, steps, warmup, nsets, dev, split=False, ceiling=True, two_pass=False):
+    """Time the full decode of `spec` (fused, indexed stack; with `two_pass`
+    the two-pass decode of the stack without its index) and, with `ceiling`,
+    the stream-mix kernel on the same buffers; with `split` also the two-pass
+    decode of the same stack and its fixed pass alone, one stack decoded over
+    and over (warm: its 85-109 MB stay in the MALL), and single calls on
+    flushed caches."""
     x = spec.generate()
     stack = mwd.prepare(x, spec.fmt).to(dev)
     sets = make_sets(mwd, torch, stack, nsets, dev)
-    launches = [mwd.Launch(s, ws) for s, ws in sets]
+    launches = [mwd.Launch(s.without_index() if two_pass else s, ws) for s, ws in sets]
     launches[0]()
     torch.cuda.synchronize()
     check_equal(torch, sets[0][1], x, spec.name)
     wall, evt = timed_loop(torch, ev, launches, steps, warmup)
-    out = dict(x=x, stack=stack, bytes=stack_bytes(stack), step_ms=max(wall, evt), wall_ms=wall, event_ms=evt)
+    out = dict(x=x, stack=stack, bytes=stack_bytes(stack.without_index() if two_pass else stack),
+               step_ms=max(wall, evt), wall_ms=wall, event_ms=evt)
     if ceiling and spec.E > 4:
         out["ceiling"] = bench_ceiling(mwd, torch, ev, sets, min(steps, 2000), warmup, dev)
     if split:
@@ -869,11 +871,16 @@ def main():
     ap.add_argument("--encode", default=None, metavar="STACK",
                     help="instead: time the GPU encoder (csf_encode_device) on a workload stack (or 'layer': "
                          "the gate-like and down-like stacks together), --steps times, and print one JSON line")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="full-stack workloads: time the two-pass decode (fixed-stream kernel, then exception "
+                         "kernel) of the stack without its tile index")
     ap.add_argument("--workload", default="gate_nvfp4",
                     choices=["gate_nvfp4", "down_nvfp4", "mxfp4", "tiny_nvfp4", "routed_paired", "routed_moe",
                              "routed_moe_mx"],
                     help="timed workload (default: the 512-expert gate-like stack)")
     args = ap.parse_args()
+    if args.two_pass and (args.workload.startswith("routed") or args.encode):
+        raise SystemExit("--two-pass applies to the full-stack workloads")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the CSF decode path is rank-local and has no "
               "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -937,7 +944,7 @@ def main():
         spec = workloads.STACKS[args.workload]
         log(f"[bench] {spec.name}: generating and encoding {spec.E}x{spec.R}x{spec.C}")
         r = bench_stack(mwd, torch, ev, spec, args.steps, args.warmup,
-                        args.sets if spec.E > 4 else 2, dev)
+                        args.sets if spec.E > 4 else 2, dev, two_pass=args.two_pass)
         stack, b = r["stack"], r["bytes"]
         step_bytes = b.metric
         fmt = "NVFP4 (E4M3 scales)" if spec.fmt == workloads.NVFP4 else "MXFP4 (UE8M0 scales)"
@@ -946,7 +953,8 @@ def main():
                         f"{spec.C} scale columns (K={spec.K}), {spec.desc.split(', ', 1)[-1]}, "
                         f"seed {spec.seed}",
             "experts": spec.E, "rows": spec.R, "cols": spec.C, "format": fmt,
-            "decode": "single pass (fused kernel, tile index)",
+            "decode": ("two-pass (csf_fixed_kernel, then csf_exc_kernel; no tile index)" if args.two_pass
+                       else "single pass (fused kernel, tile index)"),
             "exception_entries": stack.num_exceptions,
             "compressed_bytes": b.fixed + b.exc,
             "dense_bytes": b.dense,
@@ -954,6 +962,10 @@ def main():
             "index_bytes_per_step": b.index,
             "rotating_sets": args.sets if spec.E > 4 else 2,
         }
+        if args.two_pass:
+            # per pass: the fixed stream reads bases and offsets and writes the
+            # dense bytes; the exception pass reads the entries and prefix
+            config.update(fixed_pass_bytes=b.fixed + b.dense, exception_pass_bytes=b.exc)
         x_head = r["x"]
     gbps = step_bytes / (r["step_ms"] * 1e-3) / 1e9
     launch_us = r["event_ms"] * 1e3
@@ -961,7 +973,8 @@ def main():
     log(f"[bench] step {r['step_ms'] * 1e3:.2f} us (wall {r['wall_ms'] * 1e3:.2f}, events "
         f"{r['event_ms'] * 1e3:.2f}); {gbps:.1f} GB/s")
     kernel = ("csf_moe_w4a16_kernel" if moe else
-              "csf_routed_kernel" if args.workload == "routed_paired" else "csf_fused_kernel")
+              "csf_routed_kernel" if args.workload == "routed_paired" else
+              "csf_fixed_kernel + csf_exc_kernel" if args.two_pass else "csf_fused_kernel")
     traffic = pmc_traffic(kernel, args.workload)
     roof = {
         "kernel": kernel,

@@ -88,3 +88,29 @@ def test_source_hash_ignores_comments_only(tmp_path):
     p.write_text(text.replace("kMoeWaves = 8", "kMoeWaves = 4", 1))
     assert bench.source_hash("csf_moe_w4a16_kernel", str(d)) != h0
     assert bench.source_hash("csf_fused_kernel", str(d)) == bench.source_hash("csf_fused_kernel")
+
+
+@pytest.mark.parametrize("argv", [["--two-pass", "--workload", "routed_paired"],
+                                  ["--two-pass", "--workload", "routed_moe"],
+                                  ["--two-pass", "--encode", "gate_nvfp4"]])
+def test_two_pass_only_for_full_stack_workloads(argv):
+    """--two-pass times a full-stack decode without its index; the routed and
+    encode modes refuse it before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                         timeout=120)
+    assert res.returncode != 0
+    assert "--two-pass applies to the full-stack workloads" in res.stderr
+
+
+def test_two_pass_bytes_drop_the_index():
+    """The two-pass line's metric bytes are the stack's streams and dense bytes,
+    with no tile index read."""
+    import moe_weight_decode_amd as mwd
+    spec = workloads.TINY
+    stack = mwd.prepare(spec.generate(), spec.fmt)
+    b, b2 = bench.stack_bytes(stack), bench.stack_bytes(stack.without_index())
+    assert b2.index == 0 and b.index > 0
+    assert (b2.fixed, b2.exc, b2.dense) == (b.fixed, b.exc, b.dense)
