@@ -702,6 +702,31 @@ def test_routed_int64_expert_start(orc, dev, mode):
     assert_bytes_equal(ws.cpu().numpy().reshape(x.shape), want, "int64 single")
 
 
+@pytest.mark.parametrize("wide", [False, True])
+def test_two_pass_paired_many_experts(orc, dev, wide):
+    """Two-pass paired decode of 600-expert NVFP4 and MXFP4 stacks with 300
+    experts routed (int32, or int64 offsets beyond 2^32): the exception pass
+    lists the routed experts in two steps of 512 and scans their entry counts
+    in two steps of 256, for two stacks of different entry counts."""
+    E = 600
+    xa = workloads.nvfp4_stack(E, 40, 50, 8101, 0.10)
+    xb = workloads.mxfp4_stack(E, 32, 40, 8102, 0.15)
+    sa, sb = orc.encode(workloads.NVFP4, xa), orc.encode(workloads.MXFP4, xb)
+    rng = np.random.default_rng(8103)
+    act = np.zeros(E, bool)
+    act[rng.choice(E, 300, replace=False)] = True
+    es = workloads.expert_start_from_mask(act, tokens=2)
+    es_dev = es.astype(np.int64) + (np.int64(3) << 36) if wide else es
+    print(f"[parity] two-pass paired, 600 experts, 300 routed, wide {wide}", flush=True)
+    a, b = upload(sa, dev, "two_pass"), upload(sb, dev, "two_pass")
+    wa = torch.full((a.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    wb = torch.full((b.dense_bytes,), POISON, dtype=torch.uint8, device=dev)
+    mwd.decode_paired(a, wa, b, wb, torch.from_numpy(es_dev).to(dev))
+    torch.cuda.synchronize()
+    assert_bytes_equal(wa.cpu().numpy().reshape(xa.shape), oracle_expect(orc, sa, es), "NVFP4 stack")
+    assert_bytes_equal(wb.cpu().numpy().reshape(xb.shape), oracle_expect(orc, sb, es), "MXFP4 stack")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_routed_expert_start_not_16_byte_aligned(orc, dev, mode):
     """expert_start tensors that start 4 or 12 (int32) or 8 (int64) bytes past
